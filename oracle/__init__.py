@@ -1,0 +1,7 @@
+"""CPU oracle of the contextual-sparsity LoRA hot path (test infrastructure).
+
+Imported only by the tests, the smoke check and the benchmark's CPU
+baseline; the product library never loads anything from here.
+"""
+from .sparselora_oracle import *  # noqa: F401,F403
+from .sparselora_oracle import __all__  # noqa: F401

@@ -1,0 +1,336 @@
+"""ctypes binding of libsparselora.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+allocates outputs and scratch with torch, passes raw device pointers and the
+current HIP stream, and turns status codes into exceptions.  It never falls
+back to any other implementation: if the library is missing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparselora.so")
+
+SL_F32, SL_BF16 = 0, 1
+SL_CRIT_SWIGLU_L2, SL_CRIT_L2, SL_CRIT_QK_NORM = 0, 1, 2
+SL_MAX_SEQS = 64
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class SlLayout(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("seq_len", _i32), ("ctx_len", ctypes.POINTER(_i32))]
+
+
+class SlHeads(ctypes.Structure):
+    _fields_ = [("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32)]
+
+
+class SlFfnWeights(ctypes.Structure):
+    _fields_ = [("d_model", _i64), ("d_ff", _i64), ("lora_rank", _i32), ("lora_scale", ctypes.c_float),
+                ("Wg", _vp), ("Wu", _vp), ("WdT", _vp), ("Ag", _vp), ("Bg", _vp), ("Au", _vp),
+                ("Bu", _vp), ("Ad", _vp), ("Bd", _vp)]
+
+
+class SlFfnGrads(ctypes.Structure):
+    _fields_ = [("dAg", _vp), ("dBg", _vp), ("dAu", _vp), ("dBu", _vp), ("dAd", _vp), ("dBd", _vp)]
+
+
+class SlQkvoWeights(ctypes.Structure):
+    _fields_ = [("d_model", _i64), ("heads", SlHeads), ("lora_rank", _i32),
+                ("lora_scale", ctypes.c_float),
+                ("Wq", _vp), ("Wk", _vp), ("Wv", _vp), ("WoT", _vp),
+                ("Aq", _vp), ("Bq", _vp), ("Ak", _vp), ("Bk", _vp), ("Av", _vp), ("Bv", _vp),
+                ("Ao", _vp), ("Bo", _vp)]
+
+
+class SlQkvoGrads(ctypes.Structure):
+    _fields_ = [("dAq", _vp), ("dBq", _vp), ("dAk", _vp), ("dBk", _vp), ("dAv", _vp), ("dBv", _vp),
+                ("dAo", _vp), ("dBo", _vp)]
+
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "sl_abi_version": (ctypes.c_int, []),
+    "sl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sl_last_error": (ctypes.c_char_p, []),
+    "sl_estimator_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "sl_build_estimator": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                                          _vp, _sz, _vp]),
+    "sl_estimate_select_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                                 ctypes.POINTER(SlHeads), _i32, _i64]),
+    "sl_estimate_select": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(SlLayout),
+                                          ctypes.POINTER(SlHeads), _vp, _i64, _i32, _vp, _vp, _vp,
+                                          _vp, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "sl_ffn_saved_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout), _i64, _i64, _i32, _i32]),
+    "sl_ffn_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout), _i64, _i64, _i32,
+                                     _i32]),
+    "sl_ffn_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                  ctypes.POINTER(SlFfnWeights), _vp, _i32, _vp, _vp, _vp, _sz, _vp,
+                                  _sz, _vp]),
+    "sl_ffn_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                  ctypes.POINTER(SlFfnWeights), _vp, _i32, _vp, _vp, _sz, _vp, _vp,
+                                  ctypes.POINTER(SlFfnGrads), _vp, _sz, _vp]),
+    "sl_qkvo_saved_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                  ctypes.POINTER(SlQkvoWeights)]),
+    "sl_qkvo_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                      ctypes.POINTER(SlQkvoWeights), _i32, _i32]),
+    "sl_qkvo_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                   ctypes.POINTER(SlQkvoWeights), _vp, _vp, _i32, _vp, _i32, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
+    "sl_qkvo_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout),
+                                   ctypes.POINTER(SlQkvoWeights), _vp, _vp, _i32, _vp, _i32, _vp,
+                                   _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.POINTER(SlQkvoGrads), _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class SparseLoraError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SparseLoraError(
+                f"{LIB_PATH} is missing: build it with contextual_sparsity_lora_svd_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            if not hasattr(L, name):
+                continue
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise SparseLoraError(f"{what}: {L.sl_status_string(status).decode()} "
+                              f"(status {status}): {L.sl_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SL_BF16
+    if t.dtype == torch.float32:
+        return SL_F32
+    raise SparseLoraError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise SparseLoraError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Layout:
+    """Host-side sequence layout (batch, seq_len, ctx_len[b])."""
+
+    def __init__(self, ctx_len: Sequence[int], seq_len: int):
+        self.ctx = (_i32 * len(ctx_len))(*[int(c) for c in ctx_len])
+        self.c = SlLayout(len(ctx_len), int(seq_len), self.ctx)
+        self.batch = len(ctx_len)
+        self.seq_len = int(seq_len)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _bytes_tensor(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+def k_from_ratio(n: int, sparsity_pct: int) -> int:
+    """Channels kept at a per-layer sparsity percentage: round half up of
+    (100 - p) * n / 100, at least 1."""
+    return max((n * (100 - int(sparsity_pct)) + 50) // 100, 1)
+
+
+# ---------------------------------------------------------------------------
+def build_estimator(W: torch.Tensor, rank: int, iters: int = 0):
+    """Truncated-SVD factors of a frozen weight W [out, in]: Pt [rank, in],
+    Q [rank, out], sigma [rank] (fp32)."""
+    L = lib()
+    out_f, in_f = W.shape
+    Pt = torch.empty(rank, in_f, dtype=W.dtype, device=W.device)
+    Q = torch.empty(rank, out_f, dtype=W.dtype, device=W.device)
+    sig = torch.empty(rank, dtype=torch.float32, device=W.device)
+    ws = _bytes_tensor(L.sl_estimator_workspace_bytes(out_f, in_f, rank), W.device)
+    _check(L.sl_build_estimator(_dtype_code(W), _ptr(W), out_f, in_f, rank, iters, _ptr(Pt),
+                                _ptr(Q), _ptr(sig), _ptr(ws), ws.numel(), _stream()),
+           "sl_build_estimator")
+    return Pt, Q, sig
+
+
+def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, Q0, Pt1, Q1,
+                    N: int, k: int, heads: Optional[Sequence[int]] = None,
+                    want_scores: bool = False):
+    """Per-sequence channel sets idx [batch, k] (int32, ascending) and,
+    optionally, the scores [batch, N] (fp32)."""
+    L = lib()
+    h = SlHeads(*heads) if heads is not None else None
+    href = ctypes.byref(h) if h is not None else None
+    idx = torch.empty(layout.batch, k, dtype=torch.int32, device=X.device)
+    scores = torch.empty(layout.batch, N, dtype=torch.float32, device=X.device) if want_scores else None
+    ws = _bytes_tensor(L.sl_estimate_select_workspace_bytes(crit, layout.ref, href, rank, N), X.device)
+    _check(L.sl_estimate_select(crit, _dtype_code(X), layout.ref, href, _ptr(X), X.shape[1], rank,
+                                _ptr(Pt0), _ptr(Q0), _ptr(Pt1), _ptr(Q1), N, k, _ptr(idx),
+                                _ptr(scores), _ptr(ws), ws.numel(), _stream()),
+           "sl_estimate_select")
+    return idx, scores
+
+
+class FFNWeights:
+    """Device tensors of one FFN layer: Wg, Wu, WdT, Ag, Bg, Au, Bu, Ad, Bd."""
+
+    NAMES = ("Wg", "Wu", "WdT", "Ag", "Bg", "Au", "Bu", "Ad", "Bd")
+
+    def __init__(self, t: Dict[str, torch.Tensor], lora_scale: float = 1.0):
+        self.t = t
+        d_ff, d_model = t["Wg"].shape
+        r = t["Ag"].shape[0]
+        self.c = SlFfnWeights(d_model, d_ff, r, float(lora_scale),
+                              *[_ptr(t[n]) for n in self.NAMES])
+        self.d_model, self.d_ff, self.r = d_model, d_ff, r
+        self.dtype = _dtype_code(t["Wg"])
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class FFNWorkspace:
+    """Reusable saved + scratch buffers for one (layout, shape, k)."""
+
+    def __init__(self, w: FFNWeights, layout: Layout, k: int, device):
+        L = lib()
+        self.saved = _bytes_tensor(L.sl_ffn_saved_bytes(w.dtype, layout.ref, w.d_model, w.d_ff, w.r, k),
+                                   device)
+        self.ws = _bytes_tensor(L.sl_ffn_workspace_bytes(w.dtype, layout.ref, w.d_model, w.d_ff, w.r, k),
+                                device)
+
+
+def ffn_fwd(w: FFNWeights, X: torch.Tensor, layout: Layout, k: int, idx: torch.Tensor,
+            buf: Optional[FFNWorkspace] = None, Y: Optional[torch.Tensor] = None):
+    L = lib()
+    buf = buf or FFNWorkspace(w, layout, k, X.device)
+    Y = Y if Y is not None else torch.empty_like(X)
+    _check(L.sl_ffn_fwd(w.dtype, layout.ref, w.ref, _ptr(X), k, _ptr(idx), _ptr(Y),
+                        _ptr(buf.saved), buf.saved.numel(), _ptr(buf.ws), buf.ws.numel(), _stream()),
+           "sl_ffn_fwd")
+    return Y, buf
+
+
+def ffn_bwd(w: FFNWeights, X: torch.Tensor, layout: Layout, k: int, idx: torch.Tensor,
+            buf: FFNWorkspace, dY: torch.Tensor, out: Optional[Dict[str, torch.Tensor]] = None):
+    L = lib()
+    dev = X.device
+    if out is None:
+        out = {"dX": torch.empty_like(X)}
+        for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd"):
+            out["d" + n] = torch.empty(w.t[n].shape, dtype=torch.float32, device=dev)
+    g = SlFfnGrads(*[_ptr(out[n]) for n in ("dAg", "dBg", "dAu", "dBu", "dAd", "dBd")])
+    _check(L.sl_ffn_bwd(w.dtype, layout.ref, w.ref, _ptr(X), k, _ptr(idx), _ptr(buf.saved),
+                        buf.saved.numel(), _ptr(dY), _ptr(out["dX"]), ctypes.byref(g), _ptr(buf.ws),
+                        buf.ws.numel(), _stream()),
+           "sl_ffn_bwd")
+    return out
+
+
+class QKVOWeights:
+    """Device tensors of one attention block's projections."""
+
+    NAMES = ("Wq", "Wk", "Wv", "WoT", "Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo")
+
+    def __init__(self, t: Dict[str, torch.Tensor], heads: Sequence[int], lora_scale: float = 1.0):
+        self.t = t
+        self.heads = tuple(int(h) for h in heads)
+        d_model = t["Wq"].shape[1]
+        r = t["Aq"].shape[0]
+        self.c = SlQkvoWeights(d_model, SlHeads(*self.heads), r, float(lora_scale),
+                               *[_ptr(t[n]) for n in self.NAMES])
+        self.d_model, self.r = d_model, r
+        self.dtype = _dtype_code(t["Wq"])
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class QKVOWorkspace:
+    def __init__(self, w: QKVOWeights, layout: Layout, k_qk: int, k_vo: int, device):
+        L = lib()
+        self.saved = _bytes_tensor(L.sl_qkvo_saved_bytes(w.dtype, layout.ref, w.ref), device)
+        self.ws = _bytes_tensor(L.sl_qkvo_workspace_bytes(w.dtype, layout.ref, w.ref, k_qk, k_vo),
+                                device)
+
+
+def qkvo_fwd(w: QKVOWeights, X: Optional[torch.Tensor], a: Optional[torch.Tensor], layout: Layout,
+             k_qk: int, idx_qk: torch.Tensor, k_vo: int, idx_vo: torch.Tensor,
+             buf: Optional[QKVOWorkspace] = None, outs: Optional[Dict[str, torch.Tensor]] = None):
+    L = lib()
+    ref = X if X is not None else a
+    dev = ref.device
+    hq, hkv, hd = w.heads
+    T = layout.batch * layout.seq_len
+    buf = buf or QKVOWorkspace(w, layout, k_qk, k_vo, dev)
+    outs = dict(outs or {})
+    if X is not None:
+        outs.setdefault("q", torch.empty(T, hq * hd, dtype=ref.dtype, device=dev))
+        outs.setdefault("k", torch.empty(T, hkv * hd, dtype=ref.dtype, device=dev))
+        outs.setdefault("v", torch.empty(T, hkv * hd, dtype=ref.dtype, device=dev))
+    if a is not None:
+        outs.setdefault("o", torch.empty(T, w.d_model, dtype=ref.dtype, device=dev))
+    _check(L.sl_qkvo_fwd(w.dtype, layout.ref, w.ref, _ptr(X), _ptr(a), k_qk, _ptr(idx_qk), k_vo,
+                         _ptr(idx_vo), _ptr(outs.get("q")), _ptr(outs.get("k")), _ptr(outs.get("v")),
+                         _ptr(outs.get("o")), _ptr(buf.saved), buf.saved.numel(), _ptr(buf.ws),
+                         buf.ws.numel(), _stream()),
+           "sl_qkvo_fwd")
+    return outs, buf
+
+
+def qkvo_bwd(w: QKVOWeights, X: Optional[torch.Tensor], a: Optional[torch.Tensor], layout: Layout,
+             k_qk: int, idx_qk: torch.Tensor, k_vo: int, idx_vo: torch.Tensor, buf: QKVOWorkspace,
+             dq=None, dk=None, dv=None, d_out=None, out: Optional[Dict[str, torch.Tensor]] = None):
+    L = lib()
+    ref = X if X is not None else a
+    dev = ref.device
+    out = dict(out or {})
+    if dq is not None:
+        out.setdefault("dX", torch.empty_like(X))
+        for n in ("Aq", "Bq", "Ak", "Bk", "Av", "Bv"):
+            out.setdefault("d" + n, torch.empty(w.t[n].shape, dtype=torch.float32, device=dev))
+    if d_out is not None:
+        out.setdefault("da", torch.empty_like(a))
+        for n in ("Ao", "Bo"):
+            out.setdefault("d" + n, torch.empty(w.t[n].shape, dtype=torch.float32, device=dev))
+    g = SlQkvoGrads(*[_ptr(out.get(n)) for n in ("dAq", "dBq", "dAk", "dBk", "dAv", "dBv", "dAo",
+                                                  "dBo")])
+    _check(L.sl_qkvo_bwd(w.dtype, layout.ref, w.ref, _ptr(X), _ptr(a), k_qk, _ptr(idx_qk), k_vo,
+                         _ptr(idx_vo), _ptr(buf.saved), buf.saved.numel(), _ptr(dq), _ptr(dk),
+                         _ptr(dv), _ptr(d_out), _ptr(out.get("dX")), _ptr(out.get("da")),
+                         ctypes.byref(g), _ptr(buf.ws), buf.ws.numel(), _stream()),
+           "sl_qkvo_bwd")
+    return out

@@ -1,0 +1,452 @@
+// a4/a5: sparse LoRA SwiGLU FFN, forward and backward.
+//   SparseLoRA article §一 — per-input channel choice; §三 — context tokens on
+//   the selected channels, output tokens dense; §六/§七 — structured channel
+//   sparsity with sliced weights; SparseLoRA abstract — loss and gradients on
+//   the selected subset; SALR page §2.1 — LoRA notation.
+//
+// Per call (T tokens, D = d_model, F = d_ff, r = LoRA rank, rp = r rounded up
+// to 8, k channels per context group):
+//   forward   z = X [Ag;Au]^T                      (skinny, all tokens)
+//             G, U, H = SiLU(G)*U                  (N-gather GEMM, gate+up fused,
+//                                                   LoRA as an extra K segment)
+//             z_d = H Ad[:,S]^T                    (skinny, per group)
+//             Y = H WdT[S] + s z_d Bd^T            (K-gather GEMM)
+//   backward  dz_d = s dY Bd                       (skinny)
+//             dH = dY WdT[S]^T + dz_d Ad[:,S];  dG, dU from saved G, U (N-gather GEMM)
+//             dz_g = s dG Bg[S], dz_u = s dU Bu[S] (skinny, per group)
+//             dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au   (K-gather GEMM)
+//             dA*, dB* by column reductions over tokens.
+#include "sl_launch.hpp"
+
+using namespace sl;
+
+namespace {
+
+struct FfnGeom {
+  SeqTab st;
+  int T, D, F, r, rp, k, ldk, ldF;
+  size_t esz;
+  long long comp, c_out_off;
+  int ks_down, ks_dx, RM1, RM2;
+  size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
+  size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
+      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, ws_bytes;
+};
+
+int choose_ksplit(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
+  if (st.T_out == 0) return 1;
+  const long long kt_out = (K_out + bk - 1) / bk;
+  int ks;
+  if (st.T_ctx > 0 && K_ctx > 0) {
+    ks = (int)((K_out + K_ctx / 2) / K_ctx);
+  } else {
+    const int tiles = ceil_div(st.T_out, G_BM) * ceil_div(D, G_BN);
+    ks = 512 / (tiles > 0 ? tiles : 1);
+  }
+  if (ks > kt_out / 8) ks = (int)(kt_out / 8);
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
+  return ks;
+}
+
+sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, int r, int k,
+                   FfnGeom& g) {
+  if (dt != SL_F32 && dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  sl_status s = build_seqtab(lay, g.st);
+  if (s != SL_OK) return s;
+  if (D < 8 || D % 8 || F < 8 || F % 8 || D > (1 << 20) || F > (1 << 20))
+    SL_FAIL(SL_ERR_SHAPE, "d_model = %lld and d_ff = %lld must be positive multiples of 8", D, F);
+  if (r < 1 || r > 32) SL_FAIL(SL_ERR_RANGE, "lora_rank %d outside [1, 32]", r);
+  if (k < 1 || k > F) SL_FAIL(SL_ERR_RANGE, "k = %d outside [1, %lld]", k, F);
+  const SeqTab& st = g.st;
+  g.T = st.nseq * st.L;
+  g.D = (int)D; g.F = (int)F; g.r = r; g.k = k;
+  g.rp = (int)round_up(r, 8);
+  g.ldk = (int)round_up(k, 8);
+  g.ldF = (int)F;
+  g.esz = dt == SL_BF16 ? 2 : 4;
+  g.comp = (long long)st.T_ctx * g.ldk + (long long)st.T_out * g.ldF;
+  g.c_out_off = (long long)st.T_ctx * g.ldk;
+  const int bk = dt == SL_BF16 ? 64 : 32;
+  g.ks_down = choose_ksplit(st, k + g.rp, F + g.rp, g.D, bk);
+  g.ks_dx = choose_ksplit(st, 2LL * k + 2 * g.rp, 2 * F + 2 * g.rp, g.D, bk);
+  g.RM1 = pow2_rm(g.rp);
+  g.RM2 = pow2_rm(2 * g.rp);
+  const size_t T = g.T, e = g.esz;
+  Bump sv;
+  g.s_zgu = sv.take(T * 2 * g.rp * 4);
+  g.s_zd = sv.take(T * g.rp * 4);
+  g.s_G = sv.take(g.comp * e);
+  g.s_U = sv.take(g.comp * e);
+  g.s_H = sv.take(g.comp * e);
+  g.saved_bytes = sv.off;
+  Bump w;
+  g.w_zs_gu = w.take(T * 2 * g.rp * e);
+  g.w_zs_d = w.take(T * g.rp * e);
+  g.w_Pg = w.take((size_t)F * 2 * g.rp * e);
+  g.w_Pu = w.take((size_t)F * 2 * g.rp * e);
+  g.w_BdTp = w.take((size_t)g.rp * D * e);
+  g.w_Adg = w.take((size_t)st.nseq * g.rp * g.ldk * e);
+  const int ks = g.ks_down > g.ks_dx ? g.ks_down : g.ks_dx;
+  g.w_part = w.take(ks > 1 ? (size_t)ks * st.T_out * D * 4 : 0);
+  g.w_dz_d = w.take(T * g.rp * 4);
+  g.w_dzs_d = w.take(T * g.rp * e);
+  g.w_AdTp = w.take((size_t)F * g.rp * e);
+  g.w_dG = w.take(g.comp * e);
+  g.w_dU = w.take(g.comp * e);
+  g.w_Bgg = w.take((size_t)st.nseq * g.rp * g.ldk * e);
+  g.w_Bug = w.take((size_t)st.nseq * g.rp * g.ldk * e);
+  g.w_BgTo = w.take((size_t)g.rp * F * e);
+  g.w_BuTo = w.take((size_t)g.rp * F * e);
+  g.w_dz_gu = w.take(T * 2 * g.rp * 4);
+  g.w_dzs_gu = w.take(T * 2 * g.rp * e);
+  g.w_Agup = w.take((size_t)2 * g.rp * D * e);
+  long long cr = (long long)ceil_div(T, CR_CHUNK) * D * g.RM2;
+  const long long cr2 = colred_part_elems_compact(st, k, g.F, g.RM1);
+  if (cr2 > cr) cr = cr2;
+  g.w_cr = w.take((size_t)cr * 4);
+  g.w_inv = w.take((size_t)st.nseq * F * 4);
+  g.ws_bytes = w.off;
+  return SL_OK;
+}
+
+sl_status check_ffn_ptrs(const sl_ffn_weights* w, const void* X) {
+  if (!w) SL_FAIL(SL_ERR_NULL, "weights is NULL");
+  if (!X || !w->Wg || !w->Wu || !w->WdT || !w->Ag || !w->Bg || !w->Au || !w->Bu || !w->Ad || !w->Bd)
+    SL_FAIL(SL_ERR_NULL, "a weight or input pointer is NULL");
+  if (!aligned16(X) || !aligned16(w->Wg) || !aligned16(w->Wu) || !aligned16(w->WdT) ||
+      !aligned16(w->Ag) || !aligned16(w->Au))
+    SL_FAIL(SL_ERR_ALIGN, "X, Wg, Wu, WdT, Ag, Au must be 16-byte aligned");
+  return SL_OK;
+}
+
+template <typename T>
+sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X, const int* idx,
+                       void* Y, char* sv, char* ws, hipStream_t strm) {
+  const SeqTab& st = g.st;
+  const int D = g.D, F = g.F, r = g.r, rp = g.rp;
+  const float s = w->lora_scale;
+  sl_status rc;
+  float* zgu = reinterpret_cast<float*>(sv + g.s_zgu);
+  float* zd = reinterpret_cast<float*>(sv + g.s_zd);
+  T* Gc = reinterpret_cast<T*>(sv + g.s_G);
+  T* Uc = reinterpret_cast<T*>(sv + g.s_U);
+  T* Hc = reinterpret_cast<T*>(sv + g.s_H);
+  T* zs_gu = reinterpret_cast<T*>(ws + g.w_zs_gu);
+  T* zs_d = reinterpret_cast<T*>(ws + g.w_zs_d);
+  T* Pg = reinterpret_cast<T*>(ws + g.w_Pg);
+  T* Pu = reinterpret_cast<T*>(ws + g.w_Pu);
+  T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
+  T* Adg = reinterpret_cast<T*>(ws + g.w_Adg);
+  float* part = reinterpret_cast<float*>(ws + g.w_part);
+
+  // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
+  // Adg[g] = Ad[:, S_g] (gathered per context group).
+  if ((rc = fill_zero<T>(Pg, (long long)F * 2 * rp, strm))) return rc;
+  if ((rc = fill_zero<T>(Pu, (long long)F * 2 * rp, strm))) return rc;
+  if ((rc = copy2d<T>(Pg, 2 * rp, 0, 0, F, r, w->Bg, r, 0, strm))) return rc;
+  if ((rc = copy2d<T>(Pu, 2 * rp, 0, rp, F, r, w->Bu, r, 0, strm))) return rc;
+  if ((rc = fill_zero<T>(BdTp, (long long)rp * D, strm))) return rc;
+  if ((rc = copy2d<T>(BdTp, D, 0, 0, r, D, w->Bd, r, 1, strm))) return rc;
+  if ((rc = fill_zero<T>(Adg, (long long)st.nseq * rp * g.ldk, strm))) return rc;
+  if ((rc = gather_factor<T>(Adg, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Ad, F, 0,
+                             strm)))
+    return rc;
+
+  // z = X [Ag; Au]^T  (fp32 saved, s*z in T for the GEMM)
+  {
+    SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 0; a.T = g.T;
+    a.A = X; a.lda = D; a.K = D;
+    a.nblk = 2;
+    a.Bb[0] = w->Ag; a.nbk[0] = r; a.ldbb[0] = D;
+    a.Bb[1] = w->Au; a.nbk[1] = r; a.ldbb[1] = D;
+    a.out = zgu; a.ldo = 2 * rp; a.col0 = 0; a.oscale = 1.f;
+    a.outs = zs_gu; a.ldos = 2 * rp; a.scale = s;
+    if ((rc = launch_skinny<T>(a, ceil_div(g.T, SK_ROWS), strm))) return rc;
+  }
+  // G, U, H on the selected channels (context) / all channels (output rows)
+  {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st;
+    a.idx = idx; a.kidx = g.k; a.n_out = F;
+    a.nseg = 2;
+    a.seg[0] = GSeg{X, D, 0, 0, 1, w->Wg, w->Wu, D, 1, D, nullptr, 0, 0};
+    a.seg[1] = GSeg{zs_gu, 2 * rp, 0, 0, 1, Pg, Pu, 2 * rp, 1, 2 * rp, nullptr, 0, 0};
+    a.o0 = Gc; a.o1 = Uc; a.o2 = Hc;
+    a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SWIGLU, true>(a, strm)));
+  }
+  // z_d = H Ad[:, S]^T
+  {
+    SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 1; a.T = g.T;
+    a.A = Hc; a.lda = g.ldk; a.lda_out = g.ldF; a.a_out_off = g.c_out_off;
+    a.K = 0; a.kidx = g.k; a.n_out = F;
+    a.nblk = 1;
+    a.Bb[0] = Adg; a.nbk[0] = r; a.ldbb[0] = g.ldk; a.b0_gstride = (long long)rp * g.ldk;
+    a.B0o = w->Ad; a.ldb0o = F;
+    a.out = zd; a.ldo = rp; a.oscale = 1.f;
+    a.outs = zs_d; a.ldos = rp; a.scale = s;
+    const int nb = skinny_blocks_compact(st, a);
+    if ((rc = launch_skinny<T>(a, nb, strm))) return rc;
+  }
+  // Y = H WdT[S] + s z_d Bd^T
+  {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st;
+    a.kidx = 1; a.n_out = 1;
+    a.N = D;
+    a.nseg = 2;
+    a.seg[0] = GSeg{Hc, g.ldk, g.ldF, g.c_out_off, 0, w->WdT, nullptr, D, 1, 0, idx, g.k, F};
+    a.seg[1] = GSeg{zs_d, rp, 0, 0, 1, BdTp, nullptr, D, 0, rp, nullptr, 0, 0};
+    a.ksplit_out = g.ks_down;
+    a.o0 = Y; a.ldo = D;
+    a.part = part;
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm)));
+    if ((rc = splitk_reduce<T>(st, part, g.ks_down, D, Y, D, strm))) return rc;
+  }
+  return SL_OK;
+}
+
+template <typename T>
+sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X, const int* idx,
+                       const char* sv, const void* dY, void* dX, const sl_ffn_grads* gr, char* ws,
+                       hipStream_t strm) {
+  const SeqTab& st = g.st;
+  const int D = g.D, F = g.F, r = g.r, rp = g.rp;
+  const float s = w->lora_scale;
+  sl_status rc;
+  const float* zgu = reinterpret_cast<const float*>(sv + g.s_zgu);
+  const float* zd = reinterpret_cast<const float*>(sv + g.s_zd);
+  const T* Gc = reinterpret_cast<const T*>(sv + g.s_G);
+  const T* Uc = reinterpret_cast<const T*>(sv + g.s_U);
+  const T* Hc = reinterpret_cast<const T*>(sv + g.s_H);
+  float* part = reinterpret_cast<float*>(ws + g.w_part);
+  float* dz_d = reinterpret_cast<float*>(ws + g.w_dz_d);
+  T* dzs_d = reinterpret_cast<T*>(ws + g.w_dzs_d);
+  T* AdTp = reinterpret_cast<T*>(ws + g.w_AdTp);
+  T* dGc = reinterpret_cast<T*>(ws + g.w_dG);
+  T* dUc = reinterpret_cast<T*>(ws + g.w_dU);
+  T* Bgg = reinterpret_cast<T*>(ws + g.w_Bgg);
+  T* Bug = reinterpret_cast<T*>(ws + g.w_Bug);
+  T* BgTo = reinterpret_cast<T*>(ws + g.w_BgTo);
+  T* BuTo = reinterpret_cast<T*>(ws + g.w_BuTo);
+  float* dz_gu = reinterpret_cast<float*>(ws + g.w_dz_gu);
+  T* dzs_gu = reinterpret_cast<T*>(ws + g.w_dzs_gu);
+  T* Agup = reinterpret_cast<T*>(ws + g.w_Agup);
+  T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
+  float* crp = reinterpret_cast<float*>(ws + g.w_cr);
+  int* inv = reinterpret_cast<int*>(ws + g.w_inv);
+
+  // packed LoRA operands
+  if ((rc = fill_zero<T>(BdTp, (long long)rp * D, strm))) return rc;
+  if ((rc = copy2d<T>(BdTp, D, 0, 0, r, D, w->Bd, r, 1, strm))) return rc;
+  if ((rc = fill_zero<T>(AdTp, (long long)F * rp, strm))) return rc;
+  if ((rc = copy2d<T>(AdTp, rp, 0, 0, F, r, w->Ad, F, 1, strm))) return rc;
+  if ((rc = fill_zero<T>(Agup, (long long)2 * rp * D, strm))) return rc;
+  if ((rc = copy2d<T>(Agup, D, 0, 0, r, D, w->Ag, D, 0, strm))) return rc;
+  if ((rc = copy2d<T>(Agup, D, rp, 0, r, D, w->Au, D, 0, strm))) return rc;
+  if ((rc = gather_factor<T>(Bgg, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Bg, r, 1,
+                             strm)))
+    return rc;
+  if ((rc = gather_factor<T>(Bug, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Bu, r, 1,
+                             strm)))
+    return rc;
+  if ((rc = copy2d<T>(BgTo, F, 0, 0, r, F, w->Bg, r, 1, strm))) return rc;
+  if ((rc = copy2d<T>(BuTo, F, 0, 0, r, F, w->Bu, r, 1, strm))) return rc;
+  if ((rc = inverse_maps(idx, g.k, st.nseq, F, inv, strm))) return rc;
+
+  // dz_d = s dY Bd
+  {
+    SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 0; a.T = g.T;
+    a.A = dY; a.lda = D; a.K = D;
+    a.nblk = 1;
+    a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
+    a.out = dz_d; a.ldo = rp; a.oscale = s;
+    a.outs = dzs_d; a.ldos = rp; a.scale = s;
+    if ((rc = launch_skinny<T>(a, ceil_div(g.T, SK_ROWS), strm))) return rc;
+  }
+  // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
+  {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st;
+    a.idx = idx; a.kidx = g.k; a.n_out = F;
+    a.nseg = 2;
+    a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
+    a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
+    a.o0 = dGc; a.o1 = dUc;
+    a.i0 = Gc; a.i1 = Uc;
+    a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm)));
+  }
+  // dz_g = s dG Bg[S], dz_u = s dU Bu[S]
+  for (int which = 0; which < 2; ++which) {
+    SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 1; a.T = g.T;
+    a.A = which ? dUc : dGc; a.lda = g.ldk; a.lda_out = g.ldF; a.a_out_off = g.c_out_off;
+    a.K = 0; a.kidx = g.k; a.n_out = F;
+    a.nblk = 1;
+    a.Bb[0] = which ? Bug : Bgg; a.nbk[0] = r; a.ldbb[0] = g.ldk; a.b0_gstride = (long long)rp * g.ldk;
+    a.B0o = which ? BuTo : BgTo; a.ldb0o = F;
+    a.out = dz_gu; a.ldo = 2 * rp; a.col0 = which * rp; a.oscale = s;
+    a.outs = dzs_gu; a.ldos = 2 * rp; a.scale = s;
+    const int nb = skinny_blocks_compact(st, a);
+    if ((rc = launch_skinny<T>(a, nb, strm))) return rc;
+  }
+  // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au
+  {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st;
+    a.kidx = 1; a.n_out = 1;
+    a.N = D;
+    a.nseg = 3;
+    a.seg[0] = GSeg{dGc, g.ldk, g.ldF, g.c_out_off, 0, w->Wg, nullptr, D, 1, 0, idx, g.k, F};
+    a.seg[1] = GSeg{dUc, g.ldk, g.ldF, g.c_out_off, 0, w->Wu, nullptr, D, 1, 0, idx, g.k, F};
+    a.seg[2] = GSeg{dzs_gu, 2 * rp, 0, 0, 1, Agup, nullptr, D, 0, 2 * rp, nullptr, 0, 0};
+    a.ksplit_out = g.ks_dx;
+    a.o0 = dX; a.ldo = D;
+    a.part = part;
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm)));
+    if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
+  }
+  // dAg, dAu = dz^T X
+  {
+    ColredArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 0; a.T = g.T;
+    a.P = X; a.ldp = D; a.N = D;
+    a.Z = dz_gu; a.ldz = 2 * rp; a.zc0 = 0; a.R = 2 * rp;
+    a.part = crp;
+    const int nc = ceil_div(g.T, CR_CHUNK);
+    if ((rc = launch_colred<T>(a, nc, D, g.RM2, strm))) return rc;
+    FinishArgs f{crp, nc, D, g.RM2, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f};
+    hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM2), dim3(256), 0, strm, f);
+    SL_HIP(hipGetLastError());
+  }
+  // dBd = s dY^T z_d
+  {
+    ColredArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 0; a.T = g.T;
+    a.P = dY; a.ldp = D; a.N = D;
+    a.Z = zd; a.ldz = rp; a.zc0 = 0; a.R = rp;
+    a.part = crp;
+    const int nc = ceil_div(g.T, CR_CHUNK);
+    if ((rc = launch_colred<T>(a, nc, D, g.RM1, strm))) return rc;
+    FinishArgs f{crp, nc, D, g.RM1, gr->dBd, r, 0, nullptr, 0, 0, 0, s};
+    hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM1), dim3(256), 0, strm, f);
+    SL_HIP(hipGetLastError());
+  }
+  // dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u, dAd[:, S] = dz_d^T H
+  for (int which = 0; which < 3; ++which) {
+    ColredArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 1; a.T = g.T;
+    a.P = which == 0 ? (const void*)dGc : which == 1 ? (const void*)dUc : (const void*)Hc;
+    a.ldp = g.ldk; a.ldp_out = g.ldF; a.p_out_off = g.c_out_off;
+    a.kidx = g.k; a.n_out = F;
+    if (which < 2) { a.Z = zgu; a.ldz = 2 * rp; a.zc0 = which * rp; }
+    else { a.Z = dz_d; a.ldz = rp; a.zc0 = 0; }
+    a.R = rp;
+    a.part = crp;
+    const int nc = colred_chunks_compact(st, a, g.k, F, g.RM1);
+    if ((rc = launch_colred<T>(a, nc, F > g.k ? F : g.k, g.RM1, strm))) return rc;
+    FinishScatterArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.st = st; f.part = crp; f.RM = g.RM1; f.Nfull = F; f.kidx = g.k; f.inv = inv;
+    for (int q = 0; q <= st.nseq; ++q) {
+      const int m = q < st.nseq ? st.ctx[q] : st.T_out;
+      f.chunk_count[q] = ceil_div(m, CR_CHUNK);
+      f.part_off[q] = a.part_off[q];
+    }
+    f.out = which == 0 ? gr->dBg : which == 1 ? gr->dBu : gr->dAd;
+    f.r = r;
+    f.transposed = which == 2;
+    f.scale = which < 2 ? s : 1.f;
+    hipLaunchKernelGGL(finish_scatter_kernel, grid1d((long long)F * r), dim3(256), 0, strm, f);
+    SL_HIP(hipGetLastError());
+  }
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sl_ffn_saved_bytes(sl_dtype dt, const sl_layout* lay, int64_t d_model, int64_t d_ff,
+                          int32_t lora_rank, int32_t k) {
+  FfnGeom g;
+  if (ffn_geom(dt, lay, d_model, d_ff, lora_rank, k, g) != SL_OK) return 0;
+  return g.saved_bytes;
+}
+
+size_t sl_ffn_workspace_bytes(sl_dtype dt, const sl_layout* lay, int64_t d_model, int64_t d_ff,
+                              int32_t lora_rank, int32_t k) {
+  FfnGeom g;
+  if (ffn_geom(dt, lay, d_model, d_ff, lora_rank, k, g) != SL_OK) return 0;
+  return g.ws_bytes;
+}
+
+sl_status sl_ffn_fwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w, const void* X,
+                     int32_t k, const int32_t* idx, void* Y, void* saved, size_t saved_bytes,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!w) SL_FAIL(SL_ERR_NULL, "weights is NULL");
+  FfnGeom g;
+  sl_status s = ffn_geom(dt, lay, w->d_model, w->d_ff, w->lora_rank, k, g);
+  if (s != SL_OK) return s;
+  if ((s = check_ffn_ptrs(w, X)) != SL_OK) return s;
+  if (!idx || !Y || !saved || !ws) SL_FAIL(SL_ERR_NULL, "idx, Y, saved and ws must be non-NULL");
+  if (!aligned16(Y) || !aligned16(saved) || !aligned16(ws))
+    SL_FAIL(SL_ERR_ALIGN, "Y, saved and ws must be 16-byte aligned");
+  if (saved_bytes < g.saved_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "saved buffer %zu bytes < %zu needed", saved_bytes, g.saved_bytes);
+  if (ws_bytes < g.ws_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.ws_bytes);
+  if ((s = check_arch()) != SL_OK) return s;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  if (dt == SL_BF16)
+    return ffn_fwd_impl<bf16>(g, w, X, idx, Y, reinterpret_cast<char*>(saved),
+                              reinterpret_cast<char*>(ws), strm);
+  return ffn_fwd_impl<float>(g, w, X, idx, Y, reinterpret_cast<char*>(saved),
+                             reinterpret_cast<char*>(ws), strm);
+}
+
+sl_status sl_ffn_bwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w, const void* X,
+                     int32_t k, const int32_t* idx, const void* saved, size_t saved_bytes,
+                     const void* dY, void* dX, const sl_ffn_grads* gr, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!w) SL_FAIL(SL_ERR_NULL, "weights is NULL");
+  FfnGeom g;
+  sl_status s = ffn_geom(dt, lay, w->d_model, w->d_ff, w->lora_rank, k, g);
+  if (s != SL_OK) return s;
+  if ((s = check_ffn_ptrs(w, X)) != SL_OK) return s;
+  if (!gr || !gr->dAg || !gr->dBg || !gr->dAu || !gr->dBu || !gr->dAd || !gr->dBd)
+    SL_FAIL(SL_ERR_NULL, "a gradient pointer is NULL");
+  if (!idx || !saved || !dY || !dX || !ws)
+    SL_FAIL(SL_ERR_NULL, "idx, saved, dY, dX and ws must be non-NULL");
+  if (!aligned16(saved) || !aligned16(dY) || !aligned16(dX) || !aligned16(ws))
+    SL_FAIL(SL_ERR_ALIGN, "saved, dY, dX and ws must be 16-byte aligned");
+  if (saved_bytes < g.saved_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "saved buffer %zu bytes < %zu needed", saved_bytes, g.saved_bytes);
+  if (ws_bytes < g.ws_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.ws_bytes);
+  if ((s = check_arch()) != SL_OK) return s;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  if (dt == SL_BF16)
+    return ffn_bwd_impl<bf16>(g, w, X, idx, reinterpret_cast<const char*>(saved), dY, dX, gr,
+                              reinterpret_cast<char*>(ws), strm);
+  return ffn_bwd_impl<float>(g, w, X, idx, reinterpret_cast<const char*>(saved), dY, dX, gr,
+                             reinterpret_cast<char*>(ws), strm);
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Host-side helpers of the C ABI: error state, validation, layout tables and
+// workspace planning.  No device memory is ever allocated here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sl_common.hpp"
+
+namespace sl {
+
+void set_error(const char* fmt, ...);
+const char* last_error();
+
+#define SL_FAIL(code, ...)            \
+  do {                                \
+    ::sl::set_error(__VA_ARGS__);     \
+    return code;                      \
+  } while (0)
+
+#define SL_HIP(call)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      SL_FAIL(SL_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),       \
+              __FILE__, __LINE__);                                                     \
+  } while (0)
+
+sl_status check_arch();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate and tabulate a sequence layout.
+sl_status build_seqtab(const sl_layout* lay, SeqTab& st);
+
+// Bump allocator for offsets inside a caller buffer (256-byte aligned regions).
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~size_t(255);
+    return o;
+  }
+};
+
+inline int pow2_rm(int R) { return R <= 8 ? 8 : R <= 16 ? 16 : R <= 32 ? 32 : 64; }
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+inline dim3 grid1d(long long n, int threads = 256) { return dim3((unsigned)((n + threads - 1) / threads)); }
+
+}  // namespace sl

@@ -1,0 +1,134 @@
+// Launch helpers shared by the entry points.
+#pragma once
+
+#include "sl_gemm.hpp"
+#include "sl_host.hpp"
+#include "sl_small.hpp"
+
+namespace sl {
+
+template <typename T>
+inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
+  int C = 0;
+  for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
+  if (C > 64) SL_FAIL(SL_ERR_SHAPE, "skinny product with %d > 64 columns", C);
+  if (nblocks <= 0) return SL_OK;
+  const dim3 grid(nblocks), block(64 * SK_WAVES);
+  if (C <= 16) hipLaunchKernelGGL((skinny_kernel<T, 1>), grid, block, 0, s, a);
+  else if (C <= 32) hipLaunchKernelGGL((skinny_kernel<T, 2>), grid, block, 0, s, a);
+  else if (C <= 48) hipLaunchKernelGGL((skinny_kernel<T, 3>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((skinny_kernel<T, 4>), grid, block, 0, s, a);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+
+template <typename T>
+inline sl_status launch_colred(ColredArgs& a, int nchunks_total, int nmax, int RM, hipStream_t s) {
+  if (nchunks_total <= 0 || nmax <= 0) return SL_OK;
+  const dim3 grid(ceil_div(nmax, 2 * CR_THREADS), nchunks_total), block(CR_THREADS);
+  switch (RM) {
+    case 8: hipLaunchKernelGGL((colred_kernel<T, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((colred_kernel<T, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((colred_kernel<T, 32>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((colred_kernel<T, 64>), grid, block, 0, s, a); break;
+  }
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+inline sl_status fill_zero(void* p, long long n, hipStream_t s) {
+  if (n <= 0) return SL_OK;
+  hipLaunchKernelGGL((fill_kernel<T>), grid1d(n), dim3(256), 0, s, reinterpret_cast<T*>(p), n);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+inline sl_status copy2d(void* dst, long long ldd, int row_off, int col_off, int rows, int cols,
+                        const void* src, long long lds, int transposed, hipStream_t s) {
+  const long long n = (long long)rows * cols;
+  if (n <= 0) return SL_OK;
+  hipLaunchKernelGGL((copy2d_kernel<T>), grid1d(n), dim3(256), 0, s, reinterpret_cast<T*>(dst),
+                     ldd, row_off, col_off, rows, cols, reinterpret_cast<const T*>(src), lds,
+                     transposed);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+inline sl_status gather_factor(void* dst, long long ldd, long long gstride, const int* idx, int k,
+                               int nseq, int r, const void* src, long long lds, int rows_of_ch,
+                               hipStream_t s) {
+  const long long n = (long long)nseq * r * k;
+  if (n <= 0) return SL_OK;
+  hipLaunchKernelGGL((gather_factor_kernel<T>), grid1d(n), dim3(256), 0, s,
+                     reinterpret_cast<T*>(dst), ldd, gstride, idx, k, nseq, r,
+                     reinterpret_cast<const T*>(src), lds, rows_of_ch);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+inline sl_status inverse_maps(const int* idx, int k, int nseq, int Nfull, int* inv, hipStream_t s) {
+  hipLaunchKernelGGL(inverse_map_kernel, grid1d((long long)nseq * Nfull), dim3(256), 0, s, idx, k,
+                     nseq, Nfull, inv);
+  SL_HIP(hipGetLastError());
+  hipLaunchKernelGGL(inverse_scatter_kernel, grid1d((long long)nseq * k), dim3(256), 0, s, idx, k,
+                     nseq, Nfull, inv);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+inline sl_status splitk_reduce(const SeqTab& st, const float* part, int ks, int N, void* out,
+                               long long ldo, hipStream_t s) {
+  const long long n = (long long)st.T_out * N;
+  if (n <= 0 || ks <= 1) return SL_OK;
+  hipLaunchKernelGGL((splitk_reduce_kernel<T>), grid1d(n), dim3(256), 0, s, st, part, ks, N,
+                     reinterpret_cast<T*>(out), ldo);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+// Row blocks of the skinny kernel per group (mode 1: context groups + output group).
+inline int skinny_blocks_compact(const SeqTab& st, SkinnyArgs& a) {
+  int nb = 0;
+  for (int g = 0; g <= st.nseq; ++g) {
+    a.blk_start[g] = nb;
+    const int m = g < st.nseq ? st.ctx[g] : st.T_out;
+    nb += ceil_div(m, SK_ROWS);
+  }
+  a.blk_start[st.nseq + 1] = nb;
+  a.ngroups = st.nseq + 1;
+  return nb;
+}
+
+// Chunks of the column reduction per group (mode 1).
+inline int colred_chunks_compact(const SeqTab& st, ColredArgs& a, int kidx, int n_out, int RM) {
+  int nc = 0;
+  long long off = 0;
+  for (int g = 0; g <= st.nseq; ++g) {
+    a.chunk_start[g] = nc;
+    a.part_off[g] = off;
+    const int m = g < st.nseq ? st.ctx[g] : st.T_out;
+    const int c = ceil_div(m, CR_CHUNK);
+    nc += c;
+    off += (long long)c * (g < st.nseq ? kidx : n_out) * RM;
+  }
+  a.chunk_start[st.nseq + 1] = nc;
+  a.part_off[st.nseq + 1] = off;
+  a.ngroups = st.nseq + 1;
+  return nc;
+}
+
+inline long long colred_part_elems_compact(const SeqTab& st, int kidx, int n_out, int RM) {
+  long long off = 0;
+  for (int g = 0; g <= st.nseq; ++g) {
+    const int m = g < st.nseq ? st.ctx[g] : st.T_out;
+    off += (long long)ceil_div(m, CR_CHUNK) * (g < st.nseq ? kidx : n_out) * RM;
+  }
+  return off;
+}
+
+}  // namespace sl

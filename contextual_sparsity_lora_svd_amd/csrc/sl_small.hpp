@@ -1,0 +1,634 @@
+// Bandwidth-bound kernels of the contextual-sparsity LoRA path on gfx950:
+// the skinny low-rank products (estimator stage 1, LoRA activations), the
+// per-channel criterion over context tokens, the per-sequence top-k, the LoRA
+// factor gradients and a few layout helpers.
+#pragma once
+
+#include "sl_common.hpp"
+
+namespace sl {
+
+typedef __bf16 bf16x8_t_s __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ===========================================================================
+// Skinny product  out[row, c] = sum_k A[row, k] * Bm(c, k),  c < n1 + n2 <= 64
+//
+// Estimator stage 1 (SparseLoRA article §二: the input is projected onto the
+// leading right singular vectors, x V_r Sigma_r) and the LoRA activations
+// x A^T, h A_d[:,S]^T, dY B_d, dG B_g[S].  The B operand is tiny and shared by
+// every workgroup (L2 resident); A is streamed once.  16 rows per workgroup,
+// 8 waves split K, 16x16 MFMA tiles, fixed-order reduction over the waves.
+// ===========================================================================
+constexpr int SK_ROWS = 16;
+constexpr int SK_WAVES = 8;
+
+struct SkinnyArgs {
+  SeqTab st;
+  int mode;               // 0: token rows 0..T-1; 1: compact rows of every group; 2: context rows
+  int T;
+  const void* A; long long lda, lda_out, a_out_off;   // compact geometry when mode 1
+  int K;                  // > 0 fixed; <= 0: the group's channel count
+  int kidx, n_out;
+  // B operand: up to 4 row blocks; block j has nbk[j] rows, row c, column k at
+  // Bb[j][c*ldbb[j] + k].  In mode 1, block 0 of context group g is read at
+  // Bb[0] + g*b0_gstride and that of the output group at B0o (ld ldb0o).
+  int nblk;
+  const void* Bb[4]; int nbk[4]; long long ldbb[4];
+  long long b0_gstride; const void* B0o; long long ldb0o;
+  // Results at token rows; block j lands in columns [col0 + pj, col0 + pj + nbk[j])
+  // where pj = sum of the previous blocks' sizes rounded up to 8; padding is 0.
+  float* out; long long ldo; int col0; float oscale;
+  void* outs; long long ldos; float scale;   // optional copy in the call dtype
+  int blk_start[SL_MAX_SEQS + 2];           // row blocks per group (modes 1, 2)
+  int ngroups;
+};
+
+template <typename T, int NB>
+__global__ void __launch_bounds__(64 * SK_WAVES)
+skinny_kernel(const SkinnyArgs a) {
+  __shared__ float red[SK_WAVES][SK_ROWS][NB * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int g = 0, rb = blockIdx.x;
+  if (a.mode != 0) {
+    while (g + 1 < a.ngroups && a.blk_start[g + 1] <= (int)blockIdx.x) ++g;
+    rb = blockIdx.x - a.blk_start[g];
+  }
+  const bool is_out = (a.mode == 1 && g == a.st.nseq);
+  const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
+  const int nch = is_out ? a.n_out : a.kidx;
+  const int K = a.K > 0 ? a.K : nch;
+  const T* A = reinterpret_cast<const T*>(a.A);
+  const T* B0 = reinterpret_cast<const T*>(a.Bb[0]);
+  long long ldb0 = a.ldbb[0];
+  if (a.mode == 1) {
+    if (is_out && a.B0o) { B0 = reinterpret_cast<const T*>(a.B0o); ldb0 = a.ldb0o; }
+    else if (!is_out) B0 += (long long)g * a.b0_gstride;
+  }
+
+  // this lane's A row
+  int r = rb * SK_ROWS + (lane & 15);
+  if (r >= m_rows) r = m_rows - 1;   // computed and dropped
+  long long arow;
+  if (a.mode == 1)
+    arow = is_out ? a.a_out_off + (long long)r * a.lda_out
+                  : (long long)(a.st.ctx_pre[g] + r) * a.lda;
+  else
+    arow = (long long)(a.mode == 0 ? r : group_token(a.st, g, r)) * a.lda;
+
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // B row of logical column c = nb*16 + lane%16
+  const T* brow[NB];
+  bool bok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int c = nb * 16 + (lane & 15);
+    brow[nb] = B0; bok[nb] = false;
+    for (int j = 0; j < a.nblk; ++j) {
+      if (c < a.nbk[j]) {
+        brow[nb] = (j == 0 ? B0 + (long long)c * ldb0
+                           : reinterpret_cast<const T*>(a.Bb[j]) + (long long)c * a.ldbb[j]);
+        bok[nb] = true;
+        break;
+      }
+      c -= a.nbk[j];
+    }
+  }
+
+  if constexpr (sizeof(T) == 2) {
+    // k-steps of 32; lane holds 8 consecutive k at 8*(lane>>4)
+    const int nsteps = (K + 31) / 32;
+    const int per = (nsteps + SK_WAVES - 1) / SK_WAVES;
+    const int s0 = wave * per, s1 = min(nsteps, s0 + per);
+    for (int s = s0; s < s1; ++s) {
+      const int k = s * 32 + 8 * (lane >> 4);
+      uint4 av = make_uint4(0, 0, 0, 0);
+      if (k < K) {
+        av = *reinterpret_cast<const uint4*>(A + arow + k);
+        if (K - k < 8) {
+          uint32_t w[4] = {av.x, av.y, av.z, av.w};
+          for (int e = K - k; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          av = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      const bf16x8_t_s af = __builtin_bit_cast(bf16x8_t_s, av);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint4 bv = make_uint4(0, 0, 0, 0);
+        if (bok[nb] && k < K) {
+          bv = *reinterpret_cast<const uint4*>(brow[nb] + k);
+          if (K - k < 8) {
+            uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+            for (int e = K - k; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            bv = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t_s, bv),
+                                                          acc[nb], 0, 0, 0);
+      }
+    }
+  } else {
+    // k-steps of 4; lane holds k = lane>>4
+    const int nsteps = (K + 3) / 4;
+    const int per = (nsteps + SK_WAVES - 1) / SK_WAVES;
+    const int s0 = wave * per, s1 = min(nsteps, s0 + per);
+    for (int s = s0; s < s1; ++s) {
+      const int k = s * 4 + (lane >> 4);
+      const float av = k < K ? reinterpret_cast<const float*>(A)[arow + k] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float bv = (bok[nb] && k < K) ? reinterpret_cast<const float*>(brow[nb])[k] : 0.f;
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[nb], 0, 0, 0);
+      }
+    }
+  }
+  // accumulator element e: row 4*(lane>>4) + e, column lane & 15
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][4 * (lane >> 4) + e][nb * 16 + (lane & 15)] = acc[nb][e];
+  __syncthreads();
+  int ptot = 0;
+  for (int j = 0; j < a.nblk; ++j) ptot += (a.nbk[j] + 7) / 8 * 8;
+  for (int i = tid; i < SK_ROWS * ptot; i += 64 * SK_WAVES) {
+    const int rr = i / ptot, oc = i % ptot;
+    const int row = rb * SK_ROWS + rr;
+    if (row >= m_rows) continue;
+    int c = -1;   // logical column feeding padded output column oc (-1 = padding)
+    {
+      int pc = 0, lc = 0;
+      for (int j = 0; j < a.nblk; ++j) {
+        const int pj = (a.nbk[j] + 7) / 8 * 8;
+        if (oc < pc + pj) { c = (oc - pc) < a.nbk[j] ? lc + (oc - pc) : -1; break; }
+        pc += pj;
+        lc += a.nbk[j];
+      }
+    }
+    float v = 0.f;
+    if (c >= 0 && c < NB * 16) {
+#pragma unroll
+      for (int w = 0; w < SK_WAVES; ++w) v += red[w][rr][c];
+    }
+    const long long tok = a.mode == 0 ? row : group_token(a.st, g, row);
+    a.out[tok * a.ldo + a.col0 + oc] = v * a.oscale;
+    if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + a.col0 + oc, v * a.scale);
+  }
+}
+
+// ===========================================================================
+// Channel criterion over context tokens (SparseLoRA article §一, §二).
+// part[b][chunk][n] = sum over the chunk's context rows t of
+//   SWIGLU: (g/(1+exp(-g)) * u)^2, g = Zh[t, zc0:] . Q0[:, n], u = Zh[t, zc1:] . Q1[:, n]
+//   L2:     (Zh[t, zc0:] . Q0[:, n])^2
+// Chunks of 64 tokens; the select kernel adds the chunks in order.
+// ===========================================================================
+constexpr int SC_CHUNK = 64;
+constexpr int SC_THREADS = 256;
+
+struct ScoreArgs {
+  SeqTab st;
+  int swiglu;
+  const float* Zh; long long ldz; int zc0, zc1;
+  const void* Q0; const void* Q1; int rank; int N;
+  float* part; int nchunk_max;
+};
+
+template <typename T, int RM>
+__global__ void __launch_bounds__(SC_THREADS)
+score_kernel(const ScoreArgs a) {
+  __shared__ float zs[SC_CHUNK][2 * RM];
+  const int b = blockIdx.z, chunk = blockIdx.y;
+  const int ctx = a.st.ctx[b];
+  const int t0 = chunk * SC_CHUNK;
+  if (t0 >= ctx) return;
+  const int nt = min(SC_CHUNK, ctx - t0);
+  const int n = blockIdx.x * SC_THREADS + threadIdx.x;
+  const int nproj = a.swiglu ? 2 : 1;
+  for (int i = threadIdx.x; i < SC_CHUNK * 2 * RM; i += SC_THREADS) {
+    const int t = i / (2 * RM), c = i % (2 * RM);
+    const int p = c / RM, q = c % RM;
+    float v = 0.f;
+    if (t < nt && q < a.rank && p < nproj)
+      v = a.Zh[(long long)(b * a.st.L + t0 + t) * a.ldz + (p ? a.zc1 : a.zc0) + q];
+    zs[t][c] = v;
+  }
+  __syncthreads();
+  if (n >= a.N) return;
+  float q0[RM], q1[RM];
+#pragma unroll
+  for (int q = 0; q < RM; ++q) {
+    q0[q] = q < a.rank ? ldv<T>(reinterpret_cast<const T*>(a.Q0), (long long)q * a.N + n) : 0.f;
+    q1[q] = (a.swiglu && q < a.rank) ? ldv<T>(reinterpret_cast<const T*>(a.Q1), (long long)q * a.N + n) : 0.f;
+  }
+  float acc = 0.f;
+  if (a.swiglu) {
+    for (int t = 0; t < nt; ++t) {
+      float gv = 0.f, uv = 0.f;
+#pragma unroll
+      for (int q = 0; q < RM; ++q) {
+        gv = fmaf(zs[t][q], q0[q], gv);
+        uv = fmaf(zs[t][RM + q], q1[q], uv);
+      }
+      const float h = gv / (1.0f + expf(-gv)) * uv;
+      acc = fmaf(h, h, acc);
+    }
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < RM; ++q) v = fmaf(zs[t][q], q0[q], v);
+      acc = fmaf(v, v, acc);
+    }
+  }
+  a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = acc;
+}
+
+// ===========================================================================
+// Per-sequence top-k (SparseLoRA article §一: per input, keep the most active
+// channels).  One 1024-thread workgroup per sequence.  Scores are >= 0, so the
+// fp32 bit pattern is an order-preserving unsigned key.  Four 8-bit radix
+// passes find the k-th largest key tau; the set is every key > tau plus the
+// lowest-index keys == tau, written in ascending channel order.
+// ===========================================================================
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_MAXN = 32768;
+
+struct SelectArgs {
+  SeqTab st;
+  int qk;                 // 0: score = sum of part0 chunks; 1: QK combination
+  const float* part0; const float* part1;
+  int nchunk_max;
+  int N;                  // channels selected over
+  int N0;                 // columns of part0 rows (QK: Hq*hd; else N)
+  int group, head_dim;    // QK: query heads per kv head, head size
+  int k;
+  int* idx; float* scores;
+};
+
+__device__ inline int block_excl_scan_1024(int v, int* sh, int tid, int* total) {
+  // Hillis-Steele over 1024 values in shared memory (two buffers).
+  int* a = sh;
+  int* b = sh + SEL_THREADS;
+  a[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < SEL_THREADS; off <<= 1) {
+    int x = a[tid];
+    if (tid >= off) x += a[tid - off];
+    b[tid] = x;
+    __syncthreads();
+    int* t = a; a = b; b = t;
+  }
+  const int incl = a[tid];
+  if (total) *total = a[SEL_THREADS - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+static __global__ void __launch_bounds__(SEL_THREADS)
+select_kernel(const SelectArgs a) {
+  extern __shared__ uint32_t keys[];   // N keys
+  __shared__ int hist[16][256];
+  __shared__ int scan_buf[2 * SEL_THREADS];
+  __shared__ int s_sel[2];
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const int ctx = a.st.ctx[b];
+  const int nch = (ctx + SC_CHUNK - 1) / SC_CHUNK;
+  const long long pb = (long long)b * a.nchunk_max;
+
+  for (int n = tid; n < a.N; n += SEL_THREADS) {
+    float s;
+    if (!a.qk) {
+      s = 0.f;
+      for (int c = 0; c < nch; ++c) s += a.part0[(pb + c) * a.N0 + n];
+    } else {
+      const int gk = n / a.head_dim, d = n % a.head_dim;
+      float sk = 0.f;
+      for (int c = 0; c < nch; ++c) sk += a.part1[(pb + c) * a.N + n];
+      float sq = 0.f;
+      for (int j = 0; j < a.group; ++j) {
+        const int qc = (gk * a.group + j) * a.head_dim + d;
+        float v = 0.f;
+        for (int c = 0; c < nch; ++c) v += a.part0[(pb + c) * a.N0 + qc];
+        sq += v;
+      }
+      s = sk * sq;
+    }
+    if (a.scores) a.scores[(long long)b * a.N + n] = s;
+    keys[n] = __float_as_uint(s);
+  }
+  __syncthreads();
+
+  uint32_t prefix = 0, mask = 0;
+  int kr = a.k;   // still to take among keys matching prefix
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 16 * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int n = tid; n < a.N; n += SEL_THREADS) {
+      const uint32_t kv = keys[n];
+      if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> shift) & 0xFF], 1);
+    }
+    __syncthreads();
+    // bins in descending digit order: position p <-> digit 255 - p
+    int cnt = 0;
+    if (tid < 256) {
+      const int d = 255 - tid;
+      for (int w = 0; w < 16; ++w) cnt += hist[w][d];
+    }
+    const int before = block_excl_scan_1024(tid < 256 ? cnt : 0, scan_buf, tid, nullptr);
+    if (tid < 256 && before < kr && kr <= before + cnt) {
+      s_sel[0] = 255 - tid;
+      s_sel[1] = before;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    mask |= 0xFFu << shift;
+    kr -= s_sel[1];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;   // the k-th largest key; take kr of the keys equal to it
+
+  // ordered compaction over contiguous per-thread ranges
+  const int per = (a.N + SEL_THREADS - 1) / SEL_THREADS;
+  const int lo = min(a.N, tid * per), hi = min(a.N, lo + per);
+  int n_gt = 0, n_eq = 0;
+  for (int n = lo; n < hi; ++n) {
+    const uint32_t kv = keys[n];
+    n_gt += kv > tau;
+    n_eq += kv == tau;
+  }
+  const int eq_before = block_excl_scan_1024(n_eq, scan_buf, tid, nullptr);
+  int take_eq = kr - eq_before;
+  take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
+  const int pos0 = block_excl_scan_1024(n_gt + take_eq, scan_buf, tid, nullptr);
+  int pos = pos0, eq_seen = 0;
+  int* out = a.idx + (long long)b * a.k;
+  for (int n = lo; n < hi; ++n) {
+    const uint32_t kv = keys[n];
+    bool take = kv > tau;
+    if (kv == tau) { take = eq_seen < take_eq; ++eq_seen; }
+    if (take) out[pos++] = n;
+  }
+}
+
+// ===========================================================================
+// LoRA factor gradients: column reductions over tokens,
+//   part[chunk][n][q] = sum over the chunk's rows t of P[t, n] * Z[tok(t), zc0 + q]
+// (dA = dz^T X, dB = s dG^T z, dB_d = s dY^T z_d, dA_d[:,S] = dz_d^T H).  Each
+// thread owns two adjacent columns; chunks of 128 rows; the finish kernels add
+// the chunks in a fixed order (deterministic, no atomics).
+// ===========================================================================
+constexpr int CR_CHUNK = 128;
+constexpr int CR_THREADS = 256;
+
+struct ColredArgs {
+  SeqTab st;
+  int mode;                 // 0: token rows 0..T-1; 1: compact rows per group
+  int T;
+  const void* P; long long ldp, ldp_out, p_out_off;
+  int N;                    // mode 0: columns; mode 1: ignored (group channel count)
+  int kidx, n_out;
+  const float* Z; long long ldz; int zc0; int R;   // R padded to a multiple of 8
+  float* part;
+  int chunk_start[SL_MAX_SEQS + 2];   // first chunk of each group (mode 1)
+  long long part_off[SL_MAX_SEQS + 2];
+  int ngroups;
+};
+
+template <typename T, int RM>
+__global__ void __launch_bounds__(CR_THREADS)
+colred_kernel(const ColredArgs a) {
+  __shared__ float zsh[CR_CHUNK][RM];
+  int g = 0, ch = blockIdx.y;
+  if (a.mode == 1) {
+    while (g + 1 < a.ngroups && a.chunk_start[g + 1] <= (int)blockIdx.y) ++g;
+    ch = blockIdx.y - a.chunk_start[g];
+  }
+  const bool is_out = a.mode == 1 && g == a.st.nseq;
+  const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
+  const int N = a.mode == 0 ? a.N : (is_out ? a.n_out : a.kidx);
+  const int r0 = ch * CR_CHUNK;
+  const int nr = min(CR_CHUNK, m_rows - r0);
+  for (int i = threadIdx.x; i < CR_CHUNK * RM; i += CR_THREADS) {
+    const int t = i / RM, q = i % RM;
+    float v = 0.f;
+    if (t < nr && q < a.R) {
+      const long long tok = a.mode == 0 ? r0 + t : group_token(a.st, g, r0 + t);
+      v = a.Z[tok * a.ldz + a.zc0 + q];
+    }
+    zsh[t][q] = v;
+  }
+  __syncthreads();
+  const int n = (blockIdx.x * CR_THREADS + threadIdx.x) * 2;
+  if (n >= N) return;
+  const T* P = reinterpret_cast<const T*>(a.P);
+  float acc0[RM], acc1[RM];
+#pragma unroll
+  for (int q = 0; q < RM; ++q) { acc0[q] = 0.f; acc1[q] = 0.f; }
+  const bool two = n + 1 < N;
+  for (int t = 0; t < nr; ++t) {
+    long long prow;
+    if (a.mode == 0) prow = (long long)(r0 + t) * a.ldp;
+    else prow = is_out ? a.p_out_off + (long long)(r0 + t) * a.ldp_out
+                       : (long long)(a.st.ctx_pre[g] + r0 + t) * a.ldp;
+    const float p0 = ldv<T>(P, prow + n);
+    const float p1 = two ? ldv<T>(P, prow + n + 1) : 0.f;
+#pragma unroll
+    for (int q = 0; q < RM; ++q) {
+      const float z = zsh[t][q];
+      acc0[q] = fmaf(p0, z, acc0[q]);
+      acc1[q] = fmaf(p1, z, acc1[q]);
+    }
+  }
+  float* dst = a.part + (a.mode == 1 ? a.part_off[g] : 0) + ((long long)ch * N + n) * RM;
+#pragma unroll
+  for (int q = 0; q < RM; ++q) dst[q] = acc0[q];
+  if (two) {
+#pragma unroll
+    for (int q = 0; q < RM; ++q) dst[RM + q] = acc1[q];
+  }
+}
+
+// Dense finish: out[n, q] (or out[q, n] when transposed) = scale * sum_chunks part.
+// Two outputs may take column ranges [0, r1) and [off2, off2 + r2) of the part.
+struct FinishArgs {
+  const float* part; int nchunk; int N; int RM;
+  float* out1; int r1; int t1;
+  float* out2; int r2; int t2; int off2;
+  float scale;
+};
+static __global__ void finish_dense_kernel(const FinishArgs a) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.N * a.RM;
+  if (i >= total) return;
+  const int n = (int)(i / a.RM), q = (int)(i % a.RM);
+  float* out = nullptr; int oq = 0, tr = 0, rr = 0;
+  if (q < a.r1) { out = a.out1; oq = q; tr = a.t1; rr = a.r1; }
+  else if (a.out2 && q >= a.off2 && q < a.off2 + a.r2) { out = a.out2; oq = q - a.off2; tr = a.t2; rr = a.r2; }
+  if (!out) return;
+  float s = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) s += a.part[((long long)c * a.N + n) * a.RM + q];
+  s *= a.scale;
+  if (tr) out[(long long)oq * a.N + n] = s;
+  else out[(long long)n * rr + oq] = s;
+}
+
+// Scatter finish over channel sets: for channel c (of Nfull) and q < r,
+//   out = scale * sum over groups g containing c of sum_chunks part_g[pos_g(c)][q]
+// with pos from the inverse maps (context groups) or c itself (output group).
+struct FinishScatterArgs {
+  SeqTab st;
+  const float* part; int RM; int Nfull; int kidx;
+  const int* inv;                         // [nseq][Nfull], -1 = not selected
+  int chunk_count[SL_MAX_SEQS + 1];
+  long long part_off[SL_MAX_SEQS + 1];
+  float* out; int r; int transposed;      // [Nfull, r] or [r, Nfull]
+  float scale;
+};
+static __global__ void finish_scatter_kernel(const FinishScatterArgs a) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)a.Nfull * a.r) return;
+  const int c = (int)(i / a.r), q = (int)(i % a.r);
+  float s = 0.f;
+  for (int g = 0; g <= a.st.nseq; ++g) {
+    int pos, n;
+    if (g < a.st.nseq) { pos = a.inv[(long long)g * a.Nfull + c]; n = a.kidx; }
+    else { pos = c; n = a.Nfull; }
+    if (pos < 0) continue;
+    for (int ch = 0; ch < a.chunk_count[g]; ++ch)
+      s += a.part[a.part_off[g] + ((long long)ch * n + pos) * a.RM + q];
+  }
+  s *= a.scale;
+  if (a.transposed) a.out[(long long)q * a.Nfull + c] = s;
+  else a.out[(long long)c * a.r + q] = s;
+}
+
+// inv[g][c] = position of channel c in idx[g] or -1
+static __global__ void inverse_map_kernel(const int* idx, int k, int nseq, int Nfull, int* inv) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (long long)nseq * Nfull) inv[i] = -1;
+  // second phase done by a separate launch (stream-ordered)
+}
+static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, int Nfull, int* inv) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)nseq * k) return;
+  const int g = (int)(i / k), p = (int)(i % k);
+  inv[(long long)g * Nfull + idx[i]] = p;
+}
+
+// ===========================================================================
+// Layout helpers
+// ===========================================================================
+template <typename T>
+__global__ void fill_kernel(T* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) stv<T>(p, i, 0.f);
+}
+
+// dst[(row_off + i) * ldd + col_off + j] = src[i, j] (or src[j, i] when transposed),
+// for i < rows, j < cols of the destination block.
+template <typename T>
+__global__ void copy2d_kernel(T* dst, long long ldd, int row_off, int col_off, int rows, int cols,
+                              const T* src, long long lds, int transposed) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)rows * cols) return;
+  const int r = (int)(i / cols), c = (int)(i % cols);
+  const T v = transposed ? src[(long long)c * lds + r] : src[(long long)r * lds + c];
+  dst[(long long)(row_off + r) * ldd + col_off + c] = v;
+}
+
+// Per context group g: dst[g][q][p] = src(q, idx[g][p]) for q < r, p < k;
+// src(q, c) = src[q*ld + c] (factor stored [r, N]) or src[c*ld + q] ([N, r]).
+template <typename T>
+__global__ void gather_factor_kernel(T* dst, long long ldd, long long gstride, const int* idx,
+                                     int k, int nseq, int r, const T* src, long long lds,
+                                     int src_is_rows_of_channels) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)nseq * r * k) return;
+  const int p = (int)(i % k);
+  const int q = (int)((i / k) % r);
+  const int g = (int)(i / ((long long)k * r));
+  const int c = idx[(long long)g * k + p];
+  const T v = src_is_rows_of_channels ? src[(long long)c * lds + q] : src[(long long)q * lds + c];
+  dst[g * gstride + (long long)q * ldd + p] = v;
+}
+
+// Output-group split-K reduction: out[tok(i), n] = sum_s part[s][i][n].
+template <typename T>
+__global__ void splitk_reduce_kernel(const SeqTab st, const float* part, int ks, int N, T* out,
+                                     long long ldo) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)st.T_out * N) return;
+  const int row = (int)(i / N), n = (int)(i % N);
+  float s = 0.f;
+  for (int j = 0; j < ks; ++j) s += part[((long long)j * st.T_out + row) * N + n];
+  stv<T>(out, (long long)out_token(st, row) * ldo + n, s);
+}
+
+// Zero the context rows of a token-major output [T, ld] over columns [0, n).
+template <typename T>
+__global__ void zero_ctx_rows_kernel(const SeqTab st, T* out, long long ld, int n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)st.T_ctx * n) return;
+  const int r = (int)(i / n), c = (int)(i % n);
+  int b = 0;
+  while (b + 1 < st.nseq && st.ctx_pre[b + 1] <= r) ++b;
+  const long long tok = (long long)b * st.L + (r - st.ctx_pre[b]);
+  stv<T>(out, tok * ld + c, 0.f);
+}
+
+// Compact copy of the selected columns of the context rows:
+//   dst[ctx_pre[b] + t][p] = src[b*L + t][idx[b][p]],  row stride ldd.
+template <typename T>
+__global__ void gather_ctx_cols_kernel(const SeqTab st, const T* src, long long lds, const int* idx,
+                                       int k, T* dst, long long ldd) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)st.T_ctx * k) return;
+  const int r = (int)(i / k), p = (int)(i % k);
+  int b = 0;
+  while (b + 1 < st.nseq && st.ctx_pre[b + 1] <= r) ++b;
+  const long long tok = (long long)b * st.L + (r - st.ctx_pre[b]);
+  dst[(long long)r * ldd + p] = src[tok * lds + idx[(long long)b * k + p]];
+}
+
+// Compact copy of the output rows: dst[i][c] = src[tok(i)][c], c < n.
+template <typename T>
+__global__ void gather_out_rows_kernel(const SeqTab st, const T* src, long long lds, int n, T* dst,
+                                       long long ldd) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)st.T_out * n) return;
+  const int r = (int)(i / n), c = (int)(i % n);
+  dst[(long long)r * ldd + c] = src[(long long)out_token(st, r) * lds + c];
+}
+
+// kv-channel set -> query-channel set: every query head of a group keeps the
+// kv head's selected dims.  idx_q[b] has k*G entries in ascending order.
+// Thread per (sequence, kv position p, head offset j): kv channel c = (gk, d)
+// becomes q channel (gk*G + j, d) at position lo*G + j*cnt + (p - lo), where
+// [lo, lo+cnt) are the positions of kv head gk's channels in the ascending set.
+__device__ inline int lower_bound_i(const int* a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) { const int mid = (lo + hi) >> 1; if (a[mid] < v) lo = mid + 1; else hi = mid; }
+  return lo;
+}
+static __global__ void expand_kv_kernel(const int* idx_kv, int k, int nseq, int group, int head_dim,
+                                 int* idx_q) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)nseq * k * group) return;
+  const int b = (int)(i / ((long long)k * group));
+  const int rem = (int)(i % ((long long)k * group));
+  const int p = rem / group, j = rem % group;
+  const int* in = idx_kv + (long long)b * k;
+  const int c = in[p];
+  const int gk = c / head_dim, d = c % head_dim;
+  const int lo = lower_bound_i(in, k, gk * head_dim);
+  const int hi = lower_bound_i(in, k, (gk + 1) * head_dim);
+  const int cnt = hi - lo;
+  idx_q[(long long)b * k * group + (long long)lo * group + (long long)j * cnt + (p - lo)] =
+      (gk * group + j) * head_dim + d;
+}
+
+}  // namespace sl

@@ -1,0 +1,223 @@
+/* sparselora.h — C ABI of the contextual-sparsity LoRA hot path on gfx950.
+ *
+ * What the library computes (sources are the pages the method is described on):
+ *   - "SparseLoRA article": the lsdiaocha.cn write-up of SparseLoRA (ICML 2025),
+ *     sections 一 (dynamic contextual sparsity; L2-norm criterion for the FFN,
+ *     QK-norm criterion for q/k), 二 (training-free SVD sparsity estimator,
+ *     computed once offline, low-rank approximation of the activations),
+ *     三 (non-uniform per-layer sparsity; context tokens sparse, output tokens
+ *     dense), 六 (structured sparsity for real GPU speedups) and 七 (rank-8
+ *     estimator; careful slicing of sparse weights and compute order).
+ *   - "SparseLoRA abstract": the xinfinite.net page "SparseLoRA：利用上下文稀疏性
+ *     高效微调大语言模型" — loss and gradients are computed on a dynamically
+ *     selected sparse subset of the weights.
+ *   - "SALR page": the lshu.cn article, §2.1 — LoRA notation: frozen W plus a
+ *     trained product of two low-rank factors.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous arrays,
+ *     16-byte aligned, unless a comment says [host].  Element type is given by
+ *     the call's sl_dtype (fp32 or bf16) unless the comment says fp32/int32.
+ *   - Tokens are packed as T = batch * seq_len rows; sequence b owns rows
+ *     [b*seq_len, (b+1)*seq_len).  Its first ctx_len[b] rows are context tokens
+ *     (computed on the selected channels only); the remaining seq_len-ctx_len[b]
+ *     rows are output (loss) tokens and are computed dense.
+ *   - LoRA: y = x W^T + s (x A^T) B^T with A [r, in], B [out, r] and s = lora_scale.
+ *     A dropped channel drops its LoRA part too.
+ *   - Channel index sets idx [batch, k] hold, per sequence, k distinct channel
+ *     numbers in ascending order (what sl_estimate_select writes).  Callers may
+ *     pass their own; they are not re-validated on the device.
+ *   - The library never allocates device memory.  Scratch space is the caller's
+ *     `ws` buffer (query its size with the *_workspace_bytes function); state the
+ *     backward needs is written by the forward into the caller's `saved` buffer.
+ *     No pointer is kept after a call returns.
+ *   - All work is enqueued on `stream` (a hipStream_t, NULL = default stream).
+ *     Calls never synchronise, except sl_build_estimator (documented there).
+ *   - Every argument is validated on the host before anything is launched.  On
+ *     error nothing is launched, the status says which class of error, and
+ *     sl_last_error() (thread-local) holds a message.  Launch failures map to
+ *     SL_ERR_HIP; device faults surface at the caller's next synchronisation.
+ *   - Calls that share a `ws` or `saved` buffer must be stream-ordered.
+ */
+#ifndef SPARSELORA_H
+#define SPARSELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SL_ABI_VERSION 1
+#define SL_MAX_SEQS 64  /* sequences per call (batch) */
+
+typedef enum sl_status {
+  SL_OK = 0,
+  SL_ERR_NULL = 1,              /* a required pointer is NULL */
+  SL_ERR_ALIGN = 2,             /* a pointer is not 16-byte aligned */
+  SL_ERR_SHAPE = 3,             /* inconsistent or unsupported sizes */
+  SL_ERR_DTYPE = 4,             /* unknown sl_dtype / sl_criterion */
+  SL_ERR_RANGE = 5,             /* k, rank, ctx_len or batch out of range */
+  SL_ERR_WORKSPACE = 6,         /* ws or saved buffer too small */
+  SL_ERR_UNSUPPORTED_ARCH = 7,  /* current device is not gfx950 */
+  SL_ERR_HIP = 8                /* a HIP runtime call or launch failed */
+} sl_status;
+
+typedef enum sl_dtype { SL_F32 = 0, SL_BF16 = 1 } sl_dtype;
+
+/* Channel criteria (SparseLoRA article §一):
+ *   SWIGLU_L2 — FFN: sum over context tokens of h^2, h = SiLU(g) * u with g, u
+ *               the low-rank estimates of the gate and up projections.
+ *   L2        — a plain projection (v; o reuses v's set): sum of v^2.
+ *   QK_NORM   — q/k, in kv-channel space: ||k_c||^2 * sum over the query heads
+ *               sharing kv head of c of ||q_(h,d)||^2 ((||q_c|| ||k_c||)^2 when
+ *               every query head has its own kv head). */
+typedef enum sl_criterion { SL_CRIT_SWIGLU_L2 = 0, SL_CRIT_L2 = 1, SL_CRIT_QK_NORM = 2 } sl_criterion;
+
+typedef struct sl_layout {
+  int32_t batch;            /* 1..SL_MAX_SEQS sequences */
+  int32_t seq_len;          /* rows per sequence */
+  const int32_t* ctx_len;   /* [host] batch entries, 0 <= ctx_len[b] <= seq_len */
+} sl_layout;
+
+typedef struct sl_heads {
+  int32_t n_q_heads, n_kv_heads, head_dim;   /* n_q_heads % n_kv_heads == 0 */
+} sl_heads;
+
+/* Frozen weights and LoRA factors of one SwiGLU FFN layer (call dtype).
+ *   Wg, Wu  [d_ff, d_model]   gate / up projection weights
+ *   WdT     [d_ff, d_model]   TRANSPOSE of the down projection weight [d_model, d_ff]
+ *                             (a one-time copy; the weight is frozen)
+ *   Ag, Au  [r, d_model]      Bg, Bu [d_ff, r]
+ *   Ad      [r, d_ff]         Bd     [d_model, r]                               */
+typedef struct sl_ffn_weights {
+  int64_t d_model, d_ff;
+  int32_t lora_rank;
+  float lora_scale;
+  const void *Wg, *Wu, *WdT;
+  const void *Ag, *Bg, *Au, *Bu, *Ad, *Bd;
+} sl_ffn_weights;
+
+/* LoRA gradients of one FFN layer, fp32, shapes of the factors; OVERWRITTEN. */
+typedef struct sl_ffn_grads {
+  float *dAg, *dBg, *dAu, *dBu, *dAd, *dBd;
+} sl_ffn_grads;
+
+/* Frozen weights and LoRA factors of one attention block's projections.
+ *   Wq  [Hq*hd, d_model]   Wk, Wv [Hkv*hd, d_model]
+ *   WoT [Hq*hd, d_model]   TRANSPOSE of the o projection weight [d_model, Hq*hd]
+ *   Aq, Ak, Av [r, d_model]; Bq [Hq*hd, r]; Bk, Bv [Hkv*hd, r]
+ *   Ao [r, Hq*hd]; Bo [d_model, r]                                             */
+typedef struct sl_qkvo_weights {
+  int64_t d_model;
+  sl_heads heads;
+  int32_t lora_rank;
+  float lora_scale;
+  const void *Wq, *Wk, *Wv, *WoT;
+  const void *Aq, *Bq, *Ak, *Bk, *Av, *Bv, *Ao, *Bo;
+} sl_qkvo_weights;
+
+typedef struct sl_qkvo_grads {   /* fp32, shapes of the factors; OVERWRITTEN */
+  float *dAq, *dBq, *dAk, *dBk, *dAv, *dBv, *dAo, *dBo;
+} sl_qkvo_grads;
+
+int sl_abi_version(void);
+const char* sl_status_string(sl_status s);
+const char* sl_last_error(void);          /* thread-local message of the last error */
+
+/* ---------------------------------------------------------------------------
+ * a0 — offline estimator build (SparseLoRA article §二 and §七: truncated SVD of
+ * each frozen projection weight, done once before training).
+ *   W     [out_f, in_f]  frozen weight (call dtype)
+ *   Pt    [rank, in_f]   (V_r diag(sigma_r))^T, call dtype      (output)
+ *   Q     [rank, out_f]  U_r^T, call dtype                       (output)
+ *   sigma [rank] fp32, optional (NULL = not written)            (output)
+ * so that x Pt^T Q approximates x W^T.  Computed by block subspace iteration
+ * on the GPU in fp32 with a host fp64 Rayleigh-Ritz step; 1 <= rank <= 64 and
+ * rank <= min(out_f, in_f).  SYNCHRONISES `stream` (offline, untimed).
+ * ------------------------------------------------------------------------- */
+size_t sl_estimator_workspace_bytes(int64_t out_f, int64_t in_f, int32_t rank);
+sl_status sl_build_estimator(sl_dtype dt, const void* W, int64_t out_f, int64_t in_f,
+                             int32_t rank, int32_t iters, void* Pt, void* Q, float* sigma,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a1-a3 — estimate, score, select (SparseLoRA article §一, §二, §三).
+ *   X   [T, d_in]  layer input (call dtype); only context rows are read.
+ *   SWIGLU_L2: (Pt0,Q0) = gate factors, (Pt1,Q1) = up factors, N = d_ff.
+ *   L2:        (Pt0,Q0) = the projection's factors, N = its out features.
+ *   QK_NORM:   (Pt0,Q0) = q factors (Q0 [rank, Hq*hd]), (Pt1,Q1) = k factors
+ *              (Q1 [rank, Hkv*hd]); N = Hkv*hd (selection in kv-channel space).
+ *   Pt* [rank, d_in], Q* [rank, N_proj] (call dtype), 1 <= rank <= 32.
+ *   idx    [batch, k] int32 out: per sequence the k best channels, ascending;
+ *          ties in score go to the lower channel index.
+ *   scores [batch, N] fp32 out, optional (NULL = not written): the criterion
+ *          (a sum of squares over the sequence's context tokens).
+ * 1 <= k <= N <= 65536.  heads is read for QK_NORM only.
+ * ------------------------------------------------------------------------- */
+size_t sl_estimate_select_workspace_bytes(sl_criterion crit, const sl_layout* lay,
+                                          const sl_heads* heads, int32_t rank, int64_t N);
+sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* lay,
+                             const sl_heads* heads, const void* X, int64_t d_in, int32_t rank,
+                             const void* Pt0, const void* Q0, const void* Pt1, const void* Q1,
+                             int64_t N, int32_t k, int32_t* idx, float* scores,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a4/a5 — sparse SwiGLU FFN forward and backward (SparseLoRA article §一, §三,
+ * §六, §七; SparseLoRA abstract).  Context rows of sequence b use channels
+ * idx[b, :k]; output rows use all d_ff channels.
+ *   fwd:  X [T, d_model] -> Y [T, d_model]; writes `saved` for the backward.
+ *   bwd:  dY [T, d_model] + saved -> dX [T, d_model] and the six LoRA gradients.
+ *         X, w, k, idx and the layout must be those of the forward call.
+ * d_model % 8 == 0, d_ff % 8 == 0, 1 <= lora_rank <= 32, 1 <= k <= d_ff.
+ * ------------------------------------------------------------------------- */
+size_t sl_ffn_saved_bytes(sl_dtype dt, const sl_layout* lay, int64_t d_model, int64_t d_ff,
+                          int32_t lora_rank, int32_t k);
+size_t sl_ffn_workspace_bytes(sl_dtype dt, const sl_layout* lay, int64_t d_model, int64_t d_ff,
+                              int32_t lora_rank, int32_t k);
+sl_status sl_ffn_fwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w, const void* X,
+                     int32_t k, const int32_t* idx, void* Y, void* saved, size_t saved_bytes,
+                     void* ws, size_t ws_bytes, void* stream);
+sl_status sl_ffn_bwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w, const void* X,
+                     int32_t k, const int32_t* idx, const void* saved, size_t saved_bytes,
+                     const void* dY, void* dX, const sl_ffn_grads* g,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a6/a7 — sparse q/k/v/o projections (SparseLoRA article §一, §三, §六).
+ * idx_qk [batch, k_qk] and idx_vo [batch, k_vo] are kv-channel sets (as written
+ * by sl_estimate_select with QK_NORM and L2); q and o use them expanded to every
+ * query head of the group.  At context rows, unselected channels of q, k, v are
+ * written as 0 and unselected columns of the attention output a are ignored.
+ *   fwd:  X [T, d_model] -> q [T, Hq*hd], k, v [T, Hkv*hd]   (if X != NULL)
+ *         a [T, Hq*hd]   -> o [T, d_model]                  (if a != NULL)
+ *         so a caller may run q/k/v, its attention, then o, as two calls
+ *         sharing one `saved` buffer.
+ *   bwd:  d_out -> da [T, Hq*hd] and dAo, dBo                (if d_out != NULL)
+ *         dq, dk, dv -> dX and dAq..dBv                      (if dq != NULL)
+ *         X and a (the forward's inputs) are read for the factor gradients.
+ * d_model, Hq*hd and Hkv*hd multiples of 8; 1 <= lora_rank <= 32;
+ * 1 <= k_qk, k_vo <= Hkv*hd.
+ * ------------------------------------------------------------------------- */
+size_t sl_qkvo_saved_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w);
+size_t sl_qkvo_workspace_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
+                               int32_t k_qk, int32_t k_vo);
+sl_status sl_qkvo_fwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
+                      const void* X, const void* a,
+                      int32_t k_qk, const int32_t* idx_qk, int32_t k_vo, const int32_t* idx_vo,
+                      void* q, void* k, void* v, void* o, void* saved, size_t saved_bytes,
+                      void* ws, size_t ws_bytes, void* stream);
+sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
+                      const void* X, const void* a,
+                      int32_t k_qk, const int32_t* idx_qk, int32_t k_vo, const int32_t* idx_vo,
+                      const void* saved, size_t saved_bytes,
+                      const void* dq, const void* dk, const void* dv, const void* d_out,
+                      void* dX, void* da, const sl_qkvo_grads* g,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSELORA_H */

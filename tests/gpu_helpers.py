@@ -1,0 +1,76 @@
+"""Shared helpers of the GPU parity tests (not a test module)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from workloads import round_to_bf16
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+GAP = 1e-4
+
+
+def tdtype(dt: str):
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def to_dev(x: np.ndarray, dt: str) -> torch.Tensor:
+    """Upload values that are already representable in dt."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(tdtype(dt)).contiguous()
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    ref = np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / (den if den > 0 else 1.0))
+
+
+def assert_close(got, ref, dt, name):
+    e = rel_err(got, ref)
+    assert e <= TOL[dt], f"{name}: max-abs-err/|ref|_inf = {e:.3e} > {TOL[dt]:.0e}"
+    return e
+
+
+def factors(W: np.ndarray, rank: int, dt: str):
+    """Estimator factors from the oracle's SVD, rounded to the call dtype:
+    Pt [rank, in] and Q [rank, out]."""
+    P, Q, _ = O.build_estimator(W, rank)
+    Pt = np.ascontiguousarray(P.T, dtype=np.float32)
+    Q = np.ascontiguousarray(Q, dtype=np.float32)
+    if dt == "bf16":
+        Pt, Q = round_to_bf16(Pt), round_to_bf16(Q)
+    return Pt, Q
+
+
+def check_selection(gpu_idx: np.ndarray, ora_scores: np.ndarray, k: int):
+    """Index sets must be bit-exact wherever the k-th and (k+1)-th oracle scores
+    differ by more than GAP relative; otherwise the GPU set must be a valid
+    top-k of the oracle scores within that gap.  Returns the number of
+    sequences compared exactly."""
+    B, N = ora_scores.shape
+    exact = 0
+    for b in range(B):
+        g = np.asarray(gpu_idx[b])
+        assert len(np.unique(g)) == k, "indices not distinct"
+        assert np.all(np.diff(g) > 0), "indices not ascending"
+        assert g.min() >= 0 and g.max() < N
+        s = ora_scores[b].astype(np.float64)
+        ref = O.select_topk(ora_scores[b], k)
+        if k == N:
+            assert np.array_equal(g, np.arange(N))
+            exact += 1
+            continue
+        order = np.lexsort((np.arange(N), -s))
+        sk, sk1 = s[order[k - 1]], s[order[k]]
+        if sk > 0 and (sk - sk1) / sk > GAP:
+            assert np.array_equal(g, ref), f"seq {b}: index set differs with gap {(sk - sk1) / sk:.2e}"
+            exact += 1
+        else:
+            # valid within the gap: every chosen score is >= the (k+1)-th up to GAP
+            assert s[g].min() >= sk1 * (1 - GAP) - 1e-30, f"seq {b}: chosen score below threshold"
+    return exact

@@ -1,0 +1,192 @@
+"""GPU parity of the FFN hot path (estimate, select, forward, backward) against
+the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_helpers import (assert_close, check_selection, factors, rel_err, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _api():
+    import contextual_sparsity_lora_svd_amd as sl
+    return sl
+
+
+def _ffn_case(D, F, r, ctx, L, dt, seed, R_in=8):
+    rng = np.random.default_rng(seed)
+    T = len(ctx) * L
+
+    def rnd(shape, std):
+        x = (rng.standard_normal(shape) * std).astype(np.float32)
+        return W.round_to_bf16(x) if dt == "bf16" else x
+
+    z = rng.standard_normal((T, R_in)).astype(np.float32)
+    m = rng.standard_normal((R_in, D)).astype(np.float32)
+    sc = rng.lognormal(0, 1, D).astype(np.float32)
+    X = (z @ m + 0.1 * rng.standard_normal((T, D)).astype(np.float32)) * sc
+    X = W.round_to_bf16(X) if dt == "bf16" else X
+    p = {"X": X, "Wg": rnd((F, D), 0.05), "Wu": rnd((F, D), 0.05), "Wd": rnd((D, F), 0.05),
+         "Ag": rnd((r, D), 0.05), "Bg": rnd((F, r), 0.05), "Au": rnd((r, D), 0.05),
+         "Bu": rnd((F, r), 0.05), "Ad": rnd((r, F), 0.05), "Bd": rnd((D, r), 0.05),
+         "dY": rnd((T, D), 1.0)}
+    return p
+
+
+def _dev_weights(p, dt, s):
+    sl = _api()
+    t = {n: to_dev(p[n], dt) for n in ("Wg", "Wu", "Ag", "Bg", "Au", "Bu", "Ad", "Bd")}
+    t["WdT"] = to_dev(np.ascontiguousarray(p["Wd"].T), dt)
+    return sl.FFNWeights(t, lora_scale=s)
+
+
+def _run_fwd_bwd(p, ctx, L, idx, dt, s=1.0):
+    sl = _api()
+    w = _dev_weights(p, dt, s)
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], dt)
+    k = idx.shape[1]
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    Y, buf = sl.ffn_fwd(w, X, lay, k, idx_d)
+    g = sl.ffn_bwd(w, X, lay, k, idx_d, buf, to_dev(p["dY"], dt))
+    torch.cuda.synchronize()
+    return to_np(Y), {n: to_np(v) for n, v in g.items()}
+
+
+def _compare(p, ctx, L, idx, dt, s=1.0):
+    y, g = _run_fwd_bwd(p, ctx, L, idx, dt, s)
+    yr, cache = O.ffn_forward(p, ctx, L, list(idx), s)
+    gr = O.ffn_backward(p, cache, p["dY"], s)
+    errs = {"Y": assert_close(y, yr, dt, "Y")}
+    for n in ("dX", "dAg", "dBg", "dAu", "dBu", "dAd", "dBd"):
+        errs[n] = assert_close(g[n], gr[n], dt, n)
+    print(f"\n[{dt}] ctx={list(ctx)} k={idx.shape[1]} errs " +
+          " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    return errs
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ffn_ragged_groups_and_tails(dt):
+    """Three sequences (all context / all output / mixed), k and r off the
+    tile and chunk sizes, d_ff not a multiple of the tile."""
+    D, F, r, L = 64, 136, 4, 50
+    ctx = [50, 0, 37]
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=5)
+    rng = np.random.default_rng(6)
+    k = 37
+    idx = np.stack([np.sort(rng.choice(F, k, replace=False)) for _ in ctx]).astype(np.int32)
+    _compare(p, ctx, L, idx, dt, s=0.5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ffn_dense_and_single_channel(dt):
+    D, F, r, L = 128, 264, 8, 80
+    ctx = [60, 80]
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=7)
+    _compare(p, ctx, L, np.tile(np.arange(F, dtype=np.int32), (2, 1)), dt)      # k = N
+    _compare(p, ctx, L, np.array([[5], [263]], dtype=np.int32), dt)           # k = 1
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ffn_multi_tile(dt):
+    """Several M, N and K tiles and the output-group K split."""
+    D, F, r, L = 512, 1104, 16, 300
+    ctx = [290, 200, 300]
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=9)
+    rng = np.random.default_rng(10)
+    k = 300
+    idx = np.stack([np.sort(rng.choice(F, k, replace=False)) for _ in ctx]).astype(np.int32)
+    _compare(p, ctx, L, idx, dt)
+
+
+def _estimate(p, ctx, L, Pg, Qg, Pu, Qu, rank, k, dt):
+    sl = _api()
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], dt)
+    F = Qg.shape[1]
+    idx, sc = sl.estimate_select(sl.SL_CRIT_SWIGLU_L2, X, lay, rank, to_dev(Pg, dt), to_dev(Qg, dt),
+                                 to_dev(Pu, dt), to_dev(Qu, dt), F, k, want_scores=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu):
+    B = len(ctx)
+    out = []
+    for b in range(B):
+        rows = O.context_rows(ctx, L, b)
+        out.append(O.scores_swiglu_l2(p["X"][rows], Pg.T, Qg, Pu.T, Qu, dtype=np.float32))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_estimate_select_matches_oracle(dt):
+    D, F, r, L = 256, 688, 8, 200
+    ctx = [200, 37, 0, 130]
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=11)
+    Pg, Qg = factors(p["Wg"], 8, dt)
+    Pu, Qu = factors(p["Wu"], 8, dt)
+    k = 344
+    idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, 8, k, dt)
+    ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+    for b in range(len(ctx)):
+        e = np.abs(sc[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+        assert e < 1e-4, f"seq {b} score rel err {e:.2e}"
+    n_exact = check_selection(idx, ref, k)
+    assert list(idx[2]) == list(range(k))   # empty context: ties everywhere -> lowest indices
+    print(f"\n[{dt}] exact sets {n_exact}/{len(ctx)}", flush=True)
+
+
+def test_select_ties_and_k_extremes():
+    """Planted exact ties in the scores (zero factors) and k = 1, k = N."""
+    sl = _api()
+    D, F, L = 64, 96, 20
+    ctx = [20, 10]
+    p = _ffn_case(D, F, 4, ctx, L, "f32", seed=12)
+    Pg, Qg = factors(p["Wg"], 4, "f32")
+    Pu, Qu = factors(p["Wu"], 4, "f32")
+    Qu[:, 40:] = 0.0          # channels 40.. score exactly 0 -> ties
+    for k in (1, 50, 80, F):
+        idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, 4, k, "f32")
+        ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+        check_selection(idx, ref, k)
+        if k >= 50:
+            for b in range(2):
+                assert list(idx[b][40:]) == list(range(40, 40 + k - 40)), "ties must go to low indices"
+
+
+def test_cfg1_workload_end_to_end():
+    """The tiny fp32 workload: estimate, select, forward and backward."""
+    w = W.WORKLOADS[1]
+    p = W.make_ffn_tensors(w)
+    f = w.ffn[0]
+    ctx = [int(c) for c in W.ctx_lengths(w)]
+    k = O.k_from_ratio(f.d_ff, f.sparsity_pct)
+    Pg, Qg = factors(p["Wg"], w.est_rank, "f32")
+    Pu, Qu = factors(p["Wu"], w.est_rank, "f32")
+    idx, sc = _estimate(p, ctx, w.seq_len, Pg, Qg, Pu, Qu, w.est_rank, k, "f32")
+    ref = _oracle_scores(p, ctx, w.seq_len, Pg, Qg, Pu, Qu)
+    n_exact = check_selection(idx, ref, k)
+    use = idx if n_exact == len(ctx) else np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
+    _compare(p, ctx, w.seq_len, use, "f32")
+
+
+def test_cfg2_full_size_parity():
+    """LLaMA2-7B FFN shape at the benchmark's launch configuration."""
+    w = W.WORKLOADS[2]
+    p = W.make_ffn_tensors(w)
+    f = w.ffn[0]
+    ctx = [int(c) for c in W.ctx_lengths(w)]
+    k = O.k_from_ratio(f.d_ff, f.sparsity_pct)
+    Pg, Qg = factors(p["Wg"], w.est_rank, "bf16")
+    Pu, Qu = factors(p["Wu"], w.est_rank, "bf16")
+    idx, sc = _estimate(p, ctx, w.seq_len, Pg, Qg, Pu, Qu, w.est_rank, k, "bf16")
+    ref = _oracle_scores(p, ctx, w.seq_len, Pg, Qg, Pu, Qu)
+    n_exact = check_selection(idx, ref, k)
+    use = np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
+    errs = _compare(p, ctx, w.seq_len, use, "bf16")
+    print(f"exact sets {n_exact}/{len(ctx)}", flush=True)

@@ -79,6 +79,10 @@ SIGNATURES = {
     "sl_ffn_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout),
                                   ctypes.POINTER(SlFfnWeights), _vp, _i32, _vp, _vp, _sz, _vp, _vp,
                                   ctypes.POINTER(SlFfnGrads), _vp, _sz, _vp]),
+    "sl_timer_enable": (ctypes.c_int, [ctypes.c_int]),
+    "sl_timer_reset": (None, []),
+    "sl_timer_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int)]),
     "sl_qkvo_saved_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
                                   ctypes.POINTER(SlQkvoWeights)]),
     "sl_qkvo_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
@@ -108,8 +112,6 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is missing: build it with contextual_sparsity_lora_svd_amd.build.build()")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
-            if not hasattr(L, name):
-                continue
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
@@ -168,6 +170,26 @@ def k_from_ratio(n: int, sparsity_pct: int) -> int:
     return max((n * (100 - int(sparsity_pct)) + 50) // 100, 1)
 
 
+TIMER_SLOTS = {"estimate": 0, "select": 1, "gu_fwd": 2, "down_fwd": 3, "dh_bwd": 4, "dx_bwd": 5,
+               "qkv_fwd": 6, "o_fwd": 7, "da_bwd": 8, "dxqkv_bwd": 9}
+
+
+def timer_enable(max_launches: int):
+    _check(lib().sl_timer_enable(int(max_launches)), "sl_timer_enable")
+
+
+def timer_reset():
+    lib().sl_timer_reset()
+
+
+def timer_read(slot: str):
+    """(total milliseconds, launches) recorded for a slot since the last reset."""
+    t = ctypes.c_double(0)
+    n = ctypes.c_int(0)
+    _check(lib().sl_timer_read(TIMER_SLOTS[slot], ctypes.byref(t), ctypes.byref(n)), "sl_timer_read")
+    return t.value, n.value
+
+
 # ---------------------------------------------------------------------------
 def build_estimator(W: torch.Tensor, rank: int, iters: int = 0):
     """Truncated-SVD factors of a frozen weight W [out, in]: Pt [rank, in],
@@ -184,22 +206,34 @@ def build_estimator(W: torch.Tensor, rank: int, iters: int = 0):
     return Pt, Q, sig
 
 
+class EstimateBuffers:
+    """Reusable idx / scores / scratch buffers of estimate_select."""
+
+    def __init__(self, crit: int, layout: Layout, rank: int, N: int, k: int, device,
+                 heads: Optional[Sequence[int]] = None, want_scores: bool = False):
+        L = lib()
+        self.heads = SlHeads(*heads) if heads is not None else None
+        href = ctypes.byref(self.heads) if self.heads is not None else None
+        self.idx = torch.empty(layout.batch, k, dtype=torch.int32, device=device)
+        self.scores = (torch.empty(layout.batch, N, dtype=torch.float32, device=device)
+                       if want_scores else None)
+        self.ws = _bytes_tensor(L.sl_estimate_select_workspace_bytes(crit, layout.ref, href, rank, N),
+                                device)
+
+
 def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, Q0, Pt1, Q1,
                     N: int, k: int, heads: Optional[Sequence[int]] = None,
-                    want_scores: bool = False):
+                    want_scores: bool = False, bufs: Optional[EstimateBuffers] = None):
     """Per-sequence channel sets idx [batch, k] (int32, ascending) and,
     optionally, the scores [batch, N] (fp32)."""
     L = lib()
-    h = SlHeads(*heads) if heads is not None else None
-    href = ctypes.byref(h) if h is not None else None
-    idx = torch.empty(layout.batch, k, dtype=torch.int32, device=X.device)
-    scores = torch.empty(layout.batch, N, dtype=torch.float32, device=X.device) if want_scores else None
-    ws = _bytes_tensor(L.sl_estimate_select_workspace_bytes(crit, layout.ref, href, rank, N), X.device)
+    bufs = bufs or EstimateBuffers(crit, layout, rank, N, k, X.device, heads, want_scores)
+    href = ctypes.byref(bufs.heads) if bufs.heads is not None else None
     _check(L.sl_estimate_select(crit, _dtype_code(X), layout.ref, href, _ptr(X), X.shape[1], rank,
-                                _ptr(Pt0), _ptr(Q0), _ptr(Pt1), _ptr(Q1), N, k, _ptr(idx),
-                                _ptr(scores), _ptr(ws), ws.numel(), _stream()),
+                                _ptr(Pt0), _ptr(Q0), _ptr(Pt1), _ptr(Q1), N, k, _ptr(bufs.idx),
+                                _ptr(bufs.scores), _ptr(bufs.ws), bufs.ws.numel(), _stream()),
            "sl_estimate_select")
-    return idx, scores
+    return bufs.idx, bufs.scores
 
 
 class FFNWeights:

@@ -67,7 +67,9 @@ sl_status launch_select(const SelectArgs& a, int nseq, hipStream_t s) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, SEL_MAXN * 4));
     attr_set = true;
   }
+  timer_begin(TS_SELECT, s);
   hipLaunchKernelGGL(select_kernel, dim3(nseq), dim3(SEL_THREADS), lds, s, a);
+  timer_end(TS_SELECT, s);
   SL_HIP(hipGetLastError());
   return SL_OK;
 }
@@ -81,6 +83,7 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
   float* zh = reinterpret_cast<float*>(ws + g.w_zh);
   float* p0 = reinterpret_cast<float*>(ws + g.w_p0);
   float* p1 = reinterpret_cast<float*>(ws + g.w_p1);
+  timer_begin(TS_ESTIMATE, stream);
   if (st.T_ctx > 0) {
     // stage 1: Zh = X_ctx [Pt0; Pt1]^T on the context rows
     SkinnyArgs sa;
@@ -120,6 +123,7 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
       if ((s = launch_score<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
     }
   }
+  timer_end(TS_ESTIMATE, stream);
   SelectArgs se;
   std::memset(&se, 0, sizeof(se));
   se.st = st;

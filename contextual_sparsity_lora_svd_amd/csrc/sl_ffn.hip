@@ -177,7 +177,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.seg[1] = GSeg{zs_gu, 2 * rp, 0, 0, 1, Pg, Pu, 2 * rp, 1, 2 * rp, nullptr, 0, 0};
     a.o0 = Gc; a.o1 = Uc; a.o2 = Hc;
     a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
-    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SWIGLU, true>(a, strm)));
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SWIGLU, true>(a, strm, TS_GU_FWD)));
   }
   // z_d = H Ad[:, S]^T
   {
@@ -207,7 +207,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_down;
     a.o0 = Y; a.ldo = D;
     a.part = part;
-    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm)));
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DOWN_FWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_down, D, Y, D, strm))) return rc;
   }
   return SL_OK;
@@ -285,7 +285,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.o0 = dGc; a.o1 = dUc;
     a.i0 = Gc; a.i1 = Uc;
     a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
-    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm)));
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
   }
   // dz_g = s dG Bg[S], dz_u = s dU Bu[S]
   for (int which = 0; which < 2; ++which) {
@@ -316,7 +316,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_dx;
     a.o0 = dX; a.ldo = D;
     a.part = part;
-    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm)));
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DX_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
   }
   // dAg, dAu = dz^T X

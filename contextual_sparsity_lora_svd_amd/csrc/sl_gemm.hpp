@@ -134,9 +134,11 @@ gather_gemm_kernel(const GemmArgs args) {
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   int g = 0;
   while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
+  g = __builtin_amdgcn_readfirstlane(g);
   const int t_in = tile - args.tile_start[g];
   const bool is_out = (g == args.st.nseq);
   const int m_rows = group_rows(args.st, g);
+  const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];
   const int nch = is_out ? args.n_out : args.kidx;
   const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
   const int ntm = (m_rows + G_BM - 1) / G_BM;
@@ -158,11 +160,15 @@ gather_gemm_kernel(const GemmArgs args) {
   for (int s = 0; s < args.nseg; ++s) total_kt += (seg_len(s) + BK - 1) / BK;
   const int kt_begin = (int)((long long)total_kt * ks / nks);
   const int kt_end = (int)((long long)total_kt * (ks + 1) / nks);
-
   // ---- per-thread load geometry ------------------------------------------
   // A: 4 chunks per thread, rows (tid>>3) + 32 i, chunk column tid & 7.
-  // B (NG): 8 chunks per thread, rows (tid>>3) + 32 i.
+  // B (NG): 8 chunks per thread, rows (tid>>3) + 32 i; in dual mode rows
+  //         [0, BNC) come from the gate weight and [BNC, 2 BNC) from the up weight.
   // B (KG): k-rows (tid&7)*KR .. +KR, n-columns (tid>>3)*8 .. +8.
+  // Loads are unconditional (addresses clamped into the operands); elements
+  // past a segment's K or the N edge are zeroed when the tile is stored to LDS,
+  // so no wait follows a load inside the prefetch.  Segment-dependent row
+  // offsets live in registers and change only at segment boundaries.
   const int a_row0 = tid >> 3;
   const int a_kc = tid & 7;
   int a_r[4], a_t[4];   // group row and token row of each A row this thread loads
@@ -173,92 +179,139 @@ gather_gemm_kernel(const GemmArgs args) {
     a_r[i] = r;
     a_t[i] = group_token(args.st, g, r);
   }
-  int b_ch[8];
+  int b_pos[8];         // NG: channel position of each B row this thread loads
+  int b_ch[8];          // NG: its channel number
   if (MODE == MODE_NG) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      int rr = a_row0 + 32 * i;                   // row of the B tile
-      int c = n0 + (DUAL ? (rr % BNC) : rr);      // channel position
+      int c = n0 + a_row0 + ((32 * i) % BNC);
       if (c >= nch) c = nch - 1;
+      b_pos[i] = c;
       b_ch[i] = gidx ? gidx[c] : c;
     }
   }
   const int kg_kr0 = (tid & 7) * KR;
   const int kg_n = (tid >> 3) * 8;
+  const bool kg_nok = (n0 + kg_n) < args.N;      // N is a multiple of 8
+  const int kg_c0 = kg_nok ? n0 + kg_n : 0;
 
   Chunk ra[4];
   Chunk rb[8];
+  int va = VEC;          // valid elements of this thread's A / N-gather B chunks
+  int kg_rv = KR;        // K-gather: valid k-rows of this thread's B rows
+  int kg_row[KR];        // K-gather: B rows of the tile being loaded
+  int kg_row_next[KR] = {};  // ... and of the tile after it (indices fetched a tile ahead)
 
-  // load K-tile kt (global index over segments) into registers
-  auto load_tile = [&](int kt) {
-    int s = 0, kk = kt;
+  // current segment state (uniform scalars + per-thread offsets)
+  int cur_s = 0, cur_kk = 0, cur_K = 0, cur_nkt = 0;
+  const T* a_base = nullptr;
+  const T* b_base = nullptr;
+  const T* b2_base = nullptr;
+  long long a_off[4];
+  long long b_off[8];
+  long long cur_ldb = 0;
+
+  auto enter_seg = [&](int s) {
+    s = __builtin_amdgcn_readfirstlane(s);
+    const GSeg& sg = args.seg[s];
+    cur_s = s;
+    cur_K = __builtin_amdgcn_readfirstlane(seg_len(s));
+    cur_nkt = (cur_K + BK - 1) / BK;
+    a_base = reinterpret_cast<const T*>(sg.A);
+    b_base = reinterpret_cast<const T*>(sg.B);
+    b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : sg.B);
+    cur_ldb = sg.ldb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (sg.a_tok) a_off[i] = (long long)a_t[i] * sg.lda;
+      else a_off[i] = is_out ? sg.a_out_off + (long long)a_r[i] * sg.lda_out
+                             : (long long)(ctx_pre_g + a_r[i]) * sg.lda;
+    }
+    if (MODE == MODE_NG) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b_off[i] = (long long)(sg.b_gather ? b_ch[i] : b_pos[i]) * sg.ldb;
+    }
+  };
+
+  // KG: B rows of tile (s, kk) of this thread
+  auto kg_rows = [&](int s, int kk, int* rows) {
+    s = __builtin_amdgcn_readfirstlane(s);
+    const GSeg& sg = args.seg[s];
+    const int K = seg_len(s);
+    const int* sidx = (sg.b_gather && !is_out) ? sg.idx + (long long)g * sg.kidx : nullptr;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int kpos = kk * BK + kg_kr0 + i;
+      rows[i] = kpos < K ? (sidx ? sidx[kpos] : kpos) : 0;
+    }
+  };
+
+  // position the segment cursor on K-tile kt_begin
+  if (kt_begin < kt_end) {
+    int s = 0, kk = kt_begin;
     for (;;) {
       const int nkt = (seg_len(s) + BK - 1) / BK;
       if (s + 1 >= args.nseg || kk < nkt) break;
       kk -= nkt;
       ++s;
     }
-    const GSeg& sg = args.seg[s];
-    const int K = seg_len(s);
-    const int k0 = kk * BK;
-    // A
-    {
-      const T* A = reinterpret_cast<const T*>(sg.A);
-      const int kcol = k0 + a_kc * VEC;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kcol < K) {
-          const int r = a_r[i];
-          long long off;
-          if (sg.a_tok) off = (long long)a_t[i] * sg.lda;
-          else off = is_out ? sg.a_out_off + (long long)r * sg.lda_out
-                            : (long long)(args.st.ctx_pre[g] + r) * sg.lda;
-          ra[i] = load_chunk(A + off + kcol);
-          mask_chunk<T>(ra[i], K - kcol);
-        } else {
-          ra[i] = zero_chunk();
-        }
-      }
+    enter_seg(s);
+    cur_kk = __builtin_amdgcn_readfirstlane(kk);
+    if (MODE == MODE_KG) kg_rows(cur_s, cur_kk, kg_row);
+  }
+
+  // issue the global loads of the next K-tile into registers and advance the cursor
+  auto load_tile = [&](bool more) {
+    while (cur_kk >= cur_nkt) {   // segment boundary (segments may be empty)
+      enter_seg(cur_s + 1);
+      cur_kk = 0;
     }
-    // B
+    const int k0 = cur_kk * BK;
+    const int kcol = k0 + a_kc * VEC;
+    va = cur_K - kcol < 0 ? 0 : (cur_K - kcol > VEC ? VEC : cur_K - kcol);
+    const int kc = kcol < cur_K ? kcol : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = load_chunk(a_base + a_off[i] + kc);
     if (MODE == MODE_NG) {
-      const int kcol = k0 + a_kc * VEC;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (kcol < K) {
-          const int rr = a_row0 + 32 * i;
-          const T* Bm = reinterpret_cast<const T*>((DUAL && rr >= BNC) ? sg.B2 : sg.B);
-          const long long row = sg.b_gather ? b_ch[i]
-                                            : (long long)(n0 + (DUAL ? rr % BNC : rr));
-          rb[i] = load_chunk(Bm + row * sg.ldb + kcol);
-          mask_chunk<T>(rb[i], K - kcol);
-        } else {
-          rb[i] = zero_chunk();
-        }
-      }
+      for (int i = 0; i < 8; ++i)
+        rb[i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + b_off[i] + kc);
     } else {
-      const T* Bm = reinterpret_cast<const T*>(sg.B);
-      const int* sidx = (sg.b_gather && !is_out) ? sg.idx + (long long)g * sg.kidx : nullptr;
-      const int ncol = n0 + kg_n;
+      const int kr = cur_K - (k0 + kg_kr0);
+      kg_rv = kr < 0 ? 0 : (kr > KR ? KR : kr);
 #pragma unroll
-      for (int i = 0; i < KR; ++i) {
-        const int kpos = k0 + kg_kr0 + i;
+      for (int i = 0; i < KR; ++i)
 #pragma unroll
-        for (int h = 0; h < 8 / VEC; ++h) {
-          const int c0 = ncol + h * VEC;
-          if (kpos < K && c0 < args.N) {
-            const long long row = sidx ? sidx[kpos] : kpos;
-            rb[i * (8 / VEC) + h] = load_chunk(Bm + row * sg.ldb + c0);
-            mask_chunk<T>(rb[i * (8 / VEC) + h], args.N - c0);
-          } else {
-            rb[i * (8 / VEC) + h] = zero_chunk();
-          }
-        }
+        for (int h = 0; h < 8 / VEC; ++h)
+          rb[i * (8 / VEC) + h] = load_chunk(b_base + (long long)kg_row[i] * cur_ldb + kg_c0 + h * VEC);
+      if (more) {   // indices of the following tile
+        int s = cur_s, kk = cur_kk + 1;
+        while (kk >= (seg_len(s) + BK - 1) / BK && s + 1 < args.nseg) { kk = 0; ++s; }
+        kg_rows(s, kk, kg_row_next);
       }
     }
+    ++cur_kk;
   };
 
   auto store_tile = [&]() {
+    if (va < VEC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mask_chunk<T>(ra[i], va);
+      if (MODE == MODE_NG) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mask_chunk<T>(rb[i], va);
+      }
+    }
+    if (MODE == MODE_KG) {
+#pragma unroll
+      for (int i = 0; i < KR; ++i)
+        if (i >= kg_rv || !kg_nok) {
+#pragma unroll
+          for (int h = 0; h < 8 / VEC; ++h) rb[i * (8 / VEC) + h] = zero_chunk();
+        }
+#pragma unroll
+      for (int i = 0; i < KR; ++i) kg_row[i] = kg_row_next[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(&As[(a_row0 + 32 * i) * LDS_LD + a_kc * VEC]) =
@@ -307,12 +360,12 @@ gather_gemm_kernel(const GemmArgs args) {
   };
 
   if (kt_begin < kt_end) {
-    load_tile(kt_begin);
+    load_tile(kt_begin + 1 < kt_end);
     store_tile();
     __syncthreads();
     for (int kt = kt_begin; kt < kt_end; ++kt) {
       const bool more = kt + 1 < kt_end;
-      if (more) load_tile(kt + 1);
+      if (more) load_tile(kt + 2 < kt_end);
 #pragma unroll
       for (int kstep = 0; kstep < BK / KSTEP; ++kstep) {
         if constexpr (sizeof(T) == 2) {
@@ -418,8 +471,12 @@ gather_gemm_kernel(const GemmArgs args) {
 }
 
 // Host side: count tiles per group and launch.
+bool timer_on();
+void timer_begin(int slot, hipStream_t s);
+void timer_end(int slot, hipStream_t s);
+
 template <typename T, int MODE, int EPI, bool DUAL>
-hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream) {
+hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
   a.ngroups = a.st.nseq + 1;
   int total = 0;
@@ -437,9 +494,12 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream) {
   }
   a.tile_start[a.ngroups] = total;
   if (total == 0) return hipSuccess;
+  timer_begin(timer_slot, stream);
   hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL>), dim3(total), dim3(G_THREADS), 0,
                      stream, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  timer_end(timer_slot, stream);
+  return e;
 }
 
 }  // namespace sl

@@ -1,6 +1,8 @@
 // Error state, device checks and layout tables of the C ABI.
 #include "sl_host.hpp"
 
+#include <vector>
+
 namespace sl {
 
 static thread_local std::string g_err;
@@ -60,9 +62,75 @@ sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   return SL_OK;
 }
 
+// ---- launch timing ---------------------------------------------------------
+struct TimerState {
+  bool on = false;
+  std::vector<hipEvent_t> ev;      // pairs (start, stop)
+  std::vector<int> slot;
+  size_t used = 0;
+};
+static TimerState g_timer;         // single-threaded diagnostic facility
+static int g_pending_slot = -1;
+
+bool timer_on() { return g_timer.on; }
+
+void timer_begin(int slot, hipStream_t s) {
+  if (!g_timer.on || 2 * (g_timer.used + 1) > g_timer.ev.size()) { g_pending_slot = -1; return; }
+  g_pending_slot = slot;
+  hipEventRecord(g_timer.ev[2 * g_timer.used], s);
+}
+
+void timer_end(int slot, hipStream_t s) {
+  if (!g_timer.on || g_pending_slot != slot) return;
+  hipEventRecord(g_timer.ev[2 * g_timer.used + 1], s);
+  g_timer.slot[g_timer.used] = slot;
+  ++g_timer.used;
+  g_pending_slot = -1;
+}
+
 }  // namespace sl
 
 extern "C" {
+
+/* Diagnostics (not part of the computation): bracket the library's main
+ * launches with HIP events.  Enable with room for max_launches launches; read
+ * per-slot totals after synchronising; disable frees the events. */
+int sl_timer_enable(int max_launches) {
+  using namespace sl;
+  for (hipEvent_t e : g_timer.ev) hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.slot.clear();
+  g_timer.used = 0;
+  g_timer.on = false;
+  if (max_launches <= 0) return 0;
+  g_timer.ev.resize(2 * (size_t)max_launches);
+  g_timer.slot.resize(max_launches);
+  for (auto& e : g_timer.ev)
+    if (hipEventCreate(&e) != hipSuccess) return (int)SL_ERR_HIP;
+  g_timer.on = true;
+  return 0;
+}
+
+void sl_timer_reset(void) { sl::g_timer.used = 0; }
+
+/* Total milliseconds and launch count recorded for a slot since the last reset. */
+int sl_timer_read(int slot, double* total_ms, int* count) {
+  using namespace sl;
+  double t = 0;
+  int n = 0;
+  for (size_t i = 0; i < g_timer.used; ++i) {
+    if (g_timer.slot[i] != slot) continue;
+    float ms = 0;
+    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess) return (int)SL_ERR_HIP;
+    if (hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
+      return (int)SL_ERR_HIP;
+    t += ms;
+    ++n;
+  }
+  if (total_ms) *total_ms = t;
+  if (count) *count = n;
+  return 0;
+}
 
 int sl_abi_version(void) { return SL_ABI_VERSION; }
 

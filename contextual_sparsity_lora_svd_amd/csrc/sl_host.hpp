@@ -47,6 +47,16 @@ struct Bump {
   }
 };
 
+// Optional per-launch timing: when enabled (sl_timer_enable), selected launches
+// are bracketed by HIP events on their stream and attributed to a slot.
+enum TimerSlot {
+  TS_ESTIMATE = 0, TS_SELECT, TS_GU_FWD, TS_DOWN_FWD, TS_DH_BWD, TS_DX_BWD, TS_QKV_FWD, TS_O_FWD,
+  TS_DA_BWD, TS_DXQKV_BWD, TS_LORA, TS_NSLOTS
+};
+bool timer_on();
+void timer_begin(int slot, hipStream_t s);
+void timer_end(int slot, hipStream_t s);
+
 inline int pow2_rm(int R) { return R <= 8 ? 8 : R <= 16 ? 16 : R <= 32 ? 32 : 64; }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 

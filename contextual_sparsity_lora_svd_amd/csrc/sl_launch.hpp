@@ -8,11 +8,10 @@
 namespace sl {
 
 template <typename T>
-inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
+inline sl_status launch_skinny_one(SkinnyArgs& a, int nblocks, hipStream_t s) {
   int C = 0;
   for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
-  if (C > 64) SL_FAIL(SL_ERR_SHAPE, "skinny product with %d > 64 columns", C);
-  if (nblocks <= 0) return SL_OK;
+  if (nblocks <= 0 || C <= 0) return SL_OK;
   const dim3 grid(nblocks), block(64 * SK_WAVES);
   if (C <= 16) hipLaunchKernelGGL((skinny_kernel<T, 1>), grid, block, 0, s, a);
   else if (C <= 32) hipLaunchKernelGGL((skinny_kernel<T, 2>), grid, block, 0, s, a);
@@ -22,6 +21,34 @@ inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
   return SL_OK;
 }
 
+// Skinny product over any number of B blocks: blocks are grouped into launches
+// of at most 64 columns; each launch writes its padded column range.
+template <typename T>
+inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
+  int C = 0;
+  for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
+  if (C <= 64) return launch_skinny_one<T>(a, nblocks, s);
+  if (a.mode == 1) SL_FAIL(SL_ERR_SHAPE, "per-group skinny product with %d > 64 columns", C);
+  int j = 0, col = a.col0;
+  while (j < a.nblk) {
+    SkinnyArgs b = a;
+    b.nblk = 0;
+    int c = 0, pc = 0;
+    while (j < a.nblk && b.nblk < 4 && c + a.nbk[j] <= 64) {
+      b.Bb[b.nblk] = a.Bb[j]; b.nbk[b.nblk] = a.nbk[j]; b.ldbb[b.nblk] = a.ldbb[j];
+      c += a.nbk[j];
+      pc += (a.nbk[j] + 7) / 8 * 8;
+      ++b.nblk;
+      ++j;
+    }
+    if (b.nblk == 0) SL_FAIL(SL_ERR_SHAPE, "skinny block with %d > 64 columns", a.nbk[j]);
+    b.col0 = col;
+    sl_status rc = launch_skinny_one<T>(b, nblocks, s);
+    if (rc != SL_OK) return rc;
+    col += pc;
+  }
+  return SL_OK;
+}
 
 template <typename T>
 inline sl_status launch_colred(ColredArgs& a, int nchunks_total, int nmax, int RM, hipStream_t s) {

@@ -1,0 +1,552 @@
+// a6/a7: sparse LoRA q/k/v/o projections, forward and backward.
+//   SparseLoRA article §一 — QK-norm criterion picks q/k channels (one kv-channel
+//   set, shared by every query head of the group); v/o use the L2 set of v;
+//   §三 — context rows sparse, output rows dense; §六 — channel sparsity.
+//
+//   forward  q = X Wq[Sq]^T + s (X Aq^T) Bq[Sq]^T   scattered into the dense
+//            layout, unselected context channels written as 0; k, v likewise
+//            o = a[:, So] WoT[So] + s (a[:, So] Ao[:, So]^T) Bo^T
+//   backward da = (d_out WoT[So]^T + dz_o Ao[:, So]) on So, 0 elsewhere at
+//            context rows; dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + LoRA terms;
+//            factor gradients by column reductions.
+#include "sl_launch.hpp"
+
+using namespace sl;
+
+namespace {
+
+struct Comp {       // compact copy of a projection's selected columns
+  int kc, ld, n;    // channels per context group, context row stride, full width
+  long long out_off, elems;
+};
+
+Comp make_comp(const SeqTab& st, int kc, int n) {
+  Comp c;
+  c.kc = kc; c.n = n;
+  c.ld = (int)round_up(kc, 8);
+  c.out_off = (long long)st.T_ctx * c.ld;
+  c.elems = c.out_off + (long long)st.T_out * n;
+  return c;
+}
+
+struct QkvoGeom {
+  SeqTab st;
+  int T, D, Hq, Hkv, hd, G, nq, nkv, r, rp, kqk, kvo, kq, ko;
+  size_t esz;
+  Comp cq, ck, cv, co;
+  int ks_o, ks_dx;
+  size_t s_zqkv, s_zo, saved_bytes;
+  size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
+      w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
+      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, ws_bytes;
+};
+
+int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
+  if (st.T_out == 0) return 1;
+  const long long kt_out = (K_out + bk - 1) / bk;
+  int ks;
+  if (st.T_ctx > 0 && K_ctx > 0) ks = (int)((K_out + K_ctx / 2) / K_ctx);
+  else ks = 512 / std::max(1, ceil_div(st.T_out, G_BM) * ceil_div(D, G_BN));
+  if (ks > kt_out / 8) ks = (int)(kt_out / 8);
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
+  return ks;
+}
+
+sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w, int kqk, int kvo,
+                    bool check_k, QkvoGeom& g) {
+  if (dt != SL_F32 && dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (!w) SL_FAIL(SL_ERR_NULL, "weights is NULL");
+  sl_status s = build_seqtab(lay, g.st);
+  if (s != SL_OK) return s;
+  const SeqTab& st = g.st;
+  const sl_heads& h = w->heads;
+  if (h.n_q_heads < 1 || h.n_kv_heads < 1 || h.head_dim < 1 || h.n_q_heads % h.n_kv_heads)
+    SL_FAIL(SL_ERR_SHAPE, "bad heads (%d q, %d kv, dim %d)", h.n_q_heads, h.n_kv_heads, h.head_dim);
+  const long long D = w->d_model;
+  const long long nq = (long long)h.n_q_heads * h.head_dim, nkv = (long long)h.n_kv_heads * h.head_dim;
+  if (D < 8 || D % 8 || nq % 8 || nkv % 8 || D > (1 << 20) || nq > (1 << 20))
+    SL_FAIL(SL_ERR_SHAPE, "d_model, Hq*hd and Hkv*hd must be positive multiples of 8");
+  if (w->lora_rank < 1 || w->lora_rank > 32)
+    SL_FAIL(SL_ERR_RANGE, "lora_rank %d outside [1, 32]", w->lora_rank);
+  if (check_k) {
+    if (kqk < 1 || kqk > nkv) SL_FAIL(SL_ERR_RANGE, "k_qk = %d outside [1, %lld]", kqk, nkv);
+    if (kvo < 1 || kvo > nkv) SL_FAIL(SL_ERR_RANGE, "k_vo = %d outside [1, %lld]", kvo, nkv);
+  } else {
+    kqk = kqk < 1 ? 1 : kqk;
+    kvo = kvo < 1 ? 1 : kvo;
+  }
+  g.T = st.nseq * st.L;
+  g.D = (int)D; g.Hq = h.n_q_heads; g.Hkv = h.n_kv_heads; g.hd = h.head_dim;
+  g.G = g.Hq / g.Hkv;
+  g.nq = (int)nq; g.nkv = (int)nkv;
+  g.r = w->lora_rank; g.rp = (int)round_up(g.r, 8);
+  g.kqk = kqk; g.kvo = kvo; g.kq = kqk * g.G; g.ko = kvo * g.G;
+  g.esz = dt == SL_BF16 ? 2 : 4;
+  g.cq = make_comp(st, g.kq, g.nq);
+  g.ck = make_comp(st, g.kqk, g.nkv);
+  g.cv = make_comp(st, g.kvo, g.nkv);
+  g.co = make_comp(st, g.ko, g.nq);
+  const int bk = dt == SL_BF16 ? 64 : 32;
+  g.ks_o = choose_ks(st, g.ko + g.rp, g.nq + g.rp, g.D, bk);
+  g.ks_dx = choose_ks(st, (long long)g.kq + g.kqk + g.kvo + 3 * g.rp,
+                      (long long)g.nq + 2 * g.nkv + 3 * g.rp, g.D, bk);
+  const size_t T = g.T, e = g.esz, rp = g.rp, B = st.nseq;
+  Bump sv;
+  g.s_zqkv = sv.take(T * 3 * rp * 4);
+  g.s_zo = sv.take(T * rp * 4);
+  g.saved_bytes = sv.off;
+  Bump b;
+  g.w_idxq = b.take(B * g.kq * 4);
+  g.w_idxo = b.take(B * g.ko * 4);
+  g.w_zs_qkv = b.take(T * 3 * rp * e);
+  g.w_zs_o = b.take(T * rp * e);
+  g.w_Bqp = b.take((size_t)g.nq * rp * e);
+  g.w_Bkp = b.take((size_t)g.nkv * rp * e);
+  g.w_Bvp = b.take((size_t)g.nkv * rp * e);
+  g.w_BoTp = b.take(rp * D * e);
+  g.w_Aog = b.take(B * rp * g.co.ld * e);
+  g.w_ac = b.take(g.co.elems * e);
+  const int ks = std::max(g.ks_o, g.ks_dx);
+  g.w_part = b.take(ks > 1 ? (size_t)ks * st.T_out * D * 4 : 0);
+  g.w_dz_o = b.take(T * rp * 4);
+  g.w_dzs_o = b.take(T * rp * e);
+  g.w_AoTp = b.take((size_t)g.nq * rp * e);
+  g.w_dqc = b.take(g.cq.elems * e);
+  g.w_dkc = b.take(g.ck.elems * e);
+  g.w_dvc = b.take(g.cv.elems * e);
+  g.w_Bqg = b.take(B * rp * g.cq.ld * e);
+  g.w_Bkg = b.take(B * rp * g.ck.ld * e);
+  g.w_Bvg = b.take(B * rp * g.cv.ld * e);
+  g.w_BqTo = b.take(rp * g.nq * e);
+  g.w_BkTo = b.take(rp * g.nkv * e);
+  g.w_BvTo = b.take(rp * g.nkv * e);
+  g.w_dz_qkv = b.take(T * 3 * rp * 4);
+  g.w_dzs_qkv = b.take(T * 3 * rp * e);
+  g.w_Aqkvp = b.take(3 * rp * D * e);
+  long long cr = (long long)ceil_div(g.T, CR_CHUNK) * std::max(g.D, g.nq) * pow2_rm(2 * g.rp);
+  const int RM1 = pow2_rm(g.rp);
+  cr = std::max(cr, colred_part_elems_compact(st, g.kq, g.nq, RM1));
+  cr = std::max(cr, colred_part_elems_compact(st, g.ko, g.nq, RM1));
+  cr = std::max(cr, colred_part_elems_compact(st, g.kqk, g.nkv, RM1));
+  cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1));
+  g.w_cr = b.take((size_t)cr * 4);
+  g.w_inv = b.take(B * std::max(g.nq, g.nkv) * 4);
+  g.ws_bytes = b.off;
+  return SL_OK;
+}
+
+// idx_q (or idx_o) from a kv-channel set
+sl_status expand_set(const QkvoGeom& g, const int* idx_kv, int k, int* out, hipStream_t s) {
+  const long long n = (long long)g.st.nseq * k * g.G;
+  hipLaunchKernelGGL(expand_kv_kernel, grid1d(n), dim3(256), 0, s, idx_kv, k, g.st.nseq, g.G, g.hd,
+                     out);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+// compact copy: context rows' selected columns + output rows' full width
+template <typename T>
+sl_status make_compact(const QkvoGeom& g, const Comp& c, const void* src, const int* idx, void* dst,
+                       hipStream_t s) {
+  const SeqTab& st = g.st;
+  if (st.T_ctx > 0) {
+    hipLaunchKernelGGL((gather_ctx_cols_kernel<T>), grid1d((long long)st.T_ctx * c.kc), dim3(256), 0,
+                       s, st, reinterpret_cast<const T*>(src), (long long)c.n, idx, c.kc,
+                       reinterpret_cast<T*>(dst), (long long)c.ld);
+    SL_HIP(hipGetLastError());
+  }
+  if (st.T_out > 0) {
+    hipLaunchKernelGGL((gather_out_rows_kernel<T>), grid1d((long long)st.T_out * c.n), dim3(256), 0,
+                       s, st, reinterpret_cast<const T*>(src), (long long)c.n, c.n,
+                       reinterpret_cast<T*>(dst) + c.out_off, (long long)c.n);
+    SL_HIP(hipGetLastError());
+  }
+  return SL_OK;
+}
+
+template <typename T>
+sl_status zero_ctx(const QkvoGeom& g, void* out, int n, hipStream_t s) {
+  if (g.st.T_ctx == 0) return SL_OK;
+  hipLaunchKernelGGL((zero_ctx_rows_kernel<T>), grid1d((long long)g.st.T_ctx * n), dim3(256), 0, s,
+                     g.st, reinterpret_cast<T*>(out), (long long)n, n);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+// colred over a compact buffer + scatter finish into a factor gradient
+template <typename T>
+sl_status grad_scatter(const QkvoGeom& g, const Comp& c, const void* P, const float* Z, long long ldz,
+                       int zc0, const int* idx, int k_idx, int* inv, float* crp, float* out,
+                       int transposed, float scale, hipStream_t s) {
+  const SeqTab& st = g.st;
+  const int RM = pow2_rm(g.rp);
+  sl_status rc;
+  if ((rc = inverse_maps(idx, k_idx, st.nseq, c.n, inv, s))) return rc;
+  ColredArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.st = st; a.mode = 1; a.T = g.T;
+  a.P = P; a.ldp = c.ld; a.ldp_out = c.n; a.p_out_off = c.out_off;
+  a.kidx = c.kc; a.n_out = c.n;
+  a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = g.rp;
+  a.part = crp;
+  const int nc = colred_chunks_compact(st, a, c.kc, c.n, RM);
+  if ((rc = launch_colred<T>(a, nc, std::max(c.n, c.kc), RM, s))) return rc;
+  FinishScatterArgs f;
+  std::memset(&f, 0, sizeof(f));
+  f.st = st; f.part = crp; f.RM = RM; f.Nfull = c.n; f.kidx = c.kc; f.inv = inv;
+  for (int q = 0; q <= st.nseq; ++q) {
+    const int m = q < st.nseq ? st.ctx[q] : st.T_out;
+    f.chunk_count[q] = ceil_div(m, CR_CHUNK);
+    f.part_off[q] = a.part_off[q];
+  }
+  f.out = out; f.r = g.r; f.transposed = transposed; f.scale = scale;
+  hipLaunchKernelGGL(finish_scatter_kernel, grid1d((long long)c.n * g.r), dim3(256), 0, s, f);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+// colred over token-major rows (all T) + dense finish
+template <typename T>
+sl_status grad_dense(const QkvoGeom& g, const void* P, int N, const float* Z, long long ldz, int zc0,
+                     int R, float* crp, float* out1, int r1, int t1, float* out2, int r2, int t2,
+                     int off2, float scale, hipStream_t s) {
+  sl_status rc;
+  const int RM = pow2_rm(R);
+  ColredArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.st = g.st; a.mode = 0; a.T = g.T;
+  a.P = P; a.ldp = N; a.N = N;
+  a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = R;
+  a.part = crp;
+  const int nc = ceil_div(g.T, CR_CHUNK);
+  if ((rc = launch_colred<T>(a, nc, N, RM, s))) return rc;
+  FinishArgs f{crp, nc, N, RM, out1, r1, t1, out2, r2, t2, off2, scale};
+  hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)N * RM), dim3(256), 0, s, f);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void* X, const void* a,
+                        const int* idx_qk, const int* idx_vo, void* q, void* k, void* v, void* o,
+                        char* sv, char* ws, hipStream_t strm) {
+  const SeqTab& st = g.st;
+  const int D = g.D, r = g.r, rp = g.rp;
+  const float s = w->lora_scale;
+  sl_status rc;
+  float* zqkv = reinterpret_cast<float*>(sv + g.s_zqkv);
+  float* zo = reinterpret_cast<float*>(sv + g.s_zo);
+  int* idx_q = g.G > 1 ? reinterpret_cast<int*>(ws + g.w_idxq) : const_cast<int*>(idx_qk);
+  int* idx_o = g.G > 1 ? reinterpret_cast<int*>(ws + g.w_idxo) : const_cast<int*>(idx_vo);
+  T* zs_qkv = reinterpret_cast<T*>(ws + g.w_zs_qkv);
+  T* zs_o = reinterpret_cast<T*>(ws + g.w_zs_o);
+  float* part = reinterpret_cast<float*>(ws + g.w_part);
+
+  if (X) {
+    if (g.G > 1 && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
+    // z = X [Aq; Ak; Av]^T
+    SkinnyArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.st = st; sa.mode = 0; sa.T = g.T;
+    sa.A = X; sa.lda = D; sa.K = D;
+    sa.nblk = 3;
+    sa.Bb[0] = w->Aq; sa.nbk[0] = r; sa.ldbb[0] = D;
+    sa.Bb[1] = w->Ak; sa.nbk[1] = r; sa.ldbb[1] = D;
+    sa.Bb[2] = w->Av; sa.nbk[2] = r; sa.ldbb[2] = D;
+    sa.out = zqkv; sa.ldo = 3 * rp; sa.oscale = 1.f;
+    sa.outs = zs_qkv; sa.ldos = 3 * rp; sa.scale = s;
+    if ((rc = launch_skinny<T>(sa, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    // the three projections
+    const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+    const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
+    void* outp[3] = {q, k, v};
+    const int* sets[3] = {idx_q, idx_qk, idx_vo};
+    const int kk[3] = {g.kq, g.kqk, g.kvo};
+    const int nn[3] = {g.nq, g.nkv, g.nkv};
+    const size_t bp[3] = {g.w_Bqp, g.w_Bkp, g.w_Bvp};
+    for (int j = 0; j < 3; ++j) {
+      T* Bp = reinterpret_cast<T*>(ws + bp[j]);
+      if ((rc = fill_zero<T>(Bp, (long long)nn[j] * rp, strm))) return rc;
+      if ((rc = copy2d<T>(Bp, rp, 0, 0, nn[j], r, Bl[j], r, 0, strm))) return rc;
+      if (kk[j] < nn[j] && (rc = zero_ctx<T>(g, outp[j], nn[j], strm))) return rc;
+      GemmArgs ga;
+      std::memset(&ga, 0, sizeof(ga));
+      ga.st = st;
+      ga.idx = sets[j]; ga.kidx = kk[j]; ga.n_out = nn[j];
+      ga.nseg = 2;
+      ga.seg[0] = GSeg{X, D, 0, 0, 1, Wm[j], nullptr, D, 1, D, nullptr, 0, 0};
+      ga.seg[1] = GSeg{zs_qkv + j * rp, 3 * rp, 0, 0, 1, Bp, nullptr, rp, 1, rp, nullptr, 0, 0};
+      ga.o0 = outp[j]; ga.ldo = nn[j];
+      SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_QKV_FWD)));
+    }
+  }
+  if (a) {
+    if (g.G > 1 && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
+    T* ac = reinterpret_cast<T*>(ws + g.w_ac);
+    T* Aog = reinterpret_cast<T*>(ws + g.w_Aog);
+    T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
+    if ((rc = make_compact<T>(g, g.co, a, idx_o, ac, strm))) return rc;
+    if ((rc = fill_zero<T>(Aog, (long long)st.nseq * rp * g.co.ld, strm))) return rc;
+    if ((rc = gather_factor<T>(Aog, g.co.ld, (long long)rp * g.co.ld, idx_o, g.ko, st.nseq, r, w->Ao,
+                               g.nq, 0, strm)))
+      return rc;
+    // z_o = a_m Ao^T
+    SkinnyArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.st = st; sa.mode = 1; sa.T = g.T;
+    sa.A = ac; sa.lda = g.co.ld; sa.lda_out = g.nq; sa.a_out_off = g.co.out_off;
+    sa.K = 0; sa.kidx = g.ko; sa.n_out = g.nq;
+    sa.nblk = 1;
+    sa.Bb[0] = Aog; sa.nbk[0] = r; sa.ldbb[0] = g.co.ld; sa.b0_gstride = (long long)rp * g.co.ld;
+    sa.B0o = w->Ao; sa.ldb0o = g.nq;
+    sa.out = zo; sa.ldo = rp; sa.oscale = 1.f;
+    sa.outs = zs_o; sa.ldos = rp; sa.scale = s;
+    if ((rc = launch_skinny<T>(sa, skinny_blocks_compact(st, sa), strm))) return rc;
+    // o = a_m WoT[So] + s z_o Bo^T
+    if ((rc = fill_zero<T>(BoTp, (long long)rp * D, strm))) return rc;
+    if ((rc = copy2d<T>(BoTp, D, 0, 0, r, D, w->Bo, r, 1, strm))) return rc;
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.st = st;
+    ga.kidx = 1; ga.n_out = 1;
+    ga.N = D;
+    ga.nseg = 2;
+    ga.seg[0] = GSeg{ac, g.co.ld, g.nq, g.co.out_off, 0, w->WoT, nullptr, D, 1, 0, idx_o, g.ko, g.nq};
+    ga.seg[1] = GSeg{zs_o, rp, 0, 0, 1, BoTp, nullptr, D, 0, rp, nullptr, 0, 0};
+    ga.ksplit_out = g.ks_o;
+    ga.o0 = o; ga.ldo = D;
+    ga.part = part;
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_O_FWD)));
+    if ((rc = splitk_reduce<T>(st, part, g.ks_o, D, o, D, strm))) return rc;
+  }
+  return SL_OK;
+}
+
+template <typename T>
+sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void* X, const void* a,
+                        const int* idx_qk, const int* idx_vo, const char* sv, const void* dq,
+                        const void* dk, const void* dv, const void* d_out, void* dX, void* da,
+                        const sl_qkvo_grads* gr, char* ws, hipStream_t strm) {
+  const SeqTab& st = g.st;
+  const int D = g.D, r = g.r, rp = g.rp;
+  const float s = w->lora_scale;
+  sl_status rc;
+  const float* zqkv = reinterpret_cast<const float*>(sv + g.s_zqkv);
+  const float* zo = reinterpret_cast<const float*>(sv + g.s_zo);
+  int* idx_q = g.G > 1 ? reinterpret_cast<int*>(ws + g.w_idxq) : const_cast<int*>(idx_qk);
+  int* idx_o = g.G > 1 ? reinterpret_cast<int*>(ws + g.w_idxo) : const_cast<int*>(idx_vo);
+  float* part = reinterpret_cast<float*>(ws + g.w_part);
+  float* crp = reinterpret_cast<float*>(ws + g.w_cr);
+  int* inv = reinterpret_cast<int*>(ws + g.w_inv);
+
+  if (d_out) {
+    if (g.G > 1 && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
+    T* ac = reinterpret_cast<T*>(ws + g.w_ac);
+    T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
+    T* AoTp = reinterpret_cast<T*>(ws + g.w_AoTp);
+    float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
+    T* dzs_o = reinterpret_cast<T*>(ws + g.w_dzs_o);
+    if ((rc = make_compact<T>(g, g.co, a, idx_o, ac, strm))) return rc;
+    if ((rc = fill_zero<T>(BoTp, (long long)rp * D, strm))) return rc;
+    if ((rc = copy2d<T>(BoTp, D, 0, 0, r, D, w->Bo, r, 1, strm))) return rc;
+    if ((rc = fill_zero<T>(AoTp, (long long)g.nq * rp, strm))) return rc;
+    if ((rc = copy2d<T>(AoTp, rp, 0, 0, g.nq, r, w->Ao, g.nq, 1, strm))) return rc;
+    // dz_o = s d_out Bo
+    SkinnyArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.st = st; sa.mode = 0; sa.T = g.T;
+    sa.A = d_out; sa.lda = D; sa.K = D;
+    sa.nblk = 1;
+    sa.Bb[0] = BoTp; sa.nbk[0] = r; sa.ldbb[0] = D;
+    sa.out = dz_o; sa.ldo = rp; sa.oscale = s;
+    sa.outs = dzs_o; sa.ldos = rp; sa.scale = s;
+    if ((rc = launch_skinny<T>(sa, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    // da on So (dense at output rows), 0 at the other context columns
+    if (g.ko < g.nq && (rc = zero_ctx<T>(g, da, g.nq, strm))) return rc;
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.st = st;
+    ga.idx = idx_o; ga.kidx = g.ko; ga.n_out = g.nq;
+    ga.nseg = 2;
+    ga.seg[0] = GSeg{d_out, D, 0, 0, 1, w->WoT, nullptr, D, 1, D, nullptr, 0, 0};
+    ga.seg[1] = GSeg{dzs_o, rp, 0, 0, 1, AoTp, nullptr, rp, 1, rp, nullptr, 0, 0};
+    ga.o0 = da; ga.ldo = g.nq;
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
+    // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o
+    if ((rc = grad_scatter<T>(g, g.co, ac, dz_o, rp, 0, idx_o, g.ko, inv, crp, gr->dAo, 1, 1.f, strm)))
+      return rc;
+    if ((rc = grad_dense<T>(g, d_out, D, zo, rp, 0, rp, crp, gr->dBo, r, 0, nullptr, 0, 0, 0, s, strm)))
+      return rc;
+  }
+  if (dq) {
+    if (g.G > 1 && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
+    T* dqc = reinterpret_cast<T*>(ws + g.w_dqc);
+    T* dkc = reinterpret_cast<T*>(ws + g.w_dkc);
+    T* dvc = reinterpret_cast<T*>(ws + g.w_dvc);
+    float* dz = reinterpret_cast<float*>(ws + g.w_dz_qkv);
+    T* dzs = reinterpret_cast<T*>(ws + g.w_dzs_qkv);
+    T* Aqkvp = reinterpret_cast<T*>(ws + g.w_Aqkvp);
+    const void* dsrc[3] = {dq, dk, dv};
+    T* dcomp[3] = {dqc, dkc, dvc};
+    const Comp* cc[3] = {&g.cq, &g.ck, &g.cv};
+    const int* sets[3] = {idx_q, idx_qk, idx_vo};
+    const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
+    const void* Al[3] = {w->Aq, w->Ak, w->Av};
+    const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+    const size_t bg[3] = {g.w_Bqg, g.w_Bkg, g.w_Bvg};
+    const size_t bto[3] = {g.w_BqTo, g.w_BkTo, g.w_BvTo};
+    float* dB[3] = {gr->dBq, gr->dBk, gr->dBv};
+    if ((rc = fill_zero<T>(Aqkvp, (long long)3 * rp * D, strm))) return rc;
+    for (int j = 0; j < 3; ++j) {
+      const Comp& c = *cc[j];
+      if ((rc = make_compact<T>(g, c, dsrc[j], sets[j], dcomp[j], strm))) return rc;
+      T* Bgj = reinterpret_cast<T*>(ws + bg[j]);
+      T* BTo = reinterpret_cast<T*>(ws + bto[j]);
+      if ((rc = gather_factor<T>(Bgj, c.ld, (long long)rp * c.ld, sets[j], c.kc, st.nseq, r, Bl[j], r,
+                                 1, strm)))
+        return rc;
+      if ((rc = copy2d<T>(BTo, c.n, 0, 0, r, c.n, Bl[j], r, 1, strm))) return rc;
+      if ((rc = copy2d<T>(Aqkvp, D, j * rp, 0, r, D, Al[j], D, 0, strm))) return rc;
+      // dz_j = s dj_m B_j[S]
+      SkinnyArgs sa;
+      std::memset(&sa, 0, sizeof(sa));
+      sa.st = st; sa.mode = 1; sa.T = g.T;
+      sa.A = dcomp[j]; sa.lda = c.ld; sa.lda_out = c.n; sa.a_out_off = c.out_off;
+      sa.K = 0; sa.kidx = c.kc; sa.n_out = c.n;
+      sa.nblk = 1;
+      sa.Bb[0] = Bgj; sa.nbk[0] = r; sa.ldbb[0] = c.ld; sa.b0_gstride = (long long)rp * c.ld;
+      sa.B0o = BTo; sa.ldb0o = c.n;
+      sa.out = dz; sa.ldo = 3 * rp; sa.col0 = j * rp; sa.oscale = s;
+      sa.outs = dzs; sa.ldos = 3 * rp; sa.scale = s;
+      if ((rc = launch_skinny<T>(sa, skinny_blocks_compact(st, sa), strm))) return rc;
+    }
+    // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.st = st;
+    ga.kidx = 1; ga.n_out = 1;
+    ga.N = D;
+    ga.nseg = 4;
+    for (int j = 0; j < 3; ++j) {
+      const Comp& c = *cc[j];
+      ga.seg[j] = GSeg{dcomp[j], c.ld, c.n, c.out_off, 0, Wm[j], nullptr, D, 1, 0, sets[j], c.kc, c.n};
+    }
+    ga.seg[3] = GSeg{dzs, 3 * rp, 0, 0, 1, Aqkvp, nullptr, D, 0, 3 * rp, nullptr, 0, 0};
+    ga.ksplit_out = g.ks_dx;
+    ga.o0 = dX; ga.ldo = D;
+    ga.part = part;
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
+    if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
+    // dAq, dAk = dz^T X (one pass for q and k), dAv
+    if ((rc = grad_dense<T>(g, X, D, dz, 3 * rp, 0, 2 * rp, crp, gr->dAq, r, 1, gr->dAk, r, 1, rp,
+                            1.f, strm)))
+      return rc;
+    if ((rc = grad_dense<T>(g, X, D, dz, 3 * rp, 2 * rp, rp, crp, gr->dAv, r, 1, nullptr, 0, 0, 0, 1.f,
+                            strm)))
+      return rc;
+    // dB_j[S_j] = s dj_m^T z_j
+    for (int j = 0; j < 3; ++j)
+      if ((rc = grad_scatter<T>(g, *cc[j], dcomp[j], zqkv, 3 * rp, j * rp, sets[j], cc[j]->kc, inv, crp,
+                                dB[j], 0, s, strm)))
+        return rc;
+  }
+  return SL_OK;
+}
+
+sl_status check_weights(const sl_qkvo_weights* w, bool need_qkv, bool need_o) {
+  if (need_qkv) {
+    if (!w->Wq || !w->Wk || !w->Wv || !w->Aq || !w->Bq || !w->Ak || !w->Bk || !w->Av || !w->Bv)
+      SL_FAIL(SL_ERR_NULL, "a q/k/v weight pointer is NULL");
+    if (!aligned16(w->Wq) || !aligned16(w->Wk) || !aligned16(w->Wv) || !aligned16(w->Aq) ||
+        !aligned16(w->Ak) || !aligned16(w->Av))
+      SL_FAIL(SL_ERR_ALIGN, "Wq, Wk, Wv, Aq, Ak, Av must be 16-byte aligned");
+  }
+  if (need_o) {
+    if (!w->WoT || !w->Ao || !w->Bo) SL_FAIL(SL_ERR_NULL, "an o weight pointer is NULL");
+    if (!aligned16(w->WoT) || !aligned16(w->Ao)) SL_FAIL(SL_ERR_ALIGN, "WoT, Ao must be 16-byte aligned");
+  }
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sl_qkvo_saved_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w) {
+  QkvoGeom g;
+  if (qkvo_geom(dt, lay, w, 1, 1, false, g) != SL_OK) return 0;
+  return g.saved_bytes;
+}
+
+size_t sl_qkvo_workspace_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
+                               int32_t k_qk, int32_t k_vo) {
+  QkvoGeom g;
+  if (qkvo_geom(dt, lay, w, k_qk, k_vo, true, g) != SL_OK) return 0;
+  return g.ws_bytes;
+}
+
+sl_status sl_qkvo_fwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w, const void* X,
+                      const void* a, int32_t k_qk, const int32_t* idx_qk, int32_t k_vo,
+                      const int32_t* idx_vo, void* q, void* k, void* v, void* o, void* saved,
+                      size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  QkvoGeom g;
+  sl_status s = qkvo_geom(dt, lay, w, k_qk, k_vo, true, g);
+  if (s != SL_OK) return s;
+  if (!X && !a) SL_FAIL(SL_ERR_NULL, "both X and a are NULL: nothing to compute");
+  if ((s = check_weights(w, X != nullptr, a != nullptr)) != SL_OK) return s;
+  if (X && (!q || !k || !v || !idx_qk || !idx_vo))
+    SL_FAIL(SL_ERR_NULL, "q, k, v, idx_qk and idx_vo are required with X");
+  if (a && (!o || !idx_vo)) SL_FAIL(SL_ERR_NULL, "o and idx_vo are required with a");
+  if (!saved || !ws) SL_FAIL(SL_ERR_NULL, "saved and ws must be non-NULL");
+  if ((X && (!aligned16(X) || !aligned16(q) || !aligned16(k) || !aligned16(v))) ||
+      (a && (!aligned16(a) || !aligned16(o))) || !aligned16(saved) || !aligned16(ws))
+    SL_FAIL(SL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (saved_bytes < g.saved_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "saved buffer %zu bytes < %zu needed", saved_bytes, g.saved_bytes);
+  if (ws_bytes < g.ws_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.ws_bytes);
+  if ((s = check_arch()) != SL_OK) return s;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  if (dt == SL_BF16)
+    return qkvo_fwd_impl<bf16>(g, w, X, a, idx_qk, idx_vo, q, k, v, o, reinterpret_cast<char*>(saved),
+                               reinterpret_cast<char*>(ws), strm);
+  return qkvo_fwd_impl<float>(g, w, X, a, idx_qk, idx_vo, q, k, v, o, reinterpret_cast<char*>(saved),
+                              reinterpret_cast<char*>(ws), strm);
+}
+
+sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w, const void* X,
+                      const void* a, int32_t k_qk, const int32_t* idx_qk, int32_t k_vo,
+                      const int32_t* idx_vo, const void* saved, size_t saved_bytes, const void* dq,
+                      const void* dk, const void* dv, const void* d_out, void* dX, void* da,
+                      const sl_qkvo_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  QkvoGeom g;
+  sl_status s = qkvo_geom(dt, lay, w, k_qk, k_vo, true, g);
+  if (s != SL_OK) return s;
+  if (!dq && !d_out) SL_FAIL(SL_ERR_NULL, "both dq and d_out are NULL: nothing to compute");
+  if ((s = check_weights(w, dq != nullptr, d_out != nullptr)) != SL_OK) return s;
+  if (!gr) SL_FAIL(SL_ERR_NULL, "grads is NULL");
+  if (dq && (!dk || !dv || !X || !dX || !idx_qk || !idx_vo || !gr->dAq || !gr->dBq || !gr->dAk ||
+             !gr->dBk || !gr->dAv || !gr->dBv))
+    SL_FAIL(SL_ERR_NULL, "dk, dv, X, dX, idx_qk, idx_vo and the q/k/v gradients are required with dq");
+  if (d_out && (!a || !da || !idx_vo || !gr->dAo || !gr->dBo))
+    SL_FAIL(SL_ERR_NULL, "a, da, idx_vo, dAo and dBo are required with d_out");
+  if (!saved || !ws) SL_FAIL(SL_ERR_NULL, "saved and ws must be non-NULL");
+  if ((dq && (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(X) || !aligned16(dX))) ||
+      (d_out && (!aligned16(d_out) || !aligned16(a) || !aligned16(da))) || !aligned16(saved) ||
+      !aligned16(ws))
+    SL_FAIL(SL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (saved_bytes < g.saved_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "saved buffer %zu bytes < %zu needed", saved_bytes, g.saved_bytes);
+  if (ws_bytes < g.ws_bytes)
+    SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.ws_bytes);
+  if ((s = check_arch()) != SL_OK) return s;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  if (dt == SL_BF16)
+    return qkvo_bwd_impl<bf16>(g, w, X, a, idx_qk, idx_vo, reinterpret_cast<const char*>(saved), dq,
+                               dk, dv, d_out, dX, da, gr, reinterpret_cast<char*>(ws), strm);
+  return qkvo_bwd_impl<float>(g, w, X, a, idx_qk, idx_vo, reinterpret_cast<const char*>(saved), dq, dk,
+                              dv, d_out, dX, da, gr, reinterpret_cast<char*>(ws), strm);
+}
+
+}  // extern "C"

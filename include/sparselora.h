@@ -217,6 +217,28 @@ sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* 
                       void* dX, void* da, const sl_qkvo_grads* g,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Diagnostics (not part of the computation).  When enabled, the library's main
+ * launches are bracketed by HIP events on the caller's stream and attributed
+ * to the slots below, so a caller can time individual kernels inside a timed
+ * region.  Single-threaded use only.  sl_timer_enable(n) keeps room for n
+ * launches (0 disables and frees the events); sl_timer_read waits for the
+ * recorded events and returns the slot's total milliseconds and launch count
+ * since the last sl_timer_reset.
+ * ------------------------------------------------------------------------- */
+typedef enum sl_timer_slot {
+  SL_TS_ESTIMATE = 0,   /* estimator stage 1 + criterion (a1, a2) */
+  SL_TS_SELECT = 1,     /* top-k (a3) */
+  SL_TS_GU_FWD = 2,     /* gate/up gather-GEMM + SwiGLU (a4) */
+  SL_TS_DOWN_FWD = 3,   /* down K-gather GEMM (a4) */
+  SL_TS_DH_BWD = 4,     /* dH gather-GEMM + SwiGLU backward (a5) */
+  SL_TS_DX_BWD = 5,     /* dX K-gather GEMM (a5) */
+  SL_TS_QKV_FWD = 6, SL_TS_O_FWD = 7, SL_TS_DA_BWD = 8, SL_TS_DXQKV_BWD = 9
+} sl_timer_slot;
+int sl_timer_enable(int max_launches);
+void sl_timer_reset(void);
+int sl_timer_read(int slot, double* total_ms, int* count);
+
 #ifdef __cplusplus
 }
 #endif

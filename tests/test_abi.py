@@ -1,0 +1,147 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects invalid arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparselora.h")
+
+
+@pytest.fixture(scope="module")
+def sl():
+    import contextual_sparsity_lora_svd_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from contextual_sparsity_lora_svd_amd import build
+        build.build(verbose=False)
+    m.lib()
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(sl):
+    names = _declared()
+    assert len(names) >= 18
+    L = sl.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # the binding declares exactly the header's entry points
+    assert sorted(sl.SIGNATURES) == names
+
+
+def test_status_strings(sl):
+    L = sl.lib()
+    assert L.sl_abi_version() == 1
+    for code in range(9):
+        assert L.sl_status_string(code)
+    assert L.sl_status_string(99) == b"unknown status"
+
+
+def _ffn_weights(sl, D=64, F=128, r=4, ptr=16):
+    return sl.api.SlFfnWeights(D, F, r, 1.0, *([ptr] * 9))
+
+
+def test_ffn_validation_errors(sl):
+    L = sl.lib()
+    lay = sl.Layout([3, 4], 4)
+    w = _ffn_weights(sl)
+    P = 4096  # any aligned, never-dereferenced address: validation fails first
+    # null pointers
+    st = L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), None, 10, P, P, P, 1 << 30, P, 1 << 30, None)
+    assert st == 1
+    # misaligned
+    st = L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), P + 2, 10, P, P, P, 1 << 30, P, 1 << 30, None)
+    assert st == 2
+    # bad dtype
+    st = L.sl_ffn_fwd(7, lay.ref, ctypes.byref(w), P, 10, P, P, P, 1 << 30, P, 1 << 30, None)
+    assert st == 4
+    # k out of range
+    for k in (0, 129):
+        st = L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), P, k, P, P, P, 1 << 30, P, 1 << 30, None)
+        assert st == 5
+    # ctx_len beyond seq_len / batch beyond the limit
+    bad = sl.Layout([5, 1], 4)
+    assert L.sl_ffn_fwd(1, bad.ref, ctypes.byref(w), P, 10, P, P, P, 1 << 30, P, 1 << 30, None) == 5
+    big = sl.Layout([1] * 65, 4)
+    assert L.sl_ffn_fwd(1, big.ref, ctypes.byref(w), P, 10, P, P, P, 1 << 30, P, 1 << 30, None) == 5
+    # shapes not multiples of 8
+    w2 = _ffn_weights(sl, D=60)
+    assert L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w2), P, 10, P, P, P, 1 << 30, P, 1 << 30, None) == 3
+    # buffers too small
+    st = L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), P, 10, P, P, P, 16, P, 1 << 30, None)
+    assert st == 6
+    assert b"saved" in L.sl_last_error()
+    # everything valid: the host has no gfx950 device, so the call stops at the
+    # device check (an error status, nothing launched)
+    st = L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), P, 10, P, P, P, 1 << 30, P, 1 << 30, None)
+    assert st in (7, 8)
+
+
+def test_size_queries_follow_the_layout(sl):
+    L = sl.lib()
+    lay = sl.Layout([3, 4], 4)
+    s_small = L.sl_ffn_saved_bytes(1, lay.ref, 64, 128, 4, 8)
+    s_big = L.sl_ffn_saved_bytes(1, lay.ref, 64, 128, 4, 64)
+    assert 0 < s_small < s_big
+    # saved = z (fp32, T x 2rp) + z_d (T x rp) + G, U, H compact (bf16)
+    T, rp = 8, 8
+    comp = 3 * 8 + 1 * 128     # 3 context rows x ldk(8) + 1 output row x d_ff
+    def up(x):
+        return (x + 255) // 256 * 256
+    expect = up(T * 2 * rp * 4) + up(T * rp * 4) + 3 * up(comp * 2)
+    assert s_small == expect
+    assert L.sl_ffn_workspace_bytes(1, lay.ref, 64, 128, 4, 0) == 0   # invalid k
+    assert L.sl_estimator_workspace_bytes(100, 50, 65) == 0
+    assert L.sl_estimator_workspace_bytes(100, 50, 8) > 0
+
+
+def test_estimate_select_validation(sl):
+    L = sl.lib()
+    lay = sl.Layout([10], 10)
+    P = 4096
+    heads = sl.api.SlHeads(4, 2, 8)
+    # QK-norm selects over kv channels: N must be n_kv_heads * head_dim
+    st = L.sl_estimate_select(2, 1, lay.ref, ctypes.byref(heads), P, 64, 8, P, P, P, P, 32, 4, P,
+                              None, P, 1 << 30, None)
+    assert st == 3
+    st = L.sl_estimate_select(9, 1, lay.ref, None, P, 64, 8, P, P, P, P, 16, 4, P, None, P, 1 << 30,
+                              None)
+    assert st == 4
+    st = L.sl_estimate_select(0, 1, lay.ref, None, P, 64, 40, P, P, P, P, 16, 4, P, None, P, 1 << 30,
+                              None)
+    assert st == 5          # rank above 32
+    st = L.sl_estimate_select(0, 1, lay.ref, None, P, 64, 8, P, P, None, P, 16, 4, P, None, P,
+                              1 << 30, None)
+    assert st == 1          # SwiGLU needs both factor pairs
+
+
+def test_qkvo_validation(sl):
+    L = sl.lib()
+    lay = sl.Layout([5, 2], 6)
+    P = 4096
+    w = sl.api.SlQkvoWeights(64, sl.api.SlHeads(4, 3, 8), 4, 1.0, *([P] * 12))
+    st = L.sl_qkvo_fwd(1, lay.ref, ctypes.byref(w), P, P, 4, P, 4, P, P, P, P, P, P, 1 << 30, P,
+                       1 << 30, None)
+    assert st == 3          # 4 query heads do not divide into 3 kv heads
+    w = sl.api.SlQkvoWeights(64, sl.api.SlHeads(4, 2, 8), 4, 1.0, *([P] * 12))
+    st = L.sl_qkvo_fwd(1, lay.ref, ctypes.byref(w), None, None, 4, P, 4, P, P, P, P, P, P, 1 << 30, P,
+                       1 << 30, None)
+    assert st == 1          # nothing to compute
+    st = L.sl_qkvo_fwd(1, lay.ref, ctypes.byref(w), P, None, 17, P, 4, P, P, P, P, P, P, 1 << 30, P,
+                       1 << 30, None)
+    assert st == 5          # k_qk above the 16 kv channels
+
+
+def test_k_rule_matches_oracle(sl):
+    import oracle as O
+    for n in (1, 7, 688, 4096, 11008, 14336):
+        for pct in (0, 1, 30, 50, 60, 75, 90, 99):
+            assert sl.k_from_ratio(n, pct) == O.k_from_ratio(n, pct)

@@ -1,0 +1,190 @@
+"""GPU parity of the q/k/v/o projections (QK-norm and L2 selection, forward,
+backward) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_helpers import assert_close, check_selection, factors, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _api():
+    import contextual_sparsity_lora_svd_amd as sl
+    return sl
+
+
+def _case(D, heads, r, ctx, L, dt, seed):
+    hq, hkv, hd = heads
+    nq, nkv = hq * hd, hkv * hd
+    rng = np.random.default_rng(seed)
+    T = len(ctx) * L
+
+    def rnd(shape, std):
+        x = (rng.standard_normal(shape) * std).astype(np.float32)
+        return W.round_to_bf16(x) if dt == "bf16" else x
+
+    def act(n):
+        z = rng.standard_normal((T, 8)).astype(np.float32)
+        m = rng.standard_normal((8, n)).astype(np.float32)
+        x = (z @ m + 0.1 * rng.standard_normal((T, n)).astype(np.float32)) * \
+            rng.lognormal(0, 1, n).astype(np.float32)
+        return W.round_to_bf16(x) if dt == "bf16" else x
+
+    return {"X": act(D), "a": act(nq),
+            "Wq": rnd((nq, D), 0.05), "Wk": rnd((nkv, D), 0.05), "Wv": rnd((nkv, D), 0.05),
+            "Wo": rnd((D, nq), 0.05),
+            "Aq": rnd((r, D), 0.05), "Bq": rnd((nq, r), 0.05), "Ak": rnd((r, D), 0.05),
+            "Bk": rnd((nkv, r), 0.05), "Av": rnd((r, D), 0.05), "Bv": rnd((nkv, r), 0.05),
+            "Ao": rnd((r, nq), 0.05), "Bo": rnd((D, r), 0.05),
+            "dq": rnd((T, nq), 1.0), "dk": rnd((T, nkv), 1.0), "dv": rnd((T, nkv), 1.0),
+            "d_out": rnd((T, D), 1.0)}
+
+
+def _weights(p, heads, dt, s):
+    sl = _api()
+    t = {n: to_dev(p[n], dt) for n in ("Wq", "Wk", "Wv", "Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo")}
+    t["WoT"] = to_dev(np.ascontiguousarray(p["Wo"].T), dt)
+    return sl.QKVOWeights(t, heads, lora_scale=s)
+
+
+def _compare(p, heads, ctx, L, idx_qk, idx_vo, dt, s=1.0, split_calls=False):
+    sl = _api()
+    w = _weights(p, heads, dt, s)
+    lay = sl.Layout(ctx, L)
+    X, a = to_dev(p["X"], dt), to_dev(p["a"], dt)
+    kqk, kvo = idx_qk.shape[1], idx_vo.shape[1]
+    iqk = torch.from_numpy(np.ascontiguousarray(idx_qk, np.int32)).cuda()
+    ivo = torch.from_numpy(np.ascontiguousarray(idx_vo, np.int32)).cuda()
+    if split_calls:
+        outs, buf = sl.qkvo_fwd(w, X, None, lay, kqk, iqk, kvo, ivo)
+        outs, buf = sl.qkvo_fwd(w, None, a, lay, kqk, iqk, kvo, ivo, buf=buf, outs=outs)
+        g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, d_out=to_dev(p["d_out"], dt))
+        g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, dq=to_dev(p["dq"], dt),
+                        dk=to_dev(p["dk"], dt), dv=to_dev(p["dv"], dt), out=g)
+    else:
+        outs, buf = sl.qkvo_fwd(w, X, a, lay, kqk, iqk, kvo, ivo)
+        g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, dq=to_dev(p["dq"], dt),
+                        dk=to_dev(p["dk"], dt), dv=to_dev(p["dv"], dt), d_out=to_dev(p["d_out"], dt))
+    torch.cuda.synchronize()
+    ref, cache = O.qkvo_forward(p, ctx, L, list(idx_qk), list(idx_vo), heads, s)
+    gr = O.qkvo_backward(p, cache, {n: p[n] for n in ("dq", "dk", "dv", "d_out")}, s)
+    errs = {}
+    for n in ("q", "k", "v", "o"):
+        errs[n] = assert_close(to_np(outs[n]), ref[n], dt, n)
+    # unselected context channels are exactly zero
+    mq = cache["mq"]
+    assert np.all(to_np(outs["q"])[mq == 0] == 0)
+    for n in ("dX", "da", "dAq", "dBq", "dAk", "dBk", "dAv", "dBv", "dAo", "dBo"):
+        errs[n] = assert_close(to_np(g[n]), gr[n], dt, n)
+    assert np.all(to_np(g["da"])[cache["mo"] == 0] == 0)
+    print(f"\n[{dt}] heads={heads} ctx={list(ctx)} kqk={kqk} kvo={kvo} " +
+          " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+
+
+def _sets(rng, B, n, k):
+    return np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("heads", [(4, 4, 16), (8, 2, 16)])
+def test_qkvo_ragged(dt, heads):
+    D, r, L = 64, 4, 40
+    ctx = [40, 0, 23]
+    p = _case(D, heads, r, ctx, L, dt, seed=21)
+    rng = np.random.default_rng(22)
+    nkv = heads[1] * heads[2]
+    _compare(p, heads, ctx, L, _sets(rng, 3, nkv, 13), _sets(rng, 3, nkv, 21), dt, s=0.7)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_qkvo_split_calls_and_extremes(dt):
+    heads = (8, 4, 32)
+    D, r, L = 128, 8, 100
+    ctx = [80, 100]
+    p = _case(D, heads, r, ctx, L, dt, seed=23)
+    rng = np.random.default_rng(24)
+    nkv = heads[1] * heads[2]
+    _compare(p, heads, ctx, L, _sets(rng, 2, nkv, 40), _sets(rng, 2, nkv, 64), dt, split_calls=True)
+    full = np.tile(np.arange(nkv, dtype=np.int32), (2, 1))
+    _compare(p, heads, ctx, L, full, np.array([[0], [nkv - 1]], np.int32), dt)
+
+
+def test_qkvo_multi_tile_bf16():
+    heads = (16, 4, 64)
+    D, r, L = 512, 16, 300
+    ctx = [260, 300, 150]
+    p = _case(D, heads, r, ctx, L, "bf16", seed=25)
+    rng = np.random.default_rng(26)
+    nkv = heads[1] * heads[2]
+    _compare(p, heads, ctx, L, _sets(rng, 3, nkv, 130), _sets(rng, 3, nkv, 190), "bf16")
+
+
+def _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv):
+    B = len(ctx)
+    qk, vo = [], []
+    for b in range(B):
+        rows = O.context_rows(ctx, L, b)
+        qk.append(O.scores_qk_norm(p["X"][rows], Pq.T, Qq, Pk.T, Qk, *heads, dtype=np.float32))
+        vo.append(O.scores_l2(p["X"][rows], Pv.T, Qv, dtype=np.float32))
+    return np.stack(qk), np.stack(vo)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("heads", [(4, 4, 16), (8, 2, 16)])
+def test_qk_norm_and_l2_select(dt, heads):
+    sl = _api()
+    D, r, L = 64, 4, 90
+    ctx = [90, 17, 64]
+    p = _case(D, heads, r, ctx, L, dt, seed=27)
+    Pq, Qq = factors(p["Wq"], 8, dt)
+    Pk, Qk = factors(p["Wk"], 8, dt)
+    Pv, Qv = factors(p["Wv"], 8, dt)
+    nkv = heads[1] * heads[2]
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], dt)
+    ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    k = nkv // 2
+    idx, sc = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, 8, to_dev(Pq, dt), to_dev(Qq, dt),
+                                 to_dev(Pk, dt), to_dev(Qk, dt), nkv, k, heads=heads, want_scores=True)
+    idx2, sc2 = sl.estimate_select(sl.SL_CRIT_L2, X, lay, 8, to_dev(Pv, dt), to_dev(Qv, dt), None, None,
+                                   nkv, k, want_scores=True)
+    torch.cuda.synchronize()
+    for got, ref in ((sc.cpu().numpy(), ref_qk), (sc2.cpu().numpy(), ref_vo)):
+        for b in range(len(ctx)):
+            e = np.abs(got[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+            assert e < 2e-4, f"score rel err {e:.2e}"
+    check_selection(idx.cpu().numpy(), ref_qk, k)
+    check_selection(idx2.cpu().numpy(), ref_vo, k)
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_full_size_workloads(cfg):
+    """LLaMA2-7B q/k/v/o (multi-head) and LLaMA3-8B (grouped-query) at their sizes."""
+    sl = _api()
+    wl = W.WORKLOADS[cfg]
+    s = wl.attn[0]
+    heads = (s.n_q_heads, s.n_kv_heads, s.head_dim)
+    p = W.make_attn_tensors(wl)
+    ctx = [int(c) for c in W.ctx_lengths(wl)]
+    L = wl.seq_len
+    nkv = heads[1] * heads[2]
+    kqk = O.k_from_ratio(nkv, s.sparsity_qk_pct)
+    kvo = O.k_from_ratio(nkv, s.sparsity_vo_pct)
+    Pq, Qq = factors(p["Wq"], wl.est_rank, "bf16")
+    Pk, Qk = factors(p["Wk"], wl.est_rank, "bf16")
+    Pv, Qv = factors(p["Wv"], wl.est_rank, "bf16")
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], "bf16")
+    idx, _ = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, wl.est_rank, to_dev(Pq, "bf16"),
+                                to_dev(Qq, "bf16"), to_dev(Pk, "bf16"), to_dev(Qk, "bf16"), nkv, kqk,
+                                heads=heads)
+    torch.cuda.synchronize()
+    ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    n_exact = check_selection(idx.cpu().numpy(), ref_qk, kqk)
+    iqk = np.stack([O.select_topk(ref_qk[b], kqk) for b in range(len(ctx))])
+    ivo = np.stack([O.select_topk(ref_vo[b], kvo) for b in range(len(ctx))])
+    _compare(p, heads, ctx, L, iqk, ivo, "bf16", s=1.0)
+    print(f"exact qk sets {n_exact}/{len(ctx)}", flush=True)

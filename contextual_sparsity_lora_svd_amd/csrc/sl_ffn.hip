@@ -27,7 +27,7 @@ struct FfnGeom {
   int T, D, F, r, rp, k, ldk, ldF;
   size_t esz;
   long long comp, c_out_off;
-  int ks_down, ks_dx, RM1, RM2;
+  int ks_down, ks_dx, RM1, RM2, chunk;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
       w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, ws_bytes;
@@ -70,8 +70,9 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   const int bk = dt == SL_BF16 ? 64 : 32;
   g.ks_down = choose_ksplit(st, k + g.rp, F + g.rp, g.D, bk);
   g.ks_dx = choose_ksplit(st, 2LL * k + 2 * g.rp, 2 * F + 2 * g.rp, g.D, bk);
-  g.RM1 = pow2_rm(g.rp);
-  g.RM2 = pow2_rm(2 * g.rp);
+  g.RM1 = cr_rm(g.esz, g.rp);
+  g.RM2 = cr_rm(g.esz, 2 * g.rp);
+  g.chunk = cr_chunk(g.esz);
   const size_t T = g.T, e = g.esz;
   Bump sv;
   g.s_zgu = sv.take(T * 2 * g.rp * 4);
@@ -101,8 +102,8 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_dz_gu = w.take(T * 2 * g.rp * 4);
   g.w_dzs_gu = w.take(T * 2 * g.rp * e);
   g.w_Agup = w.take((size_t)2 * g.rp * D * e);
-  long long cr = (long long)ceil_div(T, CR_CHUNK) * D * g.RM2;
-  const long long cr2 = colred_part_elems_compact(st, k, g.F, g.RM1);
+  long long cr = (long long)ceil_div(T, g.chunk) * D * g.RM2;
+  const long long cr2 = colred_part_elems_compact(st, k, g.F, g.RM1, g.chunk);
   if (cr2 > cr) cr = cr2;
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
@@ -141,17 +142,15 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* part = reinterpret_cast<float*>(ws + g.w_part);
 
   // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
-  // Adg[g] = Ad[:, S_g] (gathered per context group).
-  if ((rc = fill_zero<T>(Pg, (long long)F * 2 * rp, strm))) return rc;
-  if ((rc = fill_zero<T>(Pu, (long long)F * 2 * rp, strm))) return rc;
-  if ((rc = copy2d<T>(Pg, 2 * rp, 0, 0, F, r, w->Bg, r, 0, strm))) return rc;
-  if ((rc = copy2d<T>(Pu, 2 * rp, 0, rp, F, r, w->Bu, r, 0, strm))) return rc;
-  if ((rc = fill_zero<T>(BdTp, (long long)rp * D, strm))) return rc;
-  if ((rc = copy2d<T>(BdTp, D, 0, 0, r, D, w->Bd, r, 1, strm))) return rc;
-  if ((rc = fill_zero<T>(Adg, (long long)st.nseq * rp * g.ldk, strm))) return rc;
-  if ((rc = gather_factor<T>(Adg, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Ad, F, 0,
-                             strm)))
-    return rc;
+  // Adg[g] = Ad[:, S_g] (gathered per context group); one launch.
+  {
+    Packer pk;
+    pk.copy(Pg, 2 * rp, F, 2 * rp, w->Bg, r, F, r, 0);
+    pk.copy(Pu, 2 * rp, F, 2 * rp, w->Bu, r, F, r, 0, 0, rp);
+    pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
+    pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
+    if ((rc = pk.launch<T>(strm))) return rc;
+  }
 
   // z = X [Ag; Au]^T  (fp32 saved, s*z in T for the GEMM)
   {
@@ -243,22 +242,19 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
 
-  // packed LoRA operands
-  if ((rc = fill_zero<T>(BdTp, (long long)rp * D, strm))) return rc;
-  if ((rc = copy2d<T>(BdTp, D, 0, 0, r, D, w->Bd, r, 1, strm))) return rc;
-  if ((rc = fill_zero<T>(AdTp, (long long)F * rp, strm))) return rc;
-  if ((rc = copy2d<T>(AdTp, rp, 0, 0, F, r, w->Ad, F, 1, strm))) return rc;
-  if ((rc = fill_zero<T>(Agup, (long long)2 * rp * D, strm))) return rc;
-  if ((rc = copy2d<T>(Agup, D, 0, 0, r, D, w->Ag, D, 0, strm))) return rc;
-  if ((rc = copy2d<T>(Agup, D, rp, 0, r, D, w->Au, D, 0, strm))) return rc;
-  if ((rc = gather_factor<T>(Bgg, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Bg, r, 1,
-                             strm)))
-    return rc;
-  if ((rc = gather_factor<T>(Bug, g.ldk, (long long)rp * g.ldk, idx, g.k, st.nseq, r, w->Bu, r, 1,
-                             strm)))
-    return rc;
-  if ((rc = copy2d<T>(BgTo, F, 0, 0, r, F, w->Bg, r, 1, strm))) return rc;
-  if ((rc = copy2d<T>(BuTo, F, 0, 0, r, F, w->Bu, r, 1, strm))) return rc;
+  // packed LoRA operands (one launch)
+  {
+    Packer pk;
+    pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
+    pk.copy(AdTp, rp, F, rp, w->Ad, F, F, r, 1);
+    pk.copy(Agup, D, rp, D, w->Ag, D, r, D, 0);
+    pk.copy(Agup + (long long)rp * D, D, rp, D, w->Au, D, r, D, 0);
+    pk.gather(Bgg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bg, r, r, 1, idx, g.k, st.nseq);
+    pk.gather(Bug, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bu, r, r, 1, idx, g.k, st.nseq);
+    pk.copy(BgTo, F, r, F, w->Bg, r, r, F, 1);
+    pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
+    if ((rc = pk.launch<T>(strm))) return rc;
+  }
   if ((rc = inverse_maps(idx, g.k, st.nseq, F, inv, strm))) return rc;
 
   // dz_d = s dY Bd
@@ -327,7 +323,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.P = X; a.ldp = D; a.N = D;
     a.Z = dz_gu; a.ldz = 2 * rp; a.zc0 = 0; a.R = 2 * rp;
     a.part = crp;
-    const int nc = ceil_div(g.T, CR_CHUNK);
+    const int nc = ceil_div(g.T, g.chunk);
     if ((rc = launch_colred<T>(a, nc, D, g.RM2, strm))) return rc;
     FinishArgs f{crp, nc, D, g.RM2, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f};
     hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM2), dim3(256), 0, strm, f);
@@ -341,7 +337,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.P = dY; a.ldp = D; a.N = D;
     a.Z = zd; a.ldz = rp; a.zc0 = 0; a.R = rp;
     a.part = crp;
-    const int nc = ceil_div(g.T, CR_CHUNK);
+    const int nc = ceil_div(g.T, g.chunk);
     if ((rc = launch_colred<T>(a, nc, D, g.RM1, strm))) return rc;
     FinishArgs f{crp, nc, D, g.RM1, gr->dBd, r, 0, nullptr, 0, 0, 0, s};
     hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM1), dim3(256), 0, strm, f);
@@ -359,14 +355,14 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     else { a.Z = dz_d; a.ldz = rp; a.zc0 = 0; }
     a.R = rp;
     a.part = crp;
-    const int nc = colred_chunks_compact(st, a, g.k, F, g.RM1);
+    const int nc = colred_chunks_compact(st, a, g.k, F, g.RM1, g.chunk);
     if ((rc = launch_colred<T>(a, nc, F > g.k ? F : g.k, g.RM1, strm))) return rc;
     FinishScatterArgs f;
     std::memset(&f, 0, sizeof(f));
     f.st = st; f.part = crp; f.RM = g.RM1; f.Nfull = F; f.kidx = g.k; f.inv = inv;
     for (int q = 0; q <= st.nseq; ++q) {
       const int m = q < st.nseq ? st.ctx[q] : st.T_out;
-      f.chunk_count[q] = ceil_div(m, CR_CHUNK);
+      f.chunk_count[q] = ceil_div(m, g.chunk);
       f.part_off[q] = a.part_off[q];
     }
     f.out = which == 0 ? gr->dBg : which == 1 ? gr->dBu : gr->dAd;

@@ -50,9 +50,26 @@ inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
   return SL_OK;
 }
 
+// Token rows per column-reduction chunk and the padded width of its partials.
+inline int cr_chunk(size_t esz) { return esz == 2 ? CRM_CHUNK : CR_CHUNK; }
+inline int cr_rm(size_t esz, int R) {
+  const int rm = pow2_rm(R);
+  return (esz == 2 && rm < 16) ? 16 : rm;
+}
+
 template <typename T>
 inline sl_status launch_colred(ColredArgs& a, int nchunks_total, int nmax, int RM, hipStream_t s) {
   if (nchunks_total <= 0 || nmax <= 0) return SL_OK;
+  if (sizeof(T) == 2) {
+    const dim3 grid(ceil_div(nmax, CRM_COLS), nchunks_total), block(256);
+    switch (RM) {
+      case 16: hipLaunchKernelGGL((colred_mfma_kernel<16>), grid, block, 0, s, a); break;
+      case 32: hipLaunchKernelGGL((colred_mfma_kernel<32>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((colred_mfma_kernel<64>), grid, block, 0, s, a); break;
+    }
+    SL_HIP(hipGetLastError());
+    return SL_OK;
+  }
   const dim3 grid(ceil_div(nmax, 2 * CR_THREADS), nchunks_total), block(CR_THREADS);
   switch (RM) {
     case 8: hipLaunchKernelGGL((colred_kernel<T, 8>), grid, block, 0, s, a); break;
@@ -97,6 +114,41 @@ inline sl_status gather_factor(void* dst, long long ldd, long long gstride, cons
   return SL_OK;
 }
 
+// Builder of one pack launch.
+struct Packer {
+  PackArgs a;
+  Packer() { std::memset(&a, 0, sizeof(a)); }
+  // dst region [rows x cols] (row stride ldd) holding src block at (row_off, col_off)
+  void copy(void* dst, long long ldd, int rows, int cols, const void* src, long long lds,
+            int src_rows, int src_cols, int tr, int row_off = 0, int col_off = 0) {
+    PackJob& j = a.job[a.njobs++];
+    j.type = 0; j.dst = dst; j.ldd = ldd; j.rows = rows; j.cols = cols;
+    j.row_off = row_off; j.col_off = col_off;
+    j.src = src; j.lds = lds; j.src_rows = src_rows; j.src_cols = src_cols; j.tr = tr;
+  }
+  // per context group g: dst + g*gstride, [rows x cols], src factor gathered by idx
+  void gather(void* dst, long long ldd, long long gstride, int rows, int cols, const void* src,
+              long long lds, int src_rows, int tr, const int* idx, int k, int nseq) {
+    PackJob& j = a.job[a.njobs++];
+    j.type = 1; j.dst = dst; j.ldd = ldd; j.gstride = gstride; j.rows = rows; j.cols = cols;
+    j.src = src; j.lds = lds; j.src_rows = src_rows; j.tr = tr; j.idx = idx; j.k = k; j.nseq = nseq;
+  }
+  template <typename T>
+  sl_status launch(hipStream_t s) {
+    long long n = 0;
+    for (int i = 0; i < a.njobs; ++i) {
+      a.start[i] = n;
+      const PackJob& j = a.job[i];
+      n += (long long)j.rows * j.cols * (j.type == 1 ? j.nseq : 1);
+    }
+    a.start[a.njobs] = n;
+    if (n == 0) return SL_OK;
+    hipLaunchKernelGGL((pack_kernel<T>), grid1d(n), dim3(256), 0, s, a);
+    SL_HIP(hipGetLastError());
+    return SL_OK;
+  }
+};
+
 inline sl_status inverse_maps(const int* idx, int k, int nseq, int Nfull, int* inv, hipStream_t s) {
   hipLaunchKernelGGL(inverse_map_kernel, grid1d((long long)nseq * Nfull), dim3(256), 0, s, idx, k,
                      nseq, Nfull, inv);
@@ -132,14 +184,15 @@ inline int skinny_blocks_compact(const SeqTab& st, SkinnyArgs& a) {
 }
 
 // Chunks of the column reduction per group (mode 1).
-inline int colred_chunks_compact(const SeqTab& st, ColredArgs& a, int kidx, int n_out, int RM) {
+inline int colred_chunks_compact(const SeqTab& st, ColredArgs& a, int kidx, int n_out, int RM,
+                                 int chunk) {
   int nc = 0;
   long long off = 0;
   for (int g = 0; g <= st.nseq; ++g) {
     a.chunk_start[g] = nc;
     a.part_off[g] = off;
     const int m = g < st.nseq ? st.ctx[g] : st.T_out;
-    const int c = ceil_div(m, CR_CHUNK);
+    const int c = ceil_div(m, chunk);
     nc += c;
     off += (long long)c * (g < st.nseq ? kidx : n_out) * RM;
   }
@@ -149,11 +202,12 @@ inline int colred_chunks_compact(const SeqTab& st, ColredArgs& a, int kidx, int 
   return nc;
 }
 
-inline long long colred_part_elems_compact(const SeqTab& st, int kidx, int n_out, int RM) {
+inline long long colred_part_elems_compact(const SeqTab& st, int kidx, int n_out, int RM,
+                                           int chunk) {
   long long off = 0;
   for (int g = 0; g <= st.nseq; ++g) {
     const int m = g < st.nseq ? st.ctx[g] : st.T_out;
-    off += (long long)ceil_div(m, CR_CHUNK) * (g < st.nseq ? kidx : n_out) * RM;
+    off += (long long)ceil_div(m, chunk) * (g < st.nseq ? kidx : n_out) * RM;
   }
   return off;
 }

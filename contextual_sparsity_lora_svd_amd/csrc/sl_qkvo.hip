@@ -34,7 +34,7 @@ struct QkvoGeom {
   int T, D, Hq, Hkv, hd, G, nq, nkv, r, rp, kqk, kvo, kq, ko;
   size_t esz;
   Comp cq, ck, cv, co;
-  int ks_o, ks_dx;
+  int ks_o, ks_dx, chunk;
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
@@ -124,12 +124,13 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_dz_qkv = b.take(T * 3 * rp * 4);
   g.w_dzs_qkv = b.take(T * 3 * rp * e);
   g.w_Aqkvp = b.take(3 * rp * D * e);
-  long long cr = (long long)ceil_div(g.T, CR_CHUNK) * std::max(g.D, g.nq) * pow2_rm(2 * g.rp);
-  const int RM1 = pow2_rm(g.rp);
-  cr = std::max(cr, colred_part_elems_compact(st, g.kq, g.nq, RM1));
-  cr = std::max(cr, colred_part_elems_compact(st, g.ko, g.nq, RM1));
-  cr = std::max(cr, colred_part_elems_compact(st, g.kqk, g.nkv, RM1));
-  cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1));
+  g.chunk = cr_chunk(g.esz);
+  long long cr = (long long)ceil_div(g.T, g.chunk) * std::max(g.D, g.nq) * cr_rm(g.esz, 2 * g.rp);
+  const int RM1 = cr_rm(g.esz, g.rp);
+  cr = std::max(cr, colred_part_elems_compact(st, g.kq, g.nq, RM1, g.chunk));
+  cr = std::max(cr, colred_part_elems_compact(st, g.ko, g.nq, RM1, g.chunk));
+  cr = std::max(cr, colred_part_elems_compact(st, g.kqk, g.nkv, RM1, g.chunk));
+  cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1, g.chunk));
   g.w_cr = b.take((size_t)cr * 4);
   g.w_inv = b.take(B * std::max(g.nq, g.nkv) * 4);
   g.ws_bytes = b.off;
@@ -180,7 +181,7 @@ sl_status grad_scatter(const QkvoGeom& g, const Comp& c, const void* P, const fl
                        int zc0, const int* idx, int k_idx, int* inv, float* crp, float* out,
                        int transposed, float scale, hipStream_t s) {
   const SeqTab& st = g.st;
-  const int RM = pow2_rm(g.rp);
+  const int RM = cr_rm(g.esz, g.rp);
   sl_status rc;
   if ((rc = inverse_maps(idx, k_idx, st.nseq, c.n, inv, s))) return rc;
   ColredArgs a;
@@ -190,14 +191,14 @@ sl_status grad_scatter(const QkvoGeom& g, const Comp& c, const void* P, const fl
   a.kidx = c.kc; a.n_out = c.n;
   a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = g.rp;
   a.part = crp;
-  const int nc = colred_chunks_compact(st, a, c.kc, c.n, RM);
+  const int nc = colred_chunks_compact(st, a, c.kc, c.n, RM, g.chunk);
   if ((rc = launch_colred<T>(a, nc, std::max(c.n, c.kc), RM, s))) return rc;
   FinishScatterArgs f;
   std::memset(&f, 0, sizeof(f));
   f.st = st; f.part = crp; f.RM = RM; f.Nfull = c.n; f.kidx = c.kc; f.inv = inv;
   for (int q = 0; q <= st.nseq; ++q) {
     const int m = q < st.nseq ? st.ctx[q] : st.T_out;
-    f.chunk_count[q] = ceil_div(m, CR_CHUNK);
+    f.chunk_count[q] = ceil_div(m, g.chunk);
     f.part_off[q] = a.part_off[q];
   }
   f.out = out; f.r = g.r; f.transposed = transposed; f.scale = scale;
@@ -212,14 +213,14 @@ sl_status grad_dense(const QkvoGeom& g, const void* P, int N, const float* Z, lo
                      int R, float* crp, float* out1, int r1, int t1, float* out2, int r2, int t2,
                      int off2, float scale, hipStream_t s) {
   sl_status rc;
-  const int RM = pow2_rm(R);
+  const int RM = cr_rm(g.esz, R);
   ColredArgs a;
   std::memset(&a, 0, sizeof(a));
   a.st = g.st; a.mode = 0; a.T = g.T;
   a.P = P; a.ldp = N; a.N = N;
   a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = R;
   a.part = crp;
-  const int nc = ceil_div(g.T, CR_CHUNK);
+  const int nc = ceil_div(g.T, g.chunk);
   if ((rc = launch_colred<T>(a, nc, N, RM, s))) return rc;
   FinishArgs f{crp, nc, N, RM, out1, r1, t1, out2, r2, t2, off2, scale};
   hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)N * RM), dim3(256), 0, s, f);

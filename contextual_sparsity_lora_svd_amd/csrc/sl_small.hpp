@@ -99,35 +99,46 @@ skinny_kernel(const SkinnyArgs a) {
   }
 
   if constexpr (sizeof(T) == 2) {
-    // k-steps of 32; lane holds 8 consecutive k at 8*(lane>>4)
+    // k-steps of 32; lane holds 8 consecutive k at 8*(lane>>4).  U steps are
+    // loaded before any is consumed so that each lane keeps several loads in
+    // flight; addresses are clamped and tails zeroed after the loads.
+    constexpr int U = NB <= 2 ? 8 : 4;
     const int nsteps = (K + 31) / 32;
     const int per = (nsteps + SK_WAVES - 1) / SK_WAVES;
     const int s0 = wave * per, s1 = min(nsteps, s0 + per);
-    for (int s = s0; s < s1; ++s) {
-      const int k = s * 32 + 8 * (lane >> 4);
-      uint4 av = make_uint4(0, 0, 0, 0);
-      if (k < K) {
-        av = *reinterpret_cast<const uint4*>(A + arow + k);
-        if (K - k < 8) {
-          uint32_t w[4] = {av.x, av.y, av.z, av.w};
-          for (int e = K - k; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          av = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-      const bf16x8_t_s af = __builtin_bit_cast(bf16x8_t_s, av);
+    for (int sb = s0; sb < s1; sb += U) {
+      uint4 av[U];
+      uint4 bv[U][NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint4 bv = make_uint4(0, 0, 0, 0);
-        if (bok[nb] && k < K) {
-          bv = *reinterpret_cast<const uint4*>(brow[nb] + k);
-          if (K - k < 8) {
-            uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
-            for (int e = K - k; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-            bv = make_uint4(w[0], w[1], w[2], w[3]);
-          }
+      for (int u = 0; u < U; ++u) {
+        const int k = (sb + u) * 32 + 8 * (lane >> 4);
+        const int kc = (sb + u < s1 && k < K) ? k : 0;
+        av[u] = *reinterpret_cast<const uint4*>(A + arow + kc);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bv[u][nb] = *reinterpret_cast<const uint4*>(brow[nb] + kc);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = (sb + u) * 32 + 8 * (lane >> 4);
+        const int valid = sb + u < s1 ? (K - k < 0 ? 0 : (K - k > 8 ? 8 : K - k)) : 0;
+        if (valid < 8) {
+          uint32_t w[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+          for (int e = valid; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          av[u] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t_s, bv),
-                                                          acc[nb], 0, 0, 0);
+        const bf16x8_t_s af = __builtin_bit_cast(bf16x8_t_s, av[u]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          uint4 bq = bv[u][nb];
+          if (!bok[nb]) bq = make_uint4(0, 0, 0, 0);
+          else if (valid < 8) {
+            uint32_t w[4] = {bq.x, bq.y, bq.z, bq.w};
+            for (int e = valid; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            bq = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t_s, bq),
+                                                            acc[nb], 0, 0, 0);
+        }
       }
     }
   } else {
@@ -452,6 +463,121 @@ colred_kernel(const ColredArgs a) {
   }
 }
 
+// MFMA form of the same reduction for bf16 operands.  A workgroup owns 256
+// columns of P and a chunk of CRM_CHUNK rows; it walks the chunk in slices of
+// 64 rows: the P slice is transposed into LDS as [column][row] (K-contiguous
+// for the matrix cores), Z is converted to bf16 and stored as [q][row], and
+// 16x16x32 MFMAs accumulate C[column][q].  Each wave owns 64 columns.
+constexpr int CRM_CHUNK = 256;
+constexpr int CRM_SLICE = 64;
+constexpr int CRM_COLS = 256;
+
+template <int RM>
+__global__ void __launch_bounds__(256)
+colred_mfma_kernel(const ColredArgs a) {
+  constexpr int LD = CRM_SLICE + 8;   // padded LDS row (144 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[CRM_COLS * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Zs[RM * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int g = 0, ch = blockIdx.y;
+  if (a.mode == 1) {
+    while (g + 1 < a.ngroups && a.chunk_start[g + 1] <= (int)blockIdx.y) ++g;
+    g = __builtin_amdgcn_readfirstlane(g);
+    ch = blockIdx.y - a.chunk_start[g];
+  }
+  const bool is_out = a.mode == 1 && g == a.st.nseq;
+  const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
+  const int N = a.mode == 0 ? a.N : (is_out ? a.n_out : a.kidx);
+  const int n0 = blockIdx.x * CRM_COLS;
+  if (n0 >= N) return;
+  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.P);
+  const int ctx_pre_g = (a.mode == 1 && !is_out) ? a.st.ctx_pre[g] : 0;
+  // P slice loader: rows (tid&7)*8 .. +8, columns (tid>>3)*8 .. +8
+  const int pr0 = (tid & 7) * 8;
+  const int pc = (tid >> 3) * 8;
+  const bool c_ok = n0 + pc < N;                     // N is a multiple of 8
+  const int pcol = c_ok ? n0 + pc : 0;
+  f32x4_t acc[4][RM / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RM / 16; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int r_begin = ch * CRM_CHUNK;
+  const int r_end = min(m_rows, r_begin + CRM_CHUNK);
+  for (int r0 = r_begin; r0 < r_end; r0 += CRM_SLICE) {
+    // global -> registers
+    uint4 pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int r = r0 + pr0 + i;
+      const bool ok = r < r_end && c_ok;
+      if (r >= m_rows) r = m_rows - 1;
+      long long prow;
+      if (a.mode == 0) prow = (long long)r * a.ldp;
+      else prow = is_out ? a.p_out_off + (long long)r * a.ldp_out : (long long)(ctx_pre_g + r) * a.ldp;
+      pv[i] = *reinterpret_cast<const uint4*>(P + prow + pcol);
+      if (!ok) pv[i] = make_uint4(0, 0, 0, 0);
+    }
+    // Z slice: thread -> (row zt, q range)
+    float zv[RM / 4];
+    const int zt = tid & 63;
+    const int zq0 = (tid >> 6) * (RM / 4);
+    {
+      const int r = r0 + zt;
+      const bool ok = r < r_end;
+      const long long tok = ok ? (a.mode == 0 ? r : group_token(a.st, g, r)) : 0;
+#pragma unroll
+      for (int q = 0; q < RM / 4; ++q)
+        zv[q] = (ok && zq0 + q < a.R) ? a.Z[tok * a.ldz + a.zc0 + zq0 + q] : 0.f;
+    }
+    __syncthreads();   // previous slice fully consumed
+    // transpose P: 8 rows x 8 columns -> 8 columns x 8 rows
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&pv[2 * p]);
+        const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&pv[2 * p + 1]);
+        const uint32_t lo = (c0[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        const uint32_t hi = (c1[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        w[p] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(&Ps[(pc + j) * LD + pr0]) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < RM / 4; ++q) Zs[(zq0 + q) * LD + zt] = f2bf(zv[q]);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < CRM_SLICE / 32; ++ks) {
+      bf16x8_t_s bfr[RM / 16];
+#pragma unroll
+      for (int j = 0; j < RM / 16; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t_s*>(&Zs[(16 * j + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t_s af = *reinterpret_cast<const bf16x8_t_s*>(
+            &Ps[(64 * wave + 16 * i + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+        for (int j = 0; j < RM / 16; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // C[column][q]: element e of block (i, j) is column 16 i + 4 (lane>>4) + e, q = 16 j + lane%16
+  float* dst = a.part + (a.mode == 1 ? a.part_off[g] : 0) + (long long)ch * N * RM;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = n0 + 64 * wave + 16 * i + 4 * (lane >> 4) + e;
+      if (n >= N) continue;
+#pragma unroll
+      for (int j = 0; j < RM / 16; ++j) dst[(long long)n * RM + 16 * j + (lane & 15)] = acc[i][j][e];
+    }
+}
+
 // Dense finish: out[n, q] (or out[q, n] when transposed) = scale * sum_chunks part.
 // Two outputs may take column ranges [0, r1) and [off2, off2 + r2) of the part.
 struct FinishArgs {
@@ -517,6 +643,65 @@ static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, i
   if (i >= (long long)nseq * k) return;
   const int g = (int)(i / k), p = (int)(i % k);
   inv[(long long)g * Nfull + idx[i]] = p;
+}
+
+// ===========================================================================
+// Packing of the LoRA operands in one launch.  Each job writes a whole
+// destination region (padding included):
+//   type 0:  dst[r][c] = src block placed at (row_off, col_off), 0 elsewhere;
+//            the block is src[r][c] or, transposed, src[c][r]
+//   type 1:  per context group g: dst[g][q][p] = src(q, idx[g][p]) for q < src_rows,
+//            p < k, 0 elsewhere; src(q, c) = src[q*lds + c] or, transposed, src[c*lds + q]
+// ===========================================================================
+constexpr int PK_MAXJOBS = 10;
+
+struct PackJob {
+  int type;
+  void* dst; long long ldd, gstride;
+  int rows, cols, row_off, col_off;
+  const void* src; long long lds;
+  int src_rows, src_cols, tr;
+  const int* idx; int k, nseq;
+};
+
+struct PackArgs {
+  int njobs;
+  long long start[PK_MAXJOBS + 1];
+  PackJob job[PK_MAXJOBS];
+};
+
+template <typename T>
+__global__ void pack_kernel(const PackArgs a) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.start[a.njobs]) return;
+  int j = 0;
+  while (j + 1 < a.njobs && a.start[j + 1] <= i) ++j;
+  const PackJob& b = a.job[j];
+  const long long e = i - a.start[j];
+  const T* src = reinterpret_cast<const T*>(b.src);
+  T* dst = reinterpret_cast<T*>(b.dst);
+  if (b.type == 0) {
+    const int r = (int)(e / b.cols), c = (int)(e % b.cols);
+    const int sr = r - b.row_off, sc = c - b.col_off;
+    T v;
+    if (sr >= 0 && sr < b.src_rows && sc >= 0 && sc < b.src_cols)
+      v = b.tr ? src[(long long)sc * b.lds + sr] : src[(long long)sr * b.lds + sc];
+    else
+      stv<T>(&v, 0, 0.f);
+    dst[(long long)r * b.ldd + c] = v;
+  } else {
+    const int p = (int)(e % b.cols);
+    const int q = (int)((e / b.cols) % b.rows);
+    const int g = (int)(e / ((long long)b.cols * b.rows));
+    T v;
+    if (q < b.src_rows && p < b.k) {
+      const int c = b.idx[(long long)g * b.k + p];
+      v = b.tr ? src[(long long)c * b.lds + q] : src[(long long)q * b.lds + c];
+    } else {
+      stv<T>(&v, 0, 0.f);
+    }
+    dst[g * b.gstride + (long long)q * b.ldd + p] = v;
+  }
 }
 
 // ===========================================================================

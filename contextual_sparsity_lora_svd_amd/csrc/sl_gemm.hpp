@@ -16,11 +16,14 @@
 // operand is the low-rank activation z and whose B operand the other factor,
 // so LoRA runs inside the same tiles as the frozen weight.
 //
-// Tile 128 x 256 x BK, 256 threads = 4 waves in a 2 x 2 grid, each wave a
-// 64 x 128 block of 32x32 MFMA accumulators.  bf16: v_mfma_f32_32x32x16_bf16,
-// BK = 64.  fp32: v_mfma_f32_32x32x2_f32 (true fp32), BK = 32.  Global loads of
-// tile k+1 are in flight in registers while tile k is consumed from LDS.
+// Tile BM x 256 x BK (BM = 128 or 256), 256 threads = 4 waves in a 2 x 2 grid,
+// each wave a (BM/2) x 128 block of 32x32 MFMA accumulators.  bf16:
+// v_mfma_f32_32x32x16_bf16, BK = 64.  fp32: v_mfma_f32_32x32x2_f32 (true fp32),
+// BK = 32.  The global loads of the next K-tile are in flight in registers
+// while the current tile is consumed from LDS.
 #pragma once
+
+#include <type_traits>
 
 #include "sl_common.hpp"
 
@@ -29,7 +32,10 @@ namespace sl {
 enum { MODE_NG = 0, MODE_KG = 1 };
 enum { EPI_SWIGLU = 0, EPI_DSWIGLU = 1, EPI_TOKEN = 2, EPI_SCATTER = 3 };
 
-constexpr int G_BM = 128;
+#ifndef SL_GEMM_BM
+#define SL_GEMM_BM 128      // tile rows (128 or 256)
+#endif
+constexpr int G_BM = SL_GEMM_BM;
 constexpr int G_BN = 256;
 constexpr int G_THREADS = 256;
 constexpr int G_MAXSEG = 4;
@@ -43,7 +49,7 @@ struct GSeg {
   const void* B;       // B operand (gate half in dual mode)
   const void* B2;      // dual mode: up half
   long long ldb;
-  int b_gather;        // 1: B row = a channel number; 0: its position
+  int b_gather;        // KG: 1: B row = a channel number; 0: its position.  NG: always gathered
   int K;               // > 0 fixed length; <= 0: the segment's channel count
   // KG segments with K <= 0: channel set of the segment (context group g uses
   // idx + g*kidx, kidx channels; the output group uses all n_out channels).
@@ -109,11 +115,66 @@ __device__ inline void mask_chunk(Chunk& c, int valid) {
   }
 }
 
+// Store / load N consecutive elements (N a multiple of 8) with 16-byte
+// accesses; only the first `valid` (clamped to [0, N]) are touched.  The
+// address must be 16-byte aligned when all N are valid.
+template <typename T, int N>
+__device__ inline void store_row(T* p, const float* v, int valid) {
+  if (valid >= N) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < N / 8; ++q) {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          w[t] = (uint32_t)f2bf(v[8 * q + 2 * t]) | ((uint32_t)f2bf(v[8 * q + 2 * t + 1]) << 16);
+        *reinterpret_cast<uint4*>(p + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q)
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + 4 * q) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (j < valid) stv<T>(p, j, v[j]);
+  }
+}
+
+template <typename T, int N>
+__device__ inline void load_row(const T* p, float* v, int valid) {
+  if (valid >= N) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < N / 8; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p + 8 * q);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[8 * q + 2 * t] = bf2f((uint16_t)(w[t] & 0xFFFFu));
+          v[8 * q + 2 * t + 1] = bf2f((uint16_t)(w[t] >> 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + 4 * q);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = j < valid ? ldv<T>(p, j) : 0.f;
+  }
+}
+
 __device__ inline float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 __device__ inline float sigmoid_exact(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-template <typename T, int MODE, int EPI, bool DUAL>
-__global__ void __launch_bounds__(G_THREADS, 2)
+template <typename T, int MODE, int EPI, bool DUAL, int BM>
+__global__ void __launch_bounds__(G_THREADS, BM == 128 ? 2 : 1)
 gather_gemm_kernel(const GemmArgs args) {
   constexpr int VEC = GTraits<T>::VEC;
   constexpr int BK = GTraits<T>::BK;
@@ -121,9 +182,16 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr int LDS_LD = BK + VEC;          // padded row: 144 bytes
   constexpr int BNC = DUAL ? G_BN / 2 : G_BN; // output columns (channels) per tile
   constexpr int KR = BK / 8;                // KG: k-rows per thread
+  constexpr int MB = BM / 64;               // 32-row accumulator blocks per wave
+  constexpr int ACH = BM / 32;              // A chunks per thread
+  constexpr int WM = BM / 2;                // wave tile rows
 
-  __shared__ __attribute__((aligned(16))) T As[G_BM * LDS_LD];
-  __shared__ __attribute__((aligned(16))) T Bs[G_BN * LDS_LD];
+  constexpr int EP_LD = 64 + 4;             // epilogue staging row (floats)
+  constexpr int SMEM = (BM + G_BN) * LDS_LD * (int)sizeof(T);
+  static_assert(4 * 32 * EP_LD * 4 <= SMEM, "epilogue staging must fit in the tile buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  T* As = reinterpret_cast<T*>(smem);
+  T* Bs = As + BM * LDS_LD;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,14 +209,14 @@ gather_gemm_kernel(const GemmArgs args) {
   const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];
   const int nch = is_out ? args.n_out : args.kidx;
   const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
-  const int ntm = (m_rows + G_BM - 1) / G_BM;
+  const int ntm = (m_rows + BM - 1) / BM;
   int ntn, nks;
   if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = 1; }
   else { ntn = (args.N + G_BN - 1) / G_BN; nks = is_out ? args.ksplit_out : 1; }
   const int mt = t_in % ntm;
   const int nt = (t_in / ntm) % ntn;
   const int ks = t_in / (ntm * ntn);
-  const int m0 = mt * G_BM;
+  const int m0 = mt * BM;
   const int n0 = nt * BNC;
 
   // ---- K-tile range (all segments, then this split's share) ---------------
@@ -160,8 +228,10 @@ gather_gemm_kernel(const GemmArgs args) {
   for (int s = 0; s < args.nseg; ++s) total_kt += (seg_len(s) + BK - 1) / BK;
   const int kt_begin = (int)((long long)total_kt * ks / nks);
   const int kt_end = (int)((long long)total_kt * (ks + 1) / nks);
+  const int nkt = kt_end - kt_begin;
+
   // ---- per-thread load geometry ------------------------------------------
-  // A: 4 chunks per thread, rows (tid>>3) + 32 i, chunk column tid & 7.
+  // A: ACH chunks per thread, rows (tid>>3) + 32 i, chunk column tid & 7.
   // B (NG): 8 chunks per thread, rows (tid>>3) + 32 i; in dual mode rows
   //         [0, BNC) come from the gate weight and [BNC, 2 BNC) from the up weight.
   // B (KG): k-rows (tid&7)*KR .. +KR, n-columns (tid>>3)*8 .. +8.
@@ -171,22 +241,12 @@ gather_gemm_kernel(const GemmArgs args) {
   // offsets live in registers and change only at segment boundaries.
   const int a_row0 = tid >> 3;
   const int a_kc = tid & 7;
-  int a_r[4], a_t[4];   // group row and token row of each A row this thread loads
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = m0 + a_row0 + 32 * i;
-    if (r >= m_rows) r = m_rows - 1;    // rows past the group are computed and dropped
-    a_r[i] = r;
-    a_t[i] = group_token(args.st, g, r);
-  }
-  int b_pos[8];         // NG: channel position of each B row this thread loads
-  int b_ch[8];          // NG: its channel number
+  int b_ch[8];          // NG: channel number (B row) of each B row this thread loads
   if (MODE == MODE_NG) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int c = n0 + a_row0 + ((32 * i) % BNC);
       if (c >= nch) c = nch - 1;
-      b_pos[i] = c;
       b_ch[i] = gidx ? gidx[c] : c;
     }
   }
@@ -195,21 +255,24 @@ gather_gemm_kernel(const GemmArgs args) {
   const bool kg_nok = (n0 + kg_n) < args.N;      // N is a multiple of 8
   const int kg_c0 = kg_nok ? n0 + kg_n : 0;
 
-  Chunk ra[4];
-  Chunk rb[8];
-  int va = VEC;          // valid elements of this thread's A / N-gather B chunks
-  int kg_rv = KR;        // K-gather: valid k-rows of this thread's B rows
-  int kg_row[KR];        // K-gather: B rows of the tile being loaded
-  int kg_row_next[KR] = {};  // ... and of the tile after it (indices fetched a tile ahead)
+  constexpr int PF = 1;  // register sets
+  Chunk ra[PF][ACH];
+  Chunk rb[PF][8];
+  int va[PF];            // valid elements of the A / N-gather B chunks of each set
+  int kg_rv[PF];         // K-gather: valid k-rows of each set
+  int kgr[2][KR];        // K-gather: B rows of the next two tiles to load
+#pragma unroll
+  for (int p = 0; p < PF; ++p) { va[p] = VEC; kg_rv[p] = KR; }
 
-  // current segment state (uniform scalars + per-thread offsets)
+  // loader cursor: uniform scalars + per-thread element offsets (32-bit; the
+  // host checks that every operand has fewer than 2^31 elements)
   int cur_s = 0, cur_kk = 0, cur_K = 0, cur_nkt = 0;
   const T* a_base = nullptr;
   const T* b_base = nullptr;
   const T* b2_base = nullptr;
-  long long a_off[4];
-  long long b_off[8];
-  long long cur_ldb = 0;
+  unsigned a_off[ACH];
+  unsigned b_off[8];
+  int cur_ldb = 0;
 
   auto enter_seg = [&](int s) {
     s = __builtin_amdgcn_readfirstlane(s);
@@ -220,16 +283,18 @@ gather_gemm_kernel(const GemmArgs args) {
     a_base = reinterpret_cast<const T*>(sg.A);
     b_base = reinterpret_cast<const T*>(sg.B);
     b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : sg.B);
-    cur_ldb = sg.ldb;
+    cur_ldb = (int)sg.ldb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (sg.a_tok) a_off[i] = (long long)a_t[i] * sg.lda;
-      else a_off[i] = is_out ? sg.a_out_off + (long long)a_r[i] * sg.lda_out
-                             : (long long)(ctx_pre_g + a_r[i]) * sg.lda;
+    for (int i = 0; i < ACH; ++i) {
+      int r = m0 + a_row0 + 32 * i;
+      if (r >= m_rows) r = m_rows - 1;    // rows past the group are computed and dropped
+      if (sg.a_tok) a_off[i] = (unsigned)group_token(args.st, g, r) * (unsigned)sg.lda;
+      else a_off[i] = is_out ? (unsigned)sg.a_out_off + (unsigned)r * (unsigned)sg.lda_out
+                             : (unsigned)(ctx_pre_g + r) * (unsigned)sg.lda;
     }
     if (MODE == MODE_NG) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b_off[i] = (long long)(sg.b_gather ? b_ch[i] : b_pos[i]) * sg.ldb;
+      for (int i = 0; i < 8; ++i) b_off[i] = (unsigned)b_ch[i] * (unsigned)sg.ldb;
     }
   };
 
@@ -246,81 +311,86 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   };
 
-  // position the segment cursor on K-tile kt_begin
-  if (kt_begin < kt_end) {
+  // position the cursor on K-tile kt_begin
+  if (nkt > 0) {
     int s = 0, kk = kt_begin;
     for (;;) {
-      const int nkt = (seg_len(s) + BK - 1) / BK;
-      if (s + 1 >= args.nseg || kk < nkt) break;
-      kk -= nkt;
+      const int n = (seg_len(s) + BK - 1) / BK;
+      if (s + 1 >= args.nseg || kk < n) break;
+      kk -= n;
       ++s;
     }
     enter_seg(s);
     cur_kk = __builtin_amdgcn_readfirstlane(kk);
-    if (MODE == MODE_KG) kg_rows(cur_s, cur_kk, kg_row);
+    if (MODE == MODE_KG) kg_rows(cur_s, cur_kk, kgr[0]);
   }
 
-  // issue the global loads of the next K-tile into registers and advance the cursor
-  auto load_tile = [&](bool more) {
+  // Issue the global loads of the next K-tile (the i-th of this tile's range)
+  // into register set P.  K-gather: the rows of tile i are in kgr[i % 2]; the
+  // rows of tile i + 1 are fetched first, so a later wait for them does not
+  // drain the data loads issued after them.
+  auto load_tile = [&](auto Pc, auto Qc, bool more) {
+    constexpr int P = decltype(Pc)::value;   // register set
+    constexpr int Q = decltype(Qc)::value;   // parity of the tile: kgr[Q] holds its rows
     while (cur_kk >= cur_nkt) {   // segment boundary (segments may be empty)
       enter_seg(cur_s + 1);
       cur_kk = 0;
     }
+    if (MODE == MODE_KG && more) {   // rows of the following tile
+      int s = cur_s, kk = cur_kk + 1;
+      while (kk >= (seg_len(s) + BK - 1) / BK && s + 1 < args.nseg) { kk = 0; ++s; }
+      kg_rows(s, kk, kgr[Q ^ 1]);
+    }
     const int k0 = cur_kk * BK;
     const int kcol = k0 + a_kc * VEC;
-    va = cur_K - kcol < 0 ? 0 : (cur_K - kcol > VEC ? VEC : cur_K - kcol);
+    va[P] = cur_K - kcol < 0 ? 0 : (cur_K - kcol > VEC ? VEC : cur_K - kcol);
     const int kc = kcol < cur_K ? kcol : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = load_chunk(a_base + a_off[i] + kc);
+    for (int i = 0; i < ACH; ++i) ra[P][i] = load_chunk(a_base + (a_off[i] + kc));
     if (MODE == MODE_NG) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        rb[i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + b_off[i] + kc);
+        rb[P][i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + (b_off[i] + kc));
     } else {
       const int kr = cur_K - (k0 + kg_kr0);
-      kg_rv = kr < 0 ? 0 : (kr > KR ? KR : kr);
+      kg_rv[P] = kr < 0 ? 0 : (kr > KR ? KR : kr);
 #pragma unroll
       for (int i = 0; i < KR; ++i)
 #pragma unroll
         for (int h = 0; h < 8 / VEC; ++h)
-          rb[i * (8 / VEC) + h] = load_chunk(b_base + (long long)kg_row[i] * cur_ldb + kg_c0 + h * VEC);
-      if (more) {   // indices of the following tile
-        int s = cur_s, kk = cur_kk + 1;
-        while (kk >= (seg_len(s) + BK - 1) / BK && s + 1 < args.nseg) { kk = 0; ++s; }
-        kg_rows(s, kk, kg_row_next);
-      }
+          rb[P][i * (8 / VEC) + h] =
+              load_chunk(b_base + ((unsigned)kgr[Q][i] * (unsigned)cur_ldb + kg_c0 + h * VEC));
     }
     ++cur_kk;
   };
 
-  auto store_tile = [&]() {
-    if (va < VEC) {
+  auto store_tile = [&](auto Pc) {
+    constexpr int P = decltype(Pc)::value;
+    if (va[P] < VEC) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mask_chunk<T>(ra[i], va);
+      for (int i = 0; i < ACH; ++i) mask_chunk<T>(ra[P][i], va[P]);
       if (MODE == MODE_NG) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mask_chunk<T>(rb[i], va);
+        for (int i = 0; i < 8; ++i) mask_chunk<T>(rb[P][i], va[P]);
       }
     }
     if (MODE == MODE_KG) {
 #pragma unroll
       for (int i = 0; i < KR; ++i)
-        if (i >= kg_rv || !kg_nok) {
+        if (i >= kg_rv[P] || !kg_nok) {
 #pragma unroll
-          for (int h = 0; h < 8 / VEC; ++h) rb[i * (8 / VEC) + h] = zero_chunk();
+          for (int h = 0; h < 8 / VEC; ++h) rb[P][i * (8 / VEC) + h] = zero_chunk();
         }
-#pragma unroll
-      for (int i = 0; i < KR; ++i) kg_row[i] = kg_row_next[i];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < ACH; ++i)
       *reinterpret_cast<uint4*>(&As[(a_row0 + 32 * i) * LDS_LD + a_kc * VEC]) =
-          make_uint4(ra[i].w[0], ra[i].w[1], ra[i].w[2], ra[i].w[3]);
+          make_uint4(ra[P][i].w[0], ra[P][i].w[1], ra[P][i].w[2], ra[P][i].w[3]);
     if (MODE == MODE_NG) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *reinterpret_cast<uint4*>(&Bs[(a_row0 + 32 * i) * LDS_LD + a_kc * VEC]) =
-            make_uint4(rb[i].w[0], rb[i].w[1], rb[i].w[2], rb[i].w[3]);
+            make_uint4(rb[P][i].w[0], rb[P][i].w[1], rb[P][i].w[2], rb[P][i].w[3]);
     } else {
       // transpose KR k-rows x 8 n-values into 8 n-rows x KR k-values
 #pragma unroll
@@ -329,15 +399,15 @@ gather_gemm_kernel(const GemmArgs args) {
         if (sizeof(T) == 2) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const Chunk& c0 = rb[2 * p];
-            const Chunk& c1 = rb[2 * p + 1];
+            const Chunk& c0 = rb[P][2 * p];
+            const Chunk& c1 = rb[P][2 * p + 1];
             const uint32_t lo = (c0.w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
             const uint32_t hi = (c1.w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
             w[p] = lo | (hi << 16);
           }
         } else {
 #pragma unroll
-          for (int p = 0; p < 4; ++p) w[p] = rb[p * 2 + (j >> 2)].w[j & 3];
+          for (int p = 0; p < 4; ++p) w[p] = rb[P][p * 2 + (j >> 2)].w[j & 3];
         }
         *reinterpret_cast<uint4*>(&Bs[(kg_n + j) * LDS_LD + kg_kr0]) =
             make_uint4(w[0], w[1], w[2], w[3]);
@@ -345,9 +415,9 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[MB][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -359,122 +429,160 @@ gather_gemm_kernel(const GemmArgs args) {
     return 128 * wn + 32 * nb;
   };
 
-  if (kt_begin < kt_end) {
-    load_tile(kt_begin + 1 < kt_end);
-    store_tile();
+  auto compute = [&]() {
+#pragma unroll
+    for (int kstep = 0; kstep < BK / KSTEP; ++kstep) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_t af[MB], bfr[4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          af[mb] = *reinterpret_cast<const bf16x8_t*>(
+              &As[(WM * wm + 32 * mb + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          bfr[nb] = *reinterpret_cast<const bf16x8_t*>(
+              &Bs[(brow(nb) + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      } else {
+        float af[MB], bfr[4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          af[mb] = reinterpret_cast<const float*>(As)[(WM * wm + 32 * mb + (lane & 31)) * LDS_LD +
+                                                       kstep * 2 + (lane >> 5)];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          bfr[nb] = reinterpret_cast<const float*>(Bs)[(brow(nb) + (lane & 31)) * LDS_LD +
+                                                        kstep * 2 + (lane >> 5)];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // One register set: the loads of tile i+1 are in flight while tile i is
+  // consumed from LDS.  (A second register set for a deeper prefetch needs an
+  // unrolled loop body whose register pressure spills the accumulators.)
+  using I0 = std::integral_constant<int, 0>;
+  if (nkt > 0) {
+    load_tile(I0{}, I0{}, nkt > 1);
+    store_tile(I0{});
+#pragma unroll
+    for (int j = 0; j < KR; ++j) kgr[0][j] = kgr[1][j];
     __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const bool more = kt + 1 < kt_end;
-      if (more) load_tile(kt + 2 < kt_end);
-#pragma unroll
-      for (int kstep = 0; kstep < BK / KSTEP; ++kstep) {
-        if constexpr (sizeof(T) == 2) {
-          bf16x8_t af[2], bfr[4];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            af[mb] = *reinterpret_cast<const bf16x8_t*>(
-                &As[(64 * wm + 32 * mb + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            bfr[nb] = *reinterpret_cast<const bf16x8_t*>(
-                &Bs[(brow(nb) + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-        } else {
-          float af[2], bfr[4];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            af[mb] = reinterpret_cast<const float*>(As)[(64 * wm + 32 * mb + (lane & 31)) * LDS_LD +
-                                                         kstep * 2 + (lane >> 5)];
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            bfr[nb] = reinterpret_cast<const float*>(Bs)[(brow(nb) + (lane & 31)) * LDS_LD +
-                                                          kstep * 2 + (lane >> 5)];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < nkt; ++i) {
+      if (i + 1 < nkt) load_tile(I0{}, I0{}, i + 2 < nkt);
+      compute();
       __syncthreads();
-      if (more) {
-        store_tile();
-        __syncthreads();
-      }
+      if (i + 1 >= nkt) break;
+      store_tile(I0{});
+#pragma unroll
+      for (int j = 0; j < KR; ++j) kgr[0][j] = kgr[1][j];
+      __syncthreads();
     }
   }
 
   // ---- epilogue -----------------------------------------------------------
-  // accumulator element e of block (mb, nb): row 8*(e/4) + 4*(lane/32) + e%4,
-  // column lane%32 of the block.
+  // The accumulators go through LDS: per 32-row block and pair of 32-column
+  // blocks, each wave writes a 32 x 64 fp32 tile (accumulator element e of a
+  // block sits at row 8*(e/4) + 4*(lane/32) + e%4, column lane%32), then every
+  // lane takes 32 consecutive columns of one row (half a row per lane pair
+  // in dual mode) and applies the element-wise step with 16-byte accesses.
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EP_LD;
   const long long ldc = is_out ? args.ldc_out : args.ldc_ctx;
-  const long long cbase = is_out ? args.c_out_off : (long long)args.st.ctx_pre[g] * args.ldc_ctx;
+  const long long cbase = is_out ? args.c_out_off : (long long)ctx_pre_g * args.ldc_ctx;
+  const int er = lane >> 1;            // row of the 32-row block this lane finishes
+  const int ec = (lane & 1) * 32;      // first of its 32 staged columns
+  if (nkt <= 0) __syncthreads();       // (the main loop ends with a barrier otherwise)
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = m0 + 64 * wm + 32 * mb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (r >= m_rows) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
+    for (int hp = 0; hp < 2; ++hp) {
+      // blocks staged in this pass: dual -> gate hp and up hp; else nb = 2 hp, 2 hp + 1
+      const int nb0 = DUAL ? hp : 2 * hp;
+      const int nb1 = DUAL ? hp + 2 : 2 * hp + 1;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int c = n0 + 64 * wn + 32 * nb + (lane & 31);
-          if (c >= nch) continue;
-          const float gv = acc[mb][nb][e];
-          const float uv = acc[mb][nb + 2][e];
-          const float sg = (sizeof(T) == 4) ? sigmoid_exact(gv) : sigmoidf_(gv);
-          const long long o = cbase + (long long)r * ldc + c;
-          stv<T>(reinterpret_cast<T*>(args.o0), o, gv);
-          stv<T>(reinterpret_cast<T*>(args.o1), o, uv);
-          stv<T>(reinterpret_cast<T*>(args.o2), o, gv * sg * uv);
-        }
-      } else if constexpr (EPI == EPI_DSWIGLU) {
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        ep[rr * EP_LD + (lane & 31)] = acc[mb][nb0][e];
+        ep[rr * EP_LD + 32 + (lane & 31)] = acc[mb][nb1][e];
+      }
+      __syncthreads();
+      const int r = m0 + WM * wm + 32 * mb + er;
+      const float* src = ep + er * EP_LD;
+      if (r < m_rows) {
+        // 8 columns at a time keeps the temporaries small while later
+        // accumulator blocks are still live
+#pragma unroll 1
+        for (int q = 0; q < (DUAL ? 2 : 4); ++q) {
+          if constexpr (EPI == EPI_SWIGLU) {
+            // lane pair: even lane channels 0..15, odd lane 16..31 of the 32-channel block
+            const int cl = (lane & 1) * 16 + 8 * q;
+            const int c = n0 + 64 * wn + 32 * hp + cl;
+            const long long o = cbase + (long long)r * ldc + c;
+            float gv[8], uv[8], hv[8];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = n0 + 128 * wn + 32 * nb + (lane & 31);
-          if (c >= nch) continue;
-          const long long o = cbase + (long long)r * ldc + c;
-          const float dh = acc[mb][nb][e];
-          const float gv = ldv<T>(reinterpret_cast<const T*>(args.i0), o);
-          const float uv = ldv<T>(reinterpret_cast<const T*>(args.i1), o);
-          const float sg = (sizeof(T) == 4) ? sigmoid_exact(gv) : sigmoidf_(gv);
-          stv<T>(reinterpret_cast<T*>(args.o0), o, dh * uv * sg * (1.0f + gv * (1.0f - sg)));
-          stv<T>(reinterpret_cast<T*>(args.o1), o, dh * gv * sg);
-        }
-      } else if constexpr (EPI == EPI_TOKEN) {
-        const long long tok = group_token(args.st, g, r);
+            for (int j = 0; j < 8; ++j) {
+              gv[j] = src[cl + j];
+              uv[j] = src[32 + cl + j];
+              const float sg = (sizeof(T) == 4) ? sigmoid_exact(gv[j]) : sigmoidf_(gv[j]);
+              hv[j] = gv[j] * sg * uv[j];
+            }
+            store_row<T, 8>(reinterpret_cast<T*>(args.o0) + o, gv, nch - c);
+            store_row<T, 8>(reinterpret_cast<T*>(args.o1) + o, uv, nch - c);
+            store_row<T, 8>(reinterpret_cast<T*>(args.o2) + o, hv, nch - c);
+          } else {
+            const int cl = ec + 8 * q;
+            const int c = n0 + 128 * wn + 64 * hp + cl;
+            float v[8];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = n0 + 128 * wn + 32 * nb + (lane & 31);
-          if (c >= args.N) continue;
-          if (is_out && nks > 1)
-            args.part[((long long)ks * args.st.T_out + r) * args.N + c] = acc[mb][nb][e];
-          else
-            stv<T>(reinterpret_cast<T*>(args.o0), tok * args.ldo + c, acc[mb][nb][e]);
-        }
-      } else {  // EPI_SCATTER: column = the channel number
-        const long long tok = group_token(args.st, g, r);
+            for (int j = 0; j < 8; ++j) v[j] = src[cl + j];
+            if constexpr (EPI == EPI_DSWIGLU) {
+              const long long o = cbase + (long long)r * ldc + c;
+              float gv[8], uv[8], dg[8], du[8];
+              load_row<T, 8>(reinterpret_cast<const T*>(args.i0) + o, gv, nch - c);
+              load_row<T, 8>(reinterpret_cast<const T*>(args.i1) + o, uv, nch - c);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = n0 + 128 * wn + 32 * nb + (lane & 31);
-          if (c >= nch) continue;
-          const int col = gidx ? gidx[c] : c;
-          stv<T>(reinterpret_cast<T*>(args.o0), tok * args.ldo + col, acc[mb][nb][e]);
+              for (int j = 0; j < 8; ++j) {
+                const float sg = (sizeof(T) == 4) ? sigmoid_exact(gv[j]) : sigmoidf_(gv[j]);
+                dg[j] = v[j] * uv[j] * sg * (1.0f + gv[j] * (1.0f - sg));
+                du[j] = v[j] * gv[j] * sg;
+              }
+              store_row<T, 8>(reinterpret_cast<T*>(args.o0) + o, dg, nch - c);
+              store_row<T, 8>(reinterpret_cast<T*>(args.o1) + o, du, nch - c);
+            } else if constexpr (EPI == EPI_TOKEN) {
+              if (is_out && nks > 1)
+                store_row<float, 8>(args.part + ((long long)ks * args.st.T_out + r) * args.N + c, v,
+                                    args.N - c);
+              else
+                store_row<T, 8>(reinterpret_cast<T*>(args.o0) +
+                                    (long long)group_token(args.st, g, r) * args.ldo + c,
+                                v, args.N - c);
+            } else {  // EPI_SCATTER: column = the channel number
+              T* out = reinterpret_cast<T*>(args.o0) + (long long)group_token(args.st, g, r) * args.ldo;
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (c + j < nch) stv<T>(out, gidx ? gidx[c + j] : c + j, v[j]);
+            }
+          }
         }
       }
+      __syncthreads();
     }
   }
 }
 
-// Host side: count tiles per group and launch.
 bool timer_on();
 void timer_begin(int slot, hipStream_t s);
 void timer_end(int slot, hipStream_t s);
 
+// Host side: count tiles per group and launch.
 template <typename T, int MODE, int EPI, bool DUAL>
 hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
@@ -495,8 +603,8 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   a.tile_start[a.ngroups] = total;
   if (total == 0) return hipSuccess;
   timer_begin(timer_slot, stream);
-  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL>), dim3(total), dim3(G_THREADS), 0,
-                     stream, a);
+  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM>), dim3(total),
+                     dim3(G_THREADS), 0, stream, a);
   const hipError_t e = hipGetLastError();
   timer_end(timer_slot, stream);
   return e;

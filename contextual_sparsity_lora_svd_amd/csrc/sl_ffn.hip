@@ -30,7 +30,7 @@ struct FfnGeom {
   int ks_down, ks_dx, RM1, RM2, chunk;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
-      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, ws_bytes;
+      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, ws_bytes;
 };
 
 int choose_ksplit(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -107,6 +107,7 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   if (cr2 > cr) cr = cr2;
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
+  g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
   g.ws_bytes = w.off;
   return SL_OK;
 }
@@ -149,6 +150,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(Pu, 2 * rp, F, 2 * rp, w->Bu, r, F, r, 0, 0, rp);
     pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
     pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
+    pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
     if ((rc = pk.launch<T>(strm))) return rc;
   }
 
@@ -206,6 +208,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_down;
     a.o0 = Y; a.ldo = D;
     a.part = part;
+    a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DOWN_FWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_down, D, Y, D, strm))) return rc;
   }
@@ -253,6 +256,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.gather(Bug, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bu, r, r, 1, idx, g.k, st.nseq);
     pk.copy(BgTo, F, r, F, w->Bg, r, r, F, 1);
     pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
+    pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
     if ((rc = pk.launch<T>(strm))) return rc;
   }
   if ((rc = inverse_maps(idx, g.k, st.nseq, F, inv, strm))) return rc;
@@ -312,6 +316,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_dx;
     a.o0 = dX; a.ldo = D;
     a.part = part;
+    a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DX_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
   }

@@ -73,6 +73,7 @@ struct GemmArgs {
   long long ldo;                        // TOKEN / SCATTER output row stride
   long long ldc_ctx, ldc_out, c_out_off;  // compact geometry of o*/i* buffers
   float* part;                          // KG split partials [ksplit][T_out][N]
+  const int* iota;                      // KG: 0, 1, 2, ... (rows of ungathered segments)
 };
 
 template <typename T> struct GTraits;
@@ -190,6 +191,7 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr int SMEM = (BM + G_BN) * LDS_LD * (int)sizeof(T);
   static_assert(4 * 32 * EP_LD * 4 <= SMEM, "epilogue staging must fit in the tile buffers");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  __shared__ __attribute__((aligned(16))) int krow_s[64];   // K-gather: B rows of the next tile
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + BM * LDS_LD;
 
@@ -260,7 +262,6 @@ gather_gemm_kernel(const GemmArgs args) {
   Chunk rb[PF][8];
   int va[PF];            // valid elements of the A / N-gather B chunks of each set
   int kg_rv[PF];         // K-gather: valid k-rows of each set
-  int kgr[2][KR];        // K-gather: B rows of the next two tiles to load
 #pragma unroll
   for (int p = 0; p < PF; ++p) { va[p] = VEC; kg_rv[p] = KR; }
 
@@ -298,17 +299,21 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   };
 
-  // KG: B rows of tile (s, kk) of this thread
-  auto kg_rows = [&](int s, int kk, int* rows) {
+  // KG: the B row of k-position `lane` of tile (s, kk), fetched into a
+  // register and handed to all waves through LDS at the next store phase.  Rows always come from memory (ungathered segments read the iota
+  // array) and positions past K are clamped (those rows are zeroed at store
+  // time), so the loaded index is consumed only at the store phase.
+  int krow_reg = 0;
+  auto fetch_rows = [&](int s, int kk) {
     s = __builtin_amdgcn_readfirstlane(s);
     const GSeg& sg = args.seg[s];
     const int K = seg_len(s);
-    const int* sidx = (sg.b_gather && !is_out) ? sg.idx + (long long)g * sg.kidx : nullptr;
-#pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const int kpos = kk * BK + kg_kr0 + i;
-      rows[i] = kpos < K ? (sidx ? sidx[kpos] : kpos) : 0;
-    }
+    const int* sidx = (sg.b_gather && !is_out) ? sg.idx + (long long)g * sg.kidx : args.iota;
+    // every wave loads (no divergent definition of the register; wave 0 publishes)
+    krow_reg = sidx[min(kk * BK + min(lane, BK - 1), K - 1)];
+  };
+  auto publish_rows = [&]() {
+    if (wave == 0) krow_s[lane] = krow_reg;
   };
 
   // position the cursor on K-tile kt_begin
@@ -322,24 +327,15 @@ gather_gemm_kernel(const GemmArgs args) {
     }
     enter_seg(s);
     cur_kk = __builtin_amdgcn_readfirstlane(kk);
-    if (MODE == MODE_KG) kg_rows(cur_s, cur_kk, kgr[0]);
   }
 
-  // Issue the global loads of the next K-tile (the i-th of this tile's range)
-  // into register set P.  K-gather: the rows of tile i are in kgr[i % 2]; the
-  // rows of tile i + 1 are fetched first, so a later wait for them does not
-  // drain the data loads issued after them.
-  auto load_tile = [&](auto Pc, auto Qc, bool more) {
+  // Issue the global loads of the next K-tile into register set P; K-gather
+  // rows come from krow_s.
+  auto load_tile = [&](auto Pc) {
     constexpr int P = decltype(Pc)::value;   // register set
-    constexpr int Q = decltype(Qc)::value;   // parity of the tile: kgr[Q] holds its rows
-    while (cur_kk >= cur_nkt) {   // segment boundary (segments may be empty)
+    if (cur_kk >= cur_nkt && cur_s + 1 < args.nseg) {   // segment boundary (segments are never empty)
       enter_seg(cur_s + 1);
       cur_kk = 0;
-    }
-    if (MODE == MODE_KG && more) {   // rows of the following tile
-      int s = cur_s, kk = cur_kk + 1;
-      while (kk >= (seg_len(s) + BK - 1) / BK && s + 1 < args.nseg) { kk = 0; ++s; }
-      kg_rows(s, kk, kgr[Q ^ 1]);
     }
     const int k0 = cur_kk * BK;
     const int kcol = k0 + a_kc * VEC;
@@ -354,14 +350,28 @@ gather_gemm_kernel(const GemmArgs args) {
     } else {
       const int kr = cur_K - (k0 + kg_kr0);
       kg_rv[P] = kr < 0 ? 0 : (kr > KR ? KR : kr);
+      int rows[KR];
+#pragma unroll
+      for (int i = 0; i < KR; i += 4) {
+        const int4 q = *reinterpret_cast<const int4*>(&krow_s[kg_kr0 + i]);
+        rows[i] = q.x; rows[i + 1] = q.y; rows[i + 2] = q.z; rows[i + 3] = q.w;
+      }
 #pragma unroll
       for (int i = 0; i < KR; ++i)
 #pragma unroll
         for (int h = 0; h < 8 / VEC; ++h)
           rb[P][i * (8 / VEC) + h] =
-              load_chunk(b_base + ((unsigned)kgr[Q][i] * (unsigned)cur_ldb + kg_c0 + h * VEC));
+              load_chunk(b_base + ((unsigned)rows[i] * (unsigned)cur_ldb + kg_c0 + h * VEC));
     }
     ++cur_kk;
+  };
+
+  // K-gather: fetch the rows of the tile the cursor points at (the next one to
+  // load; the cursor advances past each loaded tile).
+  auto fetch_rows_next = [&]() {
+    int s = cur_s, kk = cur_kk;
+    if (kk >= cur_nkt && s + 1 < args.nseg) { kk = 0; ++s; }
+    fetch_rows(s, kk);
   };
 
   auto store_tile = [&](auto Pc) {
@@ -467,24 +477,38 @@ gather_gemm_kernel(const GemmArgs args) {
   };
 
   // One register set: the loads of tile i+1 are in flight while tile i is
-  // consumed from LDS.  (A second register set for a deeper prefetch needs an
-  // unrolled loop body whose register pressure spills the accumulators.)
+  // consumed from LDS; they are issued right after tile i is stored.  K-gather
+  // rows of tile i+2 are fetched at the start of iteration i and used at its
+  // end, so no loaded index is carried across an iteration.  (A second
+  // register set for a deeper prefetch needs an unrolled loop body whose
+  // register pressure spills the accumulators.)
   using I0 = std::integral_constant<int, 0>;
   if (nkt > 0) {
-    load_tile(I0{}, I0{}, nkt > 1);
+    if (MODE == MODE_KG) {
+      fetch_rows(cur_s, cur_kk);
+      publish_rows();
+      __syncthreads();
+    }
+    load_tile(I0{});
+    if (MODE == MODE_KG) {
+      __syncthreads();   // everyone has read the rows of tile 0
+      fetch_rows_next();
+      publish_rows();
+    }
     store_tile(I0{});
-#pragma unroll
-    for (int j = 0; j < KR; ++j) kgr[0][j] = kgr[1][j];
     __syncthreads();
+    if (nkt > 1) load_tile(I0{});
     for (int i = 0; i < nkt; ++i) {
-      if (i + 1 < nkt) load_tile(I0{}, I0{}, i + 2 < nkt);
+      // unconditional, so every fetched row is consumed (past the range the
+      // cursor stays on the last segment and the clamped loads are never stored)
+      if (MODE == MODE_KG) fetch_rows_next();
       compute();
       __syncthreads();
       if (i + 1 >= nkt) break;
       store_tile(I0{});
-#pragma unroll
-      for (int j = 0; j < KR; ++j) kgr[0][j] = kgr[1][j];
+      if (MODE == MODE_KG) publish_rows();
       __syncthreads();
+      load_tile(I0{});
     }
   }
 

@@ -133,6 +133,11 @@ struct Packer {
     j.type = 1; j.dst = dst; j.ldd = ldd; j.gstride = gstride; j.rows = rows; j.cols = cols;
     j.src = src; j.lds = lds; j.src_rows = src_rows; j.tr = tr; j.idx = idx; j.k = k; j.nseq = nseq;
   }
+  // int32 identity rows 0 .. n-1
+  void iota(int* dst, int n) {
+    PackJob& j = a.job[a.njobs++];
+    j.type = 2; j.dst = dst; j.rows = 1; j.cols = n;
+  }
   template <typename T>
   sl_status launch(hipStream_t s) {
     long long n = 0;

@@ -38,7 +38,7 @@ struct QkvoGeom {
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
-      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, ws_bytes;
+      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, w_iota, ws_bytes;
 };
 
 int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -133,6 +133,7 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1, g.chunk));
   g.w_cr = b.take((size_t)cr * 4);
   g.w_inv = b.take(B * std::max(g.nq, g.nkv) * 4);
+  g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
   g.ws_bytes = b.off;
   return SL_OK;
 }
@@ -318,6 +319,12 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.ksplit_out = g.ks_o;
     ga.o0 = o; ga.ldo = D;
     ga.part = part;
+    {
+      Packer pk;
+      pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
+      if ((rc = pk.launch<T>(strm))) return rc;
+    }
+    ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_O_FWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_o, D, o, D, strm))) return rc;
   }
@@ -437,6 +444,12 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.ksplit_out = g.ks_dx;
     ga.o0 = dX; ga.ldo = D;
     ga.part = part;
+    {
+      Packer pk;
+      pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
+      if ((rc = pk.launch<T>(strm))) return rc;
+    }
+    ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
     // dAq, dAk = dz^T X (one pass for q and k), dAv

@@ -652,6 +652,7 @@ static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, i
 //            the block is src[r][c] or, transposed, src[c][r]
 //   type 1:  per context group g: dst[g][q][p] = src(q, idx[g][p]) for q < src_rows,
 //            p < k, 0 elsewhere; src(q, c) = src[q*lds + c] or, transposed, src[c*lds + q]
+//   type 2:  int32 dst[p] = p for p < cols (identity rows)
 // ===========================================================================
 constexpr int PK_MAXJOBS = 10;
 
@@ -680,6 +681,10 @@ __global__ void pack_kernel(const PackArgs a) {
   const long long e = i - a.start[j];
   const T* src = reinterpret_cast<const T*>(b.src);
   T* dst = reinterpret_cast<T*>(b.dst);
+  if (b.type == 2) {
+    reinterpret_cast<int*>(b.dst)[e] = (int)e;
+    return;
+  }
   if (b.type == 0) {
     const int r = (int)(e / b.cols), c = (int)(e % b.cols);
     const int sr = r - b.row_off, sc = c - b.col_off;

@@ -66,7 +66,7 @@ SIGNATURES = {
     "sl_build_estimator": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                                           _vp, _sz, _vp]),
     "sl_estimate_select_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout),
-                                                 ctypes.POINTER(SlHeads), _i32, _i64]),
+                                                 ctypes.POINTER(SlHeads), _i64, _i32, _i64]),
     "sl_estimate_select": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(SlLayout),
                                           ctypes.POINTER(SlHeads), _vp, _i64, _i32, _vp, _vp, _vp,
                                           _vp, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -80,6 +80,7 @@ SIGNATURES = {
                                   ctypes.POINTER(SlFfnWeights), _vp, _i32, _vp, _vp, _sz, _vp, _vp,
                                   ctypes.POINTER(SlFfnGrads), _vp, _sz, _vp]),
     "sl_timer_enable": (ctypes.c_int, [ctypes.c_int]),
+    "sl_timer_select": (None, [ctypes.c_uint32]),
     "sl_timer_reset": (None, []),
     "sl_timer_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int)]),
@@ -178,6 +179,12 @@ def timer_enable(max_launches: int):
     _check(lib().sl_timer_enable(int(max_launches)), "sl_timer_enable")
 
 
+def timer_select(slots):
+    """Record only the named slots (None: all)."""
+    mask = 0xFFFFFFFF if slots is None else sum(1 << TIMER_SLOTS[n] for n in slots)
+    lib().sl_timer_select(mask)
+
+
 def timer_reset():
     lib().sl_timer_reset()
 
@@ -209,7 +216,7 @@ def build_estimator(W: torch.Tensor, rank: int, iters: int = 0):
 class EstimateBuffers:
     """Reusable idx / scores / scratch buffers of estimate_select."""
 
-    def __init__(self, crit: int, layout: Layout, rank: int, N: int, k: int, device,
+    def __init__(self, crit: int, layout: Layout, d_in: int, rank: int, N: int, k: int, device,
                  heads: Optional[Sequence[int]] = None, want_scores: bool = False):
         L = lib()
         self.heads = SlHeads(*heads) if heads is not None else None
@@ -217,8 +224,8 @@ class EstimateBuffers:
         self.idx = torch.empty(layout.batch, k, dtype=torch.int32, device=device)
         self.scores = (torch.empty(layout.batch, N, dtype=torch.float32, device=device)
                        if want_scores else None)
-        self.ws = _bytes_tensor(L.sl_estimate_select_workspace_bytes(crit, layout.ref, href, rank, N),
-                                device)
+        self.ws = _bytes_tensor(L.sl_estimate_select_workspace_bytes(crit, layout.ref, href, d_in,
+                                                                     rank, N), device)
 
 
 def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, Q0, Pt1, Q1,
@@ -227,7 +234,8 @@ def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, 
     """Per-sequence channel sets idx [batch, k] (int32, ascending) and,
     optionally, the scores [batch, N] (fp32)."""
     L = lib()
-    bufs = bufs or EstimateBuffers(crit, layout, rank, N, k, X.device, heads, want_scores)
+    bufs = bufs or EstimateBuffers(crit, layout, X.shape[1], rank, N, k, X.device, heads,
+                                   want_scores)
     href = ctypes.byref(bufs.heads) if bufs.heads is not None else None
     _check(L.sl_estimate_select(crit, _dtype_code(X), layout.ref, href, _ptr(X), X.shape[1], rank,
                                 _ptr(Pt0), _ptr(Q0), _ptr(Pt1), _ptr(Q1), N, k, _ptr(bufs.idx),

@@ -12,11 +12,11 @@ namespace {
 
 struct EstGeom {
   int rep, ldz, nchunk_max, N0, nproj;
-  size_t w_zh, w_p0, w_p1, total;
+  size_t w_zh, w_p0, w_p1, w_skp, total;
 };
 
-sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, int rank,
-                   long long N, EstGeom& g) {
+sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, long long d_in,
+                   int rank, long long N, EstGeom& g) {
   if (crit != SL_CRIT_SWIGLU_L2 && crit != SL_CRIT_L2 && crit != SL_CRIT_QK_NORM)
     SL_FAIL(SL_ERR_DTYPE, "unknown criterion %d", (int)crit);
   if (rank < 1 || rank > 32) SL_FAIL(SL_ERR_RANGE, "estimator rank %d outside [1, 32]", rank);
@@ -45,6 +45,7 @@ sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, i
   g.w_zh = bp.take((size_t)T * g.ldz * 4);
   g.w_p0 = bp.take((size_t)st.nseq * g.nchunk_max * g.N0 * 4);
   g.w_p1 = bp.take(crit == SL_CRIT_QK_NORM ? (size_t)st.nseq * g.nchunk_max * N * 4 : 0);
+  g.w_skp = bp.take((size_t)skinny_part_floats(T, d_in) * 4);   // K-sliced stage 1
   g.total = bp.off;
   return SL_OK;
 }
@@ -97,11 +98,8 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
     sa.Bb[0] = Pt0; sa.nbk[0] = rank; sa.ldbb[0] = d_in;
     sa.Bb[1] = Pt1; sa.nbk[1] = g.nproj > 1 ? rank : 0; sa.ldbb[1] = d_in;
     sa.out = zh; sa.ldo = g.ldz; sa.col0 = 0; sa.oscale = 1.f;
-    sa.ngroups = st.nseq;
-    int nb = 0;
-    for (int b = 0; b < st.nseq; ++b) { sa.blk_start[b] = nb; nb += ceil_div(st.ctx[b], SK_ROWS); }
-    sa.blk_start[st.nseq] = nb;
-    sl_status s = launch_skinny<T>(sa, nb, stream);
+    sa.part = reinterpret_cast<float*>(ws + g.w_skp);
+    sl_status s = launch_skinny<T>(sa, stream);
     if (s != SL_OK) return s;
     // stage 2 + criterion, per 64-token chunk
     ScoreArgs sc;
@@ -141,11 +139,13 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
 extern "C" {
 
 size_t sl_estimate_select_workspace_bytes(sl_criterion crit, const sl_layout* lay,
-                                          const sl_heads* heads, int32_t rank, int64_t N) {
+                                          const sl_heads* heads, int64_t d_in, int32_t rank,
+                                          int64_t N) {
   SeqTab st;
   if (build_seqtab(lay, st) != SL_OK) return 0;
   EstGeom g;
-  if (est_geom(crit, st, heads, rank, N, g) != SL_OK) return 0;
+  if (d_in < 8 || d_in % 8) return 0;
+  if (est_geom(crit, st, heads, d_in, rank, N, g) != SL_OK) return 0;
   return g.total;
 }
 
@@ -159,9 +159,10 @@ sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* la
   sl_status s = build_seqtab(lay, st);
   if (s != SL_OK) return s;
   EstGeom g;
-  if ((s = est_geom(crit, st, heads, rank, N, g)) != SL_OK) return s;
+  if (d_in < 8 || d_in % 8)
+    SL_FAIL(SL_ERR_SHAPE, "d_in = %lld must be a positive multiple of 8", (long long)d_in);
+  if ((s = est_geom(crit, st, heads, d_in, rank, N, g)) != SL_OK) return s;
   if (k < 1 || k > N) SL_FAIL(SL_ERR_RANGE, "k = %d outside [1, %lld]", k, (long long)N);
-  if (d_in < 8 || d_in % 8) SL_FAIL(SL_ERR_SHAPE, "d_in = %lld must be a positive multiple of 8", (long long)d_in);
   if (rank > d_in) SL_FAIL(SL_ERR_RANGE, "rank %d > d_in %lld", rank, (long long)d_in);
   const bool two = crit != SL_CRIT_L2;
   if (!X || !Pt0 || !Q0 || !idx || !ws || (two && (!Pt1 || !Q1)))

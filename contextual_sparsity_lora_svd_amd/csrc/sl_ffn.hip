@@ -30,7 +30,8 @@ struct FfnGeom {
   int ks_down, ks_dx, RM1, RM2, chunk;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
-      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, ws_bytes;
+      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp,
+      ws_bytes;
 };
 
 int choose_ksplit(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -108,6 +109,7 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
   g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
+  g.w_skp = w.take((size_t)skinny_part_floats(g.T, D > F ? D : F) * 4);
   g.ws_bytes = w.off;
   return SL_OK;
 }
@@ -141,6 +143,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
   T* Adg = reinterpret_cast<T*>(ws + g.w_Adg);
   float* part = reinterpret_cast<float*>(ws + g.w_part);
+  float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
   // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
   // Adg[g] = Ad[:, S_g] (gathered per context group); one launch.
@@ -165,7 +168,8 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.Bb[1] = w->Au; a.nbk[1] = r; a.ldbb[1] = D;
     a.out = zgu; a.ldo = 2 * rp; a.col0 = 0; a.oscale = 1.f;
     a.outs = zs_gu; a.ldos = 2 * rp; a.scale = s;
-    if ((rc = launch_skinny<T>(a, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    a.part = skp;
+    if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
   // G, U, H on the selected channels (context) / all channels (output rows)
   {
@@ -192,8 +196,8 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.B0o = w->Ad; a.ldb0o = F;
     a.out = zd; a.ldo = rp; a.oscale = 1.f;
     a.outs = zs_d; a.ldos = rp; a.scale = s;
-    const int nb = skinny_blocks_compact(st, a);
-    if ((rc = launch_skinny<T>(a, nb, strm))) return rc;
+    a.part = skp;
+    if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
   // Y = H WdT[S] + s z_d Bd^T
   {
@@ -244,6 +248,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
+  float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
   // packed LoRA operands (one launch)
   {
@@ -271,7 +276,8 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
     a.out = dz_d; a.ldo = rp; a.oscale = s;
     a.outs = dzs_d; a.ldos = rp; a.scale = s;
-    if ((rc = launch_skinny<T>(a, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    a.part = skp;
+    if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
   // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
   {
@@ -299,8 +305,8 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.B0o = which ? BuTo : BgTo; a.ldb0o = F;
     a.out = dz_gu; a.ldo = 2 * rp; a.col0 = which * rp; a.oscale = s;
     a.outs = dzs_gu; a.ldos = 2 * rp; a.scale = s;
-    const int nb = skinny_blocks_compact(st, a);
-    if ((rc = launch_skinny<T>(a, nb, strm))) return rc;
+    a.part = skp;
+    if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
   // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au
   {

@@ -68,6 +68,7 @@ struct TimerState {
   std::vector<hipEvent_t> ev;      // pairs (start, stop)
   std::vector<int> slot;
   size_t used = 0;
+  uint32_t mask = ~0u;             // slots recorded
 };
 static TimerState g_timer;         // single-threaded diagnostic facility
 static int g_pending_slot = -1;
@@ -75,7 +76,10 @@ static int g_pending_slot = -1;
 bool timer_on() { return g_timer.on; }
 
 void timer_begin(int slot, hipStream_t s) {
-  if (!g_timer.on || 2 * (g_timer.used + 1) > g_timer.ev.size()) { g_pending_slot = -1; return; }
+  if (!g_timer.on || !((g_timer.mask >> slot) & 1u) || 2 * (g_timer.used + 1) > g_timer.ev.size()) {
+    g_pending_slot = -1;
+    return;
+  }
   g_pending_slot = slot;
   hipEventRecord(g_timer.ev[2 * g_timer.used], s);
 }
@@ -102,6 +106,7 @@ int sl_timer_enable(int max_launches) {
   g_timer.slot.clear();
   g_timer.used = 0;
   g_timer.on = false;
+  g_timer.mask = ~0u;
   if (max_launches <= 0) return 0;
   g_timer.ev.resize(2 * (size_t)max_launches);
   g_timer.slot.resize(max_launches);
@@ -110,6 +115,8 @@ int sl_timer_enable(int max_launches) {
   g_timer.on = true;
   return 0;
 }
+
+void sl_timer_select(uint32_t slot_mask) { sl::g_timer.mask = slot_mask; }
 
 void sl_timer_reset(void) { sl::g_timer.used = 0; }
 

@@ -7,27 +7,81 @@
 
 namespace sl {
 
+// Workgroup layout of a skinny product: row blocks of SK_RB rows, each cut
+// into K slices of about SK_SLICE_BYTES per row (so long rows spread over more
+// workgroups).  Returns the number of workgroups.
+inline int skinny_layout(SkinnyArgs& a, int esz) {
+  const SeqTab& st = a.st;
+  int ng;
+  if (a.mode == 0) ng = 1;
+  else if (a.mode == 1) ng = st.nseq + 1;
+  else ng = st.nseq;
+  a.ngroups = ng;
+  a.mrows = a.mode == 0 ? a.T : (a.mode == 1 ? st.T_ctx + st.T_out : st.T_ctx);
+  const int kc = SK_CB / esz, target = SK_SLICE_BYTES / esz;
+  int nb = 0;
+  for (int g = 0; g < ng; ++g) {
+    a.blk_start[g] = nb;
+    int m, K;
+    if (a.mode == 0) { m = a.T; K = a.K; }
+    else {
+      const bool is_out = a.mode == 1 && g == st.nseq;
+      m = is_out ? st.T_out : st.ctx[g];
+      K = a.K > 0 ? a.K : (is_out ? a.n_out : a.kidx);
+    }
+    int nsl = K > target ? ceil_div(K, target) : 1;
+    if (nsl > SK_MAXSL) nsl = SK_MAXSL;
+    const int ksl = (int)round_up(ceil_div(K > 0 ? K : 1, nsl), kc);
+    nsl = K > 0 ? ceil_div(K, ksl) : 1;   // no empty slices
+    a.nsl[g] = nsl;
+    a.ksl[g] = ksl;
+    nb += ceil_div(m, SK_RB) * nsl;
+  }
+  a.blk_start[ng] = nb;
+  return nb;
+}
+
+// Floats of partial sums a skinny product over at most T rows and K <= Kmax
+// may need (any element size up to 4 bytes).
+inline long long skinny_part_floats(long long T, long long Kmax) {
+  long long nsl = (Kmax * 4 + SK_SLICE_BYTES - 1) / SK_SLICE_BYTES;
+  if (nsl < 1) nsl = 1;
+  if (nsl > SK_MAXSL) nsl = SK_MAXSL;
+  return nsl > 1 ? nsl * T * SK_PC : 0;
+}
+
 template <typename T>
-inline sl_status launch_skinny_one(SkinnyArgs& a, int nblocks, hipStream_t s) {
+inline sl_status launch_skinny_one(SkinnyArgs& a, hipStream_t s) {
   int C = 0;
   for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
+  const int nblocks = skinny_layout(a, (int)sizeof(T));
   if (nblocks <= 0 || C <= 0) return SL_OK;
-  const dim3 grid(nblocks), block(64 * SK_WAVES);
+  a.pc = (C + 15) / 16 * 16;
+  bool sliced = false;
+  for (int g = 0; g < a.ngroups; ++g) sliced |= a.nsl[g] > 1;
+  if (sliced && !a.part) SL_FAIL(SL_ERR_NULL, "internal: K-sliced skinny product without scratch");
+  const dim3 grid(nblocks), block(SK_THREADS);
   if (C <= 16) hipLaunchKernelGGL((skinny_kernel<T, 1>), grid, block, 0, s, a);
   else if (C <= 32) hipLaunchKernelGGL((skinny_kernel<T, 2>), grid, block, 0, s, a);
   else if (C <= 48) hipLaunchKernelGGL((skinny_kernel<T, 3>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((skinny_kernel<T, 4>), grid, block, 0, s, a);
   SL_HIP(hipGetLastError());
+  if (sliced) {
+    int ptot = 0;
+    for (int j = 0; j < a.nblk; ++j) ptot += (a.nbk[j] + 7) / 8 * 8;
+    hipLaunchKernelGGL((skinny_finish_kernel<T>), grid1d((long long)a.mrows * ptot), dim3(256), 0, s, a);
+    SL_HIP(hipGetLastError());
+  }
   return SL_OK;
 }
 
 // Skinny product over any number of B blocks: blocks are grouped into launches
 // of at most 64 columns; each launch writes its padded column range.
 template <typename T>
-inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
+inline sl_status launch_skinny(SkinnyArgs& a, hipStream_t s) {
   int C = 0;
   for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
-  if (C <= 64) return launch_skinny_one<T>(a, nblocks, s);
+  if (C <= 64) return launch_skinny_one<T>(a, s);
   if (a.mode == 1) SL_FAIL(SL_ERR_SHAPE, "per-group skinny product with %d > 64 columns", C);
   int j = 0, col = a.col0;
   while (j < a.nblk) {
@@ -43,7 +97,7 @@ inline sl_status launch_skinny(SkinnyArgs& a, int nblocks, hipStream_t s) {
     }
     if (b.nblk == 0) SL_FAIL(SL_ERR_SHAPE, "skinny block with %d > 64 columns", a.nbk[j]);
     b.col0 = col;
-    sl_status rc = launch_skinny_one<T>(b, nblocks, s);
+    sl_status rc = launch_skinny_one<T>(b, s);
     if (rc != SL_OK) return rc;
     col += pc;
   }
@@ -117,11 +171,17 @@ inline sl_status gather_factor(void* dst, long long ldd, long long gstride, cons
 // Builder of one pack launch.
 struct Packer {
   PackArgs a;
+  PackJob spare;        // target of jobs beyond the limit (reported by launch)
+  bool overflow = false;
   Packer() { std::memset(&a, 0, sizeof(a)); }
+  PackJob& next() {
+    if (a.njobs >= PK_MAXJOBS) { overflow = true; return spare; }
+    return a.job[a.njobs++];
+  }
   // dst region [rows x cols] (row stride ldd) holding src block at (row_off, col_off)
   void copy(void* dst, long long ldd, int rows, int cols, const void* src, long long lds,
             int src_rows, int src_cols, int tr, int row_off = 0, int col_off = 0) {
-    PackJob& j = a.job[a.njobs++];
+    PackJob& j = next();
     j.type = 0; j.dst = dst; j.ldd = ldd; j.rows = rows; j.cols = cols;
     j.row_off = row_off; j.col_off = col_off;
     j.src = src; j.lds = lds; j.src_rows = src_rows; j.src_cols = src_cols; j.tr = tr;
@@ -129,17 +189,18 @@ struct Packer {
   // per context group g: dst + g*gstride, [rows x cols], src factor gathered by idx
   void gather(void* dst, long long ldd, long long gstride, int rows, int cols, const void* src,
               long long lds, int src_rows, int tr, const int* idx, int k, int nseq) {
-    PackJob& j = a.job[a.njobs++];
+    PackJob& j = next();
     j.type = 1; j.dst = dst; j.ldd = ldd; j.gstride = gstride; j.rows = rows; j.cols = cols;
     j.src = src; j.lds = lds; j.src_rows = src_rows; j.tr = tr; j.idx = idx; j.k = k; j.nseq = nseq;
   }
   // int32 identity rows 0 .. n-1
   void iota(int* dst, int n) {
-    PackJob& j = a.job[a.njobs++];
+    PackJob& j = next();
     j.type = 2; j.dst = dst; j.rows = 1; j.cols = n;
   }
   template <typename T>
   sl_status launch(hipStream_t s) {
+    if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d pack jobs", PK_MAXJOBS);
     long long n = 0;
     for (int i = 0; i < a.njobs; ++i) {
       a.start[i] = n;
@@ -173,19 +234,6 @@ inline sl_status splitk_reduce(const SeqTab& st, const float* part, int ks, int 
                      reinterpret_cast<T*>(out), ldo);
   SL_HIP(hipGetLastError());
   return SL_OK;
-}
-
-// Row blocks of the skinny kernel per group (mode 1: context groups + output group).
-inline int skinny_blocks_compact(const SeqTab& st, SkinnyArgs& a) {
-  int nb = 0;
-  for (int g = 0; g <= st.nseq; ++g) {
-    a.blk_start[g] = nb;
-    const int m = g < st.nseq ? st.ctx[g] : st.T_out;
-    nb += ceil_div(m, SK_ROWS);
-  }
-  a.blk_start[st.nseq + 1] = nb;
-  a.ngroups = st.nseq + 1;
-  return nb;
 }
 
 // Chunks of the column reduction per group (mode 1).

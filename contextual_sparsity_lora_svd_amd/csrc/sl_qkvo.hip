@@ -38,7 +38,7 @@ struct QkvoGeom {
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
-      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, w_iota, ws_bytes;
+      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, w_iota, w_skp, ws_bytes;
 };
 
 int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -134,6 +134,7 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_cr = b.take((size_t)cr * 4);
   g.w_inv = b.take(B * std::max(g.nq, g.nkv) * 4);
   g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
+  g.w_skp = b.take((size_t)skinny_part_floats(g.T, std::max(g.D, g.nq)) * 4);
   g.ws_bytes = b.off;
   return SL_OK;
 }
@@ -229,6 +230,14 @@ sl_status grad_dense(const QkvoGeom& g, const void* P, int N, const float* Z, lo
   return SL_OK;
 }
 
+// Identity rows for the K-gather GEMMs' dense segments.
+template <typename T>
+sl_status prologue(const QkvoGeom& g, char* ws, hipStream_t strm) {
+  Packer pk;
+  pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
+  return pk.launch<T>(strm);
+}
+
 template <typename T>
 sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void* X, const void* a,
                         const int* idx_qk, const int* idx_vo, void* q, void* k, void* v, void* o,
@@ -244,6 +253,8 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   T* zs_qkv = reinterpret_cast<T*>(ws + g.w_zs_qkv);
   T* zs_o = reinterpret_cast<T*>(ws + g.w_zs_o);
   float* part = reinterpret_cast<float*>(ws + g.w_part);
+  float* skp = reinterpret_cast<float*>(ws + g.w_skp);
+  if ((rc = prologue<T>(g, ws, strm))) return rc;
 
   if (X) {
     if (g.G > 1 && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
@@ -258,7 +269,8 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.Bb[2] = w->Av; sa.nbk[2] = r; sa.ldbb[2] = D;
     sa.out = zqkv; sa.ldo = 3 * rp; sa.oscale = 1.f;
     sa.outs = zs_qkv; sa.ldos = 3 * rp; sa.scale = s;
-    if ((rc = launch_skinny<T>(sa, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    sa.part = skp;
+    if ((rc = launch_skinny<T>(sa, strm))) return rc;
     // the three projections
     const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
     const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
@@ -304,7 +316,8 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.B0o = w->Ao; sa.ldb0o = g.nq;
     sa.out = zo; sa.ldo = rp; sa.oscale = 1.f;
     sa.outs = zs_o; sa.ldos = rp; sa.scale = s;
-    if ((rc = launch_skinny<T>(sa, skinny_blocks_compact(st, sa), strm))) return rc;
+    sa.part = skp;
+    if ((rc = launch_skinny<T>(sa, strm))) return rc;
     // o = a_m WoT[So] + s z_o Bo^T
     if ((rc = fill_zero<T>(BoTp, (long long)rp * D, strm))) return rc;
     if ((rc = copy2d<T>(BoTp, D, 0, 0, r, D, w->Bo, r, 1, strm))) return rc;
@@ -319,11 +332,6 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.ksplit_out = g.ks_o;
     ga.o0 = o; ga.ldo = D;
     ga.part = part;
-    {
-      Packer pk;
-      pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
-      if ((rc = pk.launch<T>(strm))) return rc;
-    }
     ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_O_FWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_o, D, o, D, strm))) return rc;
@@ -347,6 +355,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
+  float* skp = reinterpret_cast<float*>(ws + g.w_skp);
+  if ((rc = prologue<T>(g, ws, strm))) return rc;
 
   if (d_out) {
     if (g.G > 1 && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
@@ -369,7 +379,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.Bb[0] = BoTp; sa.nbk[0] = r; sa.ldbb[0] = D;
     sa.out = dz_o; sa.ldo = rp; sa.oscale = s;
     sa.outs = dzs_o; sa.ldos = rp; sa.scale = s;
-    if ((rc = launch_skinny<T>(sa, ceil_div(g.T, SK_ROWS), strm))) return rc;
+    sa.part = skp;
+    if ((rc = launch_skinny<T>(sa, strm))) return rc;
     // da on So (dense at output rows), 0 at the other context columns
     if (g.ko < g.nq && (rc = zero_ctx<T>(g, da, g.nq, strm))) return rc;
     GemmArgs ga;
@@ -427,7 +438,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       sa.B0o = BTo; sa.ldb0o = c.n;
       sa.out = dz; sa.ldo = 3 * rp; sa.col0 = j * rp; sa.oscale = s;
       sa.outs = dzs; sa.ldos = 3 * rp; sa.scale = s;
-      if ((rc = launch_skinny<T>(sa, skinny_blocks_compact(st, sa), strm))) return rc;
+      sa.part = skp;
+    if ((rc = launch_skinny<T>(sa, strm))) return rc;
     }
     // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
     GemmArgs ga;
@@ -444,11 +456,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.ksplit_out = g.ks_dx;
     ga.o0 = dX; ga.ldo = D;
     ga.part = part;
-    {
-      Packer pk;
-      pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
-      if ((rc = pk.launch<T>(strm))) return rc;
-    }
     ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;

@@ -12,16 +12,25 @@ typedef __bf16 bf16x8_t_s __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ===========================================================================
-// Skinny product  out[row, c] = sum_k A[row, k] * Bm(c, k),  c < n1 + n2 <= 64
+// Skinny product  out[row, c] = sum_k A[row, k] * Bm(c, k),  c < C <= 64
 //
 // Estimator stage 1 (SparseLoRA article §二: the input is projected onto the
 // leading right singular vectors, x V_r Sigma_r) and the LoRA activations
-// x A^T, h A_d[:,S]^T, dY B_d, dG B_g[S].  The B operand is tiny and shared by
-// every workgroup (L2 resident); A is streamed once.  16 rows per workgroup,
-// 8 waves split K, 16x16 MFMA tiles, fixed-order reduction over the waves.
+// x A^T, h A_d[:,S]^T, dY B_d, dG B_g[S].  Bandwidth-bound on A, which is
+// streamed once.  A workgroup takes SK_RB rows and one K slice; each K chunk
+// (256 bytes of a row) of A and of the (tiny, cache-resident) B operand is
+// loaded with coalesced 16-byte loads, staged in LDS and consumed by 16x16
+// MFMA tiles (one wave per 16 rows).  Rows too long for one workgroup are cut
+// into K slices whose partial sums a second, small kernel adds in slice order
+// (deterministic).
 // ===========================================================================
-constexpr int SK_ROWS = 16;
-constexpr int SK_WAVES = 8;
+constexpr int SK_RB = 32;                  // rows per workgroup (two waves of 16)
+constexpr int SK_THREADS = 64 * (SK_RB / 16);
+constexpr int SK_CB = 256;                 // bytes of a row per K chunk
+constexpr int SK_LDB = SK_CB + 16;         // LDS row pitch in bytes (bank spread)
+constexpr int SK_SLICE_BYTES = 1024;       // bytes of a row per K slice (4 chunks)
+constexpr int SK_MAXSL = 64;               // slices per row block at most
+constexpr int SK_PC = 64;                  // partial-sum row pitch at most (pc = NB*16)
 
 struct SkinnyArgs {
   SeqTab st;
@@ -40,153 +49,278 @@ struct SkinnyArgs {
   // where pj = sum of the previous blocks' sizes rounded up to 8; padding is 0.
   float* out; long long ldo; int col0; float oscale;
   void* outs; long long ldos; float scale;   // optional copy in the call dtype
-  int blk_start[SL_MAX_SEQS + 2];           // row blocks per group (modes 1, 2)
+  // Workgroups: group g owns [blk_start[g], blk_start[g+1]), row block major,
+  // nsl[g] K slices of ksl[g] elements each.
+  int blk_start[SL_MAX_SEQS + 2];
+  int nsl[SL_MAX_SEQS + 1];
+  int ksl[SL_MAX_SEQS + 1];
   int ngroups;
+  int mrows;              // rows of the launch row space (see launch_row)
+  int pc;                 // partial-sum row pitch: logical columns rounded up to 16
+  float* part;            // partial sums [slice][launch row][pc] when a group has nsl > 1
 };
 
-template <typename T, int NB>
-__global__ void __launch_bounds__(64 * SK_WAVES)
-skinny_kernel(const SkinnyArgs a) {
-  __shared__ float red[SK_WAVES][SK_ROWS][NB * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int g = 0, rb = blockIdx.x;
-  if (a.mode != 0) {
-    while (g + 1 < a.ngroups && a.blk_start[g + 1] <= (int)blockIdx.x) ++g;
-    rb = blockIdx.x - a.blk_start[g];
+// Row of the launch row space: token order in mode 0, compact order otherwise
+// (context rows of every sequence, then, in mode 1, the output rows).
+__device__ inline int launch_row(const SkinnyArgs& a, int g, int r) {
+  if (a.mode == 0) return r;
+  return g < a.st.nseq ? a.st.ctx_pre[g] + r : a.st.T_ctx + r;
+}
+__device__ inline int skinny_group_of(const SkinnyArgs& a, int lrow, int& r) {
+  if (a.mode == 0) { r = lrow; return 0; }
+  if (lrow >= a.st.T_ctx) { r = lrow - a.st.T_ctx; return a.st.nseq; }
+  int lo = 0, hi = a.st.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.st.ctx_pre[mid] <= lrow) lo = mid; else hi = mid - 1;
   }
+  r = lrow - a.st.ctx_pre[lo];
+  return lo;
+}
+// Padded output column oc -> logical column (-1 for padding).
+__device__ inline int skinny_logical_col(const SkinnyArgs& a, int oc) {
+  int pc = 0, lc = 0;
+  for (int j = 0; j < a.nblk; ++j) {
+    const int pj = (a.nbk[j] + 7) / 8 * 8;
+    if (oc < pc + pj) return (oc - pc) < a.nbk[j] ? lc + (oc - pc) : -1;
+    pc += pj;
+    lc += a.nbk[j];
+  }
+  return -1;
+}
+__device__ inline int skinny_padded_cols(const SkinnyArgs& a) {
+  int p = 0;
+  for (int j = 0; j < a.nblk; ++j) p += (a.nbk[j] + 7) / 8 * 8;
+  return p;
+}
+
+template <typename T>
+__device__ inline uint4 mask_tail(uint4 v, int valid) {
+  // keep the first `valid` elements of a 16-byte vector, zero the rest
+  constexpr int E = 16 / sizeof(T);
+  if (valid >= E) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < valid) continue;
+    if constexpr (sizeof(T) == 2) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    else w[e] = 0u;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename T, int NB>
+__global__ void __launch_bounds__(SK_THREADS)
+skinny_kernel(const SkinnyArgs a) {
+  constexpr int E = 16 / sizeof(T);          // elements per 16-byte piece
+  constexpr int KC = SK_CB / sizeof(T);      // elements per chunk
+  constexpr int PR = SK_CB / 16;             // pieces per row and chunk (16)
+  constexpr int AL = SK_RB * PR / SK_THREADS;                      // A pieces per thread
+  constexpr int BL = (NB * 16 * PR + SK_THREADS - 1) / SK_THREADS; // B pieces per thread
+  constexpr int STAGE_LD = NB * 16 + 1;
+  constexpr int LDS_AB = (SK_RB + NB * 16) * SK_LDB;
+  constexpr int LDS_ST = SK_RB * STAGE_LD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_AB > LDS_ST ? LDS_AB : LDS_ST];
+  unsigned char* As = smem;
+  unsigned char* Bs = smem + SK_RB * SK_LDB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int g = 0;
+  while (g + 1 < a.ngroups && a.blk_start[g + 1] <= (int)blockIdx.x) ++g;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int nsl = a.nsl[g];
+  const int local = blockIdx.x - a.blk_start[g];
+  const int rb = local / nsl, sl = local % nsl;
   const bool is_out = (a.mode == 1 && g == a.st.nseq);
   const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
-  const int nch = is_out ? a.n_out : a.kidx;
-  const int K = a.K > 0 ? a.K : nch;
+  const int Kfull = a.K > 0 ? a.K : (is_out ? a.n_out : a.kidx);
+  const int kbeg = sl * a.ksl[g];
+  const int kend = min(Kfull, kbeg + a.ksl[g]);
+  const int nch = kend > kbeg ? (kend - kbeg + KC - 1) / KC : 0;
+
+  // this thread's A pieces: row tid/PR + i*(SK_THREADS/PR), piece tid%PR
   const T* A = reinterpret_cast<const T*>(a.A);
-  const T* B0 = reinterpret_cast<const T*>(a.Bb[0]);
-  long long ldb0 = a.ldbb[0];
-  if (a.mode == 1) {
-    if (is_out && a.B0o) { B0 = reinterpret_cast<const T*>(a.B0o); ldb0 = a.ldb0o; }
-    else if (!is_out) B0 += (long long)g * a.b0_gstride;
+  const int q = tid % PR;
+  const T* arow[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    int r = rb * SK_RB + tid / PR + i * (SK_THREADS / PR);
+    if (r >= m_rows) r = m_rows - 1;        // loaded and dropped
+    long long off;
+    if (a.mode == 1)
+      off = is_out ? a.a_out_off + (long long)r * a.lda_out : (long long)(a.st.ctx_pre[g] + r) * a.lda;
+    else
+      off = (long long)(a.mode == 0 ? r : group_token(a.st, g, r)) * a.lda;
+    arow[i] = A + off;
+  }
+  // B pieces: logical column c = tid/PR + i*(SK_THREADS/PR)
+  const T* brow[BL];
+  bool bok[BL];
+  int C = 0;
+  for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    int c = tid / PR + i * (SK_THREADS / PR);
+    bok[i] = c < C && c < NB * 16;
+    brow[i] = nullptr;
+    if (bok[i]) {
+      for (int j = 0; j < a.nblk; ++j) {
+        if (c < a.nbk[j]) {
+          if (j == 0) {
+            const T* B0 = reinterpret_cast<const T*>(a.Bb[0]);
+            long long ldb0 = a.ldbb[0];
+            if (a.mode == 1) {
+              if (is_out && a.B0o) { B0 = reinterpret_cast<const T*>(a.B0o); ldb0 = a.ldb0o; }
+              else if (!is_out) B0 += (long long)g * a.b0_gstride;
+            }
+            brow[i] = B0 + (long long)c * ldb0;
+          } else {
+            brow[i] = reinterpret_cast<const T*>(a.Bb[j]) + (long long)c * a.ldbb[j];
+          }
+          break;
+        }
+        c -= a.nbk[j];
+      }
+    }
+    if (!brow[i]) brow[i] = reinterpret_cast<const T*>(a.A);   // never dereferenced
   }
 
-  // this lane's A row
-  int r = rb * SK_ROWS + (lane & 15);
-  if (r >= m_rows) r = m_rows - 1;   // computed and dropped
-  long long arow;
-  if (a.mode == 1)
-    arow = is_out ? a.a_out_off + (long long)r * a.lda_out
-                  : (long long)(a.st.ctx_pre[g] + r) * a.lda;
-  else
-    arow = (long long)(a.mode == 0 ? r : group_token(a.st, g, r)) * a.lda;
+  uint4 ra[AL], rbv[BL];
+  auto load = [&](int c) {
+    const int k = kbeg + c * KC + q * E;
+    const int kc = k < kend ? k : kbeg;     // in-range address for tail pieces
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const uint4*>(arow[i] + kc);
+#pragma unroll
+    for (int i = 0; i < BL; ++i)
+      if (bok[i]) rbv[i] = *reinterpret_cast<const uint4*>(brow[i] + kc);
+  };
+  auto store = [&](int c) {
+    const int valid = kend - (kbeg + c * KC + q * E);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int r = tid / PR + i * (SK_THREADS / PR);
+      *reinterpret_cast<uint4*>(As + r * SK_LDB + q * 16) = mask_tail<T>(ra[i], valid);
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int r = tid / PR + i * (SK_THREADS / PR);
+      if (r < NB * 16)
+        *reinterpret_cast<uint4*>(Bs + r * SK_LDB + q * 16) =
+            bok[i] ? mask_tail<T>(rbv[i], valid) : make_uint4(0, 0, 0, 0);
+    }
+  };
 
   f32x4_t acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // B row of logical column c = nb*16 + lane%16
-  const T* brow[NB];
-  bool bok[NB];
+  auto compute = [&]() {
+    const unsigned char* ap = As + (wave * 16 + (lane & 15)) * SK_LDB;
+    if constexpr (sizeof(T) == 2) {
+      // 4 k-steps of 32: lane holds 8 consecutive k at 8*(lane>>4)
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    int c = nb * 16 + (lane & 15);
-    brow[nb] = B0; bok[nb] = false;
-    for (int j = 0; j < a.nblk; ++j) {
-      if (c < a.nbk[j]) {
-        brow[nb] = (j == 0 ? B0 + (long long)c * ldb0
-                           : reinterpret_cast<const T*>(a.Bb[j]) + (long long)c * a.ldbb[j]);
-        bok[nb] = true;
-        break;
-      }
-      c -= a.nbk[j];
-    }
-  }
-
-  if constexpr (sizeof(T) == 2) {
-    // k-steps of 32; lane holds 8 consecutive k at 8*(lane>>4).  U steps are
-    // loaded before any is consumed so that each lane keeps several loads in
-    // flight; addresses are clamped and tails zeroed after the loads.
-    constexpr int U = NB <= 2 ? 8 : 4;
-    const int nsteps = (K + 31) / 32;
-    const int per = (nsteps + SK_WAVES - 1) / SK_WAVES;
-    const int s0 = wave * per, s1 = min(nsteps, s0 + per);
-    for (int sb = s0; sb < s1; sb += U) {
-      uint4 av[U];
-      uint4 bv[U][NB];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = (sb + u) * 32 + 8 * (lane >> 4);
-        const int kc = (sb + u < s1 && k < K) ? k : 0;
-        av[u] = *reinterpret_cast<const uint4*>(A + arow + kc);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bv[u][nb] = *reinterpret_cast<const uint4*>(brow[nb] + kc);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = (sb + u) * 32 + 8 * (lane >> 4);
-        const int valid = sb + u < s1 ? (K - k < 0 ? 0 : (K - k > 8 ? 8 : K - k)) : 0;
-        if (valid < 8) {
-          uint32_t w[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
-          for (int e = valid; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          av[u] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        const bf16x8_t_s af = __builtin_bit_cast(bf16x8_t_s, av[u]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 av = *reinterpret_cast<const uint4*>(ap + ks * 64 + 16 * (lane >> 4));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          uint4 bq = bv[u][nb];
-          if (!bok[nb]) bq = make_uint4(0, 0, 0, 0);
-          else if (valid < 8) {
-            uint32_t w[4] = {bq.x, bq.y, bq.z, bq.w};
-            for (int e = valid; e < 8; ++e) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-            bq = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t_s, bq),
-                                                            acc[nb], 0, 0, 0);
+          const uint4 bv = *reinterpret_cast<const uint4*>(Bs + (nb * 16 + (lane & 15)) * SK_LDB +
+                                                           ks * 64 + 16 * (lane >> 4));
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t_s, av),
+                                                            __builtin_bit_cast(bf16x8_t_s, bv), acc[nb],
+                                                            0, 0, 0);
+        }
+      }
+    } else {
+      // 4 groups of 16 k: lane reads k = 4*(lane>>4) + 0..3 of the group and
+      // feeds element j to MFMA j, whose k index p = lane>>4 then stands for
+      // k = 4*p + j (the four MFMAs together cover the group)
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const float4 av = *reinterpret_cast<const float4*>(ap + kg * 64 + 16 * (lane >> 4));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float4 bv = *reinterpret_cast<const float4*>(Bs + (nb * 16 + (lane & 15)) * SK_LDB +
+                                                             kg * 64 + 16 * (lane >> 4));
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[nb], 0, 0, 0);
         }
       }
     }
-  } else {
-    // k-steps of 4; lane holds k = lane>>4
-    const int nsteps = (K + 3) / 4;
-    const int per = (nsteps + SK_WAVES - 1) / SK_WAVES;
-    const int s0 = wave * per, s1 = min(nsteps, s0 + per);
-    for (int s = s0; s < s1; ++s) {
-      const int k = s * 4 + (lane >> 4);
-      const float av = k < K ? reinterpret_cast<const float*>(A)[arow + k] : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float bv = (bok[nb] && k < K) ? reinterpret_cast<const float*>(brow[nb])[k] : 0.f;
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[nb], 0, 0, 0);
-      }
-    }
+  };
+
+  if (nch > 0) load(0);
+  for (int c = 0; c < nch; ++c) {
+    store(c);
+    __syncthreads();
+    if (c + 1 < nch) load(c + 1);
+    compute();
+    __syncthreads();
   }
-  // accumulator element e: row 4*(lane>>4) + e, column lane & 15
+
+  // accumulator element e: row 4*(lane>>4) + e of the wave's 16, column lane & 15
+  if (nsl > 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rb * SK_RB + wave * 16 + 4 * (lane >> 4) + e;
+        if (r < m_rows)
+          a.part[((long long)sl * a.mrows + launch_row(a, g, r)) * a.pc + nb * 16 + (lane & 15)] =
+              acc[nb][e];
+      }
+    return;
+  }
+  float* stage = reinterpret_cast<float*>(smem);   // [SK_RB][STAGE_LD] logical columns
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * (lane >> 4) + e][nb * 16 + (lane & 15)] = acc[nb][e];
+    for (int e = 0; e < 4; ++e)
+      stage[(wave * 16 + 4 * (lane >> 4) + e) * STAGE_LD + nb * 16 + (lane & 15)] = acc[nb][e];
   __syncthreads();
-  int ptot = 0;
-  for (int j = 0; j < a.nblk; ++j) ptot += (a.nbk[j] + 7) / 8 * 8;
-  for (int i = tid; i < SK_ROWS * ptot; i += 64 * SK_WAVES) {
+  const int ptot = skinny_padded_cols(a);
+  for (int i = tid; i < SK_RB * ptot; i += SK_THREADS) {
     const int rr = i / ptot, oc = i % ptot;
-    const int row = rb * SK_ROWS + rr;
+    const int row = rb * SK_RB + rr;
     if (row >= m_rows) continue;
-    int c = -1;   // logical column feeding padded output column oc (-1 = padding)
-    {
-      int pc = 0, lc = 0;
-      for (int j = 0; j < a.nblk; ++j) {
-        const int pj = (a.nbk[j] + 7) / 8 * 8;
-        if (oc < pc + pj) { c = (oc - pc) < a.nbk[j] ? lc + (oc - pc) : -1; break; }
-        pc += pj;
-        lc += a.nbk[j];
-      }
-    }
-    float v = 0.f;
-    if (c >= 0 && c < NB * 16) {
-#pragma unroll
-      for (int w = 0; w < SK_WAVES; ++w) v += red[w][rr][c];
-    }
+    const int c = skinny_logical_col(a, oc);
+    const float v = (c >= 0 && c < NB * 16) ? stage[rr * STAGE_LD + c] : 0.f;
     const long long tok = a.mode == 0 ? row : group_token(a.st, g, row);
     a.out[tok * a.ldo + a.col0 + oc] = v * a.oscale;
     if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + a.col0 + oc, v * a.scale);
   }
+}
+
+// Adds the K slices of the groups with nsl > 1, in slice order, and writes the
+// results (one thread per launch row and padded column).
+template <typename T>
+__global__ void skinny_finish_kernel(const SkinnyArgs a) {
+  const int ptot = skinny_padded_cols(a);
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)a.mrows * ptot) return;
+  const int lrow = (int)(i / ptot), oc = (int)(i % ptot);
+  int r;
+  const int g = skinny_group_of(a, lrow, r);
+  const int nsl = a.nsl[g];
+  if (nsl <= 1) return;
+  const int c = skinny_logical_col(a, oc);
+  float v = 0.f;
+  if (c >= 0) {
+    // slices in order; loads issued in groups of 8 before they are summed
+    const float* p = a.part + (long long)lrow * a.pc + c;
+    const long long sstride = (long long)a.mrows * a.pc;
+    for (int s0 = 0; s0 < nsl; s0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = s0 + j < nsl ? p[(s0 + j) * sstride] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += t[j];
+    }
+  }
+  const long long tok = a.mode == 0 ? r : group_token(a.st, g, r);
+  a.out[tok * a.ldo + a.col0 + oc] = v * a.oscale;
+  if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + a.col0 + oc, v * a.scale);
 }
 
 // ===========================================================================
@@ -654,7 +788,7 @@ static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, i
 //            p < k, 0 elsewhere; src(q, c) = src[q*lds + c] or, transposed, src[c*lds + q]
 //   type 2:  int32 dst[p] = p for p < cols (identity rows)
 // ===========================================================================
-constexpr int PK_MAXJOBS = 10;
+constexpr int PK_MAXJOBS = 12;
 
 struct PackJob {
   int type;

@@ -154,10 +154,12 @@ sl_status sl_build_estimator(sl_dtype dt, const void* W, int64_t out_f, int64_t 
  *          ties in score go to the lower channel index.
  *   scores [batch, N] fp32 out, optional (NULL = not written): the criterion
  *          (a sum of squares over the sequence's context tokens).
- * 1 <= k <= N <= 65536.  heads is read for QK_NORM only.
+ * 1 <= k <= N <= 65536.  heads is read for QK_NORM only.  The workspace size
+ * query takes the same criterion, layout, heads, d_in, rank and N as the call.
  * ------------------------------------------------------------------------- */
 size_t sl_estimate_select_workspace_bytes(sl_criterion crit, const sl_layout* lay,
-                                          const sl_heads* heads, int32_t rank, int64_t N);
+                                          const sl_heads* heads, int64_t d_in, int32_t rank,
+                                          int64_t N);
 sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* lay,
                              const sl_heads* heads, const void* X, int64_t d_in, int32_t rank,
                              const void* Pt0, const void* Q0, const void* Pt1, const void* Q1,
@@ -224,7 +226,9 @@ sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* 
  * region.  Single-threaded use only.  sl_timer_enable(n) keeps room for n
  * launches (0 disables and frees the events); sl_timer_read waits for the
  * recorded events and returns the slot's total milliseconds and launch count
- * since the last sl_timer_reset.
+ * since the last sl_timer_reset.  sl_timer_select(mask) records only the slots
+ * whose bit (1 << slot) is set (all after sl_timer_enable), so that a timed
+ * region carries events around the kernels of interest only.
  * ------------------------------------------------------------------------- */
 typedef enum sl_timer_slot {
   SL_TS_ESTIMATE = 0,   /* estimator stage 1 + criterion (a1, a2) */
@@ -236,6 +240,7 @@ typedef enum sl_timer_slot {
   SL_TS_QKV_FWD = 6, SL_TS_O_FWD = 7, SL_TS_DA_BWD = 8, SL_TS_DXQKV_BWD = 9
 } sl_timer_slot;
 int sl_timer_enable(int max_launches);
+void sl_timer_select(uint32_t slot_mask);
 void sl_timer_reset(void);
 int sl_timer_read(int slot, double* total_ms, int* count);
 

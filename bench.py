@@ -52,6 +52,27 @@ def kernel_work(D, F, r, r_e, ctx, L, k):
     return fl, by, R
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of a gather-GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the GEMM source has changed
+    since the counters were taken."""
+    import hashlib
+    summ = os.path.join(ROOT, "profiles", "gather_gemm_llama2-7b-ffn_hbm_traffic.md")
+    src = os.path.join(ROOT, "contextual_sparsity_lora_svd_amd", "csrc", "sl_gemm.hpp")
+    if not (os.path.exists(summ) and os.path.exists(src)):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    vals, ok = {}, False
+    for line in open(summ):
+        line = line.strip()
+        if line.startswith("gemm_source_sha256:"):
+            ok = line.split(":", 1)[1].strip() == sha
+        elif line.startswith("traffic_bytes "):
+            name, v = line[len("traffic_bytes "):].split(":")
+            vals[name.strip()] = float(v)
+    return vals.get(kernel) if ok else None
+
+
 def to_dev(x, torch, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype).contiguous()
 
@@ -91,6 +112,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain bf16 -> fp32 copy of 64 Mi elements (128 MiB read, "
+                         "256 MiB written) to calibrate HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -198,6 +222,15 @@ def main():
         print(f"[bench] dense step {dense_ms:.3f} ms", file=sys.stderr, flush=True)
         del bufd
 
+    if args.copy_calibration:
+        n = 64 << 20
+        src = torch.ones(n, dtype=torch.bfloat16, device=X.device)
+        dst = torch.empty(n, dtype=torch.float32, device=X.device)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
@@ -222,7 +255,7 @@ def main():
                    "k": k, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dom_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": dom_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                      "avg_launch_ms": dom_ms, "flops_per_launch": fl[dom]},
         "effective_tflops": total_flops / (ms * 1e-3) / 1e12,
         "speedup_vs_dense": dense["speedup"] if dense else None,

@@ -478,8 +478,8 @@ gather_gemm_kernel(const GemmArgs args) {
 
   // One register set: the loads of tile i+1 are in flight while tile i is
   // consumed from LDS; they are issued right after tile i is stored.  K-gather
-  // rows of tile i+2 are fetched at the start of iteration i and used at its
-  // end, so no loaded index is carried across an iteration.  (A second
+  // rows of tile i+2 are fetched after the compute phase of iteration i and
+  // used at its end, so no loaded index is carried across an iteration.  (A second
   // register set for a deeper prefetch needs an unrolled loop body whose
   // register pressure spills the accumulators.)
   using I0 = std::integral_constant<int, 0>;
@@ -499,10 +499,13 @@ gather_gemm_kernel(const GemmArgs args) {
     __syncthreads();
     if (nkt > 1) load_tile(I0{});
     for (int i = 0; i < nkt; ++i) {
-      // unconditional, so every fetched row is consumed (past the range the
-      // cursor stays on the last segment and the clamped loads are never stored)
-      if (MODE == MODE_KG) fetch_rows_next();
       compute();
+      // K-gather rows of tile i+2, fetched after the compute phase: a load in
+      // flight across the MFMAs makes the compiler drain every outstanding
+      // load (the prefetched tile included) before them.  Unconditional, so
+      // every fetched row is consumed (past the range the cursor stays on the
+      // last segment and the clamped loads are never stored).
+      if (MODE == MODE_KG) fetch_rows_next();
       __syncthreads();
       if (i + 1 >= nkt) break;
       store_tile(I0{});

@@ -413,36 +413,48 @@ struct SelectArgs {
   int* idx; float* scores;
 };
 
-__device__ inline int block_excl_scan_1024(int v, int* sh, int tid, int* total) {
-  // Hillis-Steele over 1024 values in shared memory (two buffers).
-  int* a = sh;
-  int* b = sh + SEL_THREADS;
-  a[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < SEL_THREADS; off <<= 1) {
-    int x = a[tid];
-    if (tid >= off) x += a[tid - off];
-    b[tid] = x;
-    __syncthreads();
-    int* t = a; a = b; b = t;
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
-  const int incl = a[tid];
-  if (total) *total = a[SEL_THREADS - 1];
+  return v;
+}
+
+// Exclusive prefix over the workgroup's SEL_THREADS values (wave scans plus one
+// pass over the 16 wave totals); `total` receives the sum when non-null.
+__device__ inline int block_excl_scan(int v, int* wsum, int tid, int* total) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_THREADS / 64; ++w) {
+    const int x = wsum[w];
+    base += w < wave ? x : 0;
+    tot += x;
+  }
+  if (total) *total = tot;
+  __syncthreads();   // wsum is reused by the next scan
+  return base + incl - v;
 }
 
 static __global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs a) {
   extern __shared__ uint32_t keys[];   // N keys
   __shared__ int hist[16][256];
-  __shared__ int scan_buf[2 * SEL_THREADS];
+  __shared__ int wsum[SEL_THREADS / 64];
+  __shared__ uint32_t wmax[SEL_THREADS / 64], wmin[SEL_THREADS / 64];
   __shared__ int s_sel[2];
-  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ctx = a.st.ctx[b];
   const int nch = (ctx + SC_CHUNK - 1) / SC_CHUNK;
   const long long pb = (long long)b * a.nchunk_max;
 
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   for (int n = tid; n < a.N; n += SEL_THREADS) {
     float s;
     if (!a.qk) {
@@ -462,36 +474,60 @@ select_kernel(const SelectArgs a) {
       s = sk * sq;
     }
     if (a.scores) a.scores[(long long)b * a.N + n] = s;
-    keys[n] = __float_as_uint(s);
+    const uint32_t kv = __float_as_uint(s);
+    keys[n] = kv;
+    kmax = kv > kmax ? kv : kmax;
+    kmin = kv < kmin ? kv : kmin;
   }
+  // range of the keys: bits above the highest one in which any two differ are common
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t x = (uint32_t)__shfl_xor((int)kmax, off, 64);
+    const uint32_t y = (uint32_t)__shfl_xor((int)kmin, off, 64);
+    kmax = x > kmax ? x : kmax;
+    kmin = y < kmin ? y : kmin;
+  }
+  if (lane == 0) { wmax[wave] = kmax; wmin[wave] = kmin; }
   __syncthreads();
-
-  uint32_t prefix = 0, mask = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_THREADS / 64; ++w) {
+    kmax = wmax[w] > kmax ? wmax[w] : kmax;
+    kmin = wmin[w] < kmin ? wmin[w] : kmin;
+  }
+  const int hbit = kmax == kmin ? -1 : 31 - __clz(kmax ^ kmin);
+  const uint32_t low = hbit >= 31 ? 0xFFFFFFFFu : ((1u << (hbit + 1)) - 1u);
+  uint32_t mask = ~low, prefix = kmax & ~low;
   int kr = a.k;   // still to take among keys matching prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+
+  // radix passes of up to 8 bits from the highest differing bit down
+  for (int hi = hbit; hi >= 0;) {
+    const int w = hi + 1 < 8 ? hi + 1 : 8;
+    const int lo = hi - w + 1;
+    const int nb = 1 << w;
     for (int i = tid; i < 16 * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;
     __syncthreads();
     for (int n = tid; n < a.N; n += SEL_THREADS) {
       const uint32_t kv = keys[n];
-      if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> shift) & 0xFF], 1);
+      if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> lo) & (uint32_t)(nb - 1)], 1);
     }
     __syncthreads();
-    // bins in descending digit order: position p <-> digit 255 - p
+    // bins in descending digit order: position p <-> digit nb - 1 - p
     int cnt = 0;
-    if (tid < 256) {
-      const int d = 255 - tid;
-      for (int w = 0; w < 16; ++w) cnt += hist[w][d];
+    if (tid < nb) {
+      const int d = nb - 1 - tid;
+#pragma unroll
+      for (int wv = 0; wv < 16; ++wv) cnt += hist[wv][d];
     }
-    const int before = block_excl_scan_1024(tid < 256 ? cnt : 0, scan_buf, tid, nullptr);
-    if (tid < 256 && before < kr && kr <= before + cnt) {
-      s_sel[0] = 255 - tid;
+    const int before = block_excl_scan(tid < nb ? cnt : 0, wsum, tid, nullptr);
+    if (tid < nb && before < kr && kr <= before + cnt) {
+      s_sel[0] = nb - 1 - tid;
       s_sel[1] = before;
     }
     __syncthreads();
-    prefix |= (uint32_t)s_sel[0] << shift;
-    mask |= 0xFFu << shift;
+    prefix |= (uint32_t)s_sel[0] << lo;
+    mask |= (uint32_t)(nb - 1) << lo;
     kr -= s_sel[1];
+    hi = lo - 1;
     __syncthreads();
   }
   const uint32_t tau = prefix;   // the k-th largest key; take kr of the keys equal to it
@@ -505,10 +541,10 @@ select_kernel(const SelectArgs a) {
     n_gt += kv > tau;
     n_eq += kv == tau;
   }
-  const int eq_before = block_excl_scan_1024(n_eq, scan_buf, tid, nullptr);
+  const int eq_before = block_excl_scan(n_eq, wsum, tid, nullptr);
   int take_eq = kr - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
-  const int pos0 = block_excl_scan_1024(n_gt + take_eq, scan_buf, tid, nullptr);
+  const int pos0 = block_excl_scan(n_gt + take_eq, wsum, tid, nullptr);
   int pos = pos0, eq_seen = 0;
   int* out = a.idx + (long long)b * a.k;
   for (int n = lo; n < hi; ++n) {
@@ -598,12 +634,15 @@ colred_kernel(const ColredArgs a) {
 }
 
 // MFMA form of the same reduction for bf16 operands.  A workgroup owns 256
-// columns of P and a chunk of CRM_CHUNK rows; it walks the chunk in slices of
-// 64 rows: the P slice is transposed into LDS as [column][row] (K-contiguous
-// for the matrix cores), Z is converted to bf16 and stored as [q][row], and
-// 16x16x32 MFMAs accumulate C[column][q].  Each wave owns 64 columns.
-constexpr int CRM_CHUNK = 256;
+// columns of P and a chunk of CRM_CHUNK rows, taken as CRM_SLICES slices of 64
+// rows whose global loads are all issued before the first is consumed (the
+// work is latency-bound otherwise): each P slice is transposed into LDS as
+// [column][row] (K-contiguous for the matrix cores), Z is converted to bf16 and
+// stored as [q][row], and 16x16x32 MFMAs accumulate C[column][q].  Each wave
+// owns 64 columns.
 constexpr int CRM_SLICE = 64;
+constexpr int CRM_SLICES = 2;
+constexpr int CRM_CHUNK = CRM_SLICE * CRM_SLICES;
 constexpr int CRM_COLS = 256;
 
 template <int RM>
@@ -639,41 +678,46 @@ colred_mfma_kernel(const ColredArgs a) {
 
   const int r_begin = ch * CRM_CHUNK;
   const int r_end = min(m_rows, r_begin + CRM_CHUNK);
-  for (int r0 = r_begin; r0 < r_end; r0 += CRM_SLICE) {
-    // global -> registers
-    uint4 pv[8];
+  // all slices' loads first
+  uint4 pv[CRM_SLICES][8];
+  float zv[CRM_SLICES][RM / 4];
+  const int zt = tid & 63;
+  const int zq0 = (tid >> 6) * (RM / 4);
+#pragma unroll
+  for (int sl = 0; sl < CRM_SLICES; ++sl) {
+    const int r0 = r_begin + sl * CRM_SLICE;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int r = r0 + pr0 + i;
-      const bool ok = r < r_end && c_ok;
-      if (r >= m_rows) r = m_rows - 1;
+      if (r >= m_rows) r = m_rows - 1;   // loaded and zeroed below
       long long prow;
       if (a.mode == 0) prow = (long long)r * a.ldp;
       else prow = is_out ? a.p_out_off + (long long)r * a.ldp_out : (long long)(ctx_pre_g + r) * a.ldp;
-      pv[i] = *reinterpret_cast<const uint4*>(P + prow + pcol);
-      if (!ok) pv[i] = make_uint4(0, 0, 0, 0);
+      pv[sl][i] = *reinterpret_cast<const uint4*>(P + prow + pcol);
     }
-    // Z slice: thread -> (row zt, q range)
-    float zv[RM / 4];
-    const int zt = tid & 63;
-    const int zq0 = (tid >> 6) * (RM / 4);
-    {
-      const int r = r0 + zt;
-      const bool ok = r < r_end;
-      const long long tok = ok ? (a.mode == 0 ? r : group_token(a.st, g, r)) : 0;
+    const int r = r0 + zt;
+    const bool ok = r < r_end;
+    const long long tok = ok ? (a.mode == 0 ? r : group_token(a.st, g, r)) : 0;
 #pragma unroll
-      for (int q = 0; q < RM / 4; ++q)
-        zv[q] = (ok && zq0 + q < a.R) ? a.Z[tok * a.ldz + a.zc0 + zq0 + q] : 0.f;
-    }
-    __syncthreads();   // previous slice fully consumed
+    for (int q = 0; q < RM / 4; ++q)
+      zv[sl][q] = (ok && zq0 + q < a.R) ? a.Z[tok * a.ldz + a.zc0 + zq0 + q] : 0.f;
+  }
+#pragma unroll
+  for (int sl = 0; sl < CRM_SLICES; ++sl) {
+    const int r0 = r_begin + sl * CRM_SLICE;
+    if (r0 >= r_end) break;   // uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(r0 + pr0 + i < r_end && c_ok)) pv[sl][i] = make_uint4(0, 0, 0, 0);
+    if (sl > 0) __syncthreads();   // previous slice fully consumed
     // transpose P: 8 rows x 8 columns -> 8 columns x 8 rows
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t w[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&pv[2 * p]);
-        const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&pv[2 * p + 1]);
+        const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p]);
+        const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p + 1]);
         const uint32_t lo = (c0[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
         const uint32_t hi = (c1[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
         w[p] = lo | (hi << 16);
@@ -681,7 +725,7 @@ colred_mfma_kernel(const ColredArgs a) {
       *reinterpret_cast<uint4*>(&Ps[(pc + j) * LD + pr0]) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 #pragma unroll
-    for (int q = 0; q < RM / 4; ++q) Zs[(zq0 + q) * LD + zt] = f2bf(zv[q]);
+    for (int q = 0; q < RM / 4; ++q) Zs[(zq0 + q) * LD + zt] = f2bf(zv[sl][q]);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < CRM_SLICE / 32; ++ks) {

@@ -30,7 +30,7 @@ struct FfnGeom {
   int ks_down, ks_dx, RM1, RM2, chunk;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
-      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp,
+      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp, w_rp,
       ws_bytes;
 };
 
@@ -110,6 +110,15 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_inv = w.take((size_t)st.nseq * F * 4);
   g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
   g.w_skp = w.take((size_t)skinny_part_floats(g.T, D > F ? D : F) * 4);
+  {
+    // split last round of the gate/up (dual) and dH gather-GEMMs
+    const int bk = g.esz == 2 ? 64 : 32;
+    const int kt_gu = ceil_div(D, bk) + ceil_div(2 * g.rp, bk);
+    const int kt_dh = ceil_div(D, bk) + ceil_div(g.rp, bk);
+    const long long f1 = ng_rpart_floats(st, g.k, F, G_BN / 2, kt_gu);
+    const long long f2 = ng_rpart_floats(st, g.k, F, G_BN, kt_dh);
+    g.w_rp = w.take((size_t)(f1 > f2 ? f1 : f2) * 4);
+  }
   g.ws_bytes = w.off;
   return SL_OK;
 }
@@ -181,6 +190,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.seg[0] = GSeg{X, D, 0, 0, 1, w->Wg, w->Wu, D, 1, D, nullptr, 0, 0};
     a.seg[1] = GSeg{zs_gu, 2 * rp, 0, 0, 1, Pg, Pu, 2 * rp, 1, 2 * rp, nullptr, 0, 0};
     a.o0 = Gc; a.o1 = Uc; a.o2 = Hc;
+    a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
     a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SWIGLU, true>(a, strm, TS_GU_FWD)));
   }
@@ -290,6 +300,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
     a.o0 = dGc; a.o1 = dUc;
     a.i0 = Gc; a.i1 = Uc;
+    a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
     a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
   }

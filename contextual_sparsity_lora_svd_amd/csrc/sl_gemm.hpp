@@ -74,6 +74,11 @@ struct GemmArgs {
   long long ldc_ctx, ldc_out, c_out_off;  // compact geometry of o*/i* buffers
   float* part;                          // KG split partials [ksplit][T_out][N]
   const int* iota;                      // KG: 0, 1, 2, ... (rows of ungathered segments)
+  // NG: logical tiles [0, rem_start) run whole; every later tile runs as
+  // rem_split K pieces (the grid's last, partial round) that write fp32
+  // partial tiles [piece][G_BM][G_BN] to rpart for ng_fixup_kernel.
+  int ntiles, rem_start, rem_split;
+  float* rpart;
 };
 
 template <typename T> struct GTraits;
@@ -201,7 +206,16 @@ gather_gemm_kernel(const GemmArgs args) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- locate the tile --------------------------------------------------
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const bool split_grid = MODE == MODE_NG && args.rem_split > 1;
+  int tile, rks = 0, rnks = 1;
+  if (split_grid && (int)blockIdx.x >= args.rem_start) {
+    const int p = blockIdx.x - args.rem_start;
+    tile = args.rem_start + p / args.rem_split;
+    rks = p % args.rem_split;
+    rnks = args.rem_split;
+  } else {
+    tile = xcd_remap(blockIdx.x, split_grid ? args.rem_start : (int)gridDim.x);
+  }
   int g = 0;
   while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
   g = __builtin_amdgcn_readfirstlane(g);
@@ -213,11 +227,11 @@ gather_gemm_kernel(const GemmArgs args) {
   const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
   const int ntm = (m_rows + BM - 1) / BM;
   int ntn, nks;
-  if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = 1; }
+  if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = rnks; }
   else { ntn = (args.N + G_BN - 1) / G_BN; nks = is_out ? args.ksplit_out : 1; }
   const int mt = t_in % ntm;
   const int nt = (t_in / ntm) % ntn;
-  const int ks = t_in / (ntm * ntn);
+  const int ks = MODE == MODE_NG ? rks : t_in / (ntm * ntn);
   const int m0 = mt * BM;
   const int n0 = nt * BNC;
 
@@ -543,7 +557,16 @@ gather_gemm_kernel(const GemmArgs args) {
       __syncthreads();
       const int r = m0 + WM * wm + 32 * mb + er;
       const float* src = ep + er * EP_LD;
-      if (r < m_rows) {
+      if (MODE == MODE_NG && nks > 1) {
+        // K piece of a split tile: raw accumulators, tile-local [row][accumulator column]
+        if (r < m_rows) {
+          float* dst = args.rpart +
+                       ((long long)(blockIdx.x - args.rem_start) * BM + WM * wm + 32 * mb + er) * G_BN +
+                       128 * wn + 32 * (ec ? nb1 : nb0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) store_row<float, 8>(dst + 8 * q, src + ec + 8 * q, 8);
+        }
+      } else if (r < m_rows) {
         // 8 columns at a time keeps the temporaries small while later
         // accumulator blocks are still live
 #pragma unroll 1
@@ -605,9 +628,128 @@ gather_gemm_kernel(const GemmArgs args) {
   }
 }
 
+// Adds the K pieces of every split N-gather tile in piece order and applies
+// the tile's element-wise epilogue (the same arithmetic as the GEMM's own).
+// One thread per (split tile, row, 8 channels).
+template <typename T, int EPI, bool DUAL>
+__global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
+  constexpr int BM = G_BM;
+  constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
+  constexpr int CG = BNC / 8;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nrem = args.ntiles - args.rem_start;
+  if (i >= (long long)nrem * BM * CG) return;
+  const int cg = (int)(i % CG);
+  const int rloc = (int)((i / CG) % BM);
+  const int tr = (int)(i / ((long long)CG * BM));
+  const int tile = args.rem_start + tr;
+  int g = 0;
+  while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
+  const int t_in = tile - args.tile_start[g];
+  const bool is_out = (g == args.st.nseq);
+  const int m_rows = group_rows(args.st, g);
+  const int nch = is_out ? args.n_out : args.kidx;
+  const int ntm = (m_rows + BM - 1) / BM;
+  const int mt = t_in % ntm, nt = t_in / ntm;
+  const int r = mt * BM + rloc;
+  if (r >= m_rows) return;
+  const int cl = cg * 8;
+  const int c = nt * BNC + cl;
+  if (c >= nch) return;
+  // accumulator column of channel cl (8 consecutive channels stay in one 32-block)
+  int ag;
+  if (DUAL) ag = 128 * (cl / 64) + 32 * ((cl % 64) / 32) + (cl % 32);
+  else ag = cl;
+  float v0[8], v1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { v0[j] = 0.f; v1[j] = 0.f; }
+  for (int sp = 0; sp < args.rem_split; ++sp) {
+    const float* src = args.rpart + ((long long)(tr * args.rem_split + sp) * BM + rloc) * G_BN + ag;
+    float a0[8];
+    load_row<float, 8>(src, a0, 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v0[j] += a0[j];
+    if (DUAL) {
+      float a1[8];
+      load_row<float, 8>(src + 64, a1, 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v1[j] += a1[j];
+    }
+  }
+  const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];
+  const long long ldc = is_out ? args.ldc_out : args.ldc_ctx;
+  const long long cbase = is_out ? args.c_out_off : (long long)ctx_pre_g * args.ldc_ctx;
+  const long long o = cbase + (long long)r * ldc + c;
+  if constexpr (EPI == EPI_SWIGLU) {
+    float hv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sg = (sizeof(T) == 4) ? sigmoid_exact(v0[j]) : sigmoidf_(v0[j]);
+      hv[j] = v0[j] * sg * v1[j];
+    }
+    store_row<T, 8>(reinterpret_cast<T*>(args.o0) + o, v0, nch - c);
+    store_row<T, 8>(reinterpret_cast<T*>(args.o1) + o, v1, nch - c);
+    store_row<T, 8>(reinterpret_cast<T*>(args.o2) + o, hv, nch - c);
+  } else {   // EPI_DSWIGLU
+    float gv[8], uv[8], dg[8], du[8];
+    load_row<T, 8>(reinterpret_cast<const T*>(args.i0) + o, gv, nch - c);
+    load_row<T, 8>(reinterpret_cast<const T*>(args.i1) + o, uv, nch - c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sg = (sizeof(T) == 4) ? sigmoid_exact(gv[j]) : sigmoidf_(gv[j]);
+      dg[j] = v0[j] * uv[j] * sg * (1.0f + gv[j] * (1.0f - sg));
+      du[j] = v0[j] * gv[j] * sg;
+    }
+    store_row<T, 8>(reinterpret_cast<T*>(args.o0) + o, dg, nch - c);
+    store_row<T, 8>(reinterpret_cast<T*>(args.o1) + o, du, nch - c);
+  }
+}
+
 bool timer_on();
 void timer_begin(int slot, hipStream_t s);
 void timer_end(int slot, hipStream_t s);
+int device_cus();
+
+// N-gather tiles of a launch (all groups).
+inline long long ng_tiles(const SeqTab& st, int kidx, int n_out, int bnc) {
+  long long total = 0;
+  for (int g = 0; g <= st.nseq; ++g) {
+    const bool is_out = g == st.nseq;
+    const int m = is_out ? st.T_out : st.ctx[g];
+    const int nch = is_out ? n_out : kidx;
+    if (m <= 0 || nch <= 0) continue;
+    total += (long long)((m + G_BM - 1) / G_BM) * ((nch + bnc - 1) / bnc);
+  }
+  return total;
+}
+
+// Split of the last, partial round of an N-gather grid: with `slots` resident
+// workgroups, the remainder tiles (total mod slots, if at most half the slots)
+// run as `split` K pieces each so that the round is filled.  split = 1: none.
+inline void ng_split_plan(long long total, int total_kt, int slots, int& rem_start, int& split) {
+  rem_start = (int)total;
+  split = 1;
+  if (slots <= 0 || total <= slots) return;
+  const long long rem = total % slots;
+  if (rem == 0 || 2 * rem > slots) return;
+  int s = (int)(slots / rem);
+  if (s > 8) s = 8;
+  if (s > total_kt / 4) s = total_kt / 4;
+  if (s < 2) return;
+  split = s;
+  rem_start = (int)(total - rem);
+}
+
+// Workgroup slots of the 128-row gather-GEMM on the current device (two per CU).
+inline int gemm_slots() { return 2 * device_cus(); }
+
+// Floats of partial tiles a split N-gather launch needs (0 when it does not split).
+inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, int bnc, int total_kt) {
+  int rs, sp;
+  const long long total = ng_tiles(st, kidx, n_out, bnc);
+  ng_split_plan(total, total_kt, gemm_slots(), rs, sp);
+  return sp > 1 ? (total - rs) * sp * (long long)G_BM * G_BN : 0;
+}
 
 // Host side: count tiles per group and launch.
 template <typename T, int MODE, int EPI, bool DUAL>
@@ -628,11 +770,33 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
     total += ntm * ntn * nks;
   }
   a.tile_start[a.ngroups] = total;
+  a.ntiles = total;
+  a.rem_start = total;
+  a.rem_split = 1;
   if (total == 0) return hipSuccess;
+  long long grid = total;
+  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU)) {
+    if (a.rpart) {
+      constexpr int BK = GTraits<T>::BK;
+      int total_kt = 0;
+      for (int s = 0; s < a.nseg; ++s) total_kt += (a.seg[s].K + BK - 1) / BK;   // NG segments: fixed K
+      ng_split_plan(total, total_kt, gemm_slots(), a.rem_start, a.rem_split);
+      grid = a.rem_start + (long long)(total - a.rem_start) * a.rem_split;
+    }
+  }
   timer_begin(timer_slot, stream);
-  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM>), dim3(total),
+  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM>), dim3((unsigned)grid),
                      dim3(G_THREADS), 0, stream, a);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU)) {
+    if (e == hipSuccess && a.rem_split > 1) {
+      constexpr int CG = (DUAL ? G_BN / 2 : G_BN) / 8;
+      const long long n = (long long)(total - a.rem_start) * G_BM * CG;
+      hipLaunchKernelGGL((ng_fixup_kernel<T, EPI, DUAL>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                         0, stream, a);
+      e = hipGetLastError();
+    }
+  }
   timer_end(timer_slot, stream);
   return e;
 }

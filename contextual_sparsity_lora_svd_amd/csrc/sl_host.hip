@@ -18,6 +18,17 @@ void set_error(const char* fmt, ...) {
 
 const char* last_error() { return g_err.c_str(); }
 
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static int cus[64] = {0};   // per device, filled on first use (benign race: same value)
+  if (dev >= 0 && dev < 64 && cus[dev] > 0) return cus[dev];
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cus[dev] = prop.multiProcessorCount;
+  return prop.multiProcessorCount;
+}
+
 sl_status check_arch() {
   int dev = 0;
   SL_HIP(hipGetDevice(&dev));

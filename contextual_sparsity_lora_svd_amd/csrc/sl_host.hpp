@@ -31,6 +31,7 @@ const char* last_error();
   } while (0)
 
 sl_status check_arch();
+int device_cus();   // compute units of the current device (0 when none)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

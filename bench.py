@@ -104,6 +104,91 @@ def cpu_baseline(p, ctx, L, Pt_g, Q_g, Pt_u, Q_u, k, budget_s):
                       f"in numpy (scores fp32, fwd/bwd fp64), one run of {t:.2f} s"}
 
 
+def attn_flops(D, nq, nkv, G, r, ctx, L, kqk, kvo):
+    """Algorithmic FLOPs of q/k/v/o forward + backward (base and LoRA)."""
+    def R(kc, n):
+        return sum(c * kc + (L - c) * n for c in ctx)
+    T = len(ctx) * L
+    Rq, Rk, Rv, Ro = R(kqk * G, nq), R(kqk, nkv), R(kvo, nkv), R(kvo * G, nq)
+    Rs = Rq + Rk + Rv + Ro
+    return 4 * D * Rs + 3 * (8 * T * D * r + 2 * r * Rs)
+
+
+def attn_bench(args, torch, sl):
+    """q/k/v/o rows of the path on the LLaMA2-7B attention workload: QK-norm and
+    L2 selection over context tokens, sparse q/k/v/o forward and backward."""
+    wl = W.WORKLOADS[3]
+    s = wl.attn[0]
+    heads = (s.n_q_heads, s.n_kv_heads, s.head_dim)
+    D, r, r_e, L = s.d_model, s.lora_rank, wl.est_rank, wl.seq_len
+    nq, nkv = heads[0] * heads[2], heads[1] * heads[2]
+    G = heads[0] // heads[1]
+    ctx = [int(c) for c in W.ctx_lengths(wl)]
+    B = len(ctx)
+    T = B * L
+    kqk, kvo = sl.k_from_ratio(nkv, s.sparsity_qk_pct), sl.k_from_ratio(nkv, s.sparsity_vo_pct)
+    print(f"[bench] {wl.name}: D={D} heads={heads} r={r} B={B} L={L} ctx={ctx} k_qk={kqk} k_vo={kvo}",
+          file=sys.stderr, flush=True)
+    p = W.make_attn_tensors(wl)
+    bf = torch.bfloat16
+    t = {n: to_dev(p[n], torch, bf) for n in ("Wq", "Wk", "Wv", "Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo")}
+    t["WoT"] = to_dev(np.ascontiguousarray(p["Wo"].T), torch, bf)
+    X, a = to_dev(p["X"], torch, bf), to_dev(p["a"], torch, bf)
+    dq, dk, dv, dout = (to_dev(p[n], torch, bf) for n in ("dq", "dk", "dv", "d_out"))
+    del p
+    w = sl.QKVOWeights(t, heads)
+    lay = sl.Layout(ctx, L)
+    f = {n: sl.build_estimator(t[n], r_e) for n in ("Wq", "Wk", "Wv")}
+    torch.cuda.synchronize()
+    est_qk = sl.EstimateBuffers(sl.SL_CRIT_QK_NORM, lay, D, r_e, nkv, kqk, X.device, heads=heads)
+    est_vo = sl.EstimateBuffers(sl.SL_CRIT_L2, lay, D, r_e, nkv, kvo, X.device)
+    buf = sl.QKVOWorkspace(w, lay, kqk, kvo, X.device)
+    outs, grads = {}, {}
+
+    def step():
+        iqk, _ = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, r_e, f["Wq"][0], f["Wq"][1], f["Wk"][0],
+                                    f["Wk"][1], nkv, kqk, heads=heads, bufs=est_qk)
+        ivo, _ = sl.estimate_select(sl.SL_CRIT_L2, X, lay, r_e, f["Wv"][0], f["Wv"][1], None, None, nkv,
+                                    kvo, bufs=est_vo)
+        o, _ = sl.qkvo_fwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf=buf, outs=outs)
+        outs.update(o)
+        g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, dq=dq, dk=dk, dv=dv, d_out=dout, out=grads)
+        grads.update(g)
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    full = torch.arange(nkv, dtype=torch.int32, device=X.device).repeat(B, 1).contiguous()
+    bufd = sl.QKVOWorkspace(w, lay, nkv, nkv, X.device)
+    outs_d, grads_d = {}, {}
+
+    def step_dense():
+        o, _ = sl.qkvo_fwd(w, X, a, lay, nkv, full, nkv, full, buf=bufd, outs=outs_d)
+        outs_d.update(o)
+        g = sl.qkvo_bwd(w, X, a, lay, nkv, full, nkv, full, bufd, dq=dq, dk=dk, dv=dv, d_out=dout, out=grads_d)
+        grads_d.update(g)
+
+    dense_ms = timed(torch, step_dense, max(3, args.steps // 2), 2) if not args.no_dense else None
+    fl = attn_flops(D, nq, nkv, G, r, ctx, L, kqk, kvo)
+    print(f"[bench] attention step {ms:.3f} ms" + (f", dense {dense_ms:.3f} ms" if dense_ms else ""),
+          file=sys.stderr, flush=True)
+    return {"workload": wl.name, "batch": B, "seq_len": L, "ctx_len": ctx, "heads": list(heads),
+            "k_qk": kqk, "k_vo": kvo, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "effective_tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_gflop": fl / 1e9,
+            "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
+
+
+def timed(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +197,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-attn", action="store_true", help="skip the q/k/v/o workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain bf16 -> fp32 copy of 64 Mi elements (128 MiB read, "
                          "256 MiB written) to calibrate HBM byte counters")
@@ -143,10 +229,13 @@ def main():
     w = sl.FFNWeights(t, lora_scale=1.0)
     lay = sl.Layout(ctx, L)
 
-    # offline estimator (a0), untimed
+    # offline estimator (a0): outside the step; its one-time cost is reported
+    torch.cuda.synchronize()
+    t_b = time.perf_counter()
     Ptg, Qg, _ = sl.build_estimator(t["Wg"], r_e)
     Ptu, Qu, _ = sl.build_estimator(t["Wu"], r_e)
     torch.cuda.synchronize()
+    build_ms = (time.perf_counter() - t_b) * 1e3 / 2
 
     buf = sl.FFNWorkspace(w, lay, k, X.device)
     est = sl.EstimateBuffers(sl.SL_CRIT_SWIGLU_L2, lay, D, r_e, F, k, X.device)
@@ -160,18 +249,6 @@ def main():
         sl.ffn_fwd(w, X, lay, k, idx, buf, Y=Y)
         sl.ffn_bwd(w, X, lay, k, idx, buf, dY, out=grads)
 
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(steps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / steps
-
     # Per-kernel breakdown (events around every main kernel; the events add
     # idle gaps, so this pass is not the headline time).
     names = ("estimate", "select", "gu_fwd", "down_fwd", "dh_bwd", "dx_bwd")
@@ -180,7 +257,7 @@ def main():
         step()
     torch.cuda.synchronize()
     sl.timer_reset()
-    ms_all = timed(step, args.steps, 0)
+    ms_all = timed(torch, step, args.steps, 0)
     kern = {}
     for name in names:
         tot, n = sl.timer_read(name)
@@ -193,7 +270,7 @@ def main():
     # around the dominant kernel only.
     sl.timer_select([dom])
     sl.timer_reset()
-    ms = timed(step, args.steps, 0)
+    ms = timed(torch, step, args.steps, 0)
     tot, n = sl.timer_read(dom)
     dom_ms = tot / n
     sl.timer_enable(0)
@@ -217,10 +294,16 @@ def main():
             sl.ffn_fwd(w, X, lay, F, idx_full, bufd, Y=Y)
             sl.ffn_bwd(w, X, lay, F, idx_full, bufd, dY, out=grads)
 
-        dense_ms = timed(step_dense, max(3, args.steps // 2), 2)
+        dense_ms = timed(torch, step_dense, max(3, args.steps // 2), 2)
         dense = {"ms_per_step": dense_ms, "speedup": dense_ms / ms}
         print(f"[bench] dense step {dense_ms:.3f} ms", file=sys.stderr, flush=True)
         del bufd
+
+    attn = None
+    if not args.no_attn:
+        del buf, est
+        torch.cuda.empty_cache()
+        attn = attn_bench(args, torch, sl)
 
     if args.copy_calibration:
         n = 64 << 20
@@ -263,6 +346,8 @@ def main():
         "estimator_share": {"time": (kern.get("estimate", {}).get("share", 0) +
                                      kern.get("select", {}).get("share", 0))},
         "kernels": kern,
+        "estimator_build_ms_per_weight": build_ms,
+        "attention": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -53,9 +53,15 @@ sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, l
 template <typename T>
 sl_status launch_score(const ScoreArgs& a, int nseq, int rank, hipStream_t s) {
   const dim3 grid(ceil_div(a.N, SC_THREADS), a.nchunk_max, nseq), block(SC_THREADS);
-  if (rank <= 8) hipLaunchKernelGGL((score_kernel<T, 8>), grid, block, 0, s, a);
-  else if (rank <= 16) hipLaunchKernelGGL((score_kernel<T, 16>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((score_kernel<T, 32>), grid, block, 0, s, a);
+  if (a.swiglu) {
+    if (rank <= 8) hipLaunchKernelGGL((score_kernel<T, 8, true>), grid, block, 0, s, a);
+    else if (rank <= 16) hipLaunchKernelGGL((score_kernel<T, 16, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<T, 32, true>), grid, block, 0, s, a);
+  } else {
+    if (rank <= 8) hipLaunchKernelGGL((score_kernel<T, 8, false>), grid, block, 0, s, a);
+    else if (rank <= 16) hipLaunchKernelGGL((score_kernel<T, 16, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<T, 32, false>), grid, block, 0, s, a);
+  }
   SL_HIP(hipGetLastError());
   return SL_OK;
 }

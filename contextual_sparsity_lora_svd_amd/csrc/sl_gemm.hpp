@@ -39,6 +39,7 @@ constexpr int G_BM = SL_GEMM_BM;
 constexpr int G_BN = 256;
 constexpr int G_THREADS = 256;
 constexpr int G_MAXSEG = 4;
+constexpr int G_MAXPROB = 3;
 
 struct GSeg {
   const void* A;       // A operand base
@@ -56,10 +57,29 @@ struct GSeg {
   const int* idx; int kidx; int n_out;
 };
 
+// One problem of a launch: its channel set, the B operand of each segment, a
+// column offset into each segment's A, and its output.  Problems share the
+// token layout and every other segment field.
+struct GProb {
+  const int* idx;                       // NG: context group g uses idx + g*kidx
+  int kidx, n_out;
+  const void* B[G_MAXSEG];
+  int a_col[G_MAXSEG];
+  void* o0;
+  long long ldo;
+};
+
 struct GemmArgs {
   SeqTab st;
-  int ngroups;                          // nseq + 1
-  int tile_start[SL_MAX_SEQS + 2];
+  // Tiles run problem by problem, and within a problem group by group
+  // (context groups 0..nseq-1, then the output group): flat group
+  // p*(nseq+1) + g starts at logical tile tile_start[.].
+  int ngroups;                          // nprob * (nseq + 1)
+  int tile_start[G_MAXPROB * (SL_MAX_SEQS + 1) + 1];
+  // N-gather launches may hold up to G_MAXPROB problems (prob[1..]); a launch
+  // that leaves nprob at 0 has one, taken from idx/kidx/n_out/seg[].B/o0/ldo.
+  int nprob;
+  GProb prob[G_MAXPROB];
   // NG: output channel set (context group g: idx + g*kidx; output group: all n_out)
   const int* idx;
   int kidx;
@@ -216,15 +236,26 @@ gather_gemm_kernel(const GemmArgs args) {
   } else {
     tile = xcd_remap(blockIdx.x, split_grid ? args.rem_start : (int)gridDim.x);
   }
-  int g = 0;
-  while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
-  g = __builtin_amdgcn_readfirstlane(g);
-  const int t_in = tile - args.tile_start[g];
+  // flat group: the last one starting at or before the tile (empty groups
+  // start where the next one does)
+  int gg = 0;
+  {
+    int hi = args.ngroups - 1;
+    while (gg < hi) {
+      const int mid = (gg + hi + 1) >> 1;
+      if (args.tile_start[mid] <= tile) gg = mid; else hi = mid - 1;
+    }
+  }
+  gg = __builtin_amdgcn_readfirstlane(gg);
+  const int t_in = tile - args.tile_start[gg];
+  const int pid = gg / (args.st.nseq + 1);
+  const int g = gg - pid * (args.st.nseq + 1);
+  const GProb& pr = args.prob[pid];
   const bool is_out = (g == args.st.nseq);
   const int m_rows = group_rows(args.st, g);
   const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];
-  const int nch = is_out ? args.n_out : args.kidx;
-  const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
+  const int nch = is_out ? pr.n_out : pr.kidx;
+  const int* gidx = is_out ? nullptr : pr.idx + (long long)g * pr.kidx;
   const int ntm = (m_rows + BM - 1) / BM;
   int ntn, nks;
   if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = rnks; }
@@ -295,9 +326,9 @@ gather_gemm_kernel(const GemmArgs args) {
     cur_s = s;
     cur_K = __builtin_amdgcn_readfirstlane(seg_len(s));
     cur_nkt = (cur_K + BK - 1) / BK;
-    a_base = reinterpret_cast<const T*>(sg.A);
-    b_base = reinterpret_cast<const T*>(sg.B);
-    b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : sg.B);
+    a_base = reinterpret_cast<const T*>(sg.A) + pr.a_col[s];
+    b_base = reinterpret_cast<const T*>(pr.B[s]);
+    b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : pr.B[s]);
     cur_ldb = (int)sg.ldb;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
@@ -611,11 +642,11 @@ gather_gemm_kernel(const GemmArgs args) {
                 store_row<float, 8>(args.part + ((long long)ks * args.st.T_out + r) * args.N + c, v,
                                     args.N - c);
               else
-                store_row<T, 8>(reinterpret_cast<T*>(args.o0) +
-                                    (long long)group_token(args.st, g, r) * args.ldo + c,
+                store_row<T, 8>(reinterpret_cast<T*>(pr.o0) +
+                                    (long long)group_token(args.st, g, r) * pr.ldo + c,
                                 v, args.N - c);
             } else {  // EPI_SCATTER: column = the channel number
-              T* out = reinterpret_cast<T*>(args.o0) + (long long)group_token(args.st, g, r) * args.ldo;
+              T* out = reinterpret_cast<T*>(pr.o0) + (long long)group_token(args.st, g, r) * pr.ldo;
 #pragma unroll
               for (int j = 0; j < 8; ++j)
                 if (c + j < nch) stv<T>(out, gidx ? gidx[c + j] : c + j, v[j]);
@@ -643,7 +674,7 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
   const int rloc = (int)((i / CG) % BM);
   const int tr = (int)(i / ((long long)CG * BM));
   const int tile = args.rem_start + tr;
-  int g = 0;
+  int g = 0;   // split launches hold one problem: flat group = group
   while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
   const int t_in = tile - args.tile_start[g];
   const bool is_out = (g == args.st.nseq);
@@ -755,13 +786,25 @@ inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, int bnc,
 template <typename T, int MODE, int EPI, bool DUAL>
 hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
-  a.ngroups = a.st.nseq + 1;
+  if (a.nprob <= 0) {
+    a.nprob = 1;
+    GProb& p0 = a.prob[0];
+    p0.idx = a.idx; p0.kidx = a.kidx; p0.n_out = a.n_out;
+    for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.a_col[s] = 0; }
+    p0.o0 = a.o0; p0.ldo = a.ldo;
+  }
+  if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))
+    return hipErrorInvalidValue;
+  const int gpp = a.st.nseq + 1;
+  a.ngroups = a.nprob * gpp;
   int total = 0;
-  for (int g = 0; g < a.ngroups; ++g) {
-    a.tile_start[g] = total;
+  for (int q = 0; q < a.ngroups; ++q) {
+    a.tile_start[q] = total;
+    const GProb& pr = a.prob[q / gpp];
+    const int g = q % gpp;
     const bool is_out = g == a.st.nseq;
     const int m = is_out ? a.st.T_out : a.st.ctx[g];
-    const int nch = is_out ? a.n_out : a.kidx;
+    const int nch = is_out ? pr.n_out : pr.kidx;
     if (m <= 0 || (MODE == MODE_NG && nch <= 0)) continue;
     const int ntm = (m + G_BM - 1) / G_BM;
     int ntn, nks;

@@ -135,39 +135,6 @@ inline sl_status launch_colred(ColredArgs& a, int nchunks_total, int nmax, int R
   return SL_OK;
 }
 
-template <typename T>
-inline sl_status fill_zero(void* p, long long n, hipStream_t s) {
-  if (n <= 0) return SL_OK;
-  hipLaunchKernelGGL((fill_kernel<T>), grid1d(n), dim3(256), 0, s, reinterpret_cast<T*>(p), n);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
-}
-
-template <typename T>
-inline sl_status copy2d(void* dst, long long ldd, int row_off, int col_off, int rows, int cols,
-                        const void* src, long long lds, int transposed, hipStream_t s) {
-  const long long n = (long long)rows * cols;
-  if (n <= 0) return SL_OK;
-  hipLaunchKernelGGL((copy2d_kernel<T>), grid1d(n), dim3(256), 0, s, reinterpret_cast<T*>(dst),
-                     ldd, row_off, col_off, rows, cols, reinterpret_cast<const T*>(src), lds,
-                     transposed);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
-}
-
-template <typename T>
-inline sl_status gather_factor(void* dst, long long ldd, long long gstride, const int* idx, int k,
-                               int nseq, int r, const void* src, long long lds, int rows_of_ch,
-                               hipStream_t s) {
-  const long long n = (long long)nseq * r * k;
-  if (n <= 0) return SL_OK;
-  hipLaunchKernelGGL((gather_factor_kernel<T>), grid1d(n), dim3(256), 0, s,
-                     reinterpret_cast<T*>(dst), ldd, gstride, idx, k, nseq, r,
-                     reinterpret_cast<const T*>(src), lds, rows_of_ch);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
-}
-
 // Builder of one pack launch.
 struct Packer {
   PackArgs a;
@@ -215,14 +182,89 @@ struct Packer {
   }
 };
 
+// Builder of one inverse-map launch (up to IV_MAXSETS ascending channel sets).
+struct Inverter {
+  InvArgs a;
+  bool overflow = false;
+  explicit Inverter(int nseq) { std::memset(&a, 0, sizeof(a)); a.nseq = nseq; }
+  // inv [nseq, n] <- positions of channels 0..n-1 in idx [nseq, k]
+  void add(const int* idx, int k, int n, int* inv) {
+    if (a.nset >= IV_MAXSETS) { overflow = true; return; }
+    const int j = a.nset++;
+    a.idx[j] = idx; a.k[j] = k; a.n[j] = n; a.inv[j] = inv;
+  }
+  sl_status launch(hipStream_t s) {
+    if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d inverse maps", IV_MAXSETS);
+    long long t = 0;
+    for (int j = 0; j < a.nset; ++j) { a.start[j] = t; t += (long long)a.nseq * a.n[j]; }
+    a.start[a.nset] = t;
+    if (t == 0) return SL_OK;
+    hipLaunchKernelGGL(inverse_sets_kernel, grid1d(t), dim3(256), 0, s, a);
+    SL_HIP(hipGetLastError());
+    return SL_OK;
+  }
+};
+
+// Builder of one row-layout launch.
+struct Layouter {
+  LayArgs a;
+  bool overflow = false;
+  explicit Layouter(const SeqTab& st) { std::memset(&a, 0, sizeof(a)); a.st = st; }
+  LayJob* next() {
+    if (a.njobs >= LJ_MAXJOBS) { overflow = true; return nullptr; }
+    return &a.job[a.njobs++];
+  }
+  static int vec_ok(const void* p, long long ld) {
+    return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 8 == 0);
+  }
+  // context rows of token-major out [T, ld], columns [0, n) := 0
+  void zero_ctx(void* out, long long ld, int n) {
+    if (a.st.T_ctx == 0 || n <= 0) return;
+    LayJob* j = next();
+    if (!j) return;
+    j->type = LJ_ZERO; j->n = n; j->dst = out; j->ldd = ld;
+    j->vec = vec_ok(out, ld);
+  }
+  // compact copy: context rows' columns idx[b][0..k) at row stride ldc, then
+  // the output rows' n columns at dst + out_off, row stride n
+  void compact(const void* src, long long lds, const int* idx, int k, int n, void* dst, long long ldc,
+               long long out_off, size_t esz) {
+    if (a.st.T_ctx > 0 && k > 0) {
+      LayJob* j = next();
+      if (!j) return;
+      j->type = LJ_GATHER; j->n = k; j->dst = dst; j->ldd = ldc; j->src = src; j->lds = lds;
+      j->idx = idx; j->vec = vec_ok(dst, ldc);
+    }
+    if (a.st.T_out > 0 && n > 0) {
+      LayJob* j = next();
+      if (!j) return;
+      void* d = static_cast<char*>(dst) + out_off * (long long)esz;
+      j->type = LJ_ROWS; j->n = n; j->dst = d; j->ldd = n; j->src = src; j->lds = lds;
+      j->vec = vec_ok(d, n) && vec_ok(src, lds);
+    }
+  }
+  template <typename T>
+  sl_status launch(hipStream_t s) {
+    if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d layout jobs", LJ_MAXJOBS);
+    long long t = 0;
+    for (int i = 0; i < a.njobs; ++i) {
+      a.start[i] = t;
+      const LayJob& j = a.job[i];
+      const long long rows = j.type == LJ_ROWS ? a.st.T_out : a.st.T_ctx;
+      t += rows * ((j.n + 7) / 8);
+    }
+    a.start[a.njobs] = t;
+    if (t == 0) return SL_OK;
+    hipLaunchKernelGGL((layout_kernel<T>), grid1d(t), dim3(256), 0, s, a);
+    SL_HIP(hipGetLastError());
+    return SL_OK;
+  }
+};
+
 inline sl_status inverse_maps(const int* idx, int k, int nseq, int Nfull, int* inv, hipStream_t s) {
-  hipLaunchKernelGGL(inverse_map_kernel, grid1d((long long)nseq * Nfull), dim3(256), 0, s, idx, k,
-                     nseq, Nfull, inv);
-  SL_HIP(hipGetLastError());
-  hipLaunchKernelGGL(inverse_scatter_kernel, grid1d((long long)nseq * k), dim3(256), 0, s, idx, k,
-                     nseq, Nfull, inv);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
+  Inverter iv(nseq);
+  iv.add(idx, k, Nfull, inv);
+  return iv.launch(s);
 }
 
 template <typename T>

@@ -38,7 +38,7 @@ struct QkvoGeom {
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
-      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv, w_iota, w_skp, ws_bytes;
+      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv_o, w_inv_q, w_inv_k, w_inv_v, w_iota, w_skp, ws_bytes;
 };
 
 int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -132,7 +132,10 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   cr = std::max(cr, colred_part_elems_compact(st, g.kqk, g.nkv, RM1, g.chunk));
   cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1, g.chunk));
   g.w_cr = b.take((size_t)cr * 4);
-  g.w_inv = b.take(B * std::max(g.nq, g.nkv) * 4);
+  g.w_inv_o = b.take(B * g.nq * 4);
+  g.w_inv_q = b.take(B * g.nq * 4);
+  g.w_inv_k = b.take(B * g.nkv * 4);
+  g.w_inv_v = b.take(B * g.nkv * 4);
   g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
   g.w_skp = b.take((size_t)skinny_part_floats(g.T, std::max(g.D, g.nq)) * 4);
   g.ws_bytes = b.off;
@@ -148,44 +151,19 @@ sl_status expand_set(const QkvoGeom& g, const int* idx_kv, int k, int* out, hipS
   return SL_OK;
 }
 
-// compact copy: context rows' selected columns + output rows' full width
-template <typename T>
-sl_status make_compact(const QkvoGeom& g, const Comp& c, const void* src, const int* idx, void* dst,
-                       hipStream_t s) {
-  const SeqTab& st = g.st;
-  if (st.T_ctx > 0) {
-    hipLaunchKernelGGL((gather_ctx_cols_kernel<T>), grid1d((long long)st.T_ctx * c.kc), dim3(256), 0,
-                       s, st, reinterpret_cast<const T*>(src), (long long)c.n, idx, c.kc,
-                       reinterpret_cast<T*>(dst), (long long)c.ld);
-    SL_HIP(hipGetLastError());
-  }
-  if (st.T_out > 0) {
-    hipLaunchKernelGGL((gather_out_rows_kernel<T>), grid1d((long long)st.T_out * c.n), dim3(256), 0,
-                       s, st, reinterpret_cast<const T*>(src), (long long)c.n, c.n,
-                       reinterpret_cast<T*>(dst) + c.out_off, (long long)c.n);
-    SL_HIP(hipGetLastError());
-  }
-  return SL_OK;
-}
-
-template <typename T>
-sl_status zero_ctx(const QkvoGeom& g, void* out, int n, hipStream_t s) {
-  if (g.st.T_ctx == 0) return SL_OK;
-  hipLaunchKernelGGL((zero_ctx_rows_kernel<T>), grid1d((long long)g.st.T_ctx * n), dim3(256), 0, s,
-                     g.st, reinterpret_cast<T*>(out), (long long)n, n);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
+// compact copy of a projection's buffer (job of a layout launch)
+void add_compact(Layouter& L, const Comp& c, const void* src, const int* idx, void* dst, size_t esz) {
+  L.compact(src, c.n, idx, c.kc, c.n, dst, c.ld, c.out_off, esz);
 }
 
 // colred over a compact buffer + scatter finish into a factor gradient
 template <typename T>
 sl_status grad_scatter(const QkvoGeom& g, const Comp& c, const void* P, const float* Z, long long ldz,
-                       int zc0, const int* idx, int k_idx, int* inv, float* crp, float* out,
-                       int transposed, float scale, hipStream_t s) {
+                       int zc0, const int* inv, float* crp, float* out, int transposed, float scale,
+                       hipStream_t s) {
   const SeqTab& st = g.st;
   const int RM = cr_rm(g.esz, g.rp);
   sl_status rc;
-  if ((rc = inverse_maps(idx, k_idx, st.nseq, c.n, inv, s))) return rc;
   ColredArgs a;
   std::memset(&a, 0, sizeof(a));
   a.st = st; a.mode = 1; a.T = g.T;
@@ -230,14 +208,6 @@ sl_status grad_dense(const QkvoGeom& g, const void* P, int N, const float* Z, lo
   return SL_OK;
 }
 
-// Identity rows for the K-gather GEMMs' dense segments.
-template <typename T>
-sl_status prologue(const QkvoGeom& g, char* ws, hipStream_t strm) {
-  Packer pk;
-  pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
-  return pk.launch<T>(strm);
-}
-
 template <typename T>
 sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void* X, const void* a,
                         const int* idx_qk, const int* idx_vo, void* q, void* k, void* v, void* o,
@@ -254,10 +224,40 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   T* zs_o = reinterpret_cast<T*>(ws + g.w_zs_o);
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
-  if ((rc = prologue<T>(g, ws, strm))) return rc;
+  T* ac = reinterpret_cast<T*>(ws + g.w_ac);
+  T* Aog = reinterpret_cast<T*>(ws + g.w_Aog);
+  T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
+  const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+  const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
+  void* outp[3] = {q, k, v};
+  const int* sets[3] = {idx_q, idx_qk, idx_vo};
+  const int kk[3] = {g.kq, g.kqk, g.kvo};
+  const int nn[3] = {g.nq, g.nkv, g.nkv};
+  T* Bp[3] = {reinterpret_cast<T*>(ws + g.w_Bqp), reinterpret_cast<T*>(ws + g.w_Bkp),
+              reinterpret_cast<T*>(ws + g.w_Bvp)};
+
+  // query-channel sets, then one launch each for operand packing and row layout
+  if (g.G > 1 && X && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
+  if (g.G > 1 && a && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
+  Packer pk;
+  pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
+  Layouter L(st);
+  if (X) {
+    for (int j = 0; j < 3; ++j) {
+      pk.copy(Bp[j], rp, nn[j], rp, Bl[j], r, nn[j], r, 0);          // B_j, rank padded to rp
+      if (kk[j] < nn[j]) L.zero_ctx(outp[j], nn[j], nn[j]);
+    }
+  }
+  if (a) {
+    pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);                      // Bo^T [rp, D]
+    pk.gather(Aog, g.co.ld, (long long)rp * g.co.ld, rp, g.co.ld, w->Ao, g.nq, r, 0, idx_o, g.ko,
+              st.nseq);                                             // Ao[:, So] per sequence
+    add_compact(L, g.co, a, idx_o, ac, g.esz);
+  }
+  if ((rc = pk.launch<T>(strm))) return rc;
+  if ((rc = L.launch<T>(strm))) return rc;
 
   if (X) {
-    if (g.G > 1 && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
     // z = X [Aq; Ak; Av]^T
     SkinnyArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -271,40 +271,24 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.outs = zs_qkv; sa.ldos = 3 * rp; sa.scale = s;
     sa.part = skp;
     if ((rc = launch_skinny<T>(sa, strm))) return rc;
-    // the three projections
-    const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
-    const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
-    void* outp[3] = {q, k, v};
-    const int* sets[3] = {idx_q, idx_qk, idx_vo};
-    const int kk[3] = {g.kq, g.kqk, g.kvo};
-    const int nn[3] = {g.nq, g.nkv, g.nkv};
-    const size_t bp[3] = {g.w_Bqp, g.w_Bkp, g.w_Bvp};
+    // the three projections in one launch: y_j = X W_j[S_j]^T + (s z_j) B_j[S_j]^T
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.st = st;
+    ga.nseg = 2;
+    ga.seg[0] = GSeg{X, D, 0, 0, 1, nullptr, nullptr, D, 1, D, nullptr, 0, 0};
+    ga.seg[1] = GSeg{zs_qkv, 3 * rp, 0, 0, 1, nullptr, nullptr, rp, 1, rp, nullptr, 0, 0};
+    ga.nprob = 3;
     for (int j = 0; j < 3; ++j) {
-      T* Bp = reinterpret_cast<T*>(ws + bp[j]);
-      if ((rc = fill_zero<T>(Bp, (long long)nn[j] * rp, strm))) return rc;
-      if ((rc = copy2d<T>(Bp, rp, 0, 0, nn[j], r, Bl[j], r, 0, strm))) return rc;
-      if (kk[j] < nn[j] && (rc = zero_ctx<T>(g, outp[j], nn[j], strm))) return rc;
-      GemmArgs ga;
-      std::memset(&ga, 0, sizeof(ga));
-      ga.st = st;
-      ga.idx = sets[j]; ga.kidx = kk[j]; ga.n_out = nn[j];
-      ga.nseg = 2;
-      ga.seg[0] = GSeg{X, D, 0, 0, 1, Wm[j], nullptr, D, 1, D, nullptr, 0, 0};
-      ga.seg[1] = GSeg{zs_qkv + j * rp, 3 * rp, 0, 0, 1, Bp, nullptr, rp, 1, rp, nullptr, 0, 0};
-      ga.o0 = outp[j]; ga.ldo = nn[j];
-      SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_QKV_FWD)));
+      GProb& pr = ga.prob[j];
+      pr.idx = sets[j]; pr.kidx = kk[j]; pr.n_out = nn[j];
+      pr.B[0] = Wm[j]; pr.B[1] = Bp[j];
+      pr.a_col[0] = 0; pr.a_col[1] = j * rp;
+      pr.o0 = outp[j]; pr.ldo = nn[j];
     }
+    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_QKV_FWD)));
   }
   if (a) {
-    if (g.G > 1 && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
-    T* ac = reinterpret_cast<T*>(ws + g.w_ac);
-    T* Aog = reinterpret_cast<T*>(ws + g.w_Aog);
-    T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
-    if ((rc = make_compact<T>(g, g.co, a, idx_o, ac, strm))) return rc;
-    if ((rc = fill_zero<T>(Aog, (long long)st.nseq * rp * g.co.ld, strm))) return rc;
-    if ((rc = gather_factor<T>(Aog, g.co.ld, (long long)rp * g.co.ld, idx_o, g.ko, st.nseq, r, w->Ao,
-                               g.nq, 0, strm)))
-      return rc;
     // z_o = a_m Ao^T
     SkinnyArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -319,8 +303,6 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.part = skp;
     if ((rc = launch_skinny<T>(sa, strm))) return rc;
     // o = a_m WoT[So] + s z_o Bo^T
-    if ((rc = fill_zero<T>(BoTp, (long long)rp * D, strm))) return rc;
-    if ((rc = copy2d<T>(BoTp, D, 0, 0, r, D, w->Bo, r, 1, strm))) return rc;
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.st = st;
@@ -354,22 +336,61 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   int* idx_o = g.G > 1 ? reinterpret_cast<int*>(ws + g.w_idxo) : const_cast<int*>(idx_vo);
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
-  int* inv = reinterpret_cast<int*>(ws + g.w_inv);
+  int* inv_o = reinterpret_cast<int*>(ws + g.w_inv_o);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
-  if ((rc = prologue<T>(g, ws, strm))) return rc;
+  T* ac = reinterpret_cast<T*>(ws + g.w_ac);
+  T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
+  T* AoTp = reinterpret_cast<T*>(ws + g.w_AoTp);
+  T* Aqkvp = reinterpret_cast<T*>(ws + g.w_Aqkvp);
+  const void* dsrc[3] = {dq, dk, dv};
+  T* dcomp[3] = {reinterpret_cast<T*>(ws + g.w_dqc), reinterpret_cast<T*>(ws + g.w_dkc),
+                 reinterpret_cast<T*>(ws + g.w_dvc)};
+  const Comp* cc[3] = {&g.cq, &g.ck, &g.cv};
+  const int* sets[3] = {idx_q, idx_qk, idx_vo};
+  int* inv[3] = {reinterpret_cast<int*>(ws + g.w_inv_q), reinterpret_cast<int*>(ws + g.w_inv_k),
+                 reinterpret_cast<int*>(ws + g.w_inv_v)};
+  const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
+  const void* Al[3] = {w->Aq, w->Ak, w->Av};
+  const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+  T* Bg[3] = {reinterpret_cast<T*>(ws + g.w_Bqg), reinterpret_cast<T*>(ws + g.w_Bkg),
+              reinterpret_cast<T*>(ws + g.w_Bvg)};
+  T* BTo[3] = {reinterpret_cast<T*>(ws + g.w_BqTo), reinterpret_cast<T*>(ws + g.w_BkTo),
+               reinterpret_cast<T*>(ws + g.w_BvTo)};
+  float* dB[3] = {gr->dBq, gr->dBk, gr->dBv};
+
+  // query-channel sets; then one launch each for operand packing, row layout
+  // and the inverse maps of the channel sets
+  if (g.G > 1 && d_out && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
+  if (g.G > 1 && dq && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
+  Packer pk;
+  pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
+  Layouter L(st);
+  Inverter iv(st.nseq);
+  if (d_out) {
+    pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);          // Bo^T [rp, D]
+    pk.copy(AoTp, rp, g.nq, rp, w->Ao, g.nq, g.nq, r, 1);  // Ao^T [nq, rp]
+    add_compact(L, g.co, a, idx_o, ac, g.esz);
+    if (g.ko < g.nq) L.zero_ctx(da, g.nq, g.nq);
+    iv.add(idx_o, g.ko, g.nq, inv_o);
+  }
+  if (dq) {
+    for (int j = 0; j < 3; ++j) {
+      const Comp& c = *cc[j];
+      pk.copy(Aqkvp + (size_t)j * rp * D, D, rp, D, Al[j], D, r, D, 0);        // A_j, rank padded
+      pk.gather(Bg[j], c.ld, (long long)rp * c.ld, rp, c.ld, Bl[j], r, r, 1, sets[j], c.kc,
+                st.nseq);                                                    // B_j[S_j]^T per sequence
+      pk.copy(BTo[j], c.n, r, c.n, Bl[j], r, r, c.n, 1);                     // B_j^T
+      add_compact(L, c, dsrc[j], sets[j], dcomp[j], g.esz);
+      iv.add(sets[j], c.kc, c.n, inv[j]);
+    }
+  }
+  if ((rc = pk.launch<T>(strm))) return rc;
+  if ((rc = L.launch<T>(strm))) return rc;
+  if ((rc = iv.launch(strm))) return rc;
 
   if (d_out) {
-    if (g.G > 1 && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
-    T* ac = reinterpret_cast<T*>(ws + g.w_ac);
-    T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
-    T* AoTp = reinterpret_cast<T*>(ws + g.w_AoTp);
     float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
     T* dzs_o = reinterpret_cast<T*>(ws + g.w_dzs_o);
-    if ((rc = make_compact<T>(g, g.co, a, idx_o, ac, strm))) return rc;
-    if ((rc = fill_zero<T>(BoTp, (long long)rp * D, strm))) return rc;
-    if ((rc = copy2d<T>(BoTp, D, 0, 0, r, D, w->Bo, r, 1, strm))) return rc;
-    if ((rc = fill_zero<T>(AoTp, (long long)g.nq * rp, strm))) return rc;
-    if ((rc = copy2d<T>(AoTp, rp, 0, 0, g.nq, r, w->Ao, g.nq, 1, strm))) return rc;
     // dz_o = s d_out Bo
     SkinnyArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -382,7 +403,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.part = skp;
     if ((rc = launch_skinny<T>(sa, strm))) return rc;
     // da on So (dense at output rows), 0 at the other context columns
-    if (g.ko < g.nq && (rc = zero_ctx<T>(g, da, g.nq, strm))) return rc;
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.st = st;
@@ -393,53 +413,28 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.o0 = da; ga.ldo = g.nq;
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
     // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o
-    if ((rc = grad_scatter<T>(g, g.co, ac, dz_o, rp, 0, idx_o, g.ko, inv, crp, gr->dAo, 1, 1.f, strm)))
-      return rc;
+    if ((rc = grad_scatter<T>(g, g.co, ac, dz_o, rp, 0, inv_o, crp, gr->dAo, 1, 1.f, strm))) return rc;
     if ((rc = grad_dense<T>(g, d_out, D, zo, rp, 0, rp, crp, gr->dBo, r, 0, nullptr, 0, 0, 0, s, strm)))
       return rc;
   }
   if (dq) {
-    if (g.G > 1 && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
-    T* dqc = reinterpret_cast<T*>(ws + g.w_dqc);
-    T* dkc = reinterpret_cast<T*>(ws + g.w_dkc);
-    T* dvc = reinterpret_cast<T*>(ws + g.w_dvc);
     float* dz = reinterpret_cast<float*>(ws + g.w_dz_qkv);
     T* dzs = reinterpret_cast<T*>(ws + g.w_dzs_qkv);
-    T* Aqkvp = reinterpret_cast<T*>(ws + g.w_Aqkvp);
-    const void* dsrc[3] = {dq, dk, dv};
-    T* dcomp[3] = {dqc, dkc, dvc};
-    const Comp* cc[3] = {&g.cq, &g.ck, &g.cv};
-    const int* sets[3] = {idx_q, idx_qk, idx_vo};
-    const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
-    const void* Al[3] = {w->Aq, w->Ak, w->Av};
-    const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
-    const size_t bg[3] = {g.w_Bqg, g.w_Bkg, g.w_Bvg};
-    const size_t bto[3] = {g.w_BqTo, g.w_BkTo, g.w_BvTo};
-    float* dB[3] = {gr->dBq, gr->dBk, gr->dBv};
-    if ((rc = fill_zero<T>(Aqkvp, (long long)3 * rp * D, strm))) return rc;
     for (int j = 0; j < 3; ++j) {
       const Comp& c = *cc[j];
-      if ((rc = make_compact<T>(g, c, dsrc[j], sets[j], dcomp[j], strm))) return rc;
-      T* Bgj = reinterpret_cast<T*>(ws + bg[j]);
-      T* BTo = reinterpret_cast<T*>(ws + bto[j]);
-      if ((rc = gather_factor<T>(Bgj, c.ld, (long long)rp * c.ld, sets[j], c.kc, st.nseq, r, Bl[j], r,
-                                 1, strm)))
-        return rc;
-      if ((rc = copy2d<T>(BTo, c.n, 0, 0, r, c.n, Bl[j], r, 1, strm))) return rc;
-      if ((rc = copy2d<T>(Aqkvp, D, j * rp, 0, r, D, Al[j], D, 0, strm))) return rc;
-      // dz_j = s dj_m B_j[S]
+      // dz_j = s dj_m B_j[S_j]
       SkinnyArgs sa;
       std::memset(&sa, 0, sizeof(sa));
       sa.st = st; sa.mode = 1; sa.T = g.T;
       sa.A = dcomp[j]; sa.lda = c.ld; sa.lda_out = c.n; sa.a_out_off = c.out_off;
       sa.K = 0; sa.kidx = c.kc; sa.n_out = c.n;
       sa.nblk = 1;
-      sa.Bb[0] = Bgj; sa.nbk[0] = r; sa.ldbb[0] = c.ld; sa.b0_gstride = (long long)rp * c.ld;
-      sa.B0o = BTo; sa.ldb0o = c.n;
+      sa.Bb[0] = Bg[j]; sa.nbk[0] = r; sa.ldbb[0] = c.ld; sa.b0_gstride = (long long)rp * c.ld;
+      sa.B0o = BTo[j]; sa.ldb0o = c.n;
       sa.out = dz; sa.ldo = 3 * rp; sa.col0 = j * rp; sa.oscale = s;
       sa.outs = dzs; sa.ldos = 3 * rp; sa.scale = s;
       sa.part = skp;
-    if ((rc = launch_skinny<T>(sa, strm))) return rc;
+      if ((rc = launch_skinny<T>(sa, strm))) return rc;
     }
     // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
     GemmArgs ga;
@@ -468,8 +463,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       return rc;
     // dB_j[S_j] = s dj_m^T z_j
     for (int j = 0; j < 3; ++j)
-      if ((rc = grad_scatter<T>(g, *cc[j], dcomp[j], zqkv, 3 * rp, j * rp, sets[j], cc[j]->kc, inv, crp,
-                                dB[j], 0, s, strm)))
+      if ((rc = grad_scatter<T>(g, *cc[j], dcomp[j], zqkv, 3 * rp, j * rp, inv[j], crp, dB[j], 0, s,
+                                strm)))
         return rc;
   }
   return SL_OK;

@@ -6,6 +6,8 @@
 
 #include "sl_common.hpp"
 
+#include <type_traits>
+
 namespace sl {
 
 typedef __bf16 bf16x8_t_s __attribute__((ext_vector_type(8)));
@@ -817,17 +819,28 @@ static __global__ void finish_scatter_kernel(const FinishScatterArgs a) {
   else a.out[(long long)c * a.r + q] = s;
 }
 
-// inv[g][c] = position of channel c in idx[g] or -1
-static __global__ void inverse_map_kernel(const int* idx, int k, int nseq, int Nfull, int* inv) {
+// Inverse maps of up to IV_MAXSETS channel sets in one launch:
+// inv_j[g][c] = position of channel c in the ascending set idx_j[g], or -1.
+constexpr int IV_MAXSETS = 4;
+struct InvArgs {
+  int nset, nseq;
+  const int* idx[IV_MAXSETS];
+  int k[IV_MAXSETS], n[IV_MAXSETS];
+  int* inv[IV_MAXSETS];
+  long long start[IV_MAXSETS + 1];
+};
+static __global__ void inverse_sets_kernel(const InvArgs a) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < (long long)nseq * Nfull) inv[i] = -1;
-  // second phase done by a separate launch (stream-ordered)
-}
-static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, int Nfull, int* inv) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)nseq * k) return;
-  const int g = (int)(i / k), p = (int)(i % k);
-  inv[(long long)g * Nfull + idx[i]] = p;
+  if (i >= a.start[a.nset]) return;
+  int j = 0;
+  while (j + 1 < a.nset && a.start[j + 1] <= i) ++j;
+  const long long e = i - a.start[j];
+  const int n = a.n[j], k = a.k[j];
+  const int g = (int)(e / n), c = (int)(e % n);
+  const int* set = a.idx[j] + (long long)g * k;
+  int lo = 0, hi = k;
+  while (lo < hi) { const int mid = (lo + hi) >> 1; if (set[mid] < c) lo = mid + 1; else hi = mid; }
+  a.inv[j][e] = (lo < k && set[lo] == c) ? lo : -1;
 }
 
 // ===========================================================================
@@ -839,7 +852,7 @@ static __global__ void inverse_scatter_kernel(const int* idx, int k, int nseq, i
 //            p < k, 0 elsewhere; src(q, c) = src[q*lds + c] or, transposed, src[c*lds + q]
 //   type 2:  int32 dst[p] = p for p < cols (identity rows)
 // ===========================================================================
-constexpr int PK_MAXJOBS = 12;
+constexpr int PK_MAXJOBS = 16;
 
 struct PackJob {
   int type;
@@ -895,40 +908,92 @@ __global__ void pack_kernel(const PackArgs a) {
 }
 
 // ===========================================================================
-// Layout helpers
+// Row layout jobs over the token layout, one launch for several buffers; each
+// thread moves 8 consecutive elements of one row.
+//   LJ_ZERO:   token-major [T, ld] buffer, context rows, columns [0, n) := 0
+//   LJ_GATHER: compact copy of the selected columns of the context rows,
+//              dst[ctx_pre[b] + t][p] = src[b*L + t][idx[b][p]] for p < n (= k)
+//   LJ_ROWS:   compact copy of the output rows, dst[i][c] = src[tok(i)][c], c < n
+// `vec` (set by the host when row strides are multiples of 8 elements and the
+// bases 16-byte aligned) selects 16-byte stores (and loads, for LJ_ROWS).
 // ===========================================================================
-template <typename T>
-__global__ void fill_kernel(T* p, long long n) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) stv<T>(p, i, 0.f);
+enum { LJ_ZERO = 0, LJ_GATHER = 1, LJ_ROWS = 2 };
+constexpr int LJ_MAXJOBS = 12;
+
+struct LayJob {
+  int type, n, vec;
+  void* dst; long long ldd;
+  const void* src; long long lds;
+  const int* idx;
+};
+
+struct LayArgs {
+  SeqTab st;
+  int njobs;
+  long long start[LJ_MAXJOBS + 1];
+  LayJob job[LJ_MAXJOBS];
+};
+
+// Token row of context row r (rows of all context groups, concatenated).
+__device__ inline int ctx_token(const SeqTab& st, int r, int& b) {
+  int lo = 0, hi = st.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (st.ctx_pre[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  return lo * st.L + (r - st.ctx_pre[lo]);
 }
 
-// dst[(row_off + i) * ldd + col_off + j] = src[i, j] (or src[j, i] when transposed),
-// for i < rows, j < cols of the destination block.
 template <typename T>
-__global__ void copy2d_kernel(T* dst, long long ldd, int row_off, int col_off, int rows, int cols,
-                              const T* src, long long lds, int transposed) {
+__global__ void __launch_bounds__(256) layout_kernel(const LayArgs a) {
+  using R = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
+  constexpr int W = 8 * sizeof(T) / 16;   // 16-byte words per 8 elements
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)rows * cols) return;
-  const int r = (int)(i / cols), c = (int)(i % cols);
-  const T v = transposed ? src[(long long)c * lds + r] : src[(long long)r * lds + c];
-  dst[(long long)(row_off + r) * ldd + col_off + c] = v;
-}
-
-// Per context group g: dst[g][q][p] = src(q, idx[g][p]) for q < r, p < k;
-// src(q, c) = src[q*ld + c] (factor stored [r, N]) or src[c*ld + q] ([N, r]).
-template <typename T>
-__global__ void gather_factor_kernel(T* dst, long long ldd, long long gstride, const int* idx,
-                                     int k, int nseq, int r, const T* src, long long lds,
-                                     int src_is_rows_of_channels) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)nseq * r * k) return;
-  const int p = (int)(i % k);
-  const int q = (int)((i / k) % r);
-  const int g = (int)(i / ((long long)k * r));
-  const int c = idx[(long long)g * k + p];
-  const T v = src_is_rows_of_channels ? src[(long long)c * lds + q] : src[(long long)q * lds + c];
-  dst[g * gstride + (long long)q * ldd + p] = v;
+  if (i >= a.start[a.njobs]) return;
+  int j = 0;
+  while (j + 1 < a.njobs && a.start[j + 1] <= i) ++j;
+  const LayJob& job = a.job[j];
+  const long long e = i - a.start[j];
+  const int cg = (job.n + 7) >> 3;
+  const int r = (int)(e / cg);
+  const int c0 = (int)(e % cg) * 8;
+  const int cnt = min(8, job.n - c0);
+  union { R v[8]; uint4 w[W]; } buf;
+  R* dst;
+  if (job.type == LJ_ZERO) {
+    int b;
+    const int tok = ctx_token(a.st, r, b);
+    dst = reinterpret_cast<R*>(job.dst) + (long long)tok * job.ldd + c0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) buf.v[q] = 0;
+  } else if (job.type == LJ_GATHER) {
+    int b;
+    const int tok = ctx_token(a.st, r, b);
+    const int* sel = job.idx + (long long)b * job.n + c0;
+    const R* src = reinterpret_cast<const R*>(job.src) + (long long)tok * job.lds;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? src[sel[q]] : (R)0;
+    dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd + c0;
+  } else {
+    const R* src = reinterpret_cast<const R*>(job.src) + (long long)out_token(a.st, r) * job.lds + c0;
+    if (job.vec && cnt == 8) {
+#pragma unroll
+      for (int q = 0; q < W; ++q) buf.w[q] = reinterpret_cast<const uint4*>(src)[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? src[q] : (R)0;
+    }
+    dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd + c0;
+  }
+  if (job.vec && cnt == 8) {
+#pragma unroll
+    for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(dst)[q] = buf.w[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < cnt) dst[q] = buf.v[q];
+  }
 }
 
 // Output-group split-K reduction: out[tok(i), n] = sum_s part[s][i][n].
@@ -941,42 +1006,6 @@ __global__ void splitk_reduce_kernel(const SeqTab st, const float* part, int ks,
   float s = 0.f;
   for (int j = 0; j < ks; ++j) s += part[((long long)j * st.T_out + row) * N + n];
   stv<T>(out, (long long)out_token(st, row) * ldo + n, s);
-}
-
-// Zero the context rows of a token-major output [T, ld] over columns [0, n).
-template <typename T>
-__global__ void zero_ctx_rows_kernel(const SeqTab st, T* out, long long ld, int n) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)st.T_ctx * n) return;
-  const int r = (int)(i / n), c = (int)(i % n);
-  int b = 0;
-  while (b + 1 < st.nseq && st.ctx_pre[b + 1] <= r) ++b;
-  const long long tok = (long long)b * st.L + (r - st.ctx_pre[b]);
-  stv<T>(out, tok * ld + c, 0.f);
-}
-
-// Compact copy of the selected columns of the context rows:
-//   dst[ctx_pre[b] + t][p] = src[b*L + t][idx[b][p]],  row stride ldd.
-template <typename T>
-__global__ void gather_ctx_cols_kernel(const SeqTab st, const T* src, long long lds, const int* idx,
-                                       int k, T* dst, long long ldd) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)st.T_ctx * k) return;
-  const int r = (int)(i / k), p = (int)(i % k);
-  int b = 0;
-  while (b + 1 < st.nseq && st.ctx_pre[b + 1] <= r) ++b;
-  const long long tok = (long long)b * st.L + (r - st.ctx_pre[b]);
-  dst[(long long)r * ldd + p] = src[tok * lds + idx[(long long)b * k + p]];
-}
-
-// Compact copy of the output rows: dst[i][c] = src[tok(i)][c], c < n.
-template <typename T>
-__global__ void gather_out_rows_kernel(const SeqTab st, const T* src, long long lds, int n, T* dst,
-                                       long long ldd) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)st.T_out * n) return;
-  const int r = (int)(i / n), c = (int)(i % n);
-  dst[(long long)r * ldd + c] = src[(long long)out_token(st, r) * lds + c];
 }
 
 // kv-channel set -> query-channel set: every query head of a group keeps the

@@ -199,6 +199,20 @@ __device__ inline void load_row(const T* p, float* v, int valid) {
 __device__ inline float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 __device__ inline float sigmoid_exact(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+#ifndef SL_KG_DMA
+#define SL_KG_DMA 1
+#endif
+
+// 16-byte chunk swizzles of the KGD LDS tiles.  A rows hold 8 chunks: chunk c
+// of row r sits at c ^ kgd_aswz(r), so the 32 rows an A-fragment read touches
+// spread over all banks.  B rows (one k, 256 n = 32 chunks) XOR chunk bits 2-4
+// with kgd_bswz(k): the 8 k-rows a transposing fragment read touches (k0..k0+3,
+// k0+8..k0+11, k0 a multiple of 4) then land in 8 different 64-byte windows.
+__device__ inline int kgd_aswz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ inline int kgd_bswz(int k) { return ((k & 3) | ((k >> 1) & 4)) << 2; }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 template <typename T, int MODE, int EPI, bool DUAL, int BM>
 __global__ void __launch_bounds__(G_THREADS, BM == 128 ? 2 : 1)
 gather_gemm_kernel(const GemmArgs args) {
@@ -212,13 +226,26 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr int ACH = BM / 32;              // A chunks per thread
   constexpr int WM = BM / 2;                // wave tile rows
 
+  // K-gather in bf16 (KGD): the gathered B rows go from memory straight into
+  // LDS (global_load_lds) as [k row][n] tiles in two stages, and the matrix
+  // cores read them with transposing LDS reads; A is staged through registers
+  // into an unpadded tile with XOR-swizzled 16-byte chunks.  Two workgroups
+  // then fill the CU's 160 KB of LDS exactly.  Otherwise both operands are
+  // staged through registers into padded [row][k] tiles.
+  constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128;
+  constexpr int A_LD = KGD ? BK : LDS_LD;   // A tile row stride (elements)
+  constexpr int B_STAGE = BK * G_BN * (int)sizeof(T);   // KGD: bytes per B stage
   constexpr int EP_LD = 64 + 4;             // epilogue staging row (floats)
-  constexpr int SMEM = (BM + G_BN) * LDS_LD * (int)sizeof(T);
-  static_assert(4 * 32 * EP_LD * 4 <= SMEM, "epilogue staging must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  __shared__ __attribute__((aligned(16))) int krow_s[64];   // K-gather: B rows of the next tile
+  constexpr int SMEM_TILES = KGD ? BM * A_LD * (int)sizeof(T) + 2 * B_STAGE
+                                 : (BM + G_BN) * LDS_LD * (int)sizeof(T);
+  constexpr int SMEM = SMEM_TILES + (KGD ? 0 : 64 * (int)sizeof(int));
+  static_assert(4 * 32 * EP_LD * 4 <= SMEM_TILES, "epilogue staging must fit in the tile buffers");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  // K-gather (register path): B rows of the next tile, published by wave 0
+  int* krow_s = reinterpret_cast<int*>(smem + SMEM_TILES);
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + BM * LDS_LD;
+  unsigned char* Bst0 = smem + BM * A_LD * (int)sizeof(T);   // KGD: B stage 0 (stage 1 follows)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -358,8 +385,10 @@ gather_gemm_kernel(const GemmArgs args) {
     krow_reg = sidx[min(kk * BK + min(lane, BK - 1), K - 1)];
   };
   auto publish_rows = [&]() {
-    if (wave == 0) krow_s[lane] = krow_reg;
+    if (!KGD && wave == 0) krow_s[lane] = krow_reg;
   };
+  // KGD: B stage the next load_tile fills, and the K-tiles loaded so far
+  int b_stage = 0, n_loaded = 0;
 
   // position the cursor on K-tile kt_begin
   if (nkt > 0) {
@@ -392,6 +421,35 @@ gather_gemm_kernel(const GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         rb[P][i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + (b_off[i] + kc));
+    } else if constexpr (KGD) {
+      // The tile's 64 B rows (krow_reg of lane p = row of k-position p) as 32
+      // LDS-DMA blocks of two k-rows; wave w issues blocks 4 j + w.  Lane l
+      // fills physical chunk l%32 of k-row 2 (4 j + w) + l/32 with the logical
+      // chunk that the swizzle puts there.  Columns past N are clamped (their
+      // outputs are dropped); rows past K hold a clamped row whose A columns
+      // are zero.  Tiles past the range are not loaded.
+      // (The row indices are read on every path, so the index load never
+      // stays pending into the next compute phase.)
+      unsigned char* st = Bst0 + b_stage * B_STAGE;
+      const bool issue = n_loaded < nkt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kr0 = 8 * j + 2 * wave;
+        const int r0 = __builtin_amdgcn_readlane(krow_reg, kr0);
+        const int r1 = __builtin_amdgcn_readlane(krow_reg, kr0 + 1);
+        const int kr = kr0 + (lane >> 5);
+        const int c = (lane & 31) ^ kgd_bswz(kr);
+        int col = n0 + 8 * c;
+        if (col >= args.N) col = 0;
+        const unsigned off = ((unsigned)(lane < 32 ? r0 : r1) * (unsigned)cur_ldb + (unsigned)col) * 2u;
+        const unsigned la = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + (4 * j + wave) * 1024));
+        if (issue)
+          asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                       :: "v"(off), "s"(la), "s"(b_base) : "memory", "m0");
+      }
+      b_stage ^= 1;
+      ++n_loaded;
     } else {
       const int kr = cur_K - (k0 + kg_kr0);
       kg_rv[P] = kr < 0 ? 0 : (kr > KR ? KR : kr);
@@ -421,6 +479,7 @@ gather_gemm_kernel(const GemmArgs args) {
 
   auto store_tile = [&](auto Pc) {
     constexpr int P = decltype(Pc)::value;
+    if constexpr (KGD) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tile's B DMA has landed
     if (va[P] < VEC) {
 #pragma unroll
       for (int i = 0; i < ACH; ++i) mask_chunk<T>(ra[P][i], va[P]);
@@ -429,7 +488,7 @@ gather_gemm_kernel(const GemmArgs args) {
         for (int i = 0; i < 8; ++i) mask_chunk<T>(rb[P][i], va[P]);
       }
     }
-    if (MODE == MODE_KG) {
+    if (MODE == MODE_KG && !KGD) {
 #pragma unroll
       for (int i = 0; i < KR; ++i)
         if (i >= kg_rv[P] || !kg_nok) {
@@ -438,10 +497,14 @@ gather_gemm_kernel(const GemmArgs args) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      *reinterpret_cast<uint4*>(&As[(a_row0 + 32 * i) * LDS_LD + a_kc * VEC]) =
-          make_uint4(ra[P][i].w[0], ra[P][i].w[1], ra[P][i].w[2], ra[P][i].w[3]);
-    if (MODE == MODE_NG) {
+    for (int i = 0; i < ACH; ++i) {
+      const int ar = a_row0 + 32 * i;
+      T* dst = KGD ? &As[ar * A_LD + (a_kc ^ kgd_aswz(ar)) * VEC] : &As[ar * LDS_LD + a_kc * VEC];
+      *reinterpret_cast<uint4*>(dst) = make_uint4(ra[P][i].w[0], ra[P][i].w[1], ra[P][i].w[2], ra[P][i].w[3]);
+    }
+    if constexpr (KGD) {
+      // B arrived by DMA
+    } else if (MODE == MODE_NG) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *reinterpret_cast<uint4*>(&Bs[(a_row0 + 32 * i) * LDS_LD + a_kc * VEC]) =
@@ -484,10 +547,55 @@ gather_gemm_kernel(const GemmArgs args) {
     return 128 * wn + 32 * nb;
   };
 
+  // KGD: byte offset from stage 0 of the B words this lane supplies to the
+  // transposing reads of block nb (k-row 8 (lane/32) + (lane%16)/4 of K-step 0,
+  // first half), in the stage the next compute phase reads (bit 15 = stage).  Other K-steps and the second
+  // half are fixed offsets (the swizzle ignores k-row bits 2, 4 and 5); the
+  // stage bit flips after every compute phase.
+  unsigned boff[4];
+  if constexpr (KGD) {
+    const int grp = lane >> 4, gi = lane & 15;
+    const int kr = 8 * (grp >> 1) + (gi >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int ncol = brow(nb) + 16 * (grp & 1) + 4 * (gi & 3);
+      boff[nb] = (unsigned)(kr * (G_BN * 2)) +
+                 ((unsigned)((ncol >> 3) ^ kgd_bswz(kr)) << 4) + (unsigned)(ncol & 7) * 2u;
+    }
+  }
   auto compute = [&]() {
 #pragma unroll
     for (int kstep = 0; kstep < BK / KSTEP; ++kstep) {
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (KGD) {
+        bf16x8_t af[MB], bfr[4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int ar = WM * wm + 32 * mb + (lane & 31);
+          af[mb] = *reinterpret_cast<const bf16x8_t*>(
+              &As[ar * A_LD + ((2 * kstep + (lane >> 5)) ^ kgd_aswz(ar)) * 8]);
+        }
+        // B operand (k = 16 kstep + 8 (lane/32) + e, n = block column + lane%32)
+        // from two transposing reads: in each 16-lane group, lane i supplies
+        // the address of 4 consecutive n (4 (i%4) ..) of k-row i/4 and
+        // receives element i%4 of the words of lanes 4 e + i/4 (e < 4).
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          v4i16_t h2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const unsigned char* pa = Bst0 + boff[nb] + (16 * kstep + 4 * h) * (G_BN * 2);
+            h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(
+                    (__attribute__((address_space(3))) unsigned char*)(pa)));
+          }
+          bfr[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      } else if constexpr (sizeof(T) == 2) {
         bf16x8_t af[MB], bfr[4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -545,6 +653,10 @@ gather_gemm_kernel(const GemmArgs args) {
     if (nkt > 1) load_tile(I0{});
     for (int i = 0; i < nkt; ++i) {
       compute();
+      if constexpr (KGD) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) boff[nb] ^= (unsigned)B_STAGE;
+      }
       // K-gather rows of tile i+2, fetched after the compute phase: a load in
       // flight across the MFMAs makes the compiler drain every outstanding
       // load (the prefetched tile included) before them.  Unconditional, so
@@ -559,6 +671,7 @@ gather_gemm_kernel(const GemmArgs args) {
       load_tile(I0{});
     }
   }
+  if constexpr (KGD) __builtin_amdgcn_s_waitcnt(0x0F70);   // no LDS-DMA may land in the staging area
 
   // ---- epilogue -----------------------------------------------------------
   // The accumulators go through LDS: per 32-row block and pair of 32-column

@@ -28,6 +28,7 @@ struct FfnGeom {
   size_t esz;
   long long comp, c_out_off;
   int ks_down, ks_dx, RM1, RM2, chunk;
+  long long cr_floats;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
       w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp, w_rp,
@@ -103,9 +104,10 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_dz_gu = w.take(T * 2 * g.rp * 4);
   g.w_dzs_gu = w.take(T * 2 * g.rp * e);
   g.w_Agup = w.take((size_t)2 * g.rp * D * e);
-  long long cr = (long long)ceil_div(T, g.chunk) * D * g.RM2;
-  const long long cr2 = colred_part_elems_compact(st, k, g.F, g.RM1, g.chunk);
-  if (cr2 > cr) cr = cr2;
+  // partials of the five gradient reductions (dA_g,u; dB_d; dB_g, dB_u, dA_d)
+  const long long cr = cb_dense_floats(st, e, D, 2 * g.rp) + cb_dense_floats(st, e, D, g.rp) +
+                       3 * cb_scatter_floats(st, e, k, g.F, g.rp);
+  g.cr_floats = cr;
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
   g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
@@ -337,62 +339,17 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DX_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
   }
-  // dAg, dAu = dz^T X
+  // LoRA factor gradients (one reduction launch, one finish launch):
+  // dAg, dAu = dz^T X;  dBd = s dY^T z_d;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u;
+  // dAd[:, S] = dz_d^T H
   {
-    ColredArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.st = st; a.mode = 0; a.T = g.T;
-    a.P = X; a.ldp = D; a.N = D;
-    a.Z = dz_gu; a.ldz = 2 * rp; a.zc0 = 0; a.R = 2 * rp;
-    a.part = crp;
-    const int nc = ceil_div(g.T, g.chunk);
-    if ((rc = launch_colred<T>(a, nc, D, g.RM2, strm))) return rc;
-    FinishArgs f{crp, nc, D, g.RM2, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f};
-    hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM2), dim3(256), 0, strm, f);
-    SL_HIP(hipGetLastError());
-  }
-  // dBd = s dY^T z_d
-  {
-    ColredArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.st = st; a.mode = 0; a.T = g.T;
-    a.P = dY; a.ldp = D; a.N = D;
-    a.Z = zd; a.ldz = rp; a.zc0 = 0; a.R = rp;
-    a.part = crp;
-    const int nc = ceil_div(g.T, g.chunk);
-    if ((rc = launch_colred<T>(a, nc, D, g.RM1, strm))) return rc;
-    FinishArgs f{crp, nc, D, g.RM1, gr->dBd, r, 0, nullptr, 0, 0, 0, s};
-    hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)D * g.RM1), dim3(256), 0, strm, f);
-    SL_HIP(hipGetLastError());
-  }
-  // dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u, dAd[:, S] = dz_d^T H
-  for (int which = 0; which < 3; ++which) {
-    ColredArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.st = st; a.mode = 1; a.T = g.T;
-    a.P = which == 0 ? (const void*)dGc : which == 1 ? (const void*)dUc : (const void*)Hc;
-    a.ldp = g.ldk; a.ldp_out = g.ldF; a.p_out_off = g.c_out_off;
-    a.kidx = g.k; a.n_out = F;
-    if (which < 2) { a.Z = zgu; a.ldz = 2 * rp; a.zc0 = which * rp; }
-    else { a.Z = dz_d; a.ldz = rp; a.zc0 = 0; }
-    a.R = rp;
-    a.part = crp;
-    const int nc = colred_chunks_compact(st, a, g.k, F, g.RM1, g.chunk);
-    if ((rc = launch_colred<T>(a, nc, F > g.k ? F : g.k, g.RM1, strm))) return rc;
-    FinishScatterArgs f;
-    std::memset(&f, 0, sizeof(f));
-    f.st = st; f.part = crp; f.RM = g.RM1; f.Nfull = F; f.kidx = g.k; f.inv = inv;
-    for (int q = 0; q <= st.nseq; ++q) {
-      const int m = q < st.nseq ? st.ctx[q] : st.T_out;
-      f.chunk_count[q] = ceil_div(m, g.chunk);
-      f.part_off[q] = a.part_off[q];
-    }
-    f.out = which == 0 ? gr->dBg : which == 1 ? gr->dBu : gr->dAd;
-    f.r = r;
-    f.transposed = which == 2;
-    f.scale = which < 2 ? s : 1.f;
-    hipLaunchKernelGGL(finish_scatter_kernel, grid1d((long long)F * r), dim3(256), 0, strm, f);
-    SL_HIP(hipGetLastError());
+    ColredBatch cb(st, g.esz, crp, g.cr_floats);
+    cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
+    cb.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
+    cb.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
+    cb.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
+    cb.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
+    if ((rc = cb.launch<T>(strm))) return rc;
   }
   return SL_OK;
 }

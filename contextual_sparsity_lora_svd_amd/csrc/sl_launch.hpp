@@ -307,4 +307,147 @@ inline long long colred_part_elems_compact(const SeqTab& st, int kidx, int n_out
   return off;
 }
 
+// Partial-row width of a column-reduction job with R Z columns.
+inline int cb_rm(size_t esz, int R) { return esz == 2 ? (int)round_up(R, 16) : pow2_rm(R); }
+
+// Floats of partials of a dense job (token rows) and of a scatter job (compact rows).
+inline long long cb_dense_floats(const SeqTab& st, size_t esz, int N, int R) {
+  return (long long)ceil_div(st.nseq * st.L, cr_chunk(esz)) * N * cb_rm(esz, R);
+}
+inline long long cb_scatter_floats(const SeqTab& st, size_t esz, int kidx, int n_out, int R) {
+  return colred_part_elems_compact(st, kidx, n_out, cb_rm(esz, R), cr_chunk(esz));
+}
+
+// Builder of the LoRA-gradient column reductions of one backward pass: jobs
+// take consecutive ranges of the partial buffer; bf16 runs all reductions in
+// one launch and all finishes in another, fp32 runs each job's reduction and
+// finish in turn.
+struct ColredBatch {
+  CbArgs c;
+  FbArgs f;
+  const void* P32[CB_MAXJOBS];
+  float* part; long long cap, used = 0;
+  size_t esz;
+  bool overflow = false;
+  ColredBatch(const SeqTab& st, size_t esz_, float* part_, long long cap_) : part(part_), cap(cap_), esz(esz_) {
+    std::memset(&c, 0, sizeof(c));
+    std::memset(&f, 0, sizeof(f));
+    c.st = st; f.st = st;
+    c.T = st.nseq * st.L;
+  }
+  bool take(long long n, float*& p) {
+    if (c.njobs >= CB_MAXJOBS || used + n > cap) { overflow = true; return false; }
+    p = part + used;
+    used += n;
+    return true;
+  }
+  // out1 (r1 columns of Z from zc0) and optionally out2 (columns zc0+off2 ..):
+  // out[n, q] (transposed: [q, n]) = scale * sum over all tokens P[t, n] Z[t, zc0 + q]
+  void dense(const void* P, long long ldp, int N, const float* Z, long long ldz, int zc0, int R,
+             float* out1, int r1, int t1, float* out2, int r2, int t2, int off2, float scale) {
+    float* p;
+    if (!take(cb_dense_floats(c.st, esz, N, R), p)) return;
+    CbJob& j = c.job[c.njobs];
+    j.mode = 0; j.N = N; j.R = R; j.RM = cb_rm(esz, R);
+    j.P = P; j.ldp = ldp; j.Z = Z; j.ldz = ldz; j.zc0 = zc0; j.part = p;
+    FbJob& q = f.job[f.njobs];
+    q.kind = 0; q.part = p; q.RM = j.RM; q.N = N; q.nchunk = ceil_div(c.T, cr_chunk(esz));
+    q.out1 = out1; q.r1 = r1; q.t1 = t1; q.out2 = out2; q.r2 = r2; q.t2 = t2; q.off2 = off2; q.scale = scale;
+    ++c.njobs; ++f.njobs;
+  }
+  // out[c, q] (transposed: [q, c]) = scale * sum over the rows whose channel
+  // set holds c of P[row, pos(c)] Z[tok(row), zc0 + q], P compact
+  void scatter(const void* P, long long ldp, long long ldp_out, long long p_out_off, int kidx, int n_out,
+               const float* Z, long long ldz, int zc0, int R, const int* inv, float* out, int r,
+               int transposed, float scale) {
+    float* p;
+    if (!take(cb_scatter_floats(c.st, esz, kidx, n_out, R), p)) return;
+    CbJob& j = c.job[c.njobs];
+    j.mode = 1; j.kidx = kidx; j.n_out = n_out; j.R = R; j.RM = cb_rm(esz, R);
+    j.P = P; j.ldp = ldp; j.ldp_out = ldp_out; j.p_out_off = p_out_off;
+    j.Z = Z; j.ldz = ldz; j.zc0 = zc0; j.part = p;
+    FbJob& q = f.job[f.njobs];
+    q.kind = 1; q.part = p; q.RM = j.RM; q.N = n_out; q.kidx = kidx; q.inv = inv;
+    q.out1 = out; q.r1 = r; q.t1 = transposed; q.scale = scale;
+    ++c.njobs; ++f.njobs;
+  }
+  template <typename T>
+  sl_status launch(hipStream_t s) {
+    if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: gradient reductions exceed %d jobs or the workspace", CB_MAXJOBS);
+    if (c.njobs == 0) return SL_OK;
+    if (sizeof(T) == 2) {
+      long long items = 0, fitems = 0;
+      int rmx = 16;
+      for (int i = 0; i < c.njobs; ++i) {
+        CbJob& j = c.job[i];
+        j.item0 = items;
+        if (j.mode == 0) {
+          items += (long long)ceil_div(c.T, CRM_CHUNK) * ceil_div(j.N, CRM_COLS);
+        } else {
+          for (int g = 0; g <= c.st.nseq; ++g) {
+            const int rows = g < c.st.nseq ? c.st.ctx[g] : c.st.T_out;
+            const int cols = g < c.st.nseq ? j.kidx : j.n_out;
+            items += (long long)ceil_div(rows, CRM_CHUNK) * ceil_div(cols, CRM_COLS);
+          }
+        }
+        rmx = std::max(rmx, j.RM);
+        FbJob& q = f.job[i];
+        q.item0 = fitems;
+        fitems += q.kind == 0 ? (long long)q.N * q.RM : (long long)q.N * q.r1;
+      }
+      c.nitems = items;
+      f.nitems = fitems;
+      if (items > 0) {
+        if (items > 0x7FFFFFFFLL) SL_FAIL(SL_ERR_SHAPE, "gradient reduction grid too large");
+        const dim3 grid((unsigned)items), block(256);
+        if (rmx <= 16) hipLaunchKernelGGL((colred_batch_kernel<16>), grid, block, 0, s, c);
+        else if (rmx <= 32) hipLaunchKernelGGL((colred_batch_kernel<32>), grid, block, 0, s, c);
+        else if (rmx <= 64) hipLaunchKernelGGL((colred_batch_kernel<64>), grid, block, 0, s, c);
+        else SL_FAIL(SL_ERR_SHAPE, "gradient reduction with %d > 64 columns", rmx);
+        SL_HIP(hipGetLastError());
+      }
+      if (fitems > 0) {
+        hipLaunchKernelGGL(finish_batch_kernel, grid1d(fitems), dim3(256), 0, s, f);
+        SL_HIP(hipGetLastError());
+      }
+      return SL_OK;
+    }
+    // fp32: each job's reduction and finish with the scalar kernels
+    for (int i = 0; i < c.njobs; ++i) {
+      const CbJob& j = c.job[i];
+      const FbJob& q = f.job[i];
+      ColredArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.st = c.st; a.mode = j.mode; a.T = c.T;
+      a.P = j.P; a.ldp = j.ldp; a.ldp_out = j.ldp_out; a.p_out_off = j.p_out_off;
+      a.N = j.N; a.kidx = j.kidx; a.n_out = j.n_out;
+      a.Z = j.Z; a.ldz = j.ldz; a.zc0 = j.zc0; a.R = j.R;
+      a.part = j.part;
+      sl_status rc;
+      if (j.mode == 0) {
+        const int nc = ceil_div(c.T, cr_chunk(esz));
+        if ((rc = launch_colred<T>(a, nc, j.N, j.RM, s))) return rc;
+        FinishArgs fa{j.part, nc, j.N, j.RM, q.out1, q.r1, q.t1, q.out2, q.r2, q.t2, q.off2, q.scale};
+        hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)j.N * j.RM), dim3(256), 0, s, fa);
+        SL_HIP(hipGetLastError());
+      } else {
+        const int nc = colred_chunks_compact(c.st, a, j.kidx, j.n_out, j.RM, cr_chunk(esz));
+        if ((rc = launch_colred<T>(a, nc, std::max(j.n_out, j.kidx), j.RM, s))) return rc;
+        FinishScatterArgs fs;
+        std::memset(&fs, 0, sizeof(fs));
+        fs.st = c.st; fs.part = j.part; fs.RM = j.RM; fs.Nfull = j.n_out; fs.kidx = j.kidx; fs.inv = q.inv;
+        for (int g = 0; g <= c.st.nseq; ++g) {
+          const int m = g < c.st.nseq ? c.st.ctx[g] : c.st.T_out;
+          fs.chunk_count[g] = ceil_div(m, cr_chunk(esz));
+          fs.part_off[g] = a.part_off[g];
+        }
+        fs.out = q.out1; fs.r = q.r1; fs.transposed = q.t1; fs.scale = q.scale;
+        hipLaunchKernelGGL(finish_scatter_kernel, grid1d((long long)j.n_out * q.r1), dim3(256), 0, s, fs);
+        SL_HIP(hipGetLastError());
+      }
+    }
+    return SL_OK;
+  }
+};
+
 }  // namespace sl

@@ -35,6 +35,7 @@ struct QkvoGeom {
   size_t esz;
   Comp cq, ck, cv, co;
   int ks_o, ks_dx, chunk;
+  long long cr_floats;
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
@@ -125,12 +126,12 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_dzs_qkv = b.take(T * 3 * rp * e);
   g.w_Aqkvp = b.take(3 * rp * D * e);
   g.chunk = cr_chunk(g.esz);
-  long long cr = (long long)ceil_div(g.T, g.chunk) * std::max(g.D, g.nq) * cr_rm(g.esz, 2 * g.rp);
-  const int RM1 = cr_rm(g.esz, g.rp);
-  cr = std::max(cr, colred_part_elems_compact(st, g.kq, g.nq, RM1, g.chunk));
-  cr = std::max(cr, colred_part_elems_compact(st, g.ko, g.nq, RM1, g.chunk));
-  cr = std::max(cr, colred_part_elems_compact(st, g.kqk, g.nkv, RM1, g.chunk));
-  cr = std::max(cr, colred_part_elems_compact(st, g.kvo, g.nkv, RM1, g.chunk));
+  // partials of the seven gradient reductions of the backward
+  const size_t es = g.esz;
+  const long long cr = cb_scatter_floats(st, es, g.ko, g.nq, g.rp) + 2 * cb_dense_floats(st, es, g.D, g.rp) +
+                       cb_dense_floats(st, es, g.D, 2 * g.rp) + cb_scatter_floats(st, es, g.kq, g.nq, g.rp) +
+                       cb_scatter_floats(st, es, g.kqk, g.nkv, g.rp) + cb_scatter_floats(st, es, g.kvo, g.nkv, g.rp);
+  g.cr_floats = cr;
   g.w_cr = b.take((size_t)cr * 4);
   g.w_inv_o = b.take(B * g.nq * 4);
   g.w_inv_q = b.take(B * g.nq * 4);
@@ -154,58 +155,6 @@ sl_status expand_set(const QkvoGeom& g, const int* idx_kv, int k, int* out, hipS
 // compact copy of a projection's buffer (job of a layout launch)
 void add_compact(Layouter& L, const Comp& c, const void* src, const int* idx, void* dst, size_t esz) {
   L.compact(src, c.n, idx, c.kc, c.n, dst, c.ld, c.out_off, esz);
-}
-
-// colred over a compact buffer + scatter finish into a factor gradient
-template <typename T>
-sl_status grad_scatter(const QkvoGeom& g, const Comp& c, const void* P, const float* Z, long long ldz,
-                       int zc0, const int* inv, float* crp, float* out, int transposed, float scale,
-                       hipStream_t s) {
-  const SeqTab& st = g.st;
-  const int RM = cr_rm(g.esz, g.rp);
-  sl_status rc;
-  ColredArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.st = st; a.mode = 1; a.T = g.T;
-  a.P = P; a.ldp = c.ld; a.ldp_out = c.n; a.p_out_off = c.out_off;
-  a.kidx = c.kc; a.n_out = c.n;
-  a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = g.rp;
-  a.part = crp;
-  const int nc = colred_chunks_compact(st, a, c.kc, c.n, RM, g.chunk);
-  if ((rc = launch_colred<T>(a, nc, std::max(c.n, c.kc), RM, s))) return rc;
-  FinishScatterArgs f;
-  std::memset(&f, 0, sizeof(f));
-  f.st = st; f.part = crp; f.RM = RM; f.Nfull = c.n; f.kidx = c.kc; f.inv = inv;
-  for (int q = 0; q <= st.nseq; ++q) {
-    const int m = q < st.nseq ? st.ctx[q] : st.T_out;
-    f.chunk_count[q] = ceil_div(m, g.chunk);
-    f.part_off[q] = a.part_off[q];
-  }
-  f.out = out; f.r = g.r; f.transposed = transposed; f.scale = scale;
-  hipLaunchKernelGGL(finish_scatter_kernel, grid1d((long long)c.n * g.r), dim3(256), 0, s, f);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
-}
-
-// colred over token-major rows (all T) + dense finish
-template <typename T>
-sl_status grad_dense(const QkvoGeom& g, const void* P, int N, const float* Z, long long ldz, int zc0,
-                     int R, float* crp, float* out1, int r1, int t1, float* out2, int r2, int t2,
-                     int off2, float scale, hipStream_t s) {
-  sl_status rc;
-  const int RM = cr_rm(g.esz, R);
-  ColredArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.st = g.st; a.mode = 0; a.T = g.T;
-  a.P = P; a.ldp = N; a.N = N;
-  a.Z = Z; a.ldz = ldz; a.zc0 = zc0; a.R = R;
-  a.part = crp;
-  const int nc = ceil_div(g.T, g.chunk);
-  if ((rc = launch_colred<T>(a, nc, N, RM, s))) return rc;
-  FinishArgs f{crp, nc, N, RM, out1, r1, t1, out2, r2, t2, off2, scale};
-  hipLaunchKernelGGL(finish_dense_kernel, grid1d((long long)N * RM), dim3(256), 0, s, f);
-  SL_HIP(hipGetLastError());
-  return SL_OK;
 }
 
 template <typename T>
@@ -387,6 +336,7 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   if ((rc = pk.launch<T>(strm))) return rc;
   if ((rc = L.launch<T>(strm))) return rc;
   if ((rc = iv.launch(strm))) return rc;
+  ColredBatch cb(st, g.esz, crp, g.cr_floats);
 
   if (d_out) {
     float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
@@ -413,9 +363,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.o0 = da; ga.ldo = g.nq;
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
     // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o
-    if ((rc = grad_scatter<T>(g, g.co, ac, dz_o, rp, 0, inv_o, crp, gr->dAo, 1, 1.f, strm))) return rc;
-    if ((rc = grad_dense<T>(g, d_out, D, zo, rp, 0, rp, crp, gr->dBo, r, 0, nullptr, 0, 0, 0, s, strm)))
-      return rc;
+    cb.scatter(ac, g.co.ld, g.co.n, g.co.out_off, g.co.kc, g.co.n, dz_o, rp, 0, rp, inv_o, gr->dAo, r, 1, 1.f);
+    cb.dense(d_out, D, D, zo, rp, 0, rp, gr->dBo, r, 0, nullptr, 0, 0, 0, s);
   }
   if (dq) {
     float* dz = reinterpret_cast<float*>(ws + g.w_dz_qkv);
@@ -455,19 +404,16 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
     // dAq, dAk = dz^T X (one pass for q and k), dAv
-    if ((rc = grad_dense<T>(g, X, D, dz, 3 * rp, 0, 2 * rp, crp, gr->dAq, r, 1, gr->dAk, r, 1, rp,
-                            1.f, strm)))
-      return rc;
-    if ((rc = grad_dense<T>(g, X, D, dz, 3 * rp, 2 * rp, rp, crp, gr->dAv, r, 1, nullptr, 0, 0, 0, 1.f,
-                            strm)))
-      return rc;
+    cb.dense(X, D, D, dz, 3 * rp, 0, 2 * rp, gr->dAq, r, 1, gr->dAk, r, 1, rp, 1.f);
+    cb.dense(X, D, D, dz, 3 * rp, 2 * rp, rp, gr->dAv, r, 1, nullptr, 0, 0, 0, 1.f);
     // dB_j[S_j] = s dj_m^T z_j
-    for (int j = 0; j < 3; ++j)
-      if ((rc = grad_scatter<T>(g, *cc[j], dcomp[j], zqkv, 3 * rp, j * rp, inv[j], crp, dB[j], 0, s,
-                                strm)))
-        return rc;
+    for (int j = 0; j < 3; ++j) {
+      const Comp& c = *cc[j];
+      cb.scatter(dcomp[j], c.ld, c.n, c.out_off, c.kc, c.n, zqkv, 3 * rp, j * rp, rp, inv[j], dB[j], r, 0, s);
+    }
   }
-  return SL_OK;
+  // the factor gradients: one reduction launch and one finish launch
+  return cb.launch<T>(strm);
 }
 
 sl_status check_weights(const sl_qkvo_weights* w, bool need_qkv, bool need_o) {

@@ -765,6 +765,226 @@ colred_mfma_kernel(const ColredArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batched form for bf16: every column reduction of a backward pass in one
+// launch, then every finish in one launch.  A job is one reduction
+//   part[chunk][n][q] = sum over the chunk's rows t of P[t, n] * Z[tok(t), zc0 + q]
+// over token rows (mode 0) or over the compact rows of each group (mode 1,
+// context groups on their kidx selected columns, the output group on all
+// n_out); q < R, partial rows RM wide (RM a multiple of 16, R <= RM).  Mode-1
+// partials of group g start at part + sum over earlier groups of
+// chunks x columns x RM, the layout the finish kernels read.  Work item =
+// (job, group, chunk of CRM_CHUNK rows, block of CRM_COLS columns); the
+// arithmetic per item is that of colred_mfma_kernel.
+// ---------------------------------------------------------------------------
+constexpr int CB_MAXJOBS = 8;
+
+struct CbJob {
+  int mode, N, kidx, n_out, R, RM;
+  const void* P; long long ldp, ldp_out, p_out_off;
+  const float* Z; long long ldz; int zc0;
+  float* part;
+  long long item0;
+};
+
+struct CbArgs {
+  SeqTab st;
+  int T, njobs;
+  long long nitems;
+  CbJob job[CB_MAXJOBS];
+};
+
+__device__ inline int cb_group_cols(const CbJob& j, const SeqTab& st, int g) {
+  return g == st.nseq ? j.n_out : j.kidx;
+}
+
+template <int RMX>
+__global__ void __launch_bounds__(256)
+colred_batch_kernel(const CbArgs a) {
+  constexpr int LD = CRM_SLICE + 8;   // padded LDS row (144 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[CRM_COLS * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Zs[RMX * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long item = blockIdx.x;
+  int jb = 0;
+  while (jb + 1 < a.njobs && a.job[jb + 1].item0 <= item) ++jb;
+  jb = __builtin_amdgcn_readfirstlane(jb);
+  const CbJob& J = a.job[jb];
+  long long e = item - J.item0;
+  // locate (group, chunk, column block) and the group's partial offset
+  int g = 0, ch, cb, N, m_rows;
+  long long poff = 0;
+  if (J.mode == 0) {
+    N = J.N; m_rows = a.T;
+    const int ncb = (N + CRM_COLS - 1) / CRM_COLS;
+    ch = (int)(e / ncb); cb = (int)(e % ncb);
+  } else {
+    for (;;) {
+      const int rows = group_rows(a.st, g);
+      const int cols = cb_group_cols(J, a.st, g);
+      const int nch = (rows + CRM_CHUNK - 1) / CRM_CHUNK;
+      const int ncb = (cols + CRM_COLS - 1) / CRM_COLS;
+      const long long ni = (long long)nch * ncb;
+      if (e < ni || g == a.st.nseq) { ch = (int)(e / ncb); cb = (int)(e % ncb); N = cols; m_rows = rows; break; }
+      e -= ni;
+      poff += (long long)nch * cols * J.RM;
+      ++g;
+    }
+  }
+  const bool is_out = J.mode == 1 && g == a.st.nseq;
+  const int n0 = cb * CRM_COLS;
+  const uint16_t* P = reinterpret_cast<const uint16_t*>(J.P);
+  const int ctx_pre_g = (J.mode == 1 && !is_out) ? a.st.ctx_pre[g] : 0;
+  const int nq16 = J.RM / 16;
+  const int pr0 = (tid & 7) * 8;
+  const int pc = (tid >> 3) * 8;
+  const bool c_ok = n0 + pc < N;                     // N is a multiple of 8
+  const int pcol = c_ok ? n0 + pc : 0;
+  f32x4_t acc[4][RMX / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RMX / 16; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int r_begin = ch * CRM_CHUNK;
+  const int r_end = min(m_rows, r_begin + CRM_CHUNK);
+  uint4 pv[CRM_SLICES][8];
+  float zv[CRM_SLICES][RMX / 4];
+  const int zt = tid & 63;
+  const int zq0 = (tid >> 6) * (RMX / 4);
+#pragma unroll
+  for (int sl = 0; sl < CRM_SLICES; ++sl) {
+    const int r0 = r_begin + sl * CRM_SLICE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int r = r0 + pr0 + i;
+      if (r >= m_rows) r = m_rows - 1;   // loaded and zeroed below
+      long long prow;
+      if (J.mode == 0) prow = (long long)r * J.ldp;
+      else prow = is_out ? J.p_out_off + (long long)r * J.ldp_out : (long long)(ctx_pre_g + r) * J.ldp;
+      pv[sl][i] = *reinterpret_cast<const uint4*>(P + prow + pcol);
+    }
+    const int r = r0 + zt;
+    const bool ok = r < r_end;
+    const long long tok = ok ? (J.mode == 0 ? r : group_token(a.st, g, r)) : 0;
+#pragma unroll
+    for (int q = 0; q < RMX / 4; ++q)
+      zv[sl][q] = (ok && zq0 + q < J.R) ? J.Z[tok * J.ldz + J.zc0 + zq0 + q] : 0.f;
+  }
+#pragma unroll
+  for (int sl = 0; sl < CRM_SLICES; ++sl) {
+    const int r0 = r_begin + sl * CRM_SLICE;
+    if (r0 >= r_end) break;   // uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(r0 + pr0 + i < r_end && c_ok)) pv[sl][i] = make_uint4(0, 0, 0, 0);
+    if (sl > 0) __syncthreads();   // previous slice fully consumed
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p]);
+        const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p + 1]);
+        const uint32_t lo = (c0[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        const uint32_t hi = (c1[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        w[p] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(&Ps[(pc + j) * LD + pr0]) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < RMX / 4; ++q) Zs[(zq0 + q) * LD + zt] = f2bf(zv[sl][q]);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < CRM_SLICE / 32; ++ks) {
+      bf16x8_t_s bfr[RMX / 16];
+#pragma unroll
+      for (int j = 0; j < RMX / 16; ++j)
+        if (j < nq16)
+          bfr[j] = *reinterpret_cast<const bf16x8_t_s*>(&Zs[(16 * j + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t_s af = *reinterpret_cast<const bf16x8_t_s*>(
+            &Ps[(64 * wave + 16 * i + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+        for (int j = 0; j < RMX / 16; ++j)
+          if (j < nq16) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  float* dst = J.part + poff + (long long)ch * N * J.RM;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int n = n0 + 64 * wave + 16 * i + 4 * (lane >> 4) + e4;
+      if (n >= N) continue;
+#pragma unroll
+      for (int j = 0; j < RMX / 16; ++j)
+        if (j < nq16) dst[(long long)n * J.RM + 16 * j + (lane & 15)] = acc[i][j][e4];
+    }
+}
+
+// Batched finishes.  A dense job (mode-0 partials, nchunk chunks of N x RM)
+// writes out1 from partial columns [0, r1) and, if out2 is set, out2 from
+// [off2, off2 + r2); a scatter job (mode-1 partials) writes, for every channel
+// c < N and q < r1, the sum over the groups that hold c (context groups
+// through the inverse map inv, the output group always) into out1.  Outputs
+// are [N, r] or, transposed, [r, N], times scale.  One thread per (job, c, q).
+struct FbJob {
+  int kind;                 // 0 dense, 1 scatter
+  const float* part; int RM, N, kidx, nchunk;
+  const int* inv;
+  float* out1; int r1, t1;
+  float* out2; int r2, t2, off2;
+  float scale;
+  long long item0;
+};
+
+struct FbArgs {
+  SeqTab st;
+  int njobs;
+  long long nitems;
+  FbJob job[CB_MAXJOBS];
+};
+
+static __global__ void finish_batch_kernel(const FbArgs a) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.nitems) return;
+  int jb = 0;
+  while (jb + 1 < a.njobs && a.job[jb + 1].item0 <= i) ++jb;
+  const FbJob& J = a.job[jb];
+  const long long e = i - J.item0;
+  if (J.kind == 0) {
+    const int n = (int)(e / J.RM), q = (int)(e % J.RM);
+    float* out = nullptr; int oq = 0, tr = 0, rr = 0;
+    if (q < J.r1) { out = J.out1; oq = q; tr = J.t1; rr = J.r1; }
+    else if (J.out2 && q >= J.off2 && q < J.off2 + J.r2) { out = J.out2; oq = q - J.off2; tr = J.t2; rr = J.r2; }
+    if (!out) return;
+    float s = 0.f;
+    for (int c = 0; c < J.nchunk; ++c) s += J.part[((long long)c * J.N + n) * J.RM + q];
+    s *= J.scale;
+    if (tr) out[(long long)oq * J.N + n] = s;
+    else out[(long long)n * rr + oq] = s;
+  } else {
+    const int c = (int)(e / J.r1), q = (int)(e % J.r1);
+    float s = 0.f;
+    long long off = 0;
+    for (int g = 0; g <= a.st.nseq; ++g) {
+      const int rows = group_rows(a.st, g);
+      const int cols = g < a.st.nseq ? J.kidx : J.N;
+      const int nch = (rows + CRM_CHUNK - 1) / CRM_CHUNK;
+      const int pos = g < a.st.nseq ? J.inv[(long long)g * J.N + c] : c;
+      if (pos >= 0)
+        for (int ch = 0; ch < nch; ++ch) s += J.part[off + ((long long)ch * cols + pos) * J.RM + q];
+      off += (long long)nch * cols * J.RM;
+    }
+    s *= J.scale;
+    if (J.t1) J.out1[(long long)q * J.N + c] = s;
+    else J.out1[(long long)c * J.r1 + q] = s;
+  }
+}
+
 // Dense finish: out[n, q] (or out[q, n] when transposed) = scale * sum_chunks part.
 // Two outputs may take column ranges [0, r1) and [off2, off2 + r2) of the part.
 struct FinishArgs {

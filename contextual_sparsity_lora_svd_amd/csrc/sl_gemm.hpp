@@ -807,17 +807,25 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
   float v0[8], v1[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) { v0[j] = 0.f; v1[j] = 0.f; }
-  for (int sp = 0; sp < args.rem_split; ++sp) {
-    const float* src = args.rpart + ((long long)(tr * args.rem_split + sp) * BM + rloc) * G_BN + ag;
-    float a0[8];
-    load_row<float, 8>(src, a0, 8);
+  // pieces loaded 4 at a time, added in piece order
+  for (int sp0 = 0; sp0 < args.rem_split; sp0 += 4) {
+    float a0[4][8], a1[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v0[j] += a0[j];
-    if (DUAL) {
-      float a1[8];
-      load_row<float, 8>(src + 64, a1, 8);
+    for (int u = 0; u < 4; ++u) {
+      if (sp0 + u >= args.rem_split) break;
+      const float* src = args.rpart + ((long long)(tr * args.rem_split + sp0 + u) * BM + rloc) * G_BN + ag;
+      load_row<float, 8>(src, a0[u], 8);
+      if (DUAL) load_row<float, 8>(src + 64, a1[u], 8);
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v1[j] += a1[j];
+    for (int u = 0; u < 4; ++u) {
+      if (sp0 + u >= args.rem_split) break;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v0[j] += a0[u][j];
+      if (DUAL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v1[j] += a1[u][j];
+      }
     }
   }
   const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];

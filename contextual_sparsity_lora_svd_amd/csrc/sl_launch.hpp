@@ -225,15 +225,17 @@ struct Layouter {
     j->type = LJ_ZERO; j->n = n; j->dst = out; j->ldd = ld;
     j->vec = vec_ok(out, ld);
   }
-  // compact copy: context rows' columns idx[b][0..k) at row stride ldc, then
-  // the output rows' n columns at dst + out_off, row stride n
+  // compact copy of a [T, lds] buffer whose rows hold n channels: context
+  // rows' columns idx[b][0..k) at row stride ldc, then the output rows' n
+  // columns at dst + out_off, row stride n
   void compact(const void* src, long long lds, const int* idx, int k, int n, void* dst, long long ldc,
                long long out_off, size_t esz) {
     if (a.st.T_ctx > 0 && k > 0) {
       LayJob* j = next();
       if (!j) return;
-      j->type = LJ_GATHER; j->n = k; j->dst = dst; j->ldd = ldc; j->src = src; j->lds = lds;
+      j->type = LJ_GATHER; j->n = k; j->nsrc = n; j->dst = dst; j->ldd = ldc; j->src = src; j->lds = lds;
       j->idx = idx; j->vec = vec_ok(dst, ldc);
+      j->stage = vec_ok(src, lds) && n % 8 == 0 && (long long)n * (long long)esz <= LJ_STAGE_BYTES;
     }
     if (a.st.T_out > 0 && n > 0) {
       LayJob* j = next();
@@ -243,19 +245,22 @@ struct Layouter {
       j->vec = vec_ok(d, n) && vec_ok(src, lds);
     }
   }
+  static constexpr long long LJ_STAGE_BYTES = 64 * 1024;
   template <typename T>
   sl_status launch(hipStream_t s) {
     if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d layout jobs", LJ_MAXJOBS);
-    long long t = 0;
+    long long rows = 0;
+    size_t shm = 0;
     for (int i = 0; i < a.njobs; ++i) {
-      a.start[i] = t;
-      const LayJob& j = a.job[i];
-      const long long rows = j.type == LJ_ROWS ? a.st.T_out : a.st.T_ctx;
-      t += rows * ((j.n + 7) / 8);
+      LayJob& j = a.job[i];
+      j.row0 = (int)rows;
+      rows += j.type == LJ_ROWS ? a.st.T_out : a.st.T_ctx;
+      if (j.type == LJ_GATHER && j.stage) shm = std::max(shm, (size_t)j.nsrc * sizeof(T));
     }
-    a.start[a.njobs] = t;
-    if (t == 0) return SL_OK;
-    hipLaunchKernelGGL((layout_kernel<T>), grid1d(t), dim3(256), 0, s, a);
+    if (rows == 0) return SL_OK;
+    if (rows > 0x7FFFFFFFLL) SL_FAIL(SL_ERR_SHAPE, "layout grid too large");
+    a.nrows = (int)rows;
+    hipLaunchKernelGGL((layout_kernel<T>), dim3((unsigned)rows), dim3(LJ_THREADS), shm, s, a);
     SL_HIP(hipGetLastError());
     return SL_OK;
   }
@@ -270,7 +275,7 @@ inline sl_status inverse_maps(const int* idx, int k, int nseq, int Nfull, int* i
 template <typename T>
 inline sl_status splitk_reduce(const SeqTab& st, const float* part, int ks, int N, void* out,
                                long long ldo, hipStream_t s) {
-  const long long n = (long long)st.T_out * N;
+  const long long n = (long long)st.T_out * (N / 4);   // N is a multiple of 8
   if (n <= 0 || ks <= 1) return SL_OK;
   hipLaunchKernelGGL((splitk_reduce_kernel<T>), grid1d(n), dim3(256), 0, s, st, part, ks, N,
                      reinterpret_cast<T*>(out), ldo);

@@ -463,23 +463,30 @@ select_kernel(const SelectArgs a) {
   const int nch = (ctx + SC_CHUNK - 1) / SC_CHUNK;
   const long long pb = (long long)b * a.nchunk_max;
 
+  // sum of a column's chunk partials in chunk order, loads issued 8 at a time
+  auto chunk_sum = [&](const float* part, int ld, int col) -> float {
+    float t = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nch) v[u] = part[(pb + c0 + u) * ld + col];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nch) t += v[u];
+    }
+    return t;
+  };
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   for (int n = tid; n < a.N; n += SEL_THREADS) {
     float s;
     if (!a.qk) {
-      s = 0.f;
-      for (int c = 0; c < nch; ++c) s += a.part0[(pb + c) * a.N0 + n];
+      s = chunk_sum(a.part0, a.N0, n);
     } else {
       const int gk = n / a.head_dim, d = n % a.head_dim;
-      float sk = 0.f;
-      for (int c = 0; c < nch; ++c) sk += a.part1[(pb + c) * a.N + n];
+      const float sk = chunk_sum(a.part1, a.N, n);
       float sq = 0.f;
-      for (int j = 0; j < a.group; ++j) {
-        const int qc = (gk * a.group + j) * a.head_dim + d;
-        float v = 0.f;
-        for (int c = 0; c < nch; ++c) v += a.part0[(pb + c) * a.N0 + qc];
-        sq += v;
-      }
+      for (int j = 0; j < a.group; ++j) sq += chunk_sum(a.part0, a.N0, (gk * a.group + j) * a.head_dim + d);
       s = sk * sq;
     }
     if (a.scores) a.scores[(long long)b * a.N + n] = s;
@@ -961,8 +968,17 @@ static __global__ void finish_batch_kernel(const FbArgs a) {
     if (q < J.r1) { out = J.out1; oq = q; tr = J.t1; rr = J.r1; }
     else if (J.out2 && q >= J.off2 && q < J.off2 + J.r2) { out = J.out2; oq = q - J.off2; tr = J.t2; rr = J.r2; }
     if (!out) return;
+    // chunk loads issued 8 at a time, added in chunk order
     float s = 0.f;
-    for (int c = 0; c < J.nchunk; ++c) s += J.part[((long long)c * J.N + n) * J.RM + q];
+    for (int c0 = 0; c0 < J.nchunk; c0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < J.nchunk) v[u] = J.part[((long long)(c0 + u) * J.N + n) * J.RM + q];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < J.nchunk) s += v[u];
+    }
     s *= J.scale;
     if (tr) out[(long long)oq * J.N + n] = s;
     else out[(long long)n * rr + oq] = s;
@@ -975,8 +991,17 @@ static __global__ void finish_batch_kernel(const FbArgs a) {
       const int cols = g < a.st.nseq ? J.kidx : J.N;
       const int nch = (rows + CRM_CHUNK - 1) / CRM_CHUNK;
       const int pos = g < a.st.nseq ? J.inv[(long long)g * J.N + c] : c;
-      if (pos >= 0)
-        for (int ch = 0; ch < nch; ++ch) s += J.part[off + ((long long)ch * cols + pos) * J.RM + q];
+      if (pos >= 0) {
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (c0 + u < nch) v[u] = J.part[off + ((long long)(c0 + u) * cols + pos) * J.RM + q];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (c0 + u < nch) s += v[u];
+        }
+      }
       off += (long long)nch * cols * J.RM;
     }
     s *= J.scale;
@@ -1128,29 +1153,32 @@ __global__ void pack_kernel(const PackArgs a) {
 }
 
 // ===========================================================================
-// Row layout jobs over the token layout, one launch for several buffers; each
-// thread moves 8 consecutive elements of one row.
+// Row layout jobs over the token layout, one launch for several buffers; one
+// workgroup per (job, row), 8 consecutive elements per thread and pass.
 //   LJ_ZERO:   token-major [T, ld] buffer, context rows, columns [0, n) := 0
 //   LJ_GATHER: compact copy of the selected columns of the context rows,
-//              dst[ctx_pre[b] + t][p] = src[b*L + t][idx[b][p]] for p < n (= k)
+//              dst[ctx_pre[b] + t][p] = src[b*L + t][idx[b][p]] for p < n (= k);
+//              the source row (nsrc columns) is first staged in LDS with
+//              16-byte loads when it fits (stage = 1)
 //   LJ_ROWS:   compact copy of the output rows, dst[i][c] = src[tok(i)][c], c < n
 // `vec` (set by the host when row strides are multiples of 8 elements and the
-// bases 16-byte aligned) selects 16-byte stores (and loads, for LJ_ROWS).
+// bases 16-byte aligned) selects 16-byte accesses.
 // ===========================================================================
 enum { LJ_ZERO = 0, LJ_GATHER = 1, LJ_ROWS = 2 };
 constexpr int LJ_MAXJOBS = 12;
+constexpr int LJ_THREADS = 256;
 
 struct LayJob {
-  int type, n, vec;
+  int type, n, vec, nsrc, stage;
   void* dst; long long ldd;
   const void* src; long long lds;
   const int* idx;
+  int row0;                 // first workgroup of the job
 };
 
 struct LayArgs {
   SeqTab st;
-  int njobs;
-  long long start[LJ_MAXJOBS + 1];
+  int njobs, nrows;
   LayJob job[LJ_MAXJOBS];
 };
 
@@ -1166,53 +1194,71 @@ __device__ inline int ctx_token(const SeqTab& st, int r, int& b) {
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) layout_kernel(const LayArgs a) {
+__global__ void __launch_bounds__(LJ_THREADS) layout_kernel(const LayArgs a) {
   using R = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
   constexpr int W = 8 * sizeof(T) / 16;   // 16-byte words per 8 elements
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.start[a.njobs]) return;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lrow[];
+  const int tid = threadIdx.x;
   int j = 0;
-  while (j + 1 < a.njobs && a.start[j + 1] <= i) ++j;
+  while (j + 1 < a.njobs && a.job[j + 1].row0 <= (int)blockIdx.x) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
   const LayJob& job = a.job[j];
-  const long long e = i - a.start[j];
-  const int cg = (job.n + 7) >> 3;
-  const int r = (int)(e / cg);
-  const int c0 = (int)(e % cg) * 8;
-  const int cnt = min(8, job.n - c0);
-  union { R v[8]; uint4 w[W]; } buf;
-  R* dst;
+  const int r = blockIdx.x - job.row0;
+  union Buf { R v[8]; uint4 w[W]; };
   if (job.type == LJ_ZERO) {
     int b;
-    const int tok = ctx_token(a.st, r, b);
-    dst = reinterpret_cast<R*>(job.dst) + (long long)tok * job.ldd + c0;
+    R* dst = reinterpret_cast<R*>(job.dst) + (long long)ctx_token(a.st, r, b) * job.ldd;
+    for (int c0 = tid * 8; c0 < job.n; c0 += LJ_THREADS * 8) {
+      const int cnt = min(8, job.n - c0);
+      if (job.vec && cnt == 8) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) buf.v[q] = 0;
-  } else if (job.type == LJ_GATHER) {
-    int b;
-    const int tok = ctx_token(a.st, r, b);
-    const int* sel = job.idx + (long long)b * job.n + c0;
-    const R* src = reinterpret_cast<const R*>(job.src) + (long long)tok * job.lds;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? src[sel[q]] : (R)0;
-    dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd + c0;
-  } else {
-    const R* src = reinterpret_cast<const R*>(job.src) + (long long)out_token(a.st, r) * job.lds + c0;
-    if (job.vec && cnt == 8) {
-#pragma unroll
-      for (int q = 0; q < W; ++q) buf.w[q] = reinterpret_cast<const uint4*>(src)[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? src[q] : (R)0;
+        for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(dst + c0)[q] = make_uint4(0, 0, 0, 0);
+      } else {
+        for (int q = 0; q < cnt; ++q) dst[c0 + q] = (R)0;
+      }
     }
-    dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd + c0;
-  }
-  if (job.vec && cnt == 8) {
+  } else if (job.type == LJ_ROWS) {
+    const R* src = reinterpret_cast<const R*>(job.src) + (long long)out_token(a.st, r) * job.lds;
+    R* dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd;
+    for (int c0 = tid * 8; c0 < job.n; c0 += LJ_THREADS * 8) {
+      const int cnt = min(8, job.n - c0);
+      if (job.vec && cnt == 8) {
 #pragma unroll
-    for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(dst)[q] = buf.w[q];
+        for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(dst + c0)[q] = reinterpret_cast<const uint4*>(src + c0)[q];
+      } else {
+        for (int q = 0; q < cnt; ++q) dst[c0 + q] = src[c0 + q];
+      }
+    }
   } else {
+    int b;
+    const R* src = reinterpret_cast<const R*>(job.src) + (long long)ctx_token(a.st, r, b) * job.lds;
+    const int* sel = job.idx + (long long)b * job.n;
+    R* dst = reinterpret_cast<R*>(job.dst) + (long long)r * job.ldd;
+    const R* from = src;
+    if (job.stage) {   // uniform: the whole source row into LDS (nsrc is a multiple of 8)
+      R* rowl = reinterpret_cast<R*>(lrow);
+      for (int c0 = tid * 8; c0 < job.nsrc; c0 += LJ_THREADS * 8) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q < cnt) dst[q] = buf.v[q];
+        for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(rowl + c0)[q] = reinterpret_cast<const uint4*>(src + c0)[q];
+      }
+      __syncthreads();
+      from = rowl;
+    }
+    for (int p0 = tid * 8; p0 < job.n; p0 += LJ_THREADS * 8) {
+      const int cnt = min(8, job.n - p0);
+      Buf buf;
+      int c[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) c[q] = q < cnt ? sel[p0 + q] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? from[c[q]] : (R)0;
+      if (job.vec && cnt == 8) {
+#pragma unroll
+        for (int q = 0; q < W; ++q) reinterpret_cast<uint4*>(dst + p0)[q] = buf.w[q];
+      } else {
+        for (int q = 0; q < cnt; ++q) dst[p0 + q] = buf.v[q];
+      }
+    }
   }
 }
 
@@ -1220,12 +1266,25 @@ __global__ void __launch_bounds__(256) layout_kernel(const LayArgs a) {
 template <typename T>
 __global__ void splitk_reduce_kernel(const SeqTab st, const float* part, int ks, int N, T* out,
                                      long long ldo) {
+  // one thread per 4 consecutive columns (N is a multiple of 8); the pieces'
+  // loads are issued 8 at a time and added in piece order
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)st.T_out * N) return;
-  const int row = (int)(i / N), n = (int)(i % N);
-  float s = 0.f;
-  for (int j = 0; j < ks; ++j) s += part[((long long)j * st.T_out + row) * N + n];
-  stv<T>(out, (long long)out_token(st, row) * ldo + n, s);
+  const int N4 = N >> 2;
+  if (i >= (long long)st.T_out * N4) return;
+  const int row = (int)(i / N4), n = (int)(i % N4) * 4;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < ks; j0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < ks) v[u] = *reinterpret_cast<const float4*>(part + ((long long)(j0 + u) * st.T_out + row) * N + n);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < ks) { s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w; }
+  }
+  T* o = out + (long long)out_token(st, row) * ldo + n;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) stv<T>(o, q, s[q]);
 }
 
 // kv-channel set -> query-channel set: every query head of a group keeps the

@@ -198,6 +198,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-attn", action="store_true", help="skip the q/k/v/o workload")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="run only the q/k/v/o workload and print its measurements as the JSON line "
+                         "(for profiling that step alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain bf16 -> fp32 copy of 64 Mi elements (128 MiB read, "
                          "256 MiB written) to calibrate HBM byte counters")
@@ -210,6 +213,10 @@ def main():
 
     import torch
     import contextual_sparsity_lora_svd_amd as sl
+
+    if args.attn_only:
+        print(json.dumps(attn_bench(args, torch, sl)), flush=True)
+        return
 
     wl = W.WORKLOADS[2]
     f = wl.ffn[0]

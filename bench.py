@@ -114,10 +114,64 @@ def attn_flops(D, nq, nkv, G, r, ctx, L, kqk, kvo):
     return 4 * D * Rs + 3 * (8 * T * D * r + 2 * r * Rs)
 
 
-def attn_bench(args, torch, sl):
-    """q/k/v/o rows of the path on the LLaMA2-7B attention workload: QK-norm and
+def ffn_flops(D, F, r, ctx, L, k):
+    """Algorithmic FLOPs of FFN forward + backward (base and LoRA)."""
+    R = sum(c * k + (L - c) * F for c in ctx)
+    T = len(ctx) * L
+    return 12 * D * R + 18 * r * (T * D + R)
+
+
+def ffn_extreme_bench(args, torch, sl, cfg=6):
+    """FFN rows of the path in the extreme-sparsity regime (99 % of d_ff
+    dropped, LLaMA2-7B shape): estimate, select, forward and backward, against
+    the same kernels run dense."""
+    wl = W.WORKLOADS[cfg]
+    f = wl.ffn[0]
+    D, F, r, r_e, L = f.d_model, f.d_ff, f.lora_rank, wl.est_rank, wl.seq_len
+    ctx = [int(c) for c in W.ctx_lengths(wl)]
+    B, T = len(ctx), len(ctx) * L
+    k = sl.k_from_ratio(F, f.sparsity_pct)
+    print(f"[bench] {wl.name} FFN: D={D} F={F} r={r} B={B} L={L} ctx={ctx} k={k}", file=sys.stderr, flush=True)
+    p = W.make_ffn_tensors(wl)
+    bf = torch.bfloat16
+    t = {n: to_dev(p[n], torch, bf) for n in ("Wg", "Wu", "Ag", "Bg", "Au", "Bu", "Ad", "Bd")}
+    t["WdT"] = to_dev(np.ascontiguousarray(p["Wd"].T), torch, bf)
+    X, dY = to_dev(p["X"], torch, bf), to_dev(p["dY"], torch, bf)
+    del p
+    w = sl.FFNWeights(t, lora_scale=1.0)
+    lay = sl.Layout(ctx, L)
+    Ptg, Qg, _ = sl.build_estimator(t["Wg"], r_e)
+    Ptu, Qu, _ = sl.build_estimator(t["Wu"], r_e)
+    est = sl.EstimateBuffers(sl.SL_CRIT_SWIGLU_L2, lay, D, r_e, F, k, X.device)
+    Y = torch.empty_like(X)
+    grads = {"dX": torch.empty_like(X)}
+    for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd"):
+        grads["d" + n] = torch.empty(t[n].shape, dtype=torch.float32, device=X.device)
+
+    def run(kk, buf, idx=None):
+        if idx is None:
+            idx, _ = sl.estimate_select(sl.SL_CRIT_SWIGLU_L2, X, lay, r_e, Ptg, Qg, Ptu, Qu, F, kk, bufs=est)
+        sl.ffn_fwd(w, X, lay, kk, idx, buf, Y=Y)
+        sl.ffn_bwd(w, X, lay, kk, idx, buf, dY, out=grads)
+
+    buf = sl.FFNWorkspace(w, lay, k, X.device)
+    ms = timed(torch, lambda: run(k, buf), args.steps, args.warmup)
+    full = torch.arange(F, dtype=torch.int32, device=X.device).repeat(B, 1).contiguous()
+    bufd = sl.FFNWorkspace(w, lay, F, X.device)
+    dense_ms = timed(torch, lambda: run(F, bufd, full), max(3, args.steps // 2), 2) if not args.no_dense else None
+    fl = ffn_flops(D, F, r, ctx, L, k)
+    print(f"[bench] extreme FFN step {ms:.3f} ms" + (f", dense {dense_ms:.3f} ms" if dense_ms else ""),
+          file=sys.stderr, flush=True)
+    return {"workload": wl.name, "batch": B, "seq_len": L, "ctx_len": ctx, "sparsity_pct": f.sparsity_pct,
+            "k": k, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "effective_tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_gflop": fl / 1e9,
+            "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
+
+
+def attn_bench(args, torch, sl, cfg=3):
+    """q/k/v/o rows of the path on a LLaMA2-7B attention workload: QK-norm and
     L2 selection over context tokens, sparse q/k/v/o forward and backward."""
-    wl = W.WORKLOADS[3]
+    wl = W.WORKLOADS[cfg]
     s = wl.attn[0]
     heads = (s.n_q_heads, s.n_kv_heads, s.head_dim)
     D, r, r_e, L = s.d_model, s.lora_rank, wl.est_rank, wl.seq_len
@@ -198,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-attn", action="store_true", help="skip the q/k/v/o workload")
+    ap.add_argument("--no-extreme", action="store_true",
+                    help="skip the extreme-sparsity workload (99 %% FFN, 75 %% q/k/v/o)")
     ap.add_argument("--attn-only", action="store_true",
                     help="run only the q/k/v/o workload and print its measurements as the JSON line "
                          "(for profiling that step alone)")
@@ -311,6 +367,12 @@ def main():
         del buf, est
         torch.cuda.empty_cache()
         attn = attn_bench(args, torch, sl)
+    extreme = None
+    if not args.no_extreme:
+        torch.cuda.empty_cache()
+        extreme = {"ffn": ffn_extreme_bench(args, torch, sl)}
+        if not args.no_attn:
+            extreme["attention"] = attn_bench(args, torch, sl, cfg=6)
 
     if args.copy_calibration:
         n = 64 << 20
@@ -355,6 +417,7 @@ def main():
         "kernels": kern,
         "estimator_build_ms_per_weight": build_ms,
         "attention": attn,
+        "extreme_sparsity": extreme,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

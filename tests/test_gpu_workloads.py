@@ -61,8 +61,11 @@ def test_stack_ffn_layer(layer):
 @pytest.mark.parametrize("layer", [0, 1, 2, 3])
 def test_stack_qkvo_layer(layer):
     """4-layer stack, q/k/v/o of one layer (QK-norm and L2 selection)."""
+    _qkvo_layer(W.WORKLOADS[4], layer)
+
+
+def _qkvo_layer(wl, layer):
     sl = _api()
-    wl = W.WORKLOADS[4]
     s = wl.attn[layer]
     heads = (s.n_q_heads, s.n_kv_heads, s.head_dim)
     p = W.make_attn_tensors(wl, layer)
@@ -99,3 +102,13 @@ def test_stack_qkvo_layer(layer):
 def test_llama3_ffn_full_size():
     """LLaMA3-8B FFN (d_ff 14336, LoRA rank 32, estimator rank 16, 90 %), 4096 tokens."""
     _ffn_layer(W.WORKLOADS[5], 0)
+
+
+def test_extreme_sparsity_ffn():
+    """99 % FFN sparsity (k = 110 of 11008) at the LLaMA2-7B shape, 4 x 512 tokens."""
+    _ffn_layer(W.WORKLOADS[6], 0)
+
+
+def test_extreme_sparsity_qkvo():
+    """75 % q/k and v/o sparsity (1024 of 4096 kv channels) at the LLaMA2-7B shape."""
+    _qkvo_layer(W.WORKLOADS[6], 0)

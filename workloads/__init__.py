@@ -103,6 +103,11 @@ WORKLOADS: Dict[int, Workload] = {
     5: Workload(5, "llama3-8b-long-context", "bf16", batch=1, seq_len=4096, rank_in=128,
                 est_rank=16, ffn=[FFNShape(4096, 14336, 32, 90)],
                 attn=[AttnShape(4096, 32, 8, 128, 32, 50, 0)], out_len=512),
+    # extreme-sparsity regime at the LLaMA2-7B shapes: 99 % of d_ff dropped
+    # (k = 110 of 11008) and 75 % of the q/k and v/o channels
+    6: Workload(6, "llama2-7b-extreme-sparsity", "bf16", batch=4, seq_len=512, rank_in=64,
+                est_rank=8, ffn=[FFNShape(4096, 11008, 16, 99)],
+                attn=[AttnShape(4096, 32, 32, 128, 16, 75, 75)], out_len=128),
 }
 
 

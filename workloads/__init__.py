@@ -34,7 +34,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 __all__ = [
-    "FFNShape", "AttnShape", "Workload", "WORKLOADS", "round_to_bf16",
+    "FFNShape", "AttnShape", "Workload", "WORKLOADS", "round_to_bf16", "make_planted_weight",
     "make_activations", "make_ffn_tensors", "make_attn_tensors", "output_spans",
     "ctx_lengths",
 ]
@@ -147,6 +147,19 @@ def make_activations(cfg: int, tokens: int, d_model: int, rank_in: int, dtype: s
 def _normal(cfg: int, slot: int, layer: int, shape, std: float, dtype: str) -> np.ndarray:
     x = _rng(cfg, slot, layer).standard_normal(shape, dtype=np.float32) * np.float32(std)
     return _finish(x, dtype)
+
+
+def make_planted_weight(seed: int, out_f: int, in_f: int, alpha: float, dtype: str) -> np.ndarray:
+    """``U diag(sigma) V^T`` with Haar-like orthonormal ``U [out, m]``, ``V [in, m]``
+    (QR of Gaussians), ``m = min(out, in)`` and a power-law spectrum
+    ``sigma_i ~ i^-alpha``, scaled to the mean square of ``N(0, 0.02^2)`` entries."""
+    rng = np.random.default_rng(seed)
+    m = min(out_f, in_f)
+    U, _ = np.linalg.qr(rng.standard_normal((out_f, m)).astype(np.float32))
+    V, _ = np.linalg.qr(rng.standard_normal((in_f, m)).astype(np.float32))
+    s = np.arange(1, m + 1, dtype=np.float64) ** -float(alpha)
+    s *= np.sqrt(out_f * in_f * 4e-4 / (s * s).sum())
+    return _finish((U * s.astype(np.float32)) @ V.T, dtype)
 
 
 def make_ffn_tensors(w: Workload, layer: int = 0) -> Dict[str, np.ndarray]:

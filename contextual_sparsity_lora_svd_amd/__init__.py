@@ -8,3 +8,4 @@ from .api import (  # noqa: F401
     SIGNATURES, EstimateBuffers, FFNWeights, FFNWorkspace, Layout, QKVOWeights, QKVOWorkspace, SparseLoraError,
     TIMER_SLOTS, build_estimator, estimate_select, timer_enable, timer_read, timer_reset, timer_select, ffn_bwd, ffn_fwd, k_from_ratio, lib, qkvo_bwd, qkvo_fwd,
 )
+from .layer import LayerRatios, SparseLoRAFFN, SparseLoRAQKVO, SparsitySchedule  # noqa: F401,E402

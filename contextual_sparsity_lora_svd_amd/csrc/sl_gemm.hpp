@@ -842,6 +842,13 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
     store_row<T, 8>(reinterpret_cast<T*>(args.o0) + o, v0, nch - c);
     store_row<T, 8>(reinterpret_cast<T*>(args.o1) + o, v1, nch - c);
     store_row<T, 8>(reinterpret_cast<T*>(args.o2) + o, hv, nch - c);
+  } else if constexpr (EPI == EPI_SCATTER) {
+    // column = the channel number (single-problem launches)
+    const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
+    T* out = reinterpret_cast<T*>(args.o0) + (long long)group_token(args.st, g, r) * args.ldo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c + j < nch) stv<T>(out, gidx ? gidx[c + j] : c + j, v0[j]);
   } else {   // EPI_DSWIGLU
     float gv[8], uv[8], dg[8], du[8];
     load_row<T, 8>(reinterpret_cast<const T*>(args.i0) + o, gv, nch - c);
@@ -876,13 +883,16 @@ inline long long ng_tiles(const SeqTab& st, int kidx, int n_out, int bnc) {
 }
 
 // Split of the last, partial round of an N-gather grid: with `slots` resident
-// workgroups, the remainder tiles (total mod slots, if at most half the slots)
-// run as `split` K pieces each so that the round is filled.  split = 1: none.
+// workgroups, the remainder tiles (total mod slots, or every tile when the
+// grid is under half a round; if at most half the slots) run as `split` K
+// pieces each so that the round is filled.  split = 1: none.
 inline void ng_split_plan(long long total, int total_kt, int slots, int& rem_start, int& split) {
   rem_start = (int)total;
   split = 1;
-  if (slots <= 0 || total <= slots) return;
-  const long long rem = total % slots;
+  if (slots <= 0 || total <= 0) return;
+  // a grid under half a round splits every tile; otherwise the last round's
+  // tiles split when that round is at most half full
+  const long long rem = total <= slots ? total : total % slots;
   if (rem == 0 || 2 * rem > slots) return;
   int s = (int)(slots / rem);
   if (s > 8) s = 8;
@@ -939,8 +949,8 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   a.rem_split = 1;
   if (total == 0) return hipSuccess;
   long long grid = total;
-  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU)) {
-    if (a.rpart) {
+  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
+    if (a.rpart && a.nprob == 1) {
       constexpr int BK = GTraits<T>::BK;
       int total_kt = 0;
       for (int s = 0; s < a.nseg; ++s) total_kt += (a.seg[s].K + BK - 1) / BK;   // NG segments: fixed K
@@ -952,7 +962,7 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM>), dim3((unsigned)grid),
                      dim3(G_THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU)) {
+  if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
     if (e == hipSuccess && a.rem_split > 1) {
       constexpr int CG = (DUAL ? G_BN / 2 : G_BN) / 8;
       const long long n = (long long)(total - a.rem_start) * G_BM * CG;

@@ -39,7 +39,7 @@ struct QkvoGeom {
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
-      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv_o, w_inv_q, w_inv_k, w_inv_v, w_iota, w_skp, ws_bytes;
+      w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv_o, w_inv_q, w_inv_k, w_inv_v, w_iota, w_rp, w_skp, ws_bytes;
 };
 
 int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
@@ -139,6 +139,8 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_inv_v = b.take(B * g.nkv * 4);
   g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
   g.w_skp = b.take((size_t)skinny_part_floats(g.T, std::max(g.D, g.nq)) * 4);
+  // K pieces of the da gather-GEMM when its grid is under half a round
+  g.w_rp = b.take((size_t)ng_rpart_floats(st, g.ko, g.nq, G_BN, ceil_div(g.D, bk) + ceil_div(g.rp, bk)) * 4);
   g.ws_bytes = b.off;
   return SL_OK;
 }
@@ -361,6 +363,7 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.seg[0] = GSeg{d_out, D, 0, 0, 1, w->WoT, nullptr, D, 1, D, nullptr, 0, 0};
     ga.seg[1] = GSeg{dzs_o, rp, 0, 0, 1, AoTp, nullptr, rp, 1, rp, nullptr, 0, 0};
     ga.o0 = da; ga.ldo = g.nq;
+    ga.rpart = reinterpret_cast<float*>(ws + g.w_rp);
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
     // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o
     cb.scatter(ac, g.co.ld, g.co.n, g.co.out_off, g.co.kc, g.co.n, dz_o, rp, 0, rp, inv_o, gr->dAo, r, 1, 1.f);

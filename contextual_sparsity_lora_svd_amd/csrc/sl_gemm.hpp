@@ -844,11 +844,21 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
     store_row<T, 8>(reinterpret_cast<T*>(args.o2) + o, hv, nch - c);
   } else if constexpr (EPI == EPI_SCATTER) {
     // column = the channel number (single-problem launches)
-    const int* gidx = is_out ? nullptr : args.idx + (long long)g * args.kidx;
     T* out = reinterpret_cast<T*>(args.o0) + (long long)group_token(args.st, g, r) * args.ldo;
+    if (is_out) {
+      // dense output rows: 8 consecutive channels (16-byte stores when the row stride allows)
+      if (args.ldo % 8 == 0) store_row<T, 8>(out + c, v0, nch - c);
+      else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c + j < nch) stv<T>(out, gidx ? gidx[c + j] : c + j, v0[j]);
+        for (int j = 0; j < 8; ++j)
+          if (c + j < nch) stv<T>(out, c + j, v0[j]);
+      }
+    } else {
+      const int* gidx = args.idx + (long long)g * args.kidx;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c + j < nch) stv<T>(out, gidx[c + j], v0[j]);
+    }
   } else {   // EPI_DSWIGLU
     float gv[8], uv[8], dg[8], du[8];
     load_row<T, 8>(reinterpret_cast<const T*>(args.i0) + o, gv, nch - c);

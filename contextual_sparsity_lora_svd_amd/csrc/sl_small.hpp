@@ -463,37 +463,64 @@ select_kernel(const SelectArgs a) {
   const int nch = (ctx + SC_CHUNK - 1) / SC_CHUNK;
   const long long pb = (long long)b * a.nchunk_max;
 
-  // sum of a column's chunk partials in chunk order, loads issued 8 at a time
-  auto chunk_sum = [&](const float* part, int ld, int col) -> float {
-    float t = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 8) {
-      float v[8];
+  // Scores of SB channels at a time (n0 + j * SEL_THREADS, j < SB): the chunk
+  // partials of the SB columns are loaded 4 chunks at a time (4 SB loads in
+  // flight) and added per column in chunk order.
+  constexpr int SB = 4;
+  auto sumb = [&](const float* part, int ld, const int* col, float* out) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < nch) v[u] = part[(pb + c0 + u) * ld + col];
+    for (int j = 0; j < SB; ++j) out[j] = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+      float v[4][SB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < nch) t += v[u];
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+          if (c0 + u < nch && col[j] >= 0) v[u][j] = part[(pb + c0 + u) * ld + col[j]];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+          if (c0 + u < nch && col[j] >= 0) out[j] += v[u][j];
     }
-    return t;
   };
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  for (int n = tid; n < a.N; n += SEL_THREADS) {
-    float s;
+  for (int n0 = tid; n0 < a.N; n0 += SB * SEL_THREADS) {
+    int col[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) col[j] = n0 + j * SEL_THREADS < a.N ? n0 + j * SEL_THREADS : -1;
+    float sc[SB];
     if (!a.qk) {
-      s = chunk_sum(a.part0, a.N0, n);
+      sumb(a.part0, a.N0, col, sc);
     } else {
-      const int gk = n / a.head_dim, d = n % a.head_dim;
-      const float sk = chunk_sum(a.part1, a.N, n);
-      float sq = 0.f;
-      for (int j = 0; j < a.group; ++j) sq += chunk_sum(a.part0, a.N0, (gk * a.group + j) * a.head_dim + d);
-      s = sk * sq;
+      float sq[SB], t[SB];
+      sumb(a.part1, a.N, col, sc);   // sc = sk for now
+#pragma unroll
+      for (int j = 0; j < SB; ++j) sq[j] = 0.f;
+      for (int h = 0; h < a.group; ++h) {
+        int qcol[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int n = col[j];
+          qcol[j] = n < 0 ? -1 : ((n / a.head_dim) * a.group + h) * a.head_dim + n % a.head_dim;
+        }
+        sumb(a.part0, a.N0, qcol, t);
+#pragma unroll
+        for (int j = 0; j < SB; ++j) sq[j] += t[j];
+      }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) sc[j] *= sq[j];
     }
-    if (a.scores) a.scores[(long long)b * a.N + n] = s;
-    const uint32_t kv = __float_as_uint(s);
-    keys[n] = kv;
-    kmax = kv > kmax ? kv : kmax;
-    kmin = kv < kmin ? kv : kmin;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int n = col[j];
+      if (n < 0) continue;
+      if (a.scores) a.scores[(long long)b * a.N + n] = sc[j];
+      const uint32_t kv = __float_as_uint(sc[j]);
+      keys[n] = kv;
+      kmax = kv > kmax ? kv : kmax;
+      kmin = kv < kmin ? kv : kmin;
+    }
   }
   // range of the keys: bits above the highest one in which any two differ are common
 #pragma unroll
@@ -504,6 +531,7 @@ select_kernel(const SelectArgs a) {
     kmin = y < kmin ? y : kmin;
   }
   if (lane == 0) { wmax[wave] = kmax; wmin[wave] = kmin; }
+  for (int i = tid; i < 16 * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;   // first pass's histograms
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < SEL_THREADS / 64; ++w) {
@@ -515,36 +543,48 @@ select_kernel(const SelectArgs a) {
   uint32_t mask = ~low, prefix = kmax & ~low;
   int kr = a.k;   // still to take among keys matching prefix
 
-  // radix passes of up to 8 bits from the highest differing bit down
+  // radix passes of up to 8 bits from the highest differing bit down; three
+  // barriers per pass: each bin's per-wave counts are cleared as they are read,
+  // and one wave scans the (at most 256) bins
+  __shared__ int cnt_s[256];
   for (int hi = hbit; hi >= 0;) {
     const int w = hi + 1 < 8 ? hi + 1 : 8;
     const int lo = hi - w + 1;
     const int nb = 1 << w;
-    for (int i = tid; i < 16 * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;
-    __syncthreads();
     for (int n = tid; n < a.N; n += SEL_THREADS) {
       const uint32_t kv = keys[n];
       if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> lo) & (uint32_t)(nb - 1)], 1);
     }
     __syncthreads();
     // bins in descending digit order: position p <-> digit nb - 1 - p
-    int cnt = 0;
     if (tid < nb) {
       const int d = nb - 1 - tid;
+      int c = 0;
 #pragma unroll
-      for (int wv = 0; wv < 16; ++wv) cnt += hist[wv][d];
+      for (int wv = 0; wv < 16; ++wv) { c += hist[wv][d]; hist[wv][d] = 0; }
+      cnt_s[tid] = c;
     }
-    const int before = block_excl_scan(tid < nb ? cnt : 0, wsum, tid, nullptr);
-    if (tid < nb && before < kr && kr <= before + cnt) {
-      s_sel[0] = nb - 1 - tid;
-      s_sel[1] = before;
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds positions 4 l .. 4 l + 3
+      int c4[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { c4[q] = 4 * lane + q < nb ? cnt_s[4 * lane + q] : 0; sum += c4[q]; }
+      int before = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * lane + q < nb && before < kr && kr <= before + c4[q]) {
+          s_sel[0] = nb - 1 - (4 * lane + q);
+          s_sel[1] = before;
+        }
+        before += c4[q];
+      }
     }
     __syncthreads();
     prefix |= (uint32_t)s_sel[0] << lo;
     mask |= (uint32_t)(nb - 1) << lo;
     kr -= s_sel[1];
     hi = lo - 1;
-    __syncthreads();
   }
   const uint32_t tau = prefix;   // the k-th largest key; take kr of the keys equal to it
 
@@ -1244,12 +1284,21 @@ __global__ void __launch_bounds__(LJ_THREADS) layout_kernel(const LayArgs a) {
       __syncthreads();
       from = rowl;
     }
+    // the set row starts 16-byte aligned when b*k is a multiple of 4 (idx itself is aligned)
+    const bool sel_vec = ((reinterpret_cast<uintptr_t>(sel) & 15) == 0);
     for (int p0 = tid * 8; p0 < job.n; p0 += LJ_THREADS * 8) {
       const int cnt = min(8, job.n - p0);
       Buf buf;
       int c[8];
+      if (sel_vec && cnt == 8) {
+        const int4 i0 = reinterpret_cast<const int4*>(sel + p0)[0];
+        const int4 i1 = reinterpret_cast<const int4*>(sel + p0)[1];
+        c[0] = i0.x; c[1] = i0.y; c[2] = i0.z; c[3] = i0.w;
+        c[4] = i1.x; c[5] = i1.y; c[6] = i1.z; c[7] = i1.w;
+      } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) c[q] = q < cnt ? sel[p0 + q] : 0;
+        for (int q = 0; q < 8; ++q) c[q] = q < cnt ? sel[p0 + q] : 0;
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) buf.v[q] = q < cnt ? from[c[q]] : (R)0;
       if (job.vec && cnt == 8) {

@@ -63,6 +63,7 @@ struct GSeg {
 struct GProb {
   const int* idx;                       // NG: context group g uses idx + g*kidx
   int kidx, n_out;
+  int swidth;                           // NG scatter: columns of the output rows
   const void* B[G_MAXSEG];
   int a_col[G_MAXSEG];
   void* o0;
@@ -91,6 +92,7 @@ struct GemmArgs {
   void* o0; void* o1; void* o2;
   const void* i0; const void* i1;
   long long ldo;                        // TOKEN / SCATTER output row stride
+  int swidth;                           // SCATTER: columns of an output row (n of the channel set)
   long long ldc_ctx, ldc_out, c_out_off;  // compact geometry of o*/i* buffers
   float* part;                          // KG split partials [ksplit][T_out][N]
   const int* iota;                      // KG: 0, 1, 2, ... (rows of ungathered segments)
@@ -212,6 +214,45 @@ __device__ inline int kgd_aswz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ inline int kgd_bswz(int k) { return ((k & 3) | ((k >> 1) & 4)) << 2; }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Scatter epilogue of one context row: channels c .. c+7 (positions in the
+// row's ascending set gidx of nch channels) take the row's columns
+// [gidx[c], gidx[c + 8]) -- from column 0 for c = 0 and up to the row width
+// for the set's last 8 -- writing each selected column's value and 0 in every
+// other column.  The groups of 8 of a set cover the row exactly once, so the
+// unselected columns need no separate zeroing; whole aligned 8-column chunks
+// go out as 16-byte stores when `vec` (row 16-byte aligned).
+template <typename T>
+__device__ inline void scatter_row8(T* row, const int* gidx, int c, int nch, int width, const float* v,
+                                    bool vec) {
+  if (c >= nch) return;
+  const int cnt = nch - c < 8 ? nch - c : 8;
+  int cols[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cols[j] = j < cnt ? gidx[c + j] : 0x7FFFFFFF;
+  const int lo = c == 0 ? 0 : cols[0];
+  const int hi = c + 8 >= nch ? width : gidx[c + 8];
+  for (int a0 = lo & ~7; a0 < hi; a0 += 8) {
+    // the set's columns are distinct: at most one of the 8 lands on a column
+    float w8[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      float val = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) val = cols[j] == a0 + x ? v[j] : val;
+      w8[x] = val;
+    }
+    const int s0 = lo - a0 > 0 ? lo - a0 : 0;
+    const int s1 = hi - a0 < 8 ? hi - a0 : 8;
+    if (vec && s0 == 0 && s1 == 8) {
+      store_row<T, 8>(row + a0, w8, 8);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (x >= s0 && x < s1) stv<T>(row, a0 + x, w8[x]);
+    }
+  }
+}
 
 template <typename T, int MODE, int EPI, bool DUAL, int BM>
 __global__ void __launch_bounds__(G_THREADS, BM == 128 ? 2 : 1)
@@ -760,9 +801,17 @@ gather_gemm_kernel(const GemmArgs args) {
                                 v, args.N - c);
             } else {  // EPI_SCATTER: column = the channel number
               T* out = reinterpret_cast<T*>(pr.o0) + (long long)group_token(args.st, g, r) * pr.ldo;
+              const bool vec = pr.ldo % 8 == 0;
+              if (!gidx) {
+                if (vec) store_row<T, 8>(out + c, v, nch - c);
+                else {
 #pragma unroll
-              for (int j = 0; j < 8; ++j)
-                if (c + j < nch) stv<T>(out, gidx ? gidx[c + j] : c + j, v[j]);
+                  for (int j = 0; j < 8; ++j)
+                    if (c + j < nch) stv<T>(out, c + j, v[j]);
+                }
+              } else {
+                scatter_row8<T>(out, gidx, c, nch, pr.swidth, v, vec);
+              }
             }
           }
         }
@@ -854,10 +903,7 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
           if (c + j < nch) stv<T>(out, c + j, v0[j]);
       }
     } else {
-      const int* gidx = args.idx + (long long)g * args.kidx;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (c + j < nch) stv<T>(out, gidx[c + j], v0[j]);
+      scatter_row8<T>(out, args.idx + (long long)g * args.kidx, c, nch, args.swidth, v0, args.ldo % 8 == 0);
     }
   } else {   // EPI_DSWIGLU
     float gv[8], uv[8], dg[8], du[8];
@@ -932,7 +978,7 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
     GProb& p0 = a.prob[0];
     p0.idx = a.idx; p0.kidx = a.kidx; p0.n_out = a.n_out;
     for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.a_col[s] = 0; }
-    p0.o0 = a.o0; p0.ldo = a.ldo;
+    p0.o0 = a.o0; p0.ldo = a.ldo; p0.swidth = a.swidth;
   }
   if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))
     return hipErrorInvalidValue;

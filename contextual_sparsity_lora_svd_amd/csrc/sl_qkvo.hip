@@ -196,7 +196,6 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   if (X) {
     for (int j = 0; j < 3; ++j) {
       pk.copy(Bp[j], rp, nn[j], rp, Bl[j], r, nn[j], r, 0);          // B_j, rank padded to rp
-      if (kk[j] < nn[j]) L.zero_ctx(outp[j], nn[j], nn[j]);
     }
   }
   if (a) {
@@ -235,7 +234,7 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       pr.idx = sets[j]; pr.kidx = kk[j]; pr.n_out = nn[j];
       pr.B[0] = Wm[j]; pr.B[1] = Bp[j];
       pr.a_col[0] = 0; pr.a_col[1] = j * rp;
-      pr.o0 = outp[j]; pr.ldo = nn[j];
+      pr.o0 = outp[j]; pr.ldo = nn[j]; pr.swidth = nn[j];
     }
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_QKV_FWD)));
   }
@@ -321,7 +320,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);          // Bo^T [rp, D]
     pk.copy(AoTp, rp, g.nq, rp, w->Ao, g.nq, g.nq, r, 1);  // Ao^T [nq, rp]
     add_compact(L, g.co, a, idx_o, ac, g.esz);
-    if (g.ko < g.nq) L.zero_ctx(da, g.nq, g.nq);
     iv.add(idx_o, g.ko, g.nq, inv_o);
   }
   if (dq) {
@@ -362,7 +360,7 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.nseg = 2;
     ga.seg[0] = GSeg{d_out, D, 0, 0, 1, w->WoT, nullptr, D, 1, D, nullptr, 0, 0};
     ga.seg[1] = GSeg{dzs_o, rp, 0, 0, 1, AoTp, nullptr, rp, 1, rp, nullptr, 0, 0};
-    ga.o0 = da; ga.ldo = g.nq;
+    ga.o0 = da; ga.ldo = g.nq; ga.swidth = g.nq;
     ga.rpart = reinterpret_cast<float*>(ws + g.w_rp);
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
     // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o

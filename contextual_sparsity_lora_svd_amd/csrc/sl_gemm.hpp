@@ -605,6 +605,53 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   }
   auto compute = [&]() {
+    if constexpr (!KGD && sizeof(T) == 2) {
+      // bf16 from padded tiles, software-pipelined: the A fragments of the
+      // next K-step are read while this K-step's MFMAs run, and each B
+      // fragment is re-read for the next K-step right after the two MFMAs
+      // that use it.  Scheduling barriers keep the reads where they are (left
+      // alone, the scheduler moves each read down to its use and exposes the
+      // LDS latency twice per K-step).
+      constexpr int NKS = BK / KSTEP;
+      static_assert(NKS == 4, "the pipelined K-steps assume BK = 4 KSTEP");
+      auto lda = [&](int ks, int mb) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(
+            &As[(WM * wm + 32 * mb + (lane & 31)) * LDS_LD + ks * 16 + (lane >> 5) * 8]);
+      };
+      auto ldb = [&](int ks, int nb) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(
+            &Bs[(brow(nb) + (lane & 31)) * LDS_LD + ks * 16 + (lane >> 5) * 8]);
+      };
+      bf16x8_t a0[MB], a1[MB], b[4];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) a0[mb] = lda(0, mb);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) b[nb] = ldb(0, nb);
+      auto step = [&](auto KS, bf16x8_t (&ac)[MB], bf16x8_t (&an)[MB]) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (ks + 1 < NKS) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) an[mb] = lda(ks + 1, mb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[mb], b[nb], acc[mb][nb], 0, 0, 0);
+          if constexpr (ks + 1 < NKS) {
+            __builtin_amdgcn_sched_barrier(0);
+            b[nb] = ldb(ks + 1, nb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      };
+      step(std::integral_constant<int, 0>{}, a0, a1);
+      step(std::integral_constant<int, 1>{}, a1, a0);
+      step(std::integral_constant<int, 2>{}, a0, a1);
+      step(std::integral_constant<int, 3>{}, a1, a0);
+      return;
+    }
 #pragma unroll
     for (int kstep = 0; kstep < BK / KSTEP; ++kstep) {
       if constexpr (KGD) {
@@ -631,21 +678,6 @@ gather_gemm_kernel(const GemmArgs args) {
           }
           bfr[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-      } else if constexpr (sizeof(T) == 2) {
-        bf16x8_t af[MB], bfr[4];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[mb] = *reinterpret_cast<const bf16x8_t*>(
-              &As[(WM * wm + 32 * mb + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          bfr[nb] = *reinterpret_cast<const bf16x8_t*>(
-              &Bs[(brow(nb) + (lane & 31)) * LDS_LD + kstep * 16 + (lane >> 5) * 8]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll

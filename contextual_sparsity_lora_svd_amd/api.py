@@ -80,6 +80,7 @@ SIGNATURES = {
                                   ctypes.POINTER(SlFfnWeights), _vp, _i32, _vp, _vp, _sz, _vp, _vp,
                                   ctypes.POINTER(SlFfnGrads), _vp, _sz, _vp]),
     "sl_timer_enable": (ctypes.c_int, [ctypes.c_int]),
+    "sl_gemm_config": (ctypes.c_int, [ctypes.c_int]),
     "sl_timer_select": (None, [ctypes.c_uint32]),
     "sl_timer_reset": (None, []),
     "sl_timer_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -187,6 +188,12 @@ def timer_select(slots):
 
 def timer_reset():
     lib().sl_timer_reset()
+
+
+def gemm_config(wide_ng: int = -1) -> int:
+    """Allow (1) or forbid (0) the wide N-gather GEMM tiles; -1 only reads.
+    Returns the previous setting."""
+    return int(lib().sl_gemm_config(int(wide_ng)))
 
 
 def timer_read(slot: str):

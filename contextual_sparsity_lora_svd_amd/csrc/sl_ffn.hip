@@ -114,11 +114,8 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_skp = w.take((size_t)skinny_part_floats(g.T, D > F ? D : F) * 4);
   {
     // split last round of the gate/up (dual) and dH gather-GEMMs
-    const int bk = g.esz == 2 ? 64 : 32;
-    const int kt_gu = ceil_div(D, bk) + ceil_div(2 * g.rp, bk);
-    const int kt_dh = ceil_div(D, bk) + ceil_div(g.rp, bk);
-    const long long f1 = ng_rpart_floats(st, g.k, F, G_BN / 2, kt_gu);
-    const long long f2 = ng_rpart_floats(st, g.k, F, G_BN, kt_dh);
+    const long long f1 = ng_rpart_floats(st, g.k, F, true, g.esz, {(int)D, 2 * g.rp});
+    const long long f2 = ng_rpart_floats(st, g.k, F, false, g.esz, {(int)D, g.rp});
     g.w_rp = w.take((size_t)(f1 > f2 ? f1 : f2) * 4);
   }
   g.ws_bytes = w.off;

@@ -23,6 +23,7 @@
 // while the current tile is consumed from LDS.
 #pragma once
 
+#include <initializer_list>
 #include <type_traits>
 
 #include "sl_common.hpp"
@@ -98,7 +99,7 @@ struct GemmArgs {
   const int* iota;                      // KG: 0, 1, 2, ... (rows of ungathered segments)
   // NG: logical tiles [0, rem_start) run whole; every later tile runs as
   // rem_split K pieces (the grid's last, partial round) that write fp32
-  // partial tiles [piece][G_BM][G_BN] to rpart for ng_fixup_kernel.
+  // partial tiles [piece][G_BM][tile columns] to rpart for ng_fixup_kernel.
   int ntiles, rem_start, rem_split;
   float* rpart;
 };
@@ -212,6 +213,25 @@ __device__ inline float sigmoid_exact(float x) { return 1.0f / (1.0f + expf(-x))
 // k0+8..k0+11, k0 a multiple of 4) then land in 8 different 64-byte windows.
 __device__ inline int kgd_aswz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ inline int kgd_bswz(int k) { return ((k & 3) | ((k >> 1) & 4)) << 2; }
+// Wide N-gather tiles hold 64-element (128-byte) rows: 16-byte chunk c of row
+// r sits at c ^ wng_swz(r % 16).  The 16 rows one 16-lane phase of a fragment
+// read touches (same logical chunk) then fill the 16 bank groups of a 256-byte
+// window, and any aligned 8 of them the 8 groups of a 128-byte one.
+__device__ inline int wng_swz(int r16) { return (r16 ^ (r16 >> 3)) & 7; }
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (the LDS-DMA loads issued by inline assembly are not tracked by the
+// compiler).  The count field is split: bits 3:0 and 15:14 of the immediate.
+template <int N>
+__device__ inline void wait_vmcnt_le(int n) {
+  if constexpr (N == 0) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  } else {
+    if (n >= N) __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+    else wait_vmcnt_le<N - 1>(n);
+  }
+}
+__device__ inline void wait_vmcnt(int n) { wait_vmcnt_le<31>(n); }   // n > 31 waits for 31
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -254,18 +274,33 @@ __device__ inline void scatter_row8(T* row, const int* gidx, int c, int nch, int
   }
 }
 
-template <typename T, int MODE, int EPI, bool DUAL, int BM>
-__global__ void __launch_bounds__(G_THREADS, BM == 128 ? 2 : 1)
+template <typename T, int MODE, int EPI, bool DUAL, int BM, int WN>
+__global__ void __launch_bounds__(WN == 4 ? 512 : G_THREADS, WN == 4 ? 1 : (BM == 128 ? 2 : 1))
 gather_gemm_kernel(const GemmArgs args) {
+  // WN = 2: BM x 256 tile, 4 waves in a 2 x 2 grid of (BM/2) x 128 blocks,
+  //   two workgroups per CU, operands staged through registers (K-gather bf16:
+  //   B by LDS-DMA).
+  // WN = 4 (wide N-gather, bf16): 128 x 512 tile, 8 waves in a 2 x 4 grid of
+  //   64 x 128 blocks, one workgroup per CU.  Both operands go from memory
+  //   straight into LDS (LDS-DMA) through two stages of 64-element K-tiles, so
+  //   no register staging or LDS store phase remains, and the tile moves 17 %
+  //   fewer operand bytes per MFMA than two 128 x 256 tiles.
+  constexpr bool WIDE = WN == 4;
+  static_assert(WN == 2 || (WIDE && MODE == MODE_NG && sizeof(T) == 2 && BM == 128),
+                "the wide tile is an N-gather bf16 128-row tile");
+  constexpr int NWAVE = WIDE ? 8 : 4;       // waves per workgroup
+  constexpr int BN_T = WIDE ? 512 : 256;    // B rows (accumulator columns) per tile
   constexpr int VEC = GTraits<T>::VEC;
   constexpr int BK = GTraits<T>::BK;
   constexpr int KSTEP = GTraits<T>::KSTEP;
   constexpr int LDS_LD = BK + VEC;          // padded row: 144 bytes
-  constexpr int BNC = DUAL ? G_BN / 2 : G_BN; // output columns (channels) per tile
+  constexpr int BNC = DUAL ? BN_T / 2 : BN_T; // output columns (channels) per tile
+  constexpr int W_ROWB = 2 * BK;            // wide: bytes of a staged row (128)
+  constexpr int W_STG = (BM + BN_T) * W_ROWB;   // wide: bytes per stage (A rows, then B rows)
   constexpr int KR = BK / 8;                // KG: k-rows per thread
-  constexpr int MB = BM / 64;               // 32-row accumulator blocks per wave
-  constexpr int ACH = BM / 32;              // A chunks per thread
   constexpr int WM = BM / 2;                // wave tile rows
+  constexpr int MB = WM / 32;               // 32-row accumulator blocks per wave
+  constexpr int ACH = BM / 32;              // A chunks per thread (register staging)
 
   // K-gather in bf16 (KGD): the gathered B rows go from memory straight into
   // LDS (global_load_lds) as [k row][n] tiles in two stages, and the matrix
@@ -277,10 +312,11 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr int A_LD = KGD ? BK : LDS_LD;   // A tile row stride (elements)
   constexpr int B_STAGE = BK * G_BN * (int)sizeof(T);   // KGD: bytes per B stage
   constexpr int EP_LD = 64 + 4;             // epilogue staging row (floats)
-  constexpr int SMEM_TILES = KGD ? BM * A_LD * (int)sizeof(T) + 2 * B_STAGE
-                                 : (BM + G_BN) * LDS_LD * (int)sizeof(T);
-  constexpr int SMEM = SMEM_TILES + (KGD ? 0 : 64 * (int)sizeof(int));
-  static_assert(4 * 32 * EP_LD * 4 <= SMEM_TILES, "epilogue staging must fit in the tile buffers");
+  constexpr int SMEM_TILES = WIDE ? 2 * W_STG
+                             : KGD ? BM * A_LD * (int)sizeof(T) + 2 * B_STAGE
+                                   : (BM + G_BN) * LDS_LD * (int)sizeof(T);
+  constexpr int SMEM = SMEM_TILES + (KGD || WIDE ? 0 : 64 * (int)sizeof(int));
+  static_assert(NWAVE * 32 * EP_LD * 4 <= SMEM_TILES, "epilogue staging must fit in the tile buffers");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   // K-gather (register path): B rows of the next tile, published by wave 0
   int* krow_s = reinterpret_cast<int*>(smem + SMEM_TILES);
@@ -291,7 +327,8 @@ gather_gemm_kernel(const GemmArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = WIDE ? wave >> 2 : wave >> 1;
+  const int wn = WIDE ? wave & 3 : wave & 1;
 
   // ---- locate the tile --------------------------------------------------
   const bool split_grid = MODE == MODE_NG && args.rem_split > 1;
@@ -345,6 +382,21 @@ gather_gemm_kernel(const GemmArgs args) {
   const int kt_end = (int)((long long)total_kt * (ks + 1) / nks);
   const int nkt = kt_end - kt_begin;
 
+  f32x16_t acc[MB][4];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  // B-tile row of the first column of accumulator block nb of this wave
+  auto brow = [&](int nb) -> int {
+    if (DUAL) return (nb < 2) ? (64 * wn + 32 * nb) : (BNC + 64 * wn + 32 * (nb - 2));
+    return 128 * wn + 32 * nb;
+  };
+
+  if constexpr (!WIDE) {
   // ---- per-thread load geometry ------------------------------------------
   // A: ACH chunks per thread, rows (tid>>3) + 32 i, chunk column tid & 7.
   // B (NG): 8 chunks per thread, rows (tid>>3) + 32 i; in dual mode rows
@@ -574,20 +626,6 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   };
 
-  f32x16_t acc[MB][4];
-#pragma unroll
-  for (int a = 0; a < MB; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
-
-  // B-tile row of the first column of accumulator block nb of this wave
-  auto brow = [&](int nb) -> int {
-    if (DUAL) return (nb < 2) ? (64 * wn + 32 * nb) : (BNC + 64 * wn + 32 * (nb - 2));
-    return 128 * wn + 32 * nb;
-  };
-
   // KGD: byte offset from stage 0 of the B words this lane supplies to the
   // transposing reads of block nb (k-row 8 (lane/32) + (lane%16)/4 of K-step 0,
   // first half), in the stage the next compute phase reads (bit 15 = stage).  Other K-steps and the second
@@ -744,6 +782,192 @@ gather_gemm_kernel(const GemmArgs args) {
       load_tile(I0{});
     }
   }
+  } else {
+  // ---- wide N-gather main loop ----------------------------------------------
+  // Stage layout: A rows [0, BM) then B rows [0, BN_T), 128 bytes each, the
+  // 16-byte chunks of a row swizzled by wng_swz.  One LDS-DMA instruction fills
+  // one 1 KB block of 8 rows (lane l: row l / 8, physical chunk l % 8).  Per
+  // K-tile wave w issues A blocks 2w, 2w+1 and B blocks 8w..8w+7 (dual: blocks
+  // 0..31 hold gate rows, 32..63 up rows).  Rows past the group or channel
+  // count are clamped (their outputs are dropped).  A K-tile that ends inside
+  // its segment (k0 + BK > K) stages A through registers with the columns past
+  // K zeroed; its B columns past K are clamped to column 0 and meet those zeros.
+  constexpr int W_AB = BM / 8 / NWAVE;       // A blocks per wave
+  constexpr int W_BB = BN_T / 8 / NWAVE;     // B blocks per wave
+  static_assert(W_AB % 2 == 0 && W_BB % 2 == 0, "a block's parity must follow its index");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int w_r = lane >> 3;
+  // element offset of the logical chunk this lane fetches in even / odd blocks
+  // (bit 3 of the row, which the swizzle reads, is the block's parity)
+  int kcl[2];
+  kcl[0] = 8 * ((lane & 7) ^ wng_swz(w_r));
+  kcl[1] = 8 * ((lane & 7) ^ wng_swz(8 + w_r));
+  int arow[W_AB];
+#pragma unroll
+  for (int j = 0; j < W_AB; ++j) {
+    arow[j] = m0 + 8 * (W_AB * wv + j) + w_r;
+    if (arow[j] >= m_rows) arow[j] = m_rows - 1;
+  }
+  int bch[W_BB];
+#pragma unroll
+  for (int j = 0; j < W_BB; ++j) {
+    int c = n0 + (8 * (W_BB * wv + j) + w_r) % BNC;
+    if (c >= nch) c = nch - 1;
+    bch[j] = gidx ? gidx[c] : c;
+  }
+  int cur_s = 0, cur_kk = 0, cur_K = 0, cur_nkt = 0;
+  const T* a_base = nullptr;
+  const T* b_base = nullptr;
+  const T* b2_base = nullptr;
+  unsigned a_off[W_AB], b_off[W_BB];
+  auto enter_seg = [&](int s) {
+    s = __builtin_amdgcn_readfirstlane(s);
+    const GSeg& sg = args.seg[s];
+    cur_s = s;
+    cur_K = __builtin_amdgcn_readfirstlane(seg_len(s));
+    cur_nkt = (cur_K + BK - 1) / BK;
+    a_base = reinterpret_cast<const T*>(sg.A) + pr.a_col[s];
+    b_base = reinterpret_cast<const T*>(pr.B[s]);
+    b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : pr.B[s]);
+#pragma unroll
+    for (int j = 0; j < W_AB; ++j) {
+      if (sg.a_tok) a_off[j] = (unsigned)group_token(args.st, g, arow[j]) * (unsigned)sg.lda;
+      else a_off[j] = is_out ? (unsigned)sg.a_out_off + (unsigned)arow[j] * (unsigned)sg.lda_out
+                             : (unsigned)(ctx_pre_g + arow[j]) * (unsigned)sg.lda;
+    }
+#pragma unroll
+    for (int j = 0; j < W_BB; ++j) b_off[j] = (unsigned)bch[j] * (unsigned)sg.ldb;
+  };
+  if (nkt > 0) {
+    int s = 0, kk = kt_begin;
+    for (;;) {
+      const int n = (seg_len(s) + BK - 1) / BK;
+      if (s + 1 >= args.nseg || kk < n) break;
+      kk -= n;
+      ++s;
+    }
+    enter_seg(s);
+    cur_kk = __builtin_amdgcn_readfirstlane(kk);
+  }
+
+  // Issue the loads of the cursor's K-tile into the stage at byte offset st;
+  // returns the LDS-DMA instructions issued (a register-staged A is waited for
+  // before its LDS store, so only DMA instructions stay outstanding).
+  auto issue = [&](int st) -> int {
+    if (cur_kk >= cur_nkt && cur_s + 1 < args.nseg) {   // segments are never empty
+      enter_seg(cur_s + 1);
+      cur_kk = 0;
+    }
+    const int k0 = cur_kk * BK;
+    const bool full = k0 + BK <= cur_K;
+    unsigned char* sb = smem + st;
+    int n = W_BB;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < W_AB; ++j) {
+        const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
+            __attribute__((address_space(3))) unsigned char*)(sb + 1024 * (W_AB * wv + j)));
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                     :: "v"((a_off[j] + (unsigned)(k0 + kcl[j & 1])) * 2u), "s"(la), "s"(a_base)
+                     : "memory", "m0");
+      }
+      n += W_AB;
+    } else {
+#pragma unroll
+      for (int j = 0; j < W_AB; ++j) {
+        const int kc = k0 + kcl[j & 1];
+        Chunk v = kc < cur_K ? load_chunk(a_base + (a_off[j] + (unsigned)kc)) : zero_chunk();
+        *reinterpret_cast<uint4*>(sb + 1024 * (W_AB * wv + j) + 16 * lane) =
+            make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < W_BB; ++j) {
+      const int q = W_BB * wv + j;
+      const T* base = (DUAL && q >= BN_T / 16) ? b2_base : b_base;
+      const int kc = k0 + kcl[j & 1];
+      const unsigned kb = kc < cur_K ? (unsigned)kc : 0u;
+      const unsigned la = __builtin_amdgcn_readfirstlane(
+          (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(sb + BM * W_ROWB + 1024 * q));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                   :: "v"((b_off[j] + kb) * 2u), "s"(la), "s"(base) : "memory", "m0");
+    }
+    ++cur_kk;
+    return n;
+  };
+
+  // Fragment offsets inside a stage for K-step 0 (K-step s: byte offset ^ 32 s,
+  // the logical chunk 2 s + lane / 32 differing from K-step 0's in bits 1..2).
+  // Fragment rows start on 32-row boundaries, so a lane's row has
+  // row % 16 = lane % 16.
+  const int f_ch = (((lane >> 5) ^ wng_swz(lane & 15)) << 4);
+  unsigned fa[MB], fb[4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) fa[mb] = (unsigned)((WM * wm + 32 * mb + (lane & 31)) * W_ROWB + f_ch);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) fb[nb] = (unsigned)(BM * W_ROWB + (brow(nb) + (lane & 31)) * W_ROWB + f_ch);
+  auto rda = [&](int st, int ks, int mb) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(smem + st + (fa[mb] ^ (unsigned)(32 * ks)));
+  };
+  auto rdb = [&](int st, int ks, int nb) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(smem + st + (fb[nb] ^ (unsigned)(32 * ks)));
+  };
+  // One K-step: MFMAs on (ac, b); meanwhile the A fragments of the next step
+  // go to an and each B fragment is re-read for the next step (stage nst,
+  // K-step nks) right after its MFMAs.  nxt = false: no next step.
+  auto kstep = [&](bf16x8_t (&ac)[MB], bf16x8_t (&an)[MB], bf16x8_t (&b)[4], bool nxt, int nst, int nks) {
+    if (nxt) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) an[mb] = rda(nst, nks, mb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      if (nxt) {
+        __builtin_amdgcn_sched_barrier(0);
+        b[nb] = rdb(nst, nks, nb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Two stages: K-tile i is consumed from stage i % 2 while K-tile i+1 lands
+  // in the other.  Each K-tile's loads are issued as soon as the stage it
+  // fills is free: right after the barrier that follows the last fragment
+  // read of the K-tile two before it.
+  if (nkt > 0) {
+    static_assert(BK / KSTEP == 4, "four K-steps per K-tile");
+    bf16x8_t a0[MB], a1[MB], b[4];
+    issue(0);
+    const int n1 = nkt > 1 ? issue(W_STG) : 0;
+    wait_vmcnt(n1);    // K-tile 0 has landed (K-tile 1 may be in flight)
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a0[mb] = rda(0, 0, mb);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) b[nb] = rdb(0, 0, nb);
+    int st = 0;
+    for (int i = 0; i < nkt; ++i) {
+      const int st_next = st ^ W_STG;
+      const bool more = i + 1 < nkt;
+      kstep(a0, a1, b, true, st, 1);
+      kstep(a1, a0, b, true, st, 2);
+      kstep(a0, a1, b, true, st, 3);
+      if (more) {
+        wait_vmcnt(0);       // K-tile i+1 (the only loads in flight) has landed
+        __syncthreads();     // ... for every wave; and stage i is read by none
+        if (i + 2 < nkt) issue(st);
+      }
+      kstep(a1, a0, b, more, st_next, 0);
+      st = st_next;
+    }
+  }
+  wait_vmcnt(0);   // no LDS-DMA may land in the staging area
+  __syncthreads();
+  }
   if constexpr (KGD) __builtin_amdgcn_s_waitcnt(0x0F70);   // no LDS-DMA may land in the staging area
 
   // ---- epilogue -----------------------------------------------------------
@@ -757,7 +981,7 @@ gather_gemm_kernel(const GemmArgs args) {
   const long long cbase = is_out ? args.c_out_off : (long long)ctx_pre_g * args.ldc_ctx;
   const int er = lane >> 1;            // row of the 32-row block this lane finishes
   const int ec = (lane & 1) * 32;      // first of its 32 staged columns
-  if (nkt <= 0) __syncthreads();       // (the main loop ends with a barrier otherwise)
+  if (!WIDE && nkt <= 0) __syncthreads();   // (the main loop ends with a barrier otherwise)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -778,7 +1002,7 @@ gather_gemm_kernel(const GemmArgs args) {
         // K piece of a split tile: raw accumulators, tile-local [row][accumulator column]
         if (r < m_rows) {
           float* dst = args.rpart +
-                       ((long long)(blockIdx.x - args.rem_start) * BM + WM * wm + 32 * mb + er) * G_BN +
+                       ((long long)(blockIdx.x - args.rem_start) * BM + WM * wm + 32 * mb + er) * BN_T +
                        128 * wn + 32 * (ec ? nb1 : nb0);
 #pragma unroll
           for (int q = 0; q < 4; ++q) store_row<float, 8>(dst + 8 * q, src + ec + 8 * q, 8);
@@ -856,10 +1080,11 @@ gather_gemm_kernel(const GemmArgs args) {
 // Adds the K pieces of every split N-gather tile in piece order and applies
 // the tile's element-wise epilogue (the same arithmetic as the GEMM's own).
 // One thread per (split tile, row, 8 channels).
-template <typename T, int EPI, bool DUAL>
+template <typename T, int EPI, bool DUAL, int WN>
 __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
   constexpr int BM = G_BM;
-  constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
+  constexpr int BN_T = WN == 4 ? 512 : 256;   // partial-tile row: accumulator columns of the GEMM tile
+  constexpr int BNC = DUAL ? BN_T / 2 : BN_T;
   constexpr int CG = BNC / 8;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int nrem = args.ntiles - args.rem_start;
@@ -894,7 +1119,7 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (sp0 + u >= args.rem_split) break;
-      const float* src = args.rpart + ((long long)(tr * args.rem_split + sp0 + u) * BM + rloc) * G_BN + ag;
+      const float* src = args.rpart + ((long long)(tr * args.rem_split + sp0 + u) * BM + rloc) * BN_T + ag;
       load_row<float, 8>(src, a0[u], 8);
       if (DUAL) load_row<float, 8>(src + 64, a1[u], 8);
     }
@@ -957,7 +1182,7 @@ void timer_begin(int slot, hipStream_t s);
 void timer_end(int slot, hipStream_t s);
 int device_cus();
 
-// N-gather tiles of a launch (all groups).
+// N-gather tiles of a launch (all groups) at bnc channels per tile.
 inline long long ng_tiles(const SeqTab& st, int kidx, int n_out, int bnc) {
   long long total = 0;
   for (int g = 0; g <= st.nseq; ++g) {
@@ -990,30 +1215,62 @@ inline void ng_split_plan(long long total, int total_kt, int slots, int& rem_sta
   rem_start = (int)(total - rem);
 }
 
-// Workgroup slots of the 128-row gather-GEMM on the current device (two per CU).
-inline int gemm_slots() { return 2 * device_cus(); }
+// Workgroup slots of a gather-GEMM variant on the current device: two 128 x 256
+// workgroups or one wide 128 x 512 workgroup per CU.
+inline int gemm_slots(int wn) { return (wn == 4 ? 1 : 2) * device_cus(); }
 
-// Floats of partial tiles a split N-gather launch needs (0 when it does not split).
-inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, int bnc, int total_kt) {
-  int rs, sp;
-  const long long total = ng_tiles(st, kidx, n_out, bnc);
-  ng_split_plan(total, total_kt, gemm_slots(), rs, sp);
-  return sp > 1 ? (total - rs) * sp * (long long)G_BM * G_BN : 0;
+// N-gather variant: 1 = wide tiles where the operands allow (default), 0 = 128 x 256 only.
+inline int g_gemm_wide_ng = 1;
+
+// K-tiles of a set of N-gather segments (fixed lengths) at depth bk.
+inline int ng_ktiles(std::initializer_list<int> seg_k, int bk) {
+  int n = 0;
+  for (int k : seg_k) n += (k + bk - 1) / bk;
+  return n;
 }
 
-// Host side: count tiles per group and launch.
-template <typename T, int MODE, int EPI, bool DUAL>
-hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
-  constexpr int BNC = DUAL ? G_BN / 2 : G_BN;
-  if (a.nprob <= 0) {
-    a.nprob = 1;
-    GProb& p0 = a.prob[0];
-    p0.idx = a.idx; p0.kidx = a.kidx; p0.n_out = a.n_out;
-    for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.a_col[s] = 0; }
-    p0.o0 = a.o0; p0.ldo = a.ldo; p0.swidth = a.swidth;
+// Floats of partial tiles a split N-gather launch needs (0 when it does not
+// split): the larger of the two variants, since the variant is chosen per launch.
+inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, bool dual, int esz,
+                                 std::initializer_list<int> seg_k) {
+  long long best = 0;
+  for (int wn = 2; wn <= (esz == 2 ? 4 : 2); wn += 2) {
+    const int bn = 128 * wn;
+    const int bk = esz == 2 ? 64 : 32;
+    int rs, sp;
+    const long long total = ng_tiles(st, kidx, n_out, dual ? bn / 2 : bn);
+    ng_split_plan(total, ng_ktiles(seg_k, bk), gemm_slots(wn), rs, sp);
+    const long long f = sp > 1 ? (total - rs) * sp * (long long)G_BM * bn : 0;
+    if (f > best) best = f;
   }
-  if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))
-    return hipErrorInvalidValue;
+  return best;
+}
+
+// Whether every operand of an N-gather launch suits the wide variant's 16-byte
+// LDS-DMA loads: 16-byte aligned bases and row starts, K a multiple of 8.
+inline bool wide_ng_ok(const GemmArgs& a, int esz) {
+  if (esz != 2) return false;
+  auto al = [](const void* p, long long off_el) {
+    return ((uintptr_t)p + (uintptr_t)(off_el * 2)) % 16 == 0;
+  };
+  for (int s = 0; s < a.nseg; ++s) {
+    const GSeg& g = a.seg[s];
+    if (g.K <= 0 || g.K % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
+    if (!g.a_tok && (g.lda_out % 8 != 0 || g.a_out_off % 8 != 0)) return false;
+    for (int p = 0; p < a.nprob; ++p) {
+      if (!al(g.A, a.prob[p].a_col[s]) || !al(a.prob[p].B[s], 0)) return false;
+    }
+    if (g.B2 && !al(g.B2, 0)) return false;
+  }
+  return true;
+}
+
+// Host side: count tiles per group and launch one variant.
+template <typename T, int MODE, int EPI, bool DUAL, int WN>
+hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot) {
+  constexpr int BN_T = WN == 4 ? 512 : 256;
+  constexpr int BNC = DUAL ? BN_T / 2 : BN_T;
+  constexpr int BK = GTraits<T>::BK;
   const int gpp = a.st.nseq + 1;
   a.ngroups = a.nprob * gpp;
   int total = 0;
@@ -1039,28 +1296,45 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   long long grid = total;
   if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
     if (a.rpart && a.nprob == 1) {
-      constexpr int BK = GTraits<T>::BK;
       int total_kt = 0;
       for (int s = 0; s < a.nseg; ++s) total_kt += (a.seg[s].K + BK - 1) / BK;   // NG segments: fixed K
-      ng_split_plan(total, total_kt, gemm_slots(), a.rem_start, a.rem_split);
+      ng_split_plan(total, total_kt, gemm_slots(WN), a.rem_start, a.rem_split);
       grid = a.rem_start + (long long)(total - a.rem_start) * a.rem_split;
     }
   }
   timer_begin(timer_slot, stream);
-  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM>), dim3((unsigned)grid),
-                     dim3(G_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM, WN>), dim3((unsigned)grid),
+                     dim3(WN == 4 ? 512 : G_THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
     if (e == hipSuccess && a.rem_split > 1) {
-      constexpr int CG = (DUAL ? G_BN / 2 : G_BN) / 8;
+      constexpr int CG = BNC / 8;
       const long long n = (long long)(total - a.rem_start) * G_BM * CG;
-      hipLaunchKernelGGL((ng_fixup_kernel<T, EPI, DUAL>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+      hipLaunchKernelGGL((ng_fixup_kernel<T, EPI, DUAL, WN>), dim3((unsigned)((n + 255) / 256)), dim3(256),
                          0, stream, a);
       e = hipGetLastError();
     }
   }
   timer_end(timer_slot, stream);
   return e;
+}
+
+template <typename T, int MODE, int EPI, bool DUAL>
+hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
+  if (a.nprob <= 0) {
+    a.nprob = 1;
+    GProb& p0 = a.prob[0];
+    p0.idx = a.idx; p0.kidx = a.kidx; p0.n_out = a.n_out;
+    for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.a_col[s] = 0; }
+    p0.o0 = a.o0; p0.ldo = a.ldo; p0.swidth = a.swidth;
+  }
+  if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))
+    return hipErrorInvalidValue;
+  if constexpr (MODE == MODE_NG && sizeof(T) == 2) {
+    if (g_gemm_wide_ng && wide_ng_ok(a, 2))
+      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 4>(a, stream, timer_slot);
+  }
+  return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2>(a, stream, timer_slot);
 }
 
 }  // namespace sl

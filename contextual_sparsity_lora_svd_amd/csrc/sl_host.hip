@@ -1,5 +1,6 @@
 // Error state, device checks and layout tables of the C ABI.
 #include "sl_host.hpp"
+#include "sl_gemm.hpp"
 
 #include <vector>
 
@@ -128,6 +129,12 @@ int sl_timer_enable(int max_launches) {
 }
 
 void sl_timer_select(uint32_t slot_mask) { sl::g_timer.mask = slot_mask; }
+
+int sl_gemm_config(int wide_ng) {
+  const int prev = sl::g_gemm_wide_ng;
+  if (wide_ng >= 0) sl::g_gemm_wide_ng = wide_ng ? 1 : 0;
+  return prev;
+}
 
 void sl_timer_reset(void) { sl::g_timer.used = 0; }
 

@@ -140,7 +140,7 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
   g.w_skp = b.take((size_t)skinny_part_floats(g.T, std::max(g.D, g.nq)) * 4);
   // K pieces of the da gather-GEMM when its grid is under half a round
-  g.w_rp = b.take((size_t)ng_rpart_floats(st, g.ko, g.nq, G_BN, ceil_div(g.D, bk) + ceil_div(g.rp, bk)) * 4);
+  g.w_rp = b.take((size_t)ng_rpart_floats(st, g.ko, g.nq, false, g.esz, {g.D, g.rp}) * 4);
   g.ws_bytes = b.off;
   return SL_OK;
 }

@@ -244,6 +244,17 @@ void sl_timer_select(uint32_t slot_mask);
 void sl_timer_reset(void);
 int sl_timer_read(int slot, double* total_ms, int* count);
 
+/* ---------------------------------------------------------------------------
+ * GEMM variant (tuning and testing; results agree to the same tolerance).  The
+ * bf16 N-gather GEMMs (gate/up, dH, q/k/v, da) run as wide 128 x 512 tiles fed
+ * by LDS-DMA when every operand is 16-byte aligned with K a multiple of 8, and
+ * as 128 x 256 tiles otherwise.  wide_ng = 1 allows the wide tiles (default),
+ * 0 forbids them, a negative value leaves the setting; returns the previous
+ * setting.  Process-wide, not synchronised: set it between calls, from one
+ * thread.
+ * ------------------------------------------------------------------------- */
+int sl_gemm_config(int wide_ng);
+
 #ifdef __cplusplus
 }
 #endif

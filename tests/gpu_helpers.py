@@ -1,6 +1,8 @@
 """Shared helpers of the GPU parity tests (not a test module)."""
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 import torch
 
@@ -74,3 +76,14 @@ def check_selection(gpu_idx: np.ndarray, ora_scores: np.ndarray, k: int):
             # valid within the gap: every chosen score is >= the (k+1)-th up to GAP
             assert s[g].min() >= sk1 * (1 - GAP) - 1e-30, f"seq {b}: chosen score below threshold"
     return exact
+
+
+@contextlib.contextmanager
+def gemm_variant(wide_ng: int):
+    """Run the block with the wide N-gather GEMM tiles allowed (1) or not (0)."""
+    import contextual_sparsity_lora_svd_amd as sl
+    prev = sl.gemm_config(wide_ng)
+    try:
+        yield
+    finally:
+        sl.gemm_config(prev)

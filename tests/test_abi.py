@@ -145,3 +145,14 @@ def test_k_rule_matches_oracle(sl):
     for n in (1, 7, 688, 4096, 11008, 14336):
         for pct in (0, 1, 30, 50, 60, 75, 90, 99):
             assert sl.k_from_ratio(n, pct) == O.k_from_ratio(n, pct)
+
+
+def test_gemm_config_round_trip(sl):
+    """The GEMM variant switch is host state: set, read back, restore."""
+    prev = sl.gemm_config(-1)
+    assert prev in (0, 1)
+    assert sl.gemm_config(0) == prev
+    assert sl.gemm_config(-1) == 0
+    assert sl.gemm_config(7) == 0          # any non-zero value allows the wide tiles
+    assert sl.gemm_config(-1) == 1
+    sl.gemm_config(prev)

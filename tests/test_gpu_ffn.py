@@ -5,7 +5,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_helpers import (assert_close, check_selection, factors, rel_err, to_dev, to_np)
+from tests.gpu_helpers import (assert_close, check_selection, factors, gemm_variant, rel_err, to_dev,
+                               to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,10 @@ def _compare(p, ctx, L, idx, dt, s=1.0):
 def test_ffn_ragged_groups_and_tails(dt):
     """Three sequences (all context / all output / mixed), k and r off the
     tile and chunk sizes, d_ff not a multiple of the tile."""
+    _ragged_case(dt)
+
+
+def _ragged_case(dt):
     D, F, r, L = 64, 136, 4, 50
     ctx = [50, 0, 37]
     p = _ffn_case(D, F, r, ctx, L, dt, seed=5)
@@ -94,6 +99,18 @@ def test_ffn_dense_and_single_channel(dt):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_ffn_multi_tile(dt):
     """Several M, N and K tiles and the output-group K split."""
+    _multi_case(dt)
+
+
+@pytest.mark.parametrize("case", ["ragged", "multi"])
+def test_ffn_bf16_narrow_gather_tiles(case):
+    """The same cases with the wide N-gather tiles forbidden: the 128 x 256
+    tiles that take operands the wide ones cannot (unaligned, K off 8)."""
+    with gemm_variant(0):
+        (_ragged_case if case == "ragged" else _multi_case)("bf16")
+
+
+def _multi_case(dt):
     D, F, r, L = 512, 1104, 16, 300
     ctx = [290, 200, 300]
     p = _ffn_case(D, F, r, ctx, L, dt, seed=9)

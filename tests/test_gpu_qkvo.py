@@ -112,7 +112,15 @@ def test_qkvo_split_calls_and_extremes(dt):
     _compare(p, heads, ctx, L, full, np.array([[0], [nkv - 1]], np.int32), dt)
 
 
-def test_qkvo_multi_tile_bf16():
+@pytest.mark.parametrize("wide", [1, 0])
+def test_qkvo_multi_tile_bf16(wide):
+    """Several tiles per group; wide = 0 forbids the wide N-gather tiles."""
+    from tests.gpu_helpers import gemm_variant
+    with gemm_variant(wide):
+        _qkvo_multi_tile()
+
+
+def _qkvo_multi_tile():
     heads = (16, 4, 64)
     D, r, L = 512, 16, 300
     ctx = [260, 300, 150]

@@ -37,7 +37,8 @@ class SlHeads(ctypes.Structure):
 class SlFfnWeights(ctypes.Structure):
     _fields_ = [("d_model", _i64), ("d_ff", _i64), ("lora_rank", _i32), ("lora_scale", ctypes.c_float),
                 ("Wg", _vp), ("Wu", _vp), ("WdT", _vp), ("Ag", _vp), ("Bg", _vp), ("Au", _vp),
-                ("Bu", _vp), ("Ad", _vp), ("Bd", _vp)]
+                ("Bu", _vp), ("Ad", _vp), ("Bd", _vp),
+                ("Wg_q", _vp), ("Wu_q", _vp), ("WdT_q", _vp), ("Wg_s", _vp), ("Wu_s", _vp), ("WdT_s", _vp)]
 
 
 class SlFfnGrads(ctypes.Structure):
@@ -252,18 +253,27 @@ def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, 
 
 
 class FFNWeights:
-    """Device tensors of one FFN layer: Wg, Wu, WdT, Ag, Bg, Au, Bu, Ad, Bd."""
+    """Device tensors of one FFN layer: Wg, Wu, WdT, Ag, Bg, Au, Bu, Ad, Bd.
+
+    A 4-bit frozen base replaces Wg, Wu, WdT by Wg_q, Wu_q, WdT_q (uint8 codes
+    [d_ff, d_model / 2]) and Wg_s, Wu_s, WdT_s (fp32 scales [d_ff, d_model / 64])."""
 
     NAMES = ("Wg", "Wu", "WdT", "Ag", "Bg", "Au", "Bu", "Ad", "Bd")
+    QNAMES = ("Wg_q", "Wu_q", "WdT_q", "Wg_s", "Wu_s", "WdT_s")
 
     def __init__(self, t: Dict[str, torch.Tensor], lora_scale: float = 1.0):
         self.t = t
-        d_ff, d_model = t["Wg"].shape
+        self.quantized = "Wg_q" in t
+        if self.quantized:
+            d_ff, half = t["Wg_q"].shape
+            d_model = 2 * half
+        else:
+            d_ff, d_model = t["Wg"].shape
         r = t["Ag"].shape[0]
         self.c = SlFfnWeights(d_model, d_ff, r, float(lora_scale),
-                              *[_ptr(t[n]) for n in self.NAMES])
+                              *[_ptr(t[n]) if n in t else None for n in self.NAMES + self.QNAMES])
         self.d_model, self.d_ff, self.r = d_model, d_ff, r
-        self.dtype = _dtype_code(t["Wg"])
+        self.dtype = _dtype_code(t["Ag"])
 
     @property
     def ref(self):

@@ -122,14 +122,38 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   return SL_OK;
 }
 
-sl_status check_ffn_ptrs(const sl_ffn_weights* w, const void* X) {
+sl_status check_ffn_ptrs(sl_dtype dt, const sl_ffn_weights* w, const void* X) {
   if (!w) SL_FAIL(SL_ERR_NULL, "weights is NULL");
-  if (!X || !w->Wg || !w->Wu || !w->WdT || !w->Ag || !w->Bg || !w->Au || !w->Bu || !w->Ad || !w->Bd)
+  if (w->Wg_q) {
+    // 4-bit frozen base (SparseLoRA article §六): codes and block scales
+    if (dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "a 4-bit frozen base needs bf16 calls");
+    if (w->d_model % 64 != 0) SL_FAIL(SL_ERR_SHAPE, "a 4-bit frozen base needs d_model %% 64 == 0");
+    if (!w->Wu_q || !w->WdT_q || !w->Wg_s || !w->Wu_s || !w->WdT_s)
+      SL_FAIL(SL_ERR_NULL, "Wg_q is set: Wu_q, WdT_q, Wg_s, Wu_s, WdT_s must be non-NULL");
+    if (!aligned16(w->Wg_q) || !aligned16(w->Wu_q) || !aligned16(w->WdT_q) || !aligned16(w->Wg_s) ||
+        !aligned16(w->Wu_s) || !aligned16(w->WdT_s))
+      SL_FAIL(SL_ERR_ALIGN, "4-bit codes and scales must be 16-byte aligned");
+  } else {
+    if (!w->Wg || !w->Wu || !w->WdT) SL_FAIL(SL_ERR_NULL, "a weight or input pointer is NULL");
+    if (!aligned16(w->Wg) || !aligned16(w->Wu) || !aligned16(w->WdT))
+      SL_FAIL(SL_ERR_ALIGN, "X, Wg, Wu, WdT, Ag, Au must be 16-byte aligned");
+  }
+  if (!X || !w->Ag || !w->Bg || !w->Au || !w->Bu || !w->Ad || !w->Bd)
     SL_FAIL(SL_ERR_NULL, "a weight or input pointer is NULL");
-  if (!aligned16(X) || !aligned16(w->Wg) || !aligned16(w->Wu) || !aligned16(w->WdT) ||
-      !aligned16(w->Ag) || !aligned16(w->Au))
+  if (!aligned16(X) || !aligned16(w->Ag) || !aligned16(w->Au))
     SL_FAIL(SL_ERR_ALIGN, "X, Wg, Wu, WdT, Ag, Au must be 16-byte aligned");
   return SL_OK;
+}
+
+// Base segment of a gather-GEMM over frozen weight W (plain) or its 4-bit
+// codes Wq with scales Ws (w->Wg_q set); B2 / B2q / B2s: dual mode's up half.
+inline void set_base(GSeg& sg, const sl_ffn_weights* w, const void* W, const void* Wq, const float* Ws,
+                     const void* W2 = nullptr, const void* W2q = nullptr, const float* W2s = nullptr) {
+  if (w->Wg_q) {
+    sg.B = Wq; sg.Bs = Ws; sg.B2 = W2q; sg.B2s = W2s; sg.bq4 = 1;
+  } else {
+    sg.B = W; sg.B2 = W2;
+  }
 }
 
 template <typename T>
@@ -187,6 +211,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.idx = idx; a.kidx = g.k; a.n_out = F;
     a.nseg = 2;
     a.seg[0] = GSeg{X, D, 0, 0, 1, w->Wg, w->Wu, D, 1, D, nullptr, 0, 0};
+    set_base(a.seg[0], w, w->Wg, w->Wg_q, w->Wg_s, w->Wu, w->Wu_q, w->Wu_s);
     a.seg[1] = GSeg{zs_gu, 2 * rp, 0, 0, 1, Pg, Pu, 2 * rp, 1, 2 * rp, nullptr, 0, 0};
     a.o0 = Gc; a.o1 = Uc; a.o2 = Hc;
     a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
@@ -217,6 +242,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.N = D;
     a.nseg = 2;
     a.seg[0] = GSeg{Hc, g.ldk, g.ldF, g.c_out_off, 0, w->WdT, nullptr, D, 1, 0, idx, g.k, F};
+    set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
     a.seg[1] = GSeg{zs_d, rp, 0, 0, 1, BdTp, nullptr, D, 0, rp, nullptr, 0, 0};
     a.ksplit_out = g.ks_down;
     a.o0 = Y; a.ldo = D;
@@ -296,6 +322,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.idx = idx; a.kidx = g.k; a.n_out = F;
     a.nseg = 2;
     a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
+    set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
     a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
     a.o0 = dGc; a.o1 = dUc;
     a.i0 = Gc; a.i1 = Uc;
@@ -328,6 +355,8 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.nseg = 3;
     a.seg[0] = GSeg{dGc, g.ldk, g.ldF, g.c_out_off, 0, w->Wg, nullptr, D, 1, 0, idx, g.k, F};
     a.seg[1] = GSeg{dUc, g.ldk, g.ldF, g.c_out_off, 0, w->Wu, nullptr, D, 1, 0, idx, g.k, F};
+    set_base(a.seg[0], w, w->Wg, w->Wg_q, w->Wg_s);
+    set_base(a.seg[1], w, w->Wu, w->Wu_q, w->Wu_s);
     a.seg[2] = GSeg{dzs_gu, 2 * rp, 0, 0, 1, Agup, nullptr, D, 0, 2 * rp, nullptr, 0, 0};
     a.ksplit_out = g.ks_dx;
     a.o0 = dX; a.ldo = D;
@@ -376,7 +405,7 @@ sl_status sl_ffn_fwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w,
   FfnGeom g;
   sl_status s = ffn_geom(dt, lay, w->d_model, w->d_ff, w->lora_rank, k, g);
   if (s != SL_OK) return s;
-  if ((s = check_ffn_ptrs(w, X)) != SL_OK) return s;
+  if ((s = check_ffn_ptrs(dt, w, X)) != SL_OK) return s;
   if (!idx || !Y || !saved || !ws) SL_FAIL(SL_ERR_NULL, "idx, Y, saved and ws must be non-NULL");
   if (!aligned16(Y) || !aligned16(saved) || !aligned16(ws))
     SL_FAIL(SL_ERR_ALIGN, "Y, saved and ws must be 16-byte aligned");
@@ -401,7 +430,7 @@ sl_status sl_ffn_bwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w,
   FfnGeom g;
   sl_status s = ffn_geom(dt, lay, w->d_model, w->d_ff, w->lora_rank, k, g);
   if (s != SL_OK) return s;
-  if ((s = check_ffn_ptrs(w, X)) != SL_OK) return s;
+  if ((s = check_ffn_ptrs(dt, w, X)) != SL_OK) return s;
   if (!gr || !gr->dAg || !gr->dBg || !gr->dAu || !gr->dBu || !gr->dAd || !gr->dBd)
     SL_FAIL(SL_ERR_NULL, "a gradient pointer is NULL");
   if (!idx || !saved || !dY || !dX || !ws)

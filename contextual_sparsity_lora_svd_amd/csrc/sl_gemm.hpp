@@ -56,6 +56,11 @@ struct GSeg {
   // KG segments with K <= 0: channel set of the segment (context group g uses
   // idx + g*kidx, kidx channels; the output group uses all n_out channels).
   const int* idx; int kidx; int n_out;
+  // bq4 = 1: B (and B2) hold 4-bit codes of a quantized frozen weight, row
+  // stride ldb/2 bytes, element 2j of a row in the low nibble of byte j (two's
+  // complement), and Bs (B2s) one fp32 scale per 64 elements of a row, row
+  // stride ldb/64; the element is code * scale (ldb a multiple of 64).
+  const float* Bs; const float* B2s; int bq4;
 };
 
 // One problem of a launch: its channel set, the B operand of each segment, a
@@ -122,6 +127,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 struct alignas(16) Chunk { uint32_t w[4]; };
 
 __device__ inline Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u; return c; }
+
+// 8 consecutive 4-bit codes (element j in bits 4j..4j+3, two's complement)
+// times a scale, as 8 bf16 (round to nearest even).
+__device__ inline Chunk deq8(uint32_t code, float scale) {
+  Chunk c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = ((int)(code << (28 - 8 * j))) >> 28;
+    const int q1 = ((int)(code << (24 - 8 * j))) >> 28;
+    c.w[j] = (uint32_t)f2bf((float)q0 * scale) | ((uint32_t)f2bf((float)q1 * scale) << 16);
+  }
+  return c;
+}
 
 __device__ inline Chunk load_chunk(const void* p) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
@@ -274,9 +292,11 @@ __device__ inline void scatter_row8(T* row, const int* gidx, int c, int nch, int
   }
 }
 
-template <typename T, int MODE, int EPI, bool DUAL, int BM, int WN>
+template <typename T, int MODE, int EPI, bool DUAL, int BM, int WN, bool QB>
 __global__ void __launch_bounds__(WN == 4 ? 512 : G_THREADS, WN == 4 ? 1 : (BM == 128 ? 2 : 1))
 gather_gemm_kernel(const GemmArgs args) {
+  // QB: segments with bq4 set read their B operand as 4-bit codes and scales
+  // (bf16 only, register-staged tiles), dequantized on the way into LDS.
   // WN = 2: BM x 256 tile, 4 waves in a 2 x 2 grid of (BM/2) x 128 blocks,
   //   two workgroups per CU, operands staged through registers (K-gather bf16:
   //   B by LDS-DMA).
@@ -288,6 +308,7 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr bool WIDE = WN == 4;
   static_assert(WN == 2 || (WIDE && MODE == MODE_NG && sizeof(T) == 2 && BM == 128),
                 "the wide tile is an N-gather bf16 128-row tile");
+  static_assert(!QB || (!WIDE && sizeof(T) == 2), "quantized B: bf16 register-staged tiles");
   constexpr int NWAVE = WIDE ? 8 : 4;       // waves per workgroup
   constexpr int BN_T = WIDE ? 512 : 256;    // B rows (accumulator columns) per tile
   constexpr int VEC = GTraits<T>::VEC;
@@ -308,7 +329,7 @@ gather_gemm_kernel(const GemmArgs args) {
   // into an unpadded tile with XOR-swizzled 16-byte chunks.  Two workgroups
   // then fill the CU's 160 KB of LDS exactly.  Otherwise both operands are
   // staged through registers into padded [row][k] tiles.
-  constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128;
+  constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128 && !QB;
   constexpr int A_LD = KGD ? BK : LDS_LD;   // A tile row stride (elements)
   constexpr int B_STAGE = BK * G_BN * (int)sizeof(T);   // KGD: bytes per B stage
   constexpr int EP_LD = 64 + 4;             // epilogue staging row (floats)
@@ -427,8 +448,9 @@ gather_gemm_kernel(const GemmArgs args) {
   Chunk rb[PF][8];
   int va[PF];            // valid elements of the A / N-gather B chunks of each set
   int kg_rv[PF];         // K-gather: valid k-rows of each set
+  bool qv[PF];           // QB: the set's B chunks hold (codes, scale) still to dequantize
 #pragma unroll
-  for (int p = 0; p < PF; ++p) { va[p] = VEC; kg_rv[p] = KR; }
+  for (int p = 0; p < PF; ++p) { va[p] = VEC; kg_rv[p] = KR; qv[p] = false; }
 
   // loader cursor: uniform scalars + per-thread element offsets (32-bit; the
   // host checks that every operand has fewer than 2^31 elements)
@@ -439,6 +461,9 @@ gather_gemm_kernel(const GemmArgs args) {
   unsigned a_off[ACH];
   unsigned b_off[8];
   int cur_ldb = 0;
+  bool cur_q = false;               // QB: the segment's B is 4-bit
+  const float* bs_base = nullptr;   // QB: its scales (dual: gate rows)
+  const float* bs2_base = nullptr;  //     (dual: up rows)
 
   auto enter_seg = [&](int s) {
     s = __builtin_amdgcn_readfirstlane(s);
@@ -450,6 +475,11 @@ gather_gemm_kernel(const GemmArgs args) {
     b_base = reinterpret_cast<const T*>(pr.B[s]);
     b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : pr.B[s]);
     cur_ldb = (int)sg.ldb;
+    if constexpr (QB) {
+      cur_q = sg.bq4 != 0;
+      bs_base = sg.Bs;
+      bs2_base = DUAL ? sg.B2s : sg.Bs;
+    }
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       int r = m0 + a_row0 + 32 * i;
@@ -510,10 +540,23 @@ gather_gemm_kernel(const GemmArgs args) {
     const int kc = kcol < cur_K ? kcol : 0;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) ra[P][i] = load_chunk(a_base + (a_off[i] + kc));
+    if constexpr (QB) qv[P] = cur_q;
     if (MODE == MODE_NG) {
+      if (QB && cur_q) {
+        // 8 codes (4 bytes) and the scale of their 64-element block per row
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rb[P][i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + (b_off[i] + kc));
+        for (int i = 0; i < 8; ++i) {
+          const bool up = DUAL && 32 * i >= BNC;
+          const unsigned e = b_off[i] + (unsigned)kc;
+          const unsigned char* cb = reinterpret_cast<const unsigned char*>(up ? b2_base : b_base);
+          rb[P][i].w[0] = *reinterpret_cast<const uint32_t*>(cb + e / 2);
+          rb[P][i].w[1] = __float_as_uint((up ? bs2_base : bs_base)[e / 64]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rb[P][i] = load_chunk(((DUAL && 32 * i >= BNC) ? b2_base : b_base) + (b_off[i] + kc));
+      }
     } else if constexpr (KGD) {
       // The tile's 64 B rows (krow_reg of lane p = row of k-position p) as 32
       // LDS-DMA blocks of two k-rows; wave w issues blocks 4 j + w.  Lane l
@@ -552,12 +595,22 @@ gather_gemm_kernel(const GemmArgs args) {
         const int4 q = *reinterpret_cast<const int4*>(&krow_s[kg_kr0 + i]);
         rows[i] = q.x; rows[i + 1] = q.y; rows[i + 2] = q.z; rows[i + 3] = q.w;
       }
+      if (QB && cur_q) {
+        // 8 codes of n-columns kg_c0.. (one 64-element block) and its scale per k-row
 #pragma unroll
-      for (int i = 0; i < KR; ++i)
+        for (int i = 0; i < KR; ++i) {
+          const unsigned e = (unsigned)rows[i] * (unsigned)cur_ldb + (unsigned)kg_c0;
+          rb[P][i].w[0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(b_base) + e / 2);
+          rb[P][i].w[1] = __float_as_uint(bs_base[e / 64]);
+        }
+      } else {
 #pragma unroll
-        for (int h = 0; h < 8 / VEC; ++h)
-          rb[P][i * (8 / VEC) + h] =
-              load_chunk(b_base + ((unsigned)rows[i] * (unsigned)cur_ldb + kg_c0 + h * VEC));
+        for (int i = 0; i < KR; ++i)
+#pragma unroll
+          for (int h = 0; h < 8 / VEC; ++h)
+            rb[P][i * (8 / VEC) + h] =
+                load_chunk(b_base + ((unsigned)rows[i] * (unsigned)cur_ldb + kg_c0 + h * VEC));
+      }
     }
     ++cur_kk;
   };
@@ -573,6 +626,12 @@ gather_gemm_kernel(const GemmArgs args) {
   auto store_tile = [&](auto Pc) {
     constexpr int P = decltype(Pc)::value;
     if constexpr (KGD) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tile's B DMA has landed
+    if constexpr (QB) {
+      if (qv[P]) {   // 8 B chunks of (codes, scale) either way (bf16: KR = 8, 8 / VEC = 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[P][i] = deq8(rb[P][i].w[0], __uint_as_float(rb[P][i].w[1]));
+      }
+    }
     if (va[P] < VEC) {
 #pragma unroll
       for (int i = 0; i < ACH; ++i) mask_chunk<T>(ra[P][i], va[P]);
@@ -1266,7 +1325,7 @@ inline bool wide_ng_ok(const GemmArgs& a, int esz) {
 }
 
 // Host side: count tiles per group and launch one variant.
-template <typename T, int MODE, int EPI, bool DUAL, int WN>
+template <typename T, int MODE, int EPI, bool DUAL, int WN, bool QB>
 hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot) {
   constexpr int BN_T = WN == 4 ? 512 : 256;
   constexpr int BNC = DUAL ? BN_T / 2 : BN_T;
@@ -1303,7 +1362,7 @@ hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot
     }
   }
   timer_begin(timer_slot, stream);
-  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM, WN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM, WN, QB>), dim3((unsigned)grid),
                      dim3(WN == 4 ? 512 : G_THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
@@ -1330,11 +1389,18 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   }
   if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))
     return hipErrorInvalidValue;
+  bool quant = false;
+  for (int s = 0; s < a.nseg; ++s) quant |= a.seg[s].bq4 != 0;
+  if constexpr (sizeof(T) == 2) {
+    if (quant) return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2, true>(a, stream, timer_slot);
+  } else {
+    if (quant) return hipErrorInvalidValue;   // 4-bit weights: bf16 launches only
+  }
   if constexpr (MODE == MODE_NG && sizeof(T) == 2) {
     if (g_gemm_wide_ng && wide_ng_ok(a, 2))
-      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 4>(a, stream, timer_slot);
+      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 4, false>(a, stream, timer_slot);
   }
-  return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2>(a, stream, timer_slot);
+  return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2, false>(a, stream, timer_slot);
 }
 
 }  // namespace sl

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SL_ABI_VERSION 1
+#define SL_ABI_VERSION 2
 #define SL_MAX_SEQS 64  /* sequences per call (batch) */
 
 typedef enum sl_status {
@@ -97,6 +97,18 @@ typedef struct sl_ffn_weights {
   float lora_scale;
   const void *Wg, *Wu, *WdT;
   const void *Ag, *Bg, *Au, *Bu, *Ad, *Bd;
+  /* Optional 4-bit frozen base (SparseLoRA article §六: SparseLoRA over a
+   * QLoRA-style quantized base).  When Wg_q is not NULL the frozen weights are
+   * these, and Wg, Wu, WdT are ignored (may be NULL):
+   *   Wg_q, Wu_q, WdT_q  uint8 [d_ff, d_model / 2]: element 2j of a row in the
+   *                      low nibble of byte j, element 2j+1 in the high nibble,
+   *                      signed two's-complement codes
+   *   Wg_s, Wu_s, WdT_s  fp32 [d_ff, d_model / 64]: the scale of each block of
+   *                      64 consecutive elements of a row
+   * The weight element is code * scale.  bf16 calls only; d_model a multiple of
+   * 64; all six 16-byte aligned.  Zero-initialised (C) or NULL: plain weights. */
+  const void *Wg_q, *Wu_q, *WdT_q;
+  const float *Wg_s, *Wu_s, *WdT_s;
 } sl_ffn_weights;
 
 /* LoRA gradients of one FFN layer, fp32, shapes of the factors; OVERWRITTEN. */

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(sl):
 
 def test_status_strings(sl):
     L = sl.lib()
-    assert L.sl_abi_version() == 1
+    assert L.sl_abi_version() == 2
     for code in range(9):
         assert L.sl_status_string(code)
     assert L.sl_status_string(99) == b"unknown status"

@@ -7,8 +7,8 @@ name no quantization format.  The reading taken here is the plainest 4-bit
 one: each row of a frozen weight is cut into blocks of QBLOCK consecutive
 elements; a block holds one fp32 scale s = max|w| / 7 (0 for an all-zero
 block) and one signed 4-bit code q = round(w / s) in [-7, 7] per element
-(ties to even), and the layer computes with the dequantized value q * s in
-place of w.  So the sparse LoRA layer over a quantized base is the same
+(ties to even; w, s and the quotient in fp32), and the layer computes with
+the dequantized value q * s in place of w.  So the sparse LoRA layer over a quantized base is the same
 masked-dense layer as over a plain base, evaluated at W = dequantize(codes,
 scales): the oracle is dequantization (exact in fp64) in front of the
 existing forward and backward.
@@ -27,17 +27,21 @@ QBLOCK = 64
 
 
 def quantize_int4_rows(W: np.ndarray, block: int = QBLOCK):
-    """Codes and scales of W [rows, cols] (the reading above)."""
-    W = np.asarray(W, dtype=np.float64)
+    """Codes and scales of W [rows, cols] (the reading above).  The weight is
+    taken as fp32, and the code, an integer decided by floating point, is
+    decided in fp32: s = fp32(max|w|) / 7 and q = rint(w / s), both IEEE fp32
+    divisions, ties to even."""
+    W = np.asarray(W, dtype=np.float32)
     rows, cols = W.shape
     if cols % block:
         raise ValueError("columns must be a multiple of the block")
     Wb = W.reshape(rows, cols // block, block)
     amax = np.abs(Wb).max(axis=2)
-    scales = (amax / 7.0).astype(np.float32)
-    s64 = scales.astype(np.float64)[:, :, None]
+    scales = (amax / np.float32(7.0)).astype(np.float32)
+    s32 = scales[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.where(s64 > 0, np.rint(Wb / np.where(s64 > 0, s64, 1.0)), 0.0)
+        quot = (Wb / np.where(s32 > 0, s32, np.float32(1.0))).astype(np.float32)
+    q = np.where(s32 > 0, np.rint(quot), np.float32(0.0))
     q = np.clip(q, -7, 7).astype(np.int64).reshape(rows, cols)
     u = (q & 0xF).astype(np.uint8)
     codes = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)

@@ -168,6 +168,74 @@ def ffn_extreme_bench(args, torch, sl, cfg=6):
             "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
 
 
+def qlora_bench(args, torch, sl, cfg=2):
+    """The FFN rows over a 4-bit quantized frozen base (SparseLoRA article §六:
+    SparseLoRA combined with a QLoRA-style base): the frozen weights are
+    quantized on the GPU (sl_quantize_q4), then estimate, select, forward and
+    backward run from the codes, against the same kernels run dense over the
+    same quantized base (k = d_ff, no estimator)."""
+    wl = W.WORKLOADS[cfg]
+    f = wl.ffn[0]
+    D, F, r, r_e, L = f.d_model, f.d_ff, f.lora_rank, wl.est_rank, wl.seq_len
+    ctx = [int(c) for c in W.ctx_lengths(wl)]
+    B, T = len(ctx), len(ctx) * L
+    k = sl.k_from_ratio(F, f.sparsity_pct)
+    p = W.make_ffn_tensors(wl)
+    bf = torch.bfloat16
+    t = {n: to_dev(p[n], torch, bf) for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")}
+    X, dY = to_dev(p["X"], torch, bf), to_dev(p["dY"], torch, bf)
+    base = {"Wg": to_dev(p["Wg"], torch, bf), "Wu": to_dev(p["Wu"], torch, bf),
+            "WdT": to_dev(np.ascontiguousarray(p["Wd"].T), torch, bf)}
+    del p
+    for n, w0 in base.items():
+        t[n + "_q"], t[n + "_s"] = sl.quantize_q4(w0)
+    # the estimator factors of the frozen base the layer computes with
+    deq = lambda n: (sl_dequant(torch, t[n + "_q"], t[n + "_s"])).to(bf)
+    Ptg, Qg, _ = sl.build_estimator(deq("Wg"), r_e)
+    Ptu, Qu, _ = sl.build_estimator(deq("Wu"), r_e)
+    del base
+    torch.cuda.empty_cache()
+    w = sl.FFNWeights(t, lora_scale=1.0)
+    lay = sl.Layout(ctx, L)
+    est = sl.EstimateBuffers(sl.SL_CRIT_SWIGLU_L2, lay, D, r_e, F, k, X.device)
+    Y = torch.empty_like(X)
+    grads = {"dX": torch.empty_like(X)}
+    for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd"):
+        grads["d" + n] = torch.empty(t[n].shape, dtype=torch.float32, device=X.device)
+
+    def run(kk, buf, idx=None):
+        if idx is None:
+            idx, _ = sl.estimate_select(sl.SL_CRIT_SWIGLU_L2, X, lay, r_e, Ptg, Qg, Ptu, Qu, F, kk, bufs=est)
+        sl.ffn_fwd(w, X, lay, kk, idx, buf, Y=Y)
+        sl.ffn_bwd(w, X, lay, kk, idx, buf, dY, out=grads)
+
+    buf = sl.FFNWorkspace(w, lay, k, X.device)
+    ms = timed(torch, lambda: run(k, buf), args.steps, args.warmup)
+    full = torch.arange(F, dtype=torch.int32, device=X.device).repeat(B, 1).contiguous()
+    bufd = sl.FFNWorkspace(w, lay, F, X.device)
+    dense_ms = timed(torch, lambda: run(F, bufd, full), max(3, args.steps // 2), 2) if not args.no_dense else None
+    fl = ffn_flops(D, F, r, ctx, L, k)
+    weight_bytes = sum(t[n].numel() * t[n].element_size() for n in ("Wg_q", "Wu_q", "WdT_q", "Wg_s", "Wu_s", "WdT_s"))
+    print(f"[bench] 4-bit base FFN step {ms:.3f} ms" + (f", dense {dense_ms:.3f} ms" if dense_ms else ""),
+          file=sys.stderr, flush=True)
+    return {"workload": wl.name, "base": "int4, one fp32 scale per 64-element row block",
+            "frozen_weight_bytes": weight_bytes, "bf16_weight_bytes": 3 * F * D * 2,
+            "batch": B, "seq_len": L, "ctx_len": ctx, "sparsity_pct": f.sparsity_pct, "k": k,
+            "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "effective_tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_gflop": fl / 1e9,
+            "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
+
+
+def sl_dequant(torch, codes, scales):
+    """code * scale of packed 4-bit codes (torch ops; used only to build the
+    estimator factors of the quantized base offline)."""
+    lo = (codes & 0xF).to(torch.int16)
+    hi = (codes >> 4).to(torch.int16)
+    q = torch.stack((lo, hi), dim=2).reshape(codes.shape[0], -1)
+    q = torch.where(q >= 8, q - 16, q).float()
+    return q * scales.repeat_interleave(64, dim=1)
+
+
 def attn_bench(args, torch, sl, cfg=3):
     """q/k/v/o rows of the path on a LLaMA2-7B attention workload: QK-norm and
     L2 selection over context tokens, sparse q/k/v/o forward and backward."""
@@ -254,6 +322,8 @@ def main():
     ap.add_argument("--no-attn", action="store_true", help="skip the q/k/v/o workload")
     ap.add_argument("--no-extreme", action="store_true",
                     help="skip the extreme-sparsity workload (99 %% FFN, 75 %% q/k/v/o)")
+    ap.add_argument("--no-qlora", action="store_true",
+                    help="skip the FFN over a 4-bit quantized frozen base")
     ap.add_argument("--attn-only", action="store_true",
                     help="run only the q/k/v/o workload and print its measurements as the JSON line "
                          "(for profiling that step alone)")
@@ -374,6 +444,11 @@ def main():
         if not args.no_attn:
             extreme["attention"] = attn_bench(args, torch, sl, cfg=6)
 
+    qlora = None
+    if not args.no_qlora:
+        torch.cuda.empty_cache()
+        qlora = qlora_bench(args, torch, sl)
+
     if args.copy_calibration:
         n = 64 << 20
         src = torch.ones(n, dtype=torch.bfloat16, device=X.device)
@@ -418,6 +493,7 @@ def main():
         "estimator_build_ms_per_weight": build_ms,
         "attention": attn,
         "extreme_sparsity": extreme,
+        "quantized_base": qlora,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -82,6 +82,7 @@ SIGNATURES = {
                                   ctypes.POINTER(SlFfnGrads), _vp, _sz, _vp]),
     "sl_timer_enable": (ctypes.c_int, [ctypes.c_int]),
     "sl_gemm_config": (ctypes.c_int, [ctypes.c_int]),
+    "sl_quantize_q4": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp]),
     "sl_timer_select": (None, [ctypes.c_uint32]),
     "sl_timer_reset": (None, []),
     "sl_timer_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -189,6 +190,17 @@ def timer_select(slots):
 
 def timer_reset():
     lib().sl_timer_reset()
+
+
+def quantize_q4(W: torch.Tensor):
+    """4-bit codes (uint8 [rows, cols / 2]) and block scales (fp32 [rows, cols / 64])
+    of a frozen weight W [rows, cols], for FFNWeights' quantized base."""
+    rows, cols = W.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((rows, max(cols // 64, 1)), dtype=torch.float32, device=W.device)
+    _check(lib().sl_quantize_q4(_dtype_code(W), _ptr(W), rows, cols, _ptr(codes), _ptr(scales), _stream()),
+           "sl_quantize_q4")
+    return codes, scales
 
 
 def gemm_config(wide_ng: int = -1) -> int:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparselora.so")
 
-SOURCES = ["sl_host.hip", "sl_estimate.hip", "sl_ffn.hip", "sl_qkvo.hip", "sl_svd.hip"]
+SOURCES = ["sl_host.hip", "sl_estimate.hip", "sl_ffn.hip", "sl_qkvo.hip", "sl_svd.hip", "sl_quant.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

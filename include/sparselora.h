@@ -232,6 +232,23 @@ sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* 
                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Offline quantization of a frozen weight to the 4-bit base of sl_ffn_weights
+ * (SparseLoRA article §六: SparseLoRA over a QLoRA-style quantized base; the
+ * pages name no format, this is the plainest 4-bit one).  W [rows, cols] in dt
+ * -> codes uint8 [rows, cols/2] and scales fp32 [rows, cols/64]: each block of
+ * 64 consecutive row elements gets s = max|w| / 7 (0 for an all-zero block)
+ * and codes q = rint(w / s) in [-7, 7] (IEEE fp32 division, ties to even);
+ * element 2j of a row sits in the low nibble of byte j, element 2j+1 in the
+ * high nibble (two's complement).  cols a positive multiple of 64; all
+ * pointers device, 16-byte aligned; the caller owns every buffer.  Stream-
+ * ordered, never synchronises.  Errors: SL_ERR_NULL, SL_ERR_DTYPE,
+ * SL_ERR_SHAPE, SL_ERR_RANGE, SL_ERR_ALIGN, SL_ERR_UNSUPPORTED_ARCH,
+ * SL_ERR_HIP; nothing is launched on error.
+ * ------------------------------------------------------------------------- */
+sl_status sl_quantize_q4(sl_dtype dt, const void* W, int64_t rows, int64_t cols, void* codes, float* scales,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics (not part of the computation).  When enabled, the library's main
  * launches are bracketed by HIP events on the caller's stream and attributed
  * to the slots below, so a caller can time individual kernels inside a timed

@@ -104,3 +104,23 @@ def test_qlora_rejects_fp32_and_ragged_width():
     idx = torch.zeros((1, 4), dtype=torch.int32).cuda()
     with pytest.raises(sl.SparseLoraError):
         sl.ffn_fwd(w, to_dev(p["X"], "f32"), sl.Layout(ctx, L), 4, idx)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gpu_quantizer_matches_oracle_bit_exactly(dt):
+    """Codes and scales are integer / fp32 decisions taken in fp32 on both sides."""
+    import contextual_sparsity_lora_svd_amd as sl
+    rng = np.random.default_rng(37)
+    Wt = rng.standard_normal((300, 640)).astype(np.float32) * rng.lognormal(0, 2, (300, 1)).astype(np.float32)
+    Wt[3, :64] = 0.0                                   # all-zero block
+    Wt[4, :64] = np.arange(64) % 15 - 7.0              # exact codes, scale 1
+    Wt[5, :64] = 0.0
+    Wt[5, 0], Wt[5, 1], Wt[5, 2] = 7.0, 2.5, -3.5      # ties: rint -> 2 and -4
+    if dt == "bf16":
+        Wt = W.round_to_bf16(Wt)
+    codes_r, scales_r = O.quantize_int4_rows(Wt)
+    codes, scales = sl.quantize_q4(to_dev(Wt, dt))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), codes_r)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), scales_r.view(np.uint32))
+    assert O.int4_codes(codes_r)[5, :3].tolist() == [7, 2, -4]

@@ -129,14 +129,22 @@ struct alignas(16) Chunk { uint32_t w[4]; };
 __device__ inline Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u; return c; }
 
 // 8 consecutive 4-bit codes (element j in bits 4j..4j+3, two's complement)
-// times a scale, as 8 bf16 (round to nearest even).
+// times a scale, as 8 bf16 (round to nearest even).  Flipping each nibble's
+// sign bit gives u = q + 8 in 0..15; the even and odd nibbles, spread into
+// bytes, convert to float one instruction each, and fma(u, s, -8 s) is q * s
+// rounded once (-8 s is exact); pairs go to bf16 by the packed conversion.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ inline Chunk deq8(uint32_t code, float scale) {
+  const uint32_t u = code ^ 0x88888888u;
+  const uint32_t ev = u & 0x0F0F0F0Fu, od = (u >> 4) & 0x0F0F0F0Fu;
+  const float bias = -8.0f * scale;
   Chunk c;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int q0 = ((int)(code << (28 - 8 * j))) >> 28;
-    const int q1 = ((int)(code << (24 - 8 * j))) >> 28;
-    c.w[j] = (uint32_t)f2bf((float)q0 * scale) | ((uint32_t)f2bf((float)q1 * scale) << 16);
+    const f32x2_t f = {__builtin_fmaf((float)((ev >> (8 * j)) & 0xFFu), scale, bias),
+                       __builtin_fmaf((float)((od >> (8 * j)) & 0xFFu), scale, bias)};
+    c.w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
   }
   return c;
 }
@@ -329,6 +337,8 @@ gather_gemm_kernel(const GemmArgs args) {
   // into an unpadded tile with XOR-swizzled 16-byte chunks.  Two workgroups
   // then fill the CU's 160 KB of LDS exactly.  Otherwise both operands are
   // staged through registers into padded [row][k] tiles.
+  // (A 4-bit B takes the register path: its dequantized tile is transposed
+  // on the way into LDS.)
   constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128 && !QB;
   constexpr int A_LD = KGD ? BK : LDS_LD;   // A tile row stride (elements)
   constexpr int B_STAGE = BK * G_BN * (int)sizeof(T);   // KGD: bytes per B stage

@@ -50,7 +50,9 @@ class SlQkvoWeights(ctypes.Structure):
                 ("lora_scale", ctypes.c_float),
                 ("Wq", _vp), ("Wk", _vp), ("Wv", _vp), ("WoT", _vp),
                 ("Aq", _vp), ("Bq", _vp), ("Ak", _vp), ("Bk", _vp), ("Av", _vp), ("Bv", _vp),
-                ("Ao", _vp), ("Bo", _vp)]
+                ("Ao", _vp), ("Bo", _vp),
+                ("Wq_q", _vp), ("Wk_q", _vp), ("Wv_q", _vp), ("WoT_q", _vp),
+                ("Wq_s", _vp), ("Wk_s", _vp), ("Wv_s", _vp), ("WoT_s", _vp)]
 
 
 class SlQkvoGrads(ctypes.Structure):
@@ -331,19 +333,22 @@ def ffn_bwd(w: FFNWeights, X: torch.Tensor, layout: Layout, k: int, idx: torch.T
 
 
 class QKVOWeights:
-    """Device tensors of one attention block's projections."""
+    """Device tensors of one attention block's projections.  A 4-bit frozen
+    base replaces Wq, Wk, Wv by Wq_q, Wk_q, Wv_q with Wq_s, Wk_s, Wv_s, and WoT
+    by WoT_q with WoT_s (the format of FFNWeights' quantized base)."""
 
     NAMES = ("Wq", "Wk", "Wv", "WoT", "Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo")
+    QNAMES = ("Wq_q", "Wk_q", "Wv_q", "WoT_q", "Wq_s", "Wk_s", "Wv_s", "WoT_s")
 
     def __init__(self, t: Dict[str, torch.Tensor], heads: Sequence[int], lora_scale: float = 1.0):
         self.t = t
         self.heads = tuple(int(h) for h in heads)
-        d_model = t["Wq"].shape[1]
+        d_model = t["Aq"].shape[1]
         r = t["Aq"].shape[0]
         self.c = SlQkvoWeights(d_model, SlHeads(*self.heads), r, float(lora_scale),
-                               *[_ptr(t[n]) for n in self.NAMES])
+                               *[_ptr(t[n]) if n in t else None for n in self.NAMES + self.QNAMES])
         self.d_model, self.r = d_model, r
-        self.dtype = _dtype_code(t["Wq"])
+        self.dtype = _dtype_code(t["Aq"])
 
     @property
     def ref(self):

@@ -59,7 +59,8 @@ struct GSeg {
   // bq4 = 1: B (and B2) hold 4-bit codes of a quantized frozen weight, row
   // stride ldb/2 bytes, element 2j of a row in the low nibble of byte j (two's
   // complement), and Bs (B2s) one fp32 scale per 64 elements of a row, row
-  // stride ldb/64; the element is code * scale (ldb a multiple of 64).
+  // stride ldb/64; the element is code * scale (ldb a multiple of 64).  In
+  // multi-problem launches each problem's scales are in GProb::Bs.
   const float* Bs; const float* B2s; int bq4;
 };
 
@@ -71,6 +72,7 @@ struct GProb {
   int kidx, n_out;
   int swidth;                           // NG scatter: columns of the output rows
   const void* B[G_MAXSEG];
+  const float* Bs[G_MAXSEG];            // 4-bit segments (bq4): the scales of B[s]
   int a_col[G_MAXSEG];
   void* o0;
   long long ldo;
@@ -487,8 +489,8 @@ gather_gemm_kernel(const GemmArgs args) {
     cur_ldb = (int)sg.ldb;
     if constexpr (QB) {
       cur_q = sg.bq4 != 0;
-      bs_base = sg.Bs;
-      bs2_base = DUAL ? sg.B2s : sg.Bs;
+      bs_base = pr.Bs[s];
+      bs2_base = DUAL ? sg.B2s : pr.Bs[s];
     }
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
@@ -1394,7 +1396,7 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
     a.nprob = 1;
     GProb& p0 = a.prob[0];
     p0.idx = a.idx; p0.kidx = a.kidx; p0.n_out = a.n_out;
-    for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.a_col[s] = 0; }
+    for (int s = 0; s < G_MAXSEG; ++s) { p0.B[s] = a.seg[s].B; p0.Bs[s] = a.seg[s].Bs; p0.a_col[s] = 0; }
     p0.o0 = a.o0; p0.ldo = a.ldo; p0.swidth = a.swidth;
   }
   if (a.nprob > G_MAXPROB || (a.nprob > 1 && (MODE != MODE_NG || EPI != EPI_SCATTER)))

@@ -159,6 +159,11 @@ void add_compact(Layouter& L, const Comp& c, const void* src, const int* idx, vo
   L.compact(src, c.n, idx, c.kc, c.n, dst, c.ld, c.out_off, esz);
 }
 
+// Base segment of an o-weight gather-GEMM: WoT, or its 4-bit codes and scales.
+inline void set_o_base(GSeg& sg, const sl_qkvo_weights* w) {
+  if (w->WoT_q) { sg.B = w->WoT_q; sg.Bs = w->WoT_s; sg.bq4 = 1; }
+}
+
 template <typename T>
 sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void* X, const void* a,
                         const int* idx_qk, const int* idx_vo, void* q, void* k, void* v, void* o,
@@ -178,7 +183,9 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   T* ac = reinterpret_cast<T*>(ws + g.w_ac);
   T* Aog = reinterpret_cast<T*>(ws + g.w_Aog);
   T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
-  const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+  const bool qq = w->Wq_q != nullptr;   // 4-bit q/k/v base
+  const void* Wm[3] = {qq ? w->Wq_q : w->Wq, qq ? w->Wk_q : w->Wk, qq ? w->Wv_q : w->Wv};
+  const float* Ws[3] = {w->Wq_s, w->Wk_s, w->Wv_s};
   const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
   void* outp[3] = {q, k, v};
   const int* sets[3] = {idx_q, idx_qk, idx_vo};
@@ -228,11 +235,13 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.nseg = 2;
     ga.seg[0] = GSeg{X, D, 0, 0, 1, nullptr, nullptr, D, 1, D, nullptr, 0, 0};
     ga.seg[1] = GSeg{zs_qkv, 3 * rp, 0, 0, 1, nullptr, nullptr, rp, 1, rp, nullptr, 0, 0};
+    ga.seg[0].bq4 = qq ? 1 : 0;
     ga.nprob = 3;
     for (int j = 0; j < 3; ++j) {
       GProb& pr = ga.prob[j];
       pr.idx = sets[j]; pr.kidx = kk[j]; pr.n_out = nn[j];
       pr.B[0] = Wm[j]; pr.B[1] = Bp[j];
+      pr.Bs[0] = qq ? Ws[j] : nullptr;
       pr.a_col[0] = 0; pr.a_col[1] = j * rp;
       pr.o0 = outp[j]; pr.ldo = nn[j]; pr.swidth = nn[j];
     }
@@ -260,6 +269,7 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.N = D;
     ga.nseg = 2;
     ga.seg[0] = GSeg{ac, g.co.ld, g.nq, g.co.out_off, 0, w->WoT, nullptr, D, 1, 0, idx_o, g.ko, g.nq};
+    set_o_base(ga.seg[0], w);
     ga.seg[1] = GSeg{zs_o, rp, 0, 0, 1, BoTp, nullptr, D, 0, rp, nullptr, 0, 0};
     ga.ksplit_out = g.ks_o;
     ga.o0 = o; ga.ldo = D;
@@ -301,7 +311,9 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
                  reinterpret_cast<int*>(ws + g.w_inv_v)};
   const void* Bl[3] = {w->Bq, w->Bk, w->Bv};
   const void* Al[3] = {w->Aq, w->Ak, w->Av};
-  const void* Wm[3] = {w->Wq, w->Wk, w->Wv};
+  const bool qq = w->Wq_q != nullptr;   // 4-bit q/k/v base
+  const void* Wm[3] = {qq ? w->Wq_q : w->Wq, qq ? w->Wk_q : w->Wk, qq ? w->Wv_q : w->Wv};
+  const float* Ws[3] = {w->Wq_s, w->Wk_s, w->Wv_s};
   T* Bg[3] = {reinterpret_cast<T*>(ws + g.w_Bqg), reinterpret_cast<T*>(ws + g.w_Bkg),
               reinterpret_cast<T*>(ws + g.w_Bvg)};
   T* BTo[3] = {reinterpret_cast<T*>(ws + g.w_BqTo), reinterpret_cast<T*>(ws + g.w_BkTo),
@@ -359,6 +371,7 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.idx = idx_o; ga.kidx = g.ko; ga.n_out = g.nq;
     ga.nseg = 2;
     ga.seg[0] = GSeg{d_out, D, 0, 0, 1, w->WoT, nullptr, D, 1, D, nullptr, 0, 0};
+    set_o_base(ga.seg[0], w);
     ga.seg[1] = GSeg{dzs_o, rp, 0, 0, 1, AoTp, nullptr, rp, 1, rp, nullptr, 0, 0};
     ga.o0 = da; ga.ldo = g.nq; ga.swidth = g.nq;
     ga.rpart = reinterpret_cast<float*>(ws + g.w_rp);
@@ -396,6 +409,7 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     for (int j = 0; j < 3; ++j) {
       const Comp& c = *cc[j];
       ga.seg[j] = GSeg{dcomp[j], c.ld, c.n, c.out_off, 0, Wm[j], nullptr, D, 1, 0, sets[j], c.kc, c.n};
+      if (qq) { ga.seg[j].Bs = Ws[j]; ga.seg[j].bq4 = 1; }
     }
     ga.seg[3] = GSeg{dzs, 3 * rp, 0, 0, 1, Aqkvp, nullptr, D, 0, 3 * rp, nullptr, 0, 0};
     ga.ksplit_out = g.ks_dx;
@@ -417,20 +431,49 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   return cb.launch<T>(strm);
 }
 
-sl_status check_weights(const sl_qkvo_weights* w, bool need_qkv, bool need_o) {
+// A 4-bit frozen base (SparseLoRA article §六): bf16 calls, d_model % 64 == 0.
+sl_status check_q4(sl_dtype dt, const sl_qkvo_weights* w) {
+  if (dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "a 4-bit frozen base needs bf16 calls");
+  if (w->d_model % 64 != 0) SL_FAIL(SL_ERR_SHAPE, "a 4-bit frozen base needs d_model %% 64 == 0");
+  return SL_OK;
+}
+
+sl_status check_weights(sl_dtype dt, const sl_qkvo_weights* w, bool need_qkv, bool need_o) {
+  sl_status s;
   if (need_qkv) {
-    if (!w->Wq || !w->Wk || !w->Wv || !w->Aq || !w->Bq || !w->Ak || !w->Bk || !w->Av || !w->Bv)
+    if (w->Wq_q) {
+      if ((s = check_q4(dt, w)) != SL_OK) return s;
+      if (!w->Wk_q || !w->Wv_q || !w->Wq_s || !w->Wk_s || !w->Wv_s)
+        SL_FAIL(SL_ERR_NULL, "Wq_q is set: Wk_q, Wv_q, Wq_s, Wk_s, Wv_s must be non-NULL");
+      if (!aligned16(w->Wq_q) || !aligned16(w->Wk_q) || !aligned16(w->Wv_q) || !aligned16(w->Wq_s) ||
+          !aligned16(w->Wk_s) || !aligned16(w->Wv_s))
+        SL_FAIL(SL_ERR_ALIGN, "4-bit codes and scales must be 16-byte aligned");
+    } else {
+      if (!w->Wq || !w->Wk || !w->Wv) SL_FAIL(SL_ERR_NULL, "a q/k/v weight pointer is NULL");
+      if (!aligned16(w->Wq) || !aligned16(w->Wk) || !aligned16(w->Wv))
+        SL_FAIL(SL_ERR_ALIGN, "Wq, Wk, Wv, Aq, Ak, Av must be 16-byte aligned");
+    }
+    if (!w->Aq || !w->Bq || !w->Ak || !w->Bk || !w->Av || !w->Bv)
       SL_FAIL(SL_ERR_NULL, "a q/k/v weight pointer is NULL");
-    if (!aligned16(w->Wq) || !aligned16(w->Wk) || !aligned16(w->Wv) || !aligned16(w->Aq) ||
-        !aligned16(w->Ak) || !aligned16(w->Av))
+    if (!aligned16(w->Aq) || !aligned16(w->Ak) || !aligned16(w->Av))
       SL_FAIL(SL_ERR_ALIGN, "Wq, Wk, Wv, Aq, Ak, Av must be 16-byte aligned");
   }
   if (need_o) {
-    if (!w->WoT || !w->Ao || !w->Bo) SL_FAIL(SL_ERR_NULL, "an o weight pointer is NULL");
-    if (!aligned16(w->WoT) || !aligned16(w->Ao)) SL_FAIL(SL_ERR_ALIGN, "WoT, Ao must be 16-byte aligned");
+    if (w->WoT_q) {
+      if ((s = check_q4(dt, w)) != SL_OK) return s;
+      if (!w->WoT_s) SL_FAIL(SL_ERR_NULL, "WoT_q is set: WoT_s must be non-NULL");
+      if (!aligned16(w->WoT_q) || !aligned16(w->WoT_s))
+        SL_FAIL(SL_ERR_ALIGN, "4-bit codes and scales must be 16-byte aligned");
+    } else {
+      if (!w->WoT) SL_FAIL(SL_ERR_NULL, "an o weight pointer is NULL");
+      if (!aligned16(w->WoT)) SL_FAIL(SL_ERR_ALIGN, "WoT, Ao must be 16-byte aligned");
+    }
+    if (!w->Ao || !w->Bo) SL_FAIL(SL_ERR_NULL, "an o weight pointer is NULL");
+    if (!aligned16(w->Ao)) SL_FAIL(SL_ERR_ALIGN, "WoT, Ao must be 16-byte aligned");
   }
   return SL_OK;
 }
+
 
 }  // namespace
 
@@ -457,7 +500,7 @@ sl_status sl_qkvo_fwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* 
   sl_status s = qkvo_geom(dt, lay, w, k_qk, k_vo, true, g);
   if (s != SL_OK) return s;
   if (!X && !a) SL_FAIL(SL_ERR_NULL, "both X and a are NULL: nothing to compute");
-  if ((s = check_weights(w, X != nullptr, a != nullptr)) != SL_OK) return s;
+  if ((s = check_weights(dt, w, X != nullptr, a != nullptr)) != SL_OK) return s;
   if (X && (!q || !k || !v || !idx_qk || !idx_vo))
     SL_FAIL(SL_ERR_NULL, "q, k, v, idx_qk and idx_vo are required with X");
   if (a && (!o || !idx_vo)) SL_FAIL(SL_ERR_NULL, "o and idx_vo are required with a");
@@ -487,7 +530,7 @@ sl_status sl_qkvo_bwd(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* 
   sl_status s = qkvo_geom(dt, lay, w, k_qk, k_vo, true, g);
   if (s != SL_OK) return s;
   if (!dq && !d_out) SL_FAIL(SL_ERR_NULL, "both dq and d_out are NULL: nothing to compute");
-  if ((s = check_weights(w, dq != nullptr, d_out != nullptr)) != SL_OK) return s;
+  if ((s = check_weights(dt, w, dq != nullptr, d_out != nullptr)) != SL_OK) return s;
   if (!gr) SL_FAIL(SL_ERR_NULL, "grads is NULL");
   if (dq && (!dk || !dv || !X || !dX || !idx_qk || !idx_vo || !gr->dAq || !gr->dBq || !gr->dAk ||
              !gr->dBk || !gr->dAv || !gr->dBv))

@@ -128,6 +128,13 @@ typedef struct sl_qkvo_weights {
   float lora_scale;
   const void *Wq, *Wk, *Wv, *WoT;
   const void *Aq, *Bq, *Ak, *Bk, *Av, *Bv, *Ao, *Bo;
+  /* Optional 4-bit frozen bases, in the format of sl_ffn_weights (uint8 codes
+   * [rows, d_model / 2], fp32 scales [rows, d_model / 64]).  Wq_q set: q, k and
+   * v read Wq_q/Wk_q/Wv_q with Wq_s/Wk_s/Wv_s, and Wq, Wk, Wv are ignored.
+   * WoT_q set: o reads WoT_q with WoT_s, and WoT is ignored.  bf16 calls
+   * only; d_model a multiple of 64; 16-byte aligned.  NULL: plain weights. */
+  const void *Wq_q, *Wk_q, *Wv_q, *WoT_q;
+  const float *Wq_s, *Wk_s, *Wv_s, *WoT_s;
 } sl_qkvo_weights;
 
 typedef struct sl_qkvo_grads {   /* fp32, shapes of the factors; OVERWRITTEN */

@@ -124,3 +124,65 @@ def test_gpu_quantizer_matches_oracle_bit_exactly(dt):
     assert np.array_equal(codes.cpu().numpy(), codes_r)
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), scales_r.view(np.uint32))
     assert O.int4_codes(codes_r)[5, :3].tolist() == [7, 2, -4]
+
+
+def _qkvo_q4(D, heads, r, ctx, L, seed):
+    """The q/k/v/o case of tests/test_gpu_qkvo.py with its frozen weights
+    quantized: device codes and scales, the oracle on the dequantized weights."""
+    from tests.test_gpu_qkvo import _case as qkvo_case
+    p = qkvo_case(D, heads, r, ctx, L, "bf16", seed)
+    q = {}
+    for n in ("Wq", "Wk", "Wv"):
+        q[n + "_q"], q[n + "_s"] = O.quantize_int4_rows(p[n])
+        p[n] = O.dequantize_int4_rows(q[n + "_q"], q[n + "_s"])
+    q["WoT_q"], q["WoT_s"] = O.quantize_int4_rows(np.ascontiguousarray(p["Wo"].T))
+    p["Wo"] = np.ascontiguousarray(O.dequantize_int4_rows(q["WoT_q"], q["WoT_s"]).T)
+    return p, q
+
+
+def _qkvo_compare(p, q, heads, ctx, L, idx_qk, idx_vo, s=1.0):
+    import contextual_sparsity_lora_svd_amd as sl
+    t = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda() for n, v in q.items()}
+    for n in ("Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo"):
+        t[n] = to_dev(p[n], "bf16")
+    w = sl.QKVOWeights(t, heads, lora_scale=s)
+    lay = sl.Layout(ctx, L)
+    X, a = to_dev(p["X"], "bf16"), to_dev(p["a"], "bf16")
+    kqk, kvo = idx_qk.shape[1], idx_vo.shape[1]
+    iqk = torch.from_numpy(np.ascontiguousarray(idx_qk, np.int32)).cuda()
+    ivo = torch.from_numpy(np.ascontiguousarray(idx_vo, np.int32)).cuda()
+    outs, buf = sl.qkvo_fwd(w, X, a, lay, kqk, iqk, kvo, ivo)
+    g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, dq=to_dev(p["dq"], "bf16"),
+                    dk=to_dev(p["dk"], "bf16"), dv=to_dev(p["dv"], "bf16"), d_out=to_dev(p["d_out"], "bf16"))
+    torch.cuda.synchronize()
+    ref, cache = O.qkvo_forward(p, ctx, L, list(idx_qk), list(idx_vo), heads, s)
+    gr = O.qkvo_backward(p, cache, {n: p[n] for n in ("dq", "dk", "dv", "d_out")}, s)
+    errs = {}
+    for n in ("q", "k", "v", "o"):
+        errs[n] = assert_close(to_np(outs[n]), ref[n], "bf16", n)
+    assert np.all(to_np(outs["q"])[cache["mq"] == 0] == 0)
+    for n in ("dX", "da", "dAq", "dBq", "dAk", "dBk", "dAv", "dBv", "dAo", "dBo"):
+        errs[n] = assert_close(to_np(g[n]), gr[n], "bf16", n)
+    print(f"\n[q4] heads={heads} ctx={list(ctx)} kqk={kqk} kvo={kvo} " +
+          " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("heads", [(4, 4, 16), (8, 2, 16)])
+def test_qlora_qkvo_ragged(heads):
+    D, r, L = 128, 8, 60
+    ctx = [40, 60, 0]
+    p, q = _qkvo_q4(D, heads, r, ctx, L, seed=41)
+    nkv = heads[1] * heads[2]
+    rng = np.random.default_rng(42)
+    _qkvo_compare(p, q, heads, ctx, L, _sets(rng, 3, nkv, nkv * 5 // 16), _sets(rng, 3, nkv, nkv * 9 // 16 + 1),
+                  s=0.5)
+
+
+def test_qlora_qkvo_multi_tile():
+    heads = (16, 4, 64)
+    D, r, L = 512, 16, 300
+    ctx = [260, 300, 150]
+    p, q = _qkvo_q4(D, heads, r, ctx, L, seed=43)
+    nkv = heads[1] * heads[2]
+    rng = np.random.default_rng(44)
+    _qkvo_compare(p, q, heads, ctx, L, _sets(rng, 3, nkv, 130), _sets(rng, 3, nkv, 190))

@@ -218,12 +218,16 @@ def qlora_bench(args, torch, sl, cfg=2):
     weight_bytes = sum(t[n].numel() * t[n].element_size() for n in ("Wg_q", "Wu_q", "WdT_q", "Wg_s", "Wu_s", "WdT_s"))
     print(f"[bench] 4-bit base FFN step {ms:.3f} ms" + (f", dense {dense_ms:.3f} ms" if dense_ms else ""),
           file=sys.stderr, flush=True)
+    del t, w, buf, bufd, est, X, dY, Y, grads
+    torch.cuda.empty_cache()
+    attn = None if args.no_attn else attn_bench(args, torch, sl, quant=True)
     return {"workload": wl.name, "base": "int4, one fp32 scale per 64-element row block",
             "frozen_weight_bytes": weight_bytes, "bf16_weight_bytes": 3 * F * D * 2,
             "batch": B, "seq_len": L, "ctx_len": ctx, "sparsity_pct": f.sparsity_pct, "k": k,
             "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
             "effective_tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_gflop": fl / 1e9,
-            "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
+            "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
+            "attention": attn}
 
 
 def sl_dequant(torch, codes, scales):
@@ -236,9 +240,10 @@ def sl_dequant(torch, codes, scales):
     return q * scales.repeat_interleave(64, dim=1)
 
 
-def attn_bench(args, torch, sl, cfg=3):
+def attn_bench(args, torch, sl, cfg=3, quant=False):
     """q/k/v/o rows of the path on a LLaMA2-7B attention workload: QK-norm and
-    L2 selection over context tokens, sparse q/k/v/o forward and backward."""
+    L2 selection over context tokens, sparse q/k/v/o forward and backward
+    (quant: over 4-bit frozen bases quantized on the GPU)."""
     wl = W.WORKLOADS[cfg]
     s = wl.attn[0]
     heads = (s.n_q_heads, s.n_kv_heads, s.head_dim)
@@ -258,9 +263,18 @@ def attn_bench(args, torch, sl, cfg=3):
     X, a = to_dev(p["X"], torch, bf), to_dev(p["a"], torch, bf)
     dq, dk, dv, dout = (to_dev(p[n], torch, bf) for n in ("dq", "dk", "dv", "d_out"))
     del p
-    w = sl.QKVOWeights(t, heads)
+    if quant:
+        for n in ("Wq", "Wk", "Wv", "WoT"):
+            t[n + "_q"], t[n + "_s"] = sl.quantize_q4(t[n])
+            # the estimator factors of the base the layer computes with
+            t[n] = sl_dequant(torch, t[n + "_q"], t[n + "_s"]).to(bf)
     lay = sl.Layout(ctx, L)
     f = {n: sl.build_estimator(t[n], r_e) for n in ("Wq", "Wk", "Wv")}
+    if quant:
+        for n in ("Wq", "Wk", "Wv", "WoT"):
+            del t[n]
+        torch.cuda.empty_cache()
+    w = sl.QKVOWeights(t, heads)
     torch.cuda.synchronize()
     est_qk = sl.EstimateBuffers(sl.SL_CRIT_QK_NORM, lay, D, r_e, nkv, kqk, X.device, heads=heads)
     est_vo = sl.EstimateBuffers(sl.SL_CRIT_L2, lay, D, r_e, nkv, kvo, X.device)

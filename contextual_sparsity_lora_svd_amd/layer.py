@@ -112,17 +112,31 @@ class _FFNStep(torch.autograd.Function):
                 None, None, None, None)
 
 
+def _quantized_base(frozen, base_bits: int, dtype):
+    """The frozen weights as given (16) or as 4-bit codes and block scales (4)."""
+    if base_bits == 16:
+        return frozen
+    if base_bits != 4 or dtype != torch.bfloat16:
+        raise sl.SparseLoraError("base_bits must be 16, or 4 with bf16 weights")
+    out = {}
+    for n, w in frozen.items():
+        out[n + "_q"], out[n + "_s"] = sl.quantize_q4(w)
+    return out
+
+
 class SparseLoRAFFN(torch.nn.Module):
     """One SwiGLU FFN with LoRA on gate, up and down and contextual channel
     sparsity.  Frozen weights (``Wg, Wu [d_ff, d_model]``, ``Wd [d_model, d_ff]``)
     are held in the compute dtype, the LoRA factors as fp32 parameters (cast
     to the compute dtype for each call; their gradients arrive in fp32).  The
-    rank-``est_rank`` estimator of gate and up is built once, at construction."""
+    rank-``est_rank`` estimator of gate and up is built once, at construction.
+    ``base_bits=4`` keeps the frozen weights as 4-bit codes and block scales
+    (bf16 only; the estimator is built from the weights before quantization)."""
 
     def __init__(self, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, lora_rank: int,
                  est_rank: int = 8, lora_scale: float = 1.0, layer: int = 0,
                  schedule: Optional[SparsitySchedule] = None, init_std: float = 0.02,
-                 generator: Optional[torch.Generator] = None):
+                 generator: Optional[torch.Generator] = None, base_bits: int = 16):
         super().__init__()
         dev, dt = Wg.device, Wg.dtype
         d_ff, d_model = Wg.shape
@@ -138,6 +152,7 @@ class SparseLoRAFFN(torch.nn.Module):
         self.Ad, self.Bd = p(lora_rank, d_ff), p(d_model, lora_rank)
         self.est = (sl.build_estimator(self.frozen["Wg"], est_rank)[:2],
                     sl.build_estimator(self.frozen["Wu"], est_rank)[:2])
+        self.frozen = _quantized_base(self.frozen, base_bits, dt)
         self.last_k, self.last_idx = None, None
 
     def channel_sets(self, X: torch.Tensor, layout: sl.Layout, k: int) -> torch.Tensor:
@@ -213,11 +228,12 @@ class SparseLoRAQKVO(torch.nn.Module):
     with ``attention(q, k, v) -> a`` on token-major ``[T, H * head_dim]``
     tensors (differentiable with torch autograd).  Frozen weights ``Wq [Hq hd, D]``,
     ``Wk, Wv [Hkv hd, D]``, ``Wo [D, Hq hd]`` in the compute dtype; LoRA
-    factors fp32 parameters."""
+    factors fp32 parameters.  ``base_bits=4``: the frozen weights as 4-bit
+    codes and block scales (as in SparseLoRAFFN)."""
 
     def __init__(self, Wq, Wk, Wv, Wo, heads: Sequence[int], lora_rank: int, est_rank: int = 8,
                  lora_scale: float = 1.0, layer: int = 0, schedule: Optional[SparsitySchedule] = None,
-                 init_std: float = 0.02, generator: Optional[torch.Generator] = None):
+                 init_std: float = 0.02, generator: Optional[torch.Generator] = None, base_bits: int = 16):
         super().__init__()
         dev, dt = Wq.device, Wq.dtype
         self.heads = tuple(int(h) for h in heads)
@@ -236,6 +252,7 @@ class SparseLoRAQKVO(torch.nn.Module):
         self.Av, self.Bv = p(lora_rank, D), p(self.nkv, lora_rank)
         self.Ao, self.Bo = p(lora_rank, self.nq), p(D, lora_rank)
         self.est = {n: sl.build_estimator(self.frozen[n], est_rank)[:2] for n in ("Wq", "Wk", "Wv")}
+        self.frozen = _quantized_base(self.frozen, base_bits, Wq.dtype)
         self.last_k, self.last_idx = None, None
 
     def channel_sets(self, X, layout, k_qk, k_vo):

@@ -113,3 +113,39 @@ def test_qkvo_module_with_caller_attention(step):
     assert_close(to_np(Xd.grad), gr["dX"], "bf16", "dX")
     for n in ("Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo"):
         assert_close(to_np(getattr(mod, n).grad), gr["d" + n], "bf16", "d" + n)
+
+
+def _deq(mod, n):
+    return O.dequantize_int4_rows(mod.frozen[n + "_q"].cpu().numpy(), mod.frozen[n + "_s"].cpu().numpy())
+
+
+def test_ffn_module_over_4bit_base():
+    """A sparse step of the FFN module holding its frozen weights as 4-bit
+    codes; the oracle runs on the dequantized weights."""
+    import contextual_sparsity_lora_svd_amd as sl
+    D, F, r, L = 128, 344, 8, 64
+    ctx = [48, 40]
+    T = len(ctx) * L
+    rng = np.random.default_rng(23)
+    Wg, Wu, Wd = (_bf(rng.standard_normal(s) * 0.05) for s in ((F, D), (F, D), (D, F)))
+    X = W.make_activations(11, T, D, 16, "bf16")
+    dY = _bf(rng.standard_normal((T, D)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    mod = sl.SparseLoRAFFN(dev(Wg), dev(Wu), dev(Wd), r, est_rank=8, lora_scale=0.5,
+                           generator=torch.Generator().manual_seed(5), base_bits=4)
+    assert set(mod.frozen) == {"Wg_q", "Wg_s", "Wu_q", "Wu_s", "WdT_q", "WdT_s"}
+    lay = sl.Layout(ctx, L)
+    Xd = dev(X).requires_grad_(True)
+    k = sl.k_from_ratio(F, 60)
+    Y = mod(Xd, lay, k=k)
+    Y.backward(dev(dY))
+    torch.cuda.synchronize()
+    idx = mod.last_idx.cpu().numpy()
+    p = {"X": X, "Wg": _deq(mod, "Wg"), "Wu": _deq(mod, "Wu"), "Wd": _deq(mod, "WdT").T, "dY": dY}
+    p.update(_np_params(mod, ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")))
+    yr, cache = O.ffn_forward(p, ctx, L, list(idx), 0.5)
+    gr = O.ffn_backward(p, cache, dY, 0.5)
+    assert_close(to_np(Y), yr, "bf16", "Y")
+    assert_close(to_np(Xd.grad), gr["dX"], "bf16", "dX")
+    for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd"):
+        assert_close(to_np(getattr(mod, n).grad), gr["d" + n], "bf16", "d" + n)

@@ -40,3 +40,15 @@ def test_schedule_rejects_bad_input():
         SparsitySchedule([LayerRatios()], 0)
     with pytest.raises(ValueError):
         SparsitySchedule.from_ranges(4, 10, ffn=[(2, 5, 50)])
+
+
+def test_quantized_base_option_is_validated_on_the_host():
+    import torch
+    import contextual_sparsity_lora_svd_amd as sl
+    from contextual_sparsity_lora_svd_amd.layer import _quantized_base
+    frozen = {"Wg": torch.zeros(4, 64)}
+    assert _quantized_base(frozen, 16, torch.float32) is frozen
+    with pytest.raises(sl.SparseLoraError):
+        _quantized_base(frozen, 8, torch.bfloat16)
+    with pytest.raises(sl.SparseLoraError):
+        _quantized_base(frozen, 4, torch.float32)

@@ -11,7 +11,7 @@ using namespace sl;
 namespace {
 
 struct EstGeom {
-  int rep, ldz, nchunk_max, N0, nproj;
+  int rep, ldz, nchunk_max, chunk, N0, nproj;
   size_t w_zh, w_p0, w_p1, w_skp, total;
 };
 
@@ -38,7 +38,9 @@ sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, l
   }
   int maxctx = 0;
   for (int b = 0; b < st.nseq; ++b) maxctx = st.ctx[b] > maxctx ? st.ctx[b] : maxctx;
-  g.nchunk_max = ceil_div(maxctx, SC_CHUNK);
+  // SwiGLU partials per SW_CHUNK tokens; the L2 forms (Gram) one per sequence
+  g.chunk = crit == SL_CRIT_SWIGLU_L2 ? SW_CHUNK : (1 << 30);
+  g.nchunk_max = crit == SL_CRIT_SWIGLU_L2 ? ceil_div(maxctx, SW_CHUNK) : 1;
   if (g.nchunk_max < 1) g.nchunk_max = 1;
   const long long T = (long long)st.nseq * st.L;
   Bump bp;
@@ -51,17 +53,22 @@ sl_status est_geom(sl_criterion crit, const SeqTab& st, const sl_heads* heads, l
 }
 
 template <typename T>
-sl_status launch_score(const ScoreArgs& a, int nseq, int rank, hipStream_t s) {
-  const dim3 grid(ceil_div(a.N, SC_THREADS), a.nchunk_max, nseq), block(SC_THREADS);
-  if (a.swiglu) {
-    if (rank <= 8) hipLaunchKernelGGL((score_kernel<T, 8, true>), grid, block, 0, s, a);
-    else if (rank <= 16) hipLaunchKernelGGL((score_kernel<T, 16, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((score_kernel<T, 32, true>), grid, block, 0, s, a);
-  } else {
-    if (rank <= 8) hipLaunchKernelGGL((score_kernel<T, 8, false>), grid, block, 0, s, a);
-    else if (rank <= 16) hipLaunchKernelGGL((score_kernel<T, 16, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((score_kernel<T, 32, false>), grid, block, 0, s, a);
-  }
+sl_status launch_swiglu(const SwiArgs& a, int nseq, int rank, hipStream_t s) {
+  const dim3 grid(ceil_div(a.N, 128), a.nchunk_max, nseq), block(SW_THREADS);
+  if (rank <= 8) hipLaunchKernelGGL((score_swiglu_kernel<T, 8>), grid, block, 0, s, a);
+  else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_kernel<T, 16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((score_swiglu_kernel<T, 32>), grid, block, 0, s, a);
+  SL_HIP(hipGetLastError());
+  return SL_OK;
+}
+
+template <typename T>
+sl_status launch_gram(const GramArgs& a, int nproj, int nseq, int rank, hipStream_t s) {
+  const int nmax = nproj > 1 && a.N[1] > a.N[0] ? a.N[1] : a.N[0];
+  const dim3 grid(ceil_div(nmax, GR_THREADS), nseq, nproj), block(GR_THREADS);
+  if (rank <= 8) hipLaunchKernelGGL((score_gram_kernel<T, 8>), grid, block, 0, s, a);
+  else if (rank <= 16) hipLaunchKernelGGL((score_gram_kernel<T, 16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((score_gram_kernel<T, 32>), grid, block, 0, s, a);
   SL_HIP(hipGetLastError());
   return SL_OK;
 }
@@ -107,24 +114,23 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
     sa.part = reinterpret_cast<float*>(ws + g.w_skp);
     sl_status s = launch_skinny<T>(sa, stream);
     if (s != SL_OK) return s;
-    // stage 2 + criterion, per 64-token chunk
-    ScoreArgs sc;
-    std::memset(&sc, 0, sizeof(sc));
-    sc.st = st;
-    sc.Zh = zh; sc.ldz = g.ldz;
-    sc.rank = rank;
-    sc.nchunk_max = g.nchunk_max;
+    // stage 2 + criterion
     if (crit == SL_CRIT_SWIGLU_L2) {
-      sc.swiglu = 1; sc.zc0 = 0; sc.zc1 = g.rep; sc.Q0 = Q0; sc.Q1 = Q1; sc.N = (int)N; sc.part = p0;
-      if ((s = launch_score<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
-    } else if (crit == SL_CRIT_L2) {
-      sc.swiglu = 0; sc.zc0 = 0; sc.Q0 = Q0; sc.N = (int)N; sc.part = p0;
-      if ((s = launch_score<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
+      SwiArgs sc;
+      std::memset(&sc, 0, sizeof(sc));
+      sc.st = st;
+      sc.Zh = zh; sc.ldz = g.ldz; sc.zc0 = 0; sc.zc1 = g.rep;
+      sc.Q0 = Q0; sc.Q1 = Q1; sc.rank = rank; sc.N = (int)N;
+      sc.part = p0; sc.nchunk_max = g.nchunk_max;
+      if ((s = launch_swiglu<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
     } else {
-      sc.swiglu = 0; sc.zc0 = 0; sc.Q0 = Q0; sc.N = g.N0; sc.part = p0;
-      if ((s = launch_score<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
-      sc.zc0 = g.rep; sc.Q0 = Q1; sc.N = (int)N; sc.part = p1;
-      if ((s = launch_score<T>(sc, st.nseq, rank, stream)) != SL_OK) return s;
+      GramArgs ga;
+      std::memset(&ga, 0, sizeof(ga));
+      ga.st = st;
+      ga.Zh = zh; ga.ldz = g.ldz; ga.rank = rank;
+      ga.zc[0] = 0; ga.Q[0] = Q0; ga.N[0] = g.N0; ga.part[0] = p0;
+      if (crit == SL_CRIT_QK_NORM) { ga.zc[1] = g.rep; ga.Q[1] = Q1; ga.N[1] = (int)N; ga.part[1] = p1; }
+      if ((s = launch_gram<T>(ga, crit == SL_CRIT_QK_NORM ? 2 : 1, st.nseq, rank, stream)) != SL_OK) return s;
     }
   }
   timer_end(TS_ESTIMATE, stream);
@@ -134,6 +140,7 @@ sl_status estimate_select_impl(sl_criterion crit, const SeqTab& st, const sl_hea
   se.qk = crit == SL_CRIT_QK_NORM;
   se.part0 = p0; se.part1 = p1;
   se.nchunk_max = g.nchunk_max;
+  se.chunk = g.chunk;
   se.N = (int)N; se.N0 = g.N0;
   if (se.qk) { se.group = heads->n_q_heads / heads->n_kv_heads; se.head_dim = heads->head_dim; }
   se.k = k; se.idx = idx; se.scores = scores;

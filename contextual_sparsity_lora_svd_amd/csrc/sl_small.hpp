@@ -12,6 +12,7 @@ namespace sl {
 
 typedef __bf16 bf16x8_t_s __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_s __attribute__((ext_vector_type(16)));
 
 // ===========================================================================
 // Skinny product  out[row, c] = sum_k A[row, k] * Bm(c, k),  c < C <= 64
@@ -327,77 +328,205 @@ __global__ void skinny_finish_kernel(const SkinnyArgs a) {
 
 // ===========================================================================
 // Channel criterion over context tokens (SparseLoRA article §一, §二).
-// part[b][chunk][n] = sum over the chunk's context rows t of
-//   SWIGLU: (g/(1+exp(-g)) * u)^2, g = Zh[t, zc0:] . Q0[:, n], u = Zh[t, zc1:] . Q1[:, n]
-//   L2:     (Zh[t, zc0:] . Q0[:, n])^2
-// Chunks of 64 tokens; the select kernel adds the chunks in order.
+// The estimate of channel n at context token t is z_t . Q[:, n], where z_t is
+// the token's projection onto the estimator's leading directions (rank r).
+// Each kernel writes per-sequence partial sums part[b][chunk][n] over chunks of
+// context tokens; the select kernel adds a sequence's chunks in chunk order.
 // ===========================================================================
-constexpr int SC_CHUNK = 64;
-constexpr int SC_THREADS = 256;
 
-struct ScoreArgs {
+// L2 criterion, sum over context rows t of (z_t . q_n)^2.  The identity
+//   sum_t (z_t . q_n)^2 = q_n^T G q_n,   G = sum_t z_t z_t^T  (r x r),
+// turns the token loop into one Gram matrix per sequence and a quadratic form
+// per channel.  G and the form are taken in fp64: every product in G is exact
+// (fp32 times fp32), so the fp32 result is at least as accurate as a direct
+// fp32 sum of squares.  One partial per sequence.  One launch covers up to two
+// projections (the QK-norm criterion's q and k): grid (channel blocks, nseq,
+// projections); every workgroup rebuilds its sequence's G and scores
+// GR_THREADS channels.
+//
+// G = Z^T Z runs on the fp64 matrix cores (16x16x4, K = 4 tokens per step):
+// lane l supplies z[t][c], t = 4 g + l / 16, c = 16 blk + l % 16, to both the
+// A (= Z^T) and the B (= Z) operand.  Wave w takes token groups w, w + 4, ...,
+// loading GR_BATCH groups ahead of the matrix cores; the four waves' partial
+// tiles are added in LDS in wave order.
+constexpr int GR_THREADS = 256;
+constexpr int GR_BATCH = 16;
+typedef double f64x4_s __attribute__((ext_vector_type(4)));
+
+struct GramArgs {
   SeqTab st;
-  int swiglu;
+  const float* Zh; long long ldz;
+  int rank;
+  int zc[2]; const void* Q[2]; int N[2]; float* part[2];
+};
+
+template <typename T, int RM>
+__global__ void __launch_bounds__(GR_THREADS)
+score_gram_kernel(const GramArgs a) {
+  constexpr int NB = RM <= 16 ? 1 : 2;        // 16-wide blocks per side of G
+  constexpr int NW = GR_THREADS / 64;
+  __shared__ double gs[NW][NB * NB][256];
+  __shared__ double G[RM * RM];
+  const int p = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N[p];
+  const int n = blockIdx.x * GR_THREADS + tid;
+  if ((int)blockIdx.x * GR_THREADS >= N) return;   // uniform
+  const int ctx = a.st.ctx[b];
+  if (ctx == 0) return;                            // no partial: the select reads none
+  const T* Q = reinterpret_cast<const T*>(a.Q[p]);
+  float qv[RM];
+#pragma unroll
+  for (int q = 0; q < RM; ++q) qv[q] = (n < N && q < a.rank) ? ldv<T>(Q, (long long)q * N + n) : 0.f;
+
+  const float* zb = a.Zh + (long long)b * a.st.L * a.ldz + a.zc[p];
+  const int ngrp = (ctx + 3) / 4;
+  const int tl = lane >> 4, cl = lane & 15;
+  auto load = [&](int g0, float (&z)[GR_BATCH][NB]) {
+#pragma unroll
+    for (int i = 0; i < GR_BATCH; ++i) {
+      const int t = 4 * (g0 + NW * i) + tl;
+#pragma unroll
+      for (int bk = 0; bk < NB; ++bk) {
+        const int c = 16 * bk + cl;
+        z[i][bk] = (t < ctx && c < a.rank) ? zb[(long long)t * a.ldz + c] : 0.f;
+      }
+    }
+  };
+  f64x4_s acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f64x4_s{0.0, 0.0, 0.0, 0.0};
+  float zcur[GR_BATCH][NB], zn[GR_BATCH][NB];
+  load(wave, zcur);
+  for (int g0 = wave; g0 < ngrp; g0 += NW * GR_BATCH) {
+    if (g0 + NW * GR_BATCH < ngrp) load(g0 + NW * GR_BATCH, zn);
+#pragma unroll
+    for (int i = 0; i < GR_BATCH; ++i)
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)zcur[i][bi], (double)zcur[i][bj], acc[bi][bj],
+                                                             0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < GR_BATCH; ++i)
+#pragma unroll
+      for (int bk = 0; bk < NB; ++bk) zcur[i][bk] = zn[i][bk];
+  }
+  // element r of a lane's 16x16 fp64 tile: row lane / 16 + 4 r, column lane % 16
+  // (rows strided by 4, unlike the fp32 16x16 tiles)
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gs[wave][bi * NB + bj][(tl + 4 * r) * 16 + cl] = acc[bi][bj][r];
+  __syncthreads();
+  for (int e = tid; e < RM * RM; e += GR_THREADS) {
+    const int r = e / RM, c = e % RM;
+    const int blk = (r / 16) * NB + c / 16, off = (r % 16) * 16 + c % 16;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += gs[w][blk][off];
+    G[e] = v;
+  }
+  __syncthreads();
+  if (n >= N) return;
+  double sc = 0.0;
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    double row = 0.0;
+#pragma unroll
+    for (int c = 0; c < RM; ++c) row = fma(G[r * RM + c], (double)qv[c], row);
+    sc = fma((double)qv[r], row, sc);
+  }
+  a.part[p][(long long)b * N + n] = (float)sc;
+}
+
+// SwiGLU criterion, sum over context rows t of (SiLU(g) u)^2 with
+// g = z_t . Qg[:, n] and u = z'_t . Qu[:, n].  The rank-r products run on the
+// fp32 matrix cores (32x32x2): per wave a tile of 32 tokens x 32 channels, A =
+// the tokens' projections (from LDS), B = the wave's 32 columns of Qg and Qu
+// (registers).  The k order is permuted (lane half h takes k = h r/2 + s at
+// step s, on both operands) so each lane reads contiguous LDS and factor rows;
+// the sum over k does not depend on it.  Every accumulator element of a lane
+// belongs to its column (lane % 32), so SiLU, the square and the sum over
+// tokens stay in the lane; the two lane halves are added at the end.  Rows past
+// the context are zero in LDS and contribute (SiLU(0) 0)^2 = 0.
+// Workgroup: 4 waves = 128 channels over a chunk of SW_CHUNK tokens.
+constexpr int SW_CHUNK = 128;
+constexpr int SW_THREADS = 256;
+
+struct SwiArgs {
+  SeqTab st;
   const float* Zh; long long ldz; int zc0, zc1;
   const void* Q0; const void* Q1; int rank; int N;
   float* part; int nchunk_max;
 };
 
-template <typename T, int RM, bool SW>
-__global__ void __launch_bounds__(SC_THREADS)
-score_kernel(const ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) float zs[SC_CHUNK][2 * RM];
+template <typename T, int RM>
+__global__ void __launch_bounds__(SW_THREADS)
+score_swiglu_kernel(const SwiArgs a) {
+  constexpr int LDZ = 2 * RM + 4;        // padded LDS row: g part, u part
+  constexpr int KH = RM / 2;             // k steps per projection
+  __shared__ __attribute__((aligned(16))) float zs[SW_CHUNK * LDZ];
   const int b = blockIdx.z, chunk = blockIdx.y;
   const int ctx = a.st.ctx[b];
-  const int t0 = chunk * SC_CHUNK;
+  const int t0 = chunk * SW_CHUNK;
   if (t0 >= ctx) return;
-  const int nt = min(SC_CHUNK, ctx - t0);
-  const int n = blockIdx.x * SC_THREADS + threadIdx.x;
-  const int nproj = SW ? 2 : 1;
-  for (int i = threadIdx.x; i < SC_CHUNK * 2 * RM; i += SC_THREADS) {
+  const int nt = min(SW_CHUNK, ctx - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n = blockIdx.x * 128 + wave * 32 + (lane & 31);
+  // B operands first (latency overlaps the Z staging)
+  float bg[KH], bu[KH];
+  const T* Q0 = reinterpret_cast<const T*>(a.Q0);
+  const T* Q1 = reinterpret_cast<const T*>(a.Q1);
+#pragma unroll
+  for (int s = 0; s < KH; ++s) {
+    const int k = h * KH + s;
+    const bool ok = n < a.N && k < a.rank;
+    bg[s] = ok ? ldv<T>(Q0, (long long)k * a.N + n) : 0.f;
+    bu[s] = ok ? ldv<T>(Q1, (long long)k * a.N + n) : 0.f;
+  }
+  const float* zb = a.Zh + (long long)(b * a.st.L + t0) * a.ldz;
+  for (int i = tid; i < SW_CHUNK * 2 * RM; i += SW_THREADS) {
     const int t = i / (2 * RM), c = i % (2 * RM);
-    const int p = c / RM, q = c % RM;
-    float v = 0.f;
-    if (t < nt && q < a.rank && p < nproj)
-      v = a.Zh[(long long)(b * a.st.L + t0 + t) * a.ldz + (p ? a.zc1 : a.zc0) + q];
-    zs[t][c] = v;
+    const int pj = c / RM, q = c % RM;
+    zs[t * LDZ + c] = (t < nt && q < a.rank) ? zb[(long long)t * a.ldz + (pj ? a.zc1 : a.zc0) + q] : 0.f;
   }
   __syncthreads();
-  if (n >= a.N) return;
-  float q0[RM], q1[RM];
+  const int ntile = (nt + 31) / 32;
+  float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-  for (int q = 0; q < RM; ++q) {
-    q0[q] = q < a.rank ? ldv<T>(reinterpret_cast<const T*>(a.Q0), (long long)q * a.N + n) : 0.f;
-    q1[q] = (SW && q < a.rank) ? ldv<T>(reinterpret_cast<const T*>(a.Q1), (long long)q * a.N + n) : 0.f;
-  }
-  // four tokens per step with their own accumulators (independent work to
-  // hide LDS and transcendental latency), added in a fixed order at the end;
-  // SiLU uses the hardware exp and reciprocal (relative error ~1e-6)
-  constexpr int TU = 4;
-  float acc[TU] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < nt; t += TU) {
+  for (int tt = 0; tt < SW_CHUNK / 32; ++tt) {
+    if (tt >= ntile) break;   // uniform
+    const float* zr = &zs[(tt * 32 + (lane & 31)) * LDZ + h * KH];
+    float ag[KH], au[KH];
 #pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      const int tt = t + u < nt ? t + u : t;   // rows past nt are zero in zs
-      float gv = 0.f, uv = 0.f;
+    for (int s = 0; s < KH; s += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(zr + s);
+      const float4 y = *reinterpret_cast<const float4*>(zr + RM + s);
+      ag[s] = x.x; ag[s + 1] = x.y; ag[s + 2] = x.z; ag[s + 3] = x.w;
+      au[s] = y.x; au[s + 1] = y.y; au[s + 2] = y.z; au[s + 3] = y.w;
+    }
+    f32x16_s g = {}, u = {};
 #pragma unroll
-      for (int q = 0; q < RM; q += 4) {
-        const float4 z0 = *reinterpret_cast<const float4*>(&zs[tt][q]);
-        gv = fmaf(z0.x, q0[q], gv); gv = fmaf(z0.y, q0[q + 1], gv);
-        gv = fmaf(z0.z, q0[q + 2], gv); gv = fmaf(z0.w, q0[q + 3], gv);
-        if constexpr (SW) {
-          const float4 z1 = *reinterpret_cast<const float4*>(&zs[tt][RM + q]);
-          uv = fmaf(z1.x, q1[q], uv); uv = fmaf(z1.y, q1[q + 1], uv);
-          uv = fmaf(z1.z, q1[q + 2], uv); uv = fmaf(z1.w, q1[q + 3], uv);
-        }
-      }
-      float h;
-      if constexpr (SW) h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-      else h = gv;
-      acc[u] = t + u < nt ? fmaf(h, h, acc[u]) : acc[u];
+    for (int s = 0; s < KH; ++s) {
+      g = __builtin_amdgcn_mfma_f32_32x32x2f32(ag[s], bg[s], g, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_32x32x2f32(au[s], bu[s], u, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float h0 = g[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e])) * u[e];
+      const float h1 = g[e + 1] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e + 1])) * u[e + 1];
+      acc0 = fmaf(h0, h0, acc0);
+      acc1 = fmaf(h1, h1, acc1);
     }
   }
-  a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  float v = acc0 + acc1;
+  v += __shfl_xor(v, 32, 64);
+  if (h == 0 && n < a.N) a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = v;
 }
 
 // ===========================================================================
@@ -415,6 +544,7 @@ struct SelectArgs {
   int qk;                 // 0: score = sum of part0 chunks; 1: QK combination
   const float* part0; const float* part1;
   int nchunk_max;
+  int chunk;              // context tokens per partial (a sequence has ceil(ctx / chunk))
   int N;                  // channels selected over
   int N0;                 // columns of part0 rows (QK: Hq*hd; else N)
   int group, head_dim;    // QK: query heads per kv head, head size
@@ -460,7 +590,7 @@ select_kernel(const SelectArgs a) {
   __shared__ int s_sel[2];
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ctx = a.st.ctx[b];
-  const int nch = (ctx + SC_CHUNK - 1) / SC_CHUNK;
+  const int nch = (int)(((long long)ctx + a.chunk - 1) / a.chunk);
   const long long pb = (long long)b * a.nchunk_max;
 
   // Scores of SB channels at a time (n0 + j * SEL_THREADS, j < SB): the chunk

@@ -158,6 +158,24 @@ def test_estimate_select_matches_oracle(dt):
     print(f"\n[{dt}] exact sets {n_exact}/{len(ctx)}", flush=True)
 
 
+@pytest.mark.parametrize("rank", [12, 32])
+def test_estimate_select_high_rank(rank):
+    """SwiGLU criterion at estimator ranks past 8 (16- and 32-wide factor
+    tiles on the matrix cores), a ragged channel block and a ragged token chunk."""
+    D, F, r, L = 128, 360, 8, 140
+    ctx = [140, 33]
+    p = _ffn_case(D, F, r, ctx, L, "f32", seed=13, R_in=rank)
+    Pg, Qg = factors(p["Wg"], rank, "f32")
+    Pu, Qu = factors(p["Wu"], rank, "f32")
+    k = 120
+    idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, rank, k, "f32")
+    ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+    for b in range(len(ctx)):
+        e = np.abs(sc[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+        assert e < 1e-4, f"rank {rank} seq {b} score rel err {e:.2e}"
+    check_selection(idx, ref, k)
+
+
 def test_select_ties_and_k_extremes():
     """Planted exact ties in the scores (zero factors) and k = 1, k = N."""
     sl = _api()

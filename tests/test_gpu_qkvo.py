@@ -168,6 +168,38 @@ def test_qk_norm_and_l2_select(dt, heads):
     check_selection(idx2.cpu().numpy(), ref_vo, k)
 
 
+@pytest.mark.parametrize("rank", [12, 32])
+def test_qk_norm_and_l2_select_high_rank(rank):
+    """Estimator ranks past 8: the criterion's Gram matrix as one 16 x 16 tile
+    (rank 12) and as 2 x 2 tiles (rank 32), context lengths off the 4-token
+    step, and an all-output sequence."""
+    sl = _api()
+    heads = (4, 2, 16)
+    D, r, L = 64, 4, 151
+    ctx = [151, 45, 0]
+    p = _case(D, heads, r, ctx, L, "f32", seed=28)
+    Pq, Qq = factors(p["Wq"], rank, "f32")
+    Pk, Qk = factors(p["Wk"], rank, "f32")
+    Pv, Qv = factors(p["Wv"], rank, "f32")
+    nkv = heads[1] * heads[2]
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], "f32")
+    ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    k = nkv // 2
+    idx, sc = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, rank, to_dev(Pq, "f32"), to_dev(Qq, "f32"),
+                                 to_dev(Pk, "f32"), to_dev(Qk, "f32"), nkv, k, heads=heads, want_scores=True)
+    idx2, sc2 = sl.estimate_select(sl.SL_CRIT_L2, X, lay, rank, to_dev(Pv, "f32"), to_dev(Qv, "f32"), None, None,
+                                   nkv, k, want_scores=True)
+    torch.cuda.synchronize()
+    for got, ref in ((sc.cpu().numpy(), ref_qk), (sc2.cpu().numpy(), ref_vo)):
+        for b in range(len(ctx)):
+            e = np.abs(got[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+            assert e < 2e-4, f"rank {rank} seq {b} score rel err {e:.2e}"
+        assert np.all(got[2] == 0.0)
+    check_selection(idx.cpu().numpy(), ref_qk, k)
+    check_selection(idx2.cpu().numpy(), ref_vo, k)
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_full_size_workloads(cfg):
     """LLaMA2-7B q/k/v/o (multi-head) and LLaMA3-8B (grouped-query) at their sizes."""

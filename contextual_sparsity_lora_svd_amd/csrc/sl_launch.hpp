@@ -114,16 +114,7 @@ inline int cr_rm(size_t esz, int R) {
 template <typename T>
 inline sl_status launch_colred(ColredArgs& a, int nchunks_total, int nmax, int RM, hipStream_t s) {
   if (nchunks_total <= 0 || nmax <= 0) return SL_OK;
-  if (sizeof(T) == 2) {
-    const dim3 grid(ceil_div(nmax, CRM_COLS), nchunks_total), block(256);
-    switch (RM) {
-      case 16: hipLaunchKernelGGL((colred_mfma_kernel<16>), grid, block, 0, s, a); break;
-      case 32: hipLaunchKernelGGL((colred_mfma_kernel<32>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((colred_mfma_kernel<64>), grid, block, 0, s, a); break;
-    }
-    SL_HIP(hipGetLastError());
-    return SL_OK;
-  }
+  if (sizeof(T) == 2) SL_FAIL(SL_ERR_DTYPE, "internal: bf16 column reductions run batched");
   const dim3 grid(ceil_div(nmax, 2 * CR_THREADS), nchunks_total), block(CR_THREADS);
   switch (RM) {
     case 8: hipLaunchKernelGGL((colred_kernel<T, 8>), grid, block, 0, s, a); break;

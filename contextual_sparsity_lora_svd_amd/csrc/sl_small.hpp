@@ -819,128 +819,14 @@ colred_kernel(const ColredArgs a) {
   }
 }
 
-// MFMA form of the same reduction for bf16 operands.  A workgroup owns 256
-// columns of P and a chunk of CRM_CHUNK rows, taken as CRM_SLICES slices of 64
-// rows whose global loads are all issued before the first is consumed (the
-// work is latency-bound otherwise): each P slice is transposed into LDS as
-// [column][row] (K-contiguous for the matrix cores), Z is converted to bf16 and
-// stored as [q][row], and 16x16x32 MFMAs accumulate C[column][q].  Each wave
-// owns 64 columns.
+// Geometry of the bf16 (matrix-core) form below: a workgroup owns CRM_COLS
+// columns of P and a chunk of CRM_CHUNK rows, taken as CRM_SLICES slices of
+// CRM_SLICE rows whose global loads are all issued before the first is
+// consumed (the work is latency-bound otherwise).
 constexpr int CRM_SLICE = 64;
 constexpr int CRM_SLICES = 2;
 constexpr int CRM_CHUNK = CRM_SLICE * CRM_SLICES;
 constexpr int CRM_COLS = 256;
-
-template <int RM>
-__global__ void __launch_bounds__(256)
-colred_mfma_kernel(const ColredArgs a) {
-  constexpr int LD = CRM_SLICE + 8;   // padded LDS row (144 bytes)
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[CRM_COLS * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Zs[RM * LD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int g = 0, ch = blockIdx.y;
-  if (a.mode == 1) {
-    while (g + 1 < a.ngroups && a.chunk_start[g + 1] <= (int)blockIdx.y) ++g;
-    g = __builtin_amdgcn_readfirstlane(g);
-    ch = blockIdx.y - a.chunk_start[g];
-  }
-  const bool is_out = a.mode == 1 && g == a.st.nseq;
-  const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
-  const int N = a.mode == 0 ? a.N : (is_out ? a.n_out : a.kidx);
-  const int n0 = blockIdx.x * CRM_COLS;
-  if (n0 >= N) return;
-  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.P);
-  const int ctx_pre_g = (a.mode == 1 && !is_out) ? a.st.ctx_pre[g] : 0;
-  // P slice loader: rows (tid&7)*8 .. +8, columns (tid>>3)*8 .. +8
-  const int pr0 = (tid & 7) * 8;
-  const int pc = (tid >> 3) * 8;
-  const bool c_ok = n0 + pc < N;                     // N is a multiple of 8
-  const int pcol = c_ok ? n0 + pc : 0;
-  f32x4_t acc[4][RM / 16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < RM / 16; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int r_begin = ch * CRM_CHUNK;
-  const int r_end = min(m_rows, r_begin + CRM_CHUNK);
-  // all slices' loads first
-  uint4 pv[CRM_SLICES][8];
-  float zv[CRM_SLICES][RM / 4];
-  const int zt = tid & 63;
-  const int zq0 = (tid >> 6) * (RM / 4);
-#pragma unroll
-  for (int sl = 0; sl < CRM_SLICES; ++sl) {
-    const int r0 = r_begin + sl * CRM_SLICE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = r0 + pr0 + i;
-      if (r >= m_rows) r = m_rows - 1;   // loaded and zeroed below
-      long long prow;
-      if (a.mode == 0) prow = (long long)r * a.ldp;
-      else prow = is_out ? a.p_out_off + (long long)r * a.ldp_out : (long long)(ctx_pre_g + r) * a.ldp;
-      pv[sl][i] = *reinterpret_cast<const uint4*>(P + prow + pcol);
-    }
-    const int r = r0 + zt;
-    const bool ok = r < r_end;
-    const long long tok = ok ? (a.mode == 0 ? r : group_token(a.st, g, r)) : 0;
-#pragma unroll
-    for (int q = 0; q < RM / 4; ++q)
-      zv[sl][q] = (ok && zq0 + q < a.R) ? a.Z[tok * a.ldz + a.zc0 + zq0 + q] : 0.f;
-  }
-#pragma unroll
-  for (int sl = 0; sl < CRM_SLICES; ++sl) {
-    const int r0 = r_begin + sl * CRM_SLICE;
-    if (r0 >= r_end) break;   // uniform
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (!(r0 + pr0 + i < r_end && c_ok)) pv[sl][i] = make_uint4(0, 0, 0, 0);
-    if (sl > 0) __syncthreads();   // previous slice fully consumed
-    // transpose P: 8 rows x 8 columns -> 8 columns x 8 rows
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t w[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p]);
-        const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&pv[sl][2 * p + 1]);
-        const uint32_t lo = (c0[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        const uint32_t hi = (c1[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        w[p] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint4*>(&Ps[(pc + j) * LD + pr0]) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-#pragma unroll
-    for (int q = 0; q < RM / 4; ++q) Zs[(zq0 + q) * LD + zt] = f2bf(zv[sl][q]);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < CRM_SLICE / 32; ++ks) {
-      bf16x8_t_s bfr[RM / 16];
-#pragma unroll
-      for (int j = 0; j < RM / 16; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t_s*>(&Zs[(16 * j + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8_t_s af = *reinterpret_cast<const bf16x8_t_s*>(
-            &Ps[(64 * wave + 16 * i + (lane & 15)) * LD + ks * 32 + 8 * (lane >> 4)]);
-#pragma unroll
-        for (int j = 0; j < RM / 16; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-  // C[column][q]: element e of block (i, j) is column 16 i + 4 (lane>>4) + e, q = 16 j + lane%16
-  float* dst = a.part + (a.mode == 1 ? a.part_off[g] : 0) + (long long)ch * N * RM;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int n = n0 + 64 * wave + 16 * i + 4 * (lane >> 4) + e;
-      if (n >= N) continue;
-#pragma unroll
-      for (int j = 0; j < RM / 16; ++j) dst[(long long)n * RM + 16 * j + (lane & 15)] = acc[i][j][e];
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Batched form for bf16: every column reduction of a backward pass in one
@@ -951,8 +837,12 @@ colred_mfma_kernel(const ColredArgs a) {
 // n_out); q < R, partial rows RM wide (RM a multiple of 16, R <= RM).  Mode-1
 // partials of group g start at part + sum over earlier groups of
 // chunks x columns x RM, the layout the finish kernels read.  Work item =
-// (job, group, chunk of CRM_CHUNK rows, block of CRM_COLS columns); the
-// arithmetic per item is that of colred_mfma_kernel.
+// (job, group, chunk of CRM_CHUNK rows, block of CRM_COLS columns).  Each
+// slice of P is transposed into LDS as [column][row] (K-contiguous for the
+// matrix cores) and Z is converted to bf16 and stored as [q][row]; 16x16x32
+// MFMAs accumulate C[column][q], each wave owning 64 columns.  (Chunks of 4
+// slices, walked with the next slice's loads in flight, measured slower: half
+// the partials, but too few workgroups to hide the latency.)
 // ---------------------------------------------------------------------------
 constexpr int CB_MAXJOBS = 8;
 

@@ -28,7 +28,7 @@ struct FfnGeom {
   size_t esz;
   long long comp, c_out_off;
   int ks_down, ks_dx, RM1, RM2, chunk;
-  long long cr_floats;
+  long long cr_floats, skp_floats;
   size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
       w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp, w_rp,
@@ -111,7 +111,9 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
   g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
-  g.w_skp = w.take((size_t)skinny_part_floats(g.T, D > F ? D : F) * 4);
+  // skinny partial sums: room for the two problems of the dz_g / dz_u launch
+  g.skp_floats = skinny_part_floats(g.T, D > F ? D : F);
+  g.w_skp = w.take((size_t)g.skp_floats * 2 * 4);
   {
     // split last round of the gate/up (dual) and dH gather-GEMMs
     const long long f1 = ng_rpart_floats(st, g.k, F, true, g.esz, {(int)D, 2 * g.rp});
@@ -330,19 +332,25 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
   }
-  // dz_g = s dG Bg[S], dz_u = s dU Bu[S]
-  for (int which = 0; which < 2; ++which) {
+  // dz_g = s dG Bg[S], dz_u = s dU Bu[S]: one launch, two problems
+  {
     SkinnyArgs a;
     std::memset(&a, 0, sizeof(a));
     a.st = st; a.mode = 1; a.T = g.T;
-    a.A = which ? dUc : dGc; a.lda = g.ldk; a.lda_out = g.ldF; a.a_out_off = g.c_out_off;
+    a.A = dGc; a.lda = g.ldk; a.lda_out = g.ldF; a.a_out_off = g.c_out_off;
     a.K = 0; a.kidx = g.k; a.n_out = F;
     a.nblk = 1;
-    a.Bb[0] = which ? Bug : Bgg; a.nbk[0] = r; a.ldbb[0] = g.ldk; a.b0_gstride = (long long)rp * g.ldk;
-    a.B0o = which ? BuTo : BgTo; a.ldb0o = F;
-    a.out = dz_gu; a.ldo = 2 * rp; a.col0 = which * rp; a.oscale = s;
+    a.Bb[0] = Bgg; a.nbk[0] = r; a.ldbb[0] = g.ldk; a.b0_gstride = (long long)rp * g.ldk;
+    a.B0o = BgTo; a.ldb0o = F;
+    a.out = dz_gu; a.ldo = 2 * rp; a.col0 = 0; a.oscale = s;
     a.outs = dzs_gu; a.ldos = 2 * rp; a.scale = s;
     a.part = skp;
+    a.nprob = 2; a.pstride = g.skp_floats;
+    auto& u = a.xp[0];
+    u.A = dUc; u.lda = g.ldk; u.lda_out = g.ldF; u.a_out_off = g.c_out_off;
+    u.B0 = Bug; u.ldb0 = g.ldk; u.b0_gstride = (long long)rp * g.ldk;
+    u.B0o = BuTo; u.ldb0o = F;
+    u.col0 = rp;
     if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
   // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au

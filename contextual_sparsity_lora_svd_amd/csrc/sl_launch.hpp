@@ -56,11 +56,14 @@ inline sl_status launch_skinny_one(SkinnyArgs& a, hipStream_t s) {
   for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
   const int nblocks = skinny_layout(a, (int)sizeof(T));
   if (nblocks <= 0 || C <= 0) return SL_OK;
+  if (a.nprob < 1) a.nprob = 1;
+  if (a.nprob > SK_MAXPROB) SL_FAIL(SL_ERR_SHAPE, "internal: %d > %d skinny problems", a.nprob, SK_MAXPROB);
+  if ((long long)nblocks * a.nprob > 0x7FFFFFFFLL) SL_FAIL(SL_ERR_SHAPE, "skinny grid too large");
   a.pc = (C + 15) / 16 * 16;
   bool sliced = false;
   for (int g = 0; g < a.ngroups; ++g) sliced |= a.nsl[g] > 1;
   if (sliced && !a.part) SL_FAIL(SL_ERR_NULL, "internal: K-sliced skinny product without scratch");
-  const dim3 grid(nblocks), block(SK_THREADS);
+  const dim3 grid(nblocks * a.nprob), block(SK_THREADS);
   if (C <= 16) hipLaunchKernelGGL((skinny_kernel<T, 1>), grid, block, 0, s, a);
   else if (C <= 32) hipLaunchKernelGGL((skinny_kernel<T, 2>), grid, block, 0, s, a);
   else if (C <= 48) hipLaunchKernelGGL((skinny_kernel<T, 3>), grid, block, 0, s, a);
@@ -69,7 +72,8 @@ inline sl_status launch_skinny_one(SkinnyArgs& a, hipStream_t s) {
   if (sliced) {
     int ptot = 0;
     for (int j = 0; j < a.nblk; ++j) ptot += (a.nbk[j] + 7) / 8 * 8;
-    hipLaunchKernelGGL((skinny_finish_kernel<T>), grid1d((long long)a.mrows * ptot), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((skinny_finish_kernel<T>), grid1d((long long)a.mrows * ptot * a.nprob), dim3(256), 0,
+                       s, a);
     SL_HIP(hipGetLastError());
   }
   return SL_OK;
@@ -83,6 +87,7 @@ inline sl_status launch_skinny(SkinnyArgs& a, hipStream_t s) {
   for (int j = 0; j < a.nblk; ++j) C += a.nbk[j];
   if (C <= 64) return launch_skinny_one<T>(a, s);
   if (a.mode == 1) SL_FAIL(SL_ERR_SHAPE, "per-group skinny product with %d > 64 columns", C);
+  if (a.nprob > 1) SL_FAIL(SL_ERR_SHAPE, "internal: multi-problem skinny product with %d > 64 columns", C);
   int j = 0, col = a.col0;
   while (j < a.nblk) {
     SkinnyArgs b = a;

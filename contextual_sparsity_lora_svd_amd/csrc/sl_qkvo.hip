@@ -35,7 +35,7 @@ struct QkvoGeom {
   size_t esz;
   Comp cq, ck, cv, co;
   int ks_o, ks_dx, chunk;
-  long long cr_floats;
+  long long cr_floats, skp_floats;
   size_t s_zqkv, s_zo, saved_bytes;
   size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
       w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
@@ -138,7 +138,9 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_inv_k = b.take(B * g.nkv * 4);
   g.w_inv_v = b.take(B * g.nkv * 4);
   g.w_iota = b.take((size_t)std::max(g.nq, 3 * g.rp) * 4);
-  g.w_skp = b.take((size_t)skinny_part_floats(g.T, std::max(g.D, g.nq)) * 4);
+  // skinny partial sums: room for the three problems of the dz_q / dz_k / dz_v launch
+  g.skp_floats = skinny_part_floats(g.T, std::max(g.D, g.nq));
+  g.w_skp = b.take((size_t)g.skp_floats * 3 * 4);
   // K pieces of the da gather-GEMM when its grid is under half a round
   g.w_rp = b.take((size_t)ng_rpart_floats(st, g.ko, g.nq, false, g.esz, {g.D, g.rp}) * 4);
   g.ws_bytes = b.off;
@@ -383,21 +385,34 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   if (dq) {
     float* dz = reinterpret_cast<float*>(ws + g.w_dz_qkv);
     T* dzs = reinterpret_cast<T*>(ws + g.w_dzs_qkv);
-    for (int j = 0; j < 3; ++j) {
-      const Comp& c = *cc[j];
-      // dz_j = s dj_m B_j[S_j]
+    // dz_j = s dj_m B_j[S_j]; products whose channel counts match (all three
+    // when the q, k and v sets have equal sizes) share one launch
+    for (int j0 = 0; j0 < 3;) {
+      const Comp& c = *cc[j0];
       SkinnyArgs sa;
       std::memset(&sa, 0, sizeof(sa));
       sa.st = st; sa.mode = 1; sa.T = g.T;
-      sa.A = dcomp[j]; sa.lda = c.ld; sa.lda_out = c.n; sa.a_out_off = c.out_off;
+      sa.A = dcomp[j0]; sa.lda = c.ld; sa.lda_out = c.n; sa.a_out_off = c.out_off;
       sa.K = 0; sa.kidx = c.kc; sa.n_out = c.n;
       sa.nblk = 1;
-      sa.Bb[0] = Bg[j]; sa.nbk[0] = r; sa.ldbb[0] = c.ld; sa.b0_gstride = (long long)rp * c.ld;
-      sa.B0o = BTo[j]; sa.ldb0o = c.n;
-      sa.out = dz; sa.ldo = 3 * rp; sa.col0 = j * rp; sa.oscale = s;
+      sa.Bb[0] = Bg[j0]; sa.nbk[0] = r; sa.ldbb[0] = c.ld; sa.b0_gstride = (long long)rp * c.ld;
+      sa.B0o = BTo[j0]; sa.ldb0o = c.n;
+      sa.out = dz; sa.ldo = 3 * rp; sa.col0 = j0 * rp; sa.oscale = s;
       sa.outs = dzs; sa.ldos = 3 * rp; sa.scale = s;
       sa.part = skp;
+      sa.nprob = 1; sa.pstride = g.skp_floats;
+      int j = j0 + 1;
+      for (; j < 3 && cc[j]->kc == c.kc && cc[j]->n == c.n; ++j) {
+        const Comp& cj = *cc[j];
+        auto& x = sa.xp[sa.nprob - 1];
+        x.A = dcomp[j]; x.lda = cj.ld; x.lda_out = cj.n; x.a_out_off = cj.out_off;
+        x.B0 = Bg[j]; x.ldb0 = cj.ld; x.b0_gstride = (long long)rp * cj.ld;
+        x.B0o = BTo[j]; x.ldb0o = cj.n;
+        x.col0 = j * rp;
+        ++sa.nprob;
+      }
       if ((rc = launch_skinny<T>(sa, strm))) return rc;
+      j0 = j;
     }
     // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
     GemmArgs ga;

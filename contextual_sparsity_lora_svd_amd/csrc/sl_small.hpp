@@ -61,7 +61,45 @@ struct SkinnyArgs {
   int mrows;              // rows of the launch row space (see launch_row)
   int pc;                 // partial-sum row pitch: logical columns rounded up to 16
   float* part;            // partial sums [slice][launch row][pc] when a group has nsl > 1
+  // Further problems of the same launch (nprob > 1, at most SK_MAXPROB): the
+  // same mode, rows, K per group and B block sizes, with their own A operand,
+  // block-0 B operand, output column offset and partial sums at part + p *
+  // pstride.  Problem 0 is the fields above; the grid is nprob copies of the
+  // one-problem layout.
+  int nprob;
+  long long pstride;
+  struct {
+    const void* A; long long lda, lda_out, a_out_off;
+    const void* B0; long long ldb0, b0_gstride;
+    const void* B0o; long long ldb0o;
+    int col0;
+  } xp[2];
 };
+constexpr int SK_MAXPROB = 3;
+
+// Operands of problem p of a skinny launch.
+struct SkProbView {
+  const void* A; long long lda, lda_out, a_out_off;
+  const void* B0; long long ldb0, b0_gstride;
+  const void* B0o; long long ldb0o;
+  int col0;
+  float* part;
+};
+__device__ inline SkProbView skinny_prob(const SkinnyArgs& a, int p) {
+  SkProbView v;
+  if (p == 0) {
+    v.A = a.A; v.lda = a.lda; v.lda_out = a.lda_out; v.a_out_off = a.a_out_off;
+    v.B0 = a.Bb[0]; v.ldb0 = a.ldbb[0]; v.b0_gstride = a.b0_gstride;
+    v.B0o = a.B0o; v.ldb0o = a.ldb0o; v.col0 = a.col0;
+  } else {
+    const auto& x = a.xp[p - 1];
+    v.A = x.A; v.lda = x.lda; v.lda_out = x.lda_out; v.a_out_off = x.a_out_off;
+    v.B0 = x.B0; v.ldb0 = x.ldb0; v.b0_gstride = x.b0_gstride;
+    v.B0o = x.B0o; v.ldb0o = x.ldb0o; v.col0 = x.col0;
+  }
+  v.part = a.part ? a.part + p * a.pstride : nullptr;
+  return v;
+}
 
 // Row of the launch row space: token order in mode 0, compact order otherwise
 // (context rows of every sequence, then, in mode 1, the output rows).
@@ -128,11 +166,15 @@ skinny_kernel(const SkinnyArgs a) {
   unsigned char* Bs = smem + SK_RB * SK_LDB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nbs = a.blk_start[a.ngroups];              // workgroups per problem
+  const int prob = a.nprob > 1 ? (int)blockIdx.x / nbs : 0;
+  const int bid = (int)blockIdx.x - prob * nbs;
+  const SkProbView pv = skinny_prob(a, prob);
   int g = 0;
-  while (g + 1 < a.ngroups && a.blk_start[g + 1] <= (int)blockIdx.x) ++g;
+  while (g + 1 < a.ngroups && a.blk_start[g + 1] <= bid) ++g;
   g = __builtin_amdgcn_readfirstlane(g);
   const int nsl = a.nsl[g];
-  const int local = blockIdx.x - a.blk_start[g];
+  const int local = bid - a.blk_start[g];
   const int rb = local / nsl, sl = local % nsl;
   const bool is_out = (a.mode == 1 && g == a.st.nseq);
   const int m_rows = a.mode == 0 ? a.T : group_rows(a.st, g);
@@ -142,7 +184,7 @@ skinny_kernel(const SkinnyArgs a) {
   const int nch = kend > kbeg ? (kend - kbeg + KC - 1) / KC : 0;
 
   // this thread's A pieces: row tid/PR + i*(SK_THREADS/PR), piece tid%PR
-  const T* A = reinterpret_cast<const T*>(a.A);
+  const T* A = reinterpret_cast<const T*>(pv.A);
   const int q = tid % PR;
   const T* arow[AL];
 #pragma unroll
@@ -151,9 +193,9 @@ skinny_kernel(const SkinnyArgs a) {
     if (r >= m_rows) r = m_rows - 1;        // loaded and dropped
     long long off;
     if (a.mode == 1)
-      off = is_out ? a.a_out_off + (long long)r * a.lda_out : (long long)(a.st.ctx_pre[g] + r) * a.lda;
+      off = is_out ? pv.a_out_off + (long long)r * pv.lda_out : (long long)(a.st.ctx_pre[g] + r) * pv.lda;
     else
-      off = (long long)(a.mode == 0 ? r : group_token(a.st, g, r)) * a.lda;
+      off = (long long)(a.mode == 0 ? r : group_token(a.st, g, r)) * pv.lda;
     arow[i] = A + off;
   }
   // B pieces: logical column c = tid/PR + i*(SK_THREADS/PR)
@@ -170,11 +212,11 @@ skinny_kernel(const SkinnyArgs a) {
       for (int j = 0; j < a.nblk; ++j) {
         if (c < a.nbk[j]) {
           if (j == 0) {
-            const T* B0 = reinterpret_cast<const T*>(a.Bb[0]);
-            long long ldb0 = a.ldbb[0];
+            const T* B0 = reinterpret_cast<const T*>(pv.B0);
+            long long ldb0 = pv.ldb0;
             if (a.mode == 1) {
-              if (is_out && a.B0o) { B0 = reinterpret_cast<const T*>(a.B0o); ldb0 = a.ldb0o; }
-              else if (!is_out) B0 += (long long)g * a.b0_gstride;
+              if (is_out && pv.B0o) { B0 = reinterpret_cast<const T*>(pv.B0o); ldb0 = pv.ldb0o; }
+              else if (!is_out) B0 += (long long)g * pv.b0_gstride;
             }
             brow[i] = B0 + (long long)c * ldb0;
           } else {
@@ -185,7 +227,7 @@ skinny_kernel(const SkinnyArgs a) {
         c -= a.nbk[j];
       }
     }
-    if (!brow[i]) brow[i] = reinterpret_cast<const T*>(a.A);   // never dereferenced
+    if (!brow[i]) brow[i] = A;   // never dereferenced
   }
 
   uint4 ra[AL], rbv[BL];
@@ -270,7 +312,7 @@ skinny_kernel(const SkinnyArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = rb * SK_RB + wave * 16 + 4 * (lane >> 4) + e;
         if (r < m_rows)
-          a.part[((long long)sl * a.mrows + launch_row(a, g, r)) * a.pc + nb * 16 + (lane & 15)] =
+          pv.part[((long long)sl * a.mrows + launch_row(a, g, r)) * a.pc + nb * 16 + (lane & 15)] =
               acc[nb][e];
       }
     return;
@@ -290,18 +332,23 @@ skinny_kernel(const SkinnyArgs a) {
     const int c = skinny_logical_col(a, oc);
     const float v = (c >= 0 && c < NB * 16) ? stage[rr * STAGE_LD + c] : 0.f;
     const long long tok = a.mode == 0 ? row : group_token(a.st, g, row);
-    a.out[tok * a.ldo + a.col0 + oc] = v * a.oscale;
-    if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + a.col0 + oc, v * a.scale);
+    a.out[tok * a.ldo + pv.col0 + oc] = v * a.oscale;
+    if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + pv.col0 + oc, v * a.scale);
   }
 }
 
 // Adds the K slices of the groups with nsl > 1, in slice order, and writes the
-// results (one thread per launch row and padded column).
+// results (one thread per problem, launch row and padded column).
 template <typename T>
 __global__ void skinny_finish_kernel(const SkinnyArgs a) {
   const int ptot = skinny_padded_cols(a);
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)a.mrows * ptot) return;
+  const long long per = (long long)a.mrows * ptot;
+  const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int np = a.nprob > 1 ? a.nprob : 1;
+  if (i0 >= per * np) return;
+  const int prob = (int)(i0 / per);
+  const long long i = i0 - prob * per;
+  const SkProbView pv = skinny_prob(a, prob);
   const int lrow = (int)(i / ptot), oc = (int)(i % ptot);
   int r;
   const int g = skinny_group_of(a, lrow, r);
@@ -311,7 +358,7 @@ __global__ void skinny_finish_kernel(const SkinnyArgs a) {
   float v = 0.f;
   if (c >= 0) {
     // slices in order; loads issued in groups of 8 before they are summed
-    const float* p = a.part + (long long)lrow * a.pc + c;
+    const float* p = pv.part + (long long)lrow * a.pc + c;
     const long long sstride = (long long)a.mrows * a.pc;
     for (int s0 = 0; s0 < nsl; s0 += 8) {
       float t[8];
@@ -322,8 +369,8 @@ __global__ void skinny_finish_kernel(const SkinnyArgs a) {
     }
   }
   const long long tok = a.mode == 0 ? r : group_token(a.st, g, r);
-  a.out[tok * a.ldo + a.col0 + oc] = v * a.oscale;
-  if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + a.col0 + oc, v * a.scale);
+  a.out[tok * a.ldo + pv.col0 + oc] = v * a.oscale;
+  if (a.outs) stv<T>(reinterpret_cast<T*>(a.outs), tok * a.ldos + pv.col0 + oc, v * a.scale);
 }
 
 // ===========================================================================

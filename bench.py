@@ -276,16 +276,16 @@ def attn_bench(args, torch, sl, cfg=3, quant=False):
         torch.cuda.empty_cache()
     w = sl.QKVOWeights(t, heads)
     torch.cuda.synchronize()
-    est_qk = sl.EstimateBuffers(sl.SL_CRIT_QK_NORM, lay, D, r_e, nkv, kqk, X.device, heads=heads)
-    est_vo = sl.EstimateBuffers(sl.SL_CRIT_L2, lay, D, r_e, nkv, kvo, X.device)
+    # q/k by the QK-norm and v/o by the L2 criterion, one estimate call over X
+    jobs = [dict(crit=sl.SL_CRIT_QK_NORM, Pt0=f["Wq"][0], Q0=f["Wq"][1], Pt1=f["Wk"][0], Q1=f["Wk"][1], N=nkv,
+                 k=kqk, heads=heads),
+            dict(crit=sl.SL_CRIT_L2, Pt0=f["Wv"][0], Q0=f["Wv"][1], N=nkv, k=kvo)]
+    est = sl.EstimateMultiBuffers(lay, D, r_e, jobs, X.device)
     buf = sl.QKVOWorkspace(w, lay, kqk, kvo, X.device)
     outs, grads = {}, {}
 
     def step():
-        iqk, _ = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, r_e, f["Wq"][0], f["Wq"][1], f["Wk"][0],
-                                    f["Wk"][1], nkv, kqk, heads=heads, bufs=est_qk)
-        ivo, _ = sl.estimate_select(sl.SL_CRIT_L2, X, lay, r_e, f["Wv"][0], f["Wv"][1], None, None, nkv,
-                                    kvo, bufs=est_vo)
+        (iqk, _), (ivo, _) = sl.estimate_select_multi(X, lay, r_e, jobs, bufs=est)
         o, _ = sl.qkvo_fwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf=buf, outs=outs)
         outs.update(o)
         g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, dq=dq, dk=dk, dv=dv, d_out=dout, out=grads)

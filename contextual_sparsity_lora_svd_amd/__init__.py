@@ -5,7 +5,7 @@ C ABI in include/sparselora.h); this package is its Python binding.
 """
 from .api import (  # noqa: F401
     SL_BF16, SL_CRIT_L2, SL_CRIT_QK_NORM, SL_CRIT_SWIGLU_L2, SL_F32, SL_MAX_SEQS, LIB_PATH,
-    SIGNATURES, EstimateBuffers, FFNWeights, FFNWorkspace, Layout, QKVOWeights, QKVOWorkspace, SparseLoraError,
-    TIMER_SLOTS, build_estimator, estimate_select, gemm_config, quantize_q4, timer_enable, timer_read, timer_reset, timer_select, ffn_bwd, ffn_fwd, k_from_ratio, lib, qkvo_bwd, qkvo_fwd,
+    SIGNATURES, SL_EST_MAXJOBS, EstimateBuffers, EstimateMultiBuffers, FFNWeights, FFNWorkspace, Layout, QKVOWeights, QKVOWorkspace, SparseLoraError,
+    TIMER_SLOTS, build_estimator, estimate_select, estimate_select_multi, gemm_config, quantize_q4, timer_enable, timer_read, timer_reset, timer_select, ffn_bwd, ffn_fwd, k_from_ratio, lib, qkvo_bwd, qkvo_fwd,
 )
 from .layer import LayerRatios, SparseLoRAFFN, SparseLoRAQKVO, SparsitySchedule  # noqa: F401,E402

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsparselora.so")
 SL_F32, SL_BF16 = 0, 1
 SL_CRIT_SWIGLU_L2, SL_CRIT_L2, SL_CRIT_QK_NORM = 0, 1, 2
 SL_MAX_SEQS = 64
+SL_EST_MAXJOBS = 3
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -32,6 +33,11 @@ class SlLayout(ctypes.Structure):
 
 class SlHeads(ctypes.Structure):
     _fields_ = [("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32)]
+
+
+class SlEstJob(ctypes.Structure):
+    _fields_ = [("crit", ctypes.c_int), ("heads", SlHeads), ("Pt0", _vp), ("Q0", _vp), ("Pt1", _vp),
+                ("Q1", _vp), ("N", _i64), ("k", _i32), ("idx", _vp), ("scores", _vp)]
 
 
 class SlFfnWeights(ctypes.Structure):
@@ -73,6 +79,10 @@ SIGNATURES = {
     "sl_estimate_select": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(SlLayout),
                                           ctypes.POINTER(SlHeads), _vp, _i64, _i32, _vp, _vp, _vp,
                                           _vp, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "sl_estimate_select_multi_workspace_bytes": (_sz, [ctypes.POINTER(SlLayout), _i64, _i32, _i32,
+                                                       ctypes.POINTER(SlEstJob)]),
+    "sl_estimate_select_multi": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout), _vp, _i64, _i32,
+                                                _i32, ctypes.POINTER(SlEstJob), _vp, _sz, _vp]),
     "sl_ffn_saved_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout), _i64, _i64, _i32, _i32]),
     "sl_ffn_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(SlLayout), _i64, _i64, _i32,
                                      _i32]),
@@ -264,6 +274,47 @@ def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, 
                                 _ptr(bufs.scores), _ptr(bufs.ws), bufs.ws.numel(), _stream()),
            "sl_estimate_select")
     return bufs.idx, bufs.scores
+
+
+class EstimateMultiBuffers:
+    """Reusable idx / scores / scratch buffers of estimate_select_multi.  Each
+    job is a dict with crit, N, k and optionally heads and want_scores."""
+
+    def __init__(self, layout: Layout, d_in: int, rank: int, jobs: Sequence[dict], device):
+        L = lib()
+        if not 1 <= len(jobs) <= SL_EST_MAXJOBS:
+            raise ValueError(f"1..{SL_EST_MAXJOBS} jobs")
+        self.c = (SlEstJob * len(jobs))()
+        self.idx, self.scores = [], []
+        for j, job in enumerate(jobs):
+            c = self.c[j]
+            c.crit, c.N, c.k = job["crit"], job["N"], job["k"]
+            if job.get("heads") is not None:
+                c.heads = SlHeads(*job["heads"])
+            self.idx.append(torch.empty(layout.batch, job["k"], dtype=torch.int32, device=device))
+            self.scores.append(torch.empty(layout.batch, job["N"], dtype=torch.float32, device=device)
+                               if job.get("want_scores") else None)
+        self.ws = _bytes_tensor(L.sl_estimate_select_multi_workspace_bytes(layout.ref, d_in, rank, len(jobs),
+                                                                           self.c), device)
+
+
+def estimate_select_multi(X: torch.Tensor, layout: Layout, rank: int, jobs: Sequence[dict],
+                          bufs: Optional[EstimateMultiBuffers] = None):
+    """Several criteria over one input X in one call.  Each job is a dict with
+    crit, Pt0, Q0 (and Pt1, Q1 unless L2), N, k and optionally heads (QK-norm)
+    and want_scores.  Returns [(idx, scores)] in job order, as separate
+    estimate_select calls would."""
+    L = lib()
+    bufs = bufs or EstimateMultiBuffers(layout, X.shape[1], rank, jobs, X.device)
+    for j, job in enumerate(jobs):
+        c = bufs.c[j]
+        c.Pt0, c.Q0 = _ptr(job["Pt0"]), _ptr(job["Q0"])
+        c.Pt1, c.Q1 = _ptr(job.get("Pt1")), _ptr(job.get("Q1"))
+        c.idx, c.scores = _ptr(bufs.idx[j]), _ptr(bufs.scores[j])
+    _check(L.sl_estimate_select_multi(_dtype_code(X), layout.ref, _ptr(X), X.shape[1], rank, len(jobs), bufs.c,
+                                      _ptr(bufs.ws), bufs.ws.numel(), _stream()),
+           "sl_estimate_select_multi")
+    return list(zip(bufs.idx, bufs.scores))
 
 
 class FFNWeights:

@@ -386,9 +386,9 @@ __global__ void skinny_finish_kernel(const SkinnyArgs a) {
 // turns the token loop into one Gram matrix per sequence and a quadratic form
 // per channel.  G and the form are taken in fp64: every product in G is exact
 // (fp32 times fp32), so the fp32 result is at least as accurate as a direct
-// fp32 sum of squares.  One partial per sequence.  One launch covers up to two
-// projections (the QK-norm criterion's q and k): grid (channel blocks, nseq,
-// projections); every workgroup rebuilds its sequence's G and scores
+// fp32 sum of squares.  One partial per sequence.  One launch covers up to four
+// projections (the QK-norm criterion's q and k, the L2 criterion's v of the
+// same layer input): grid (channel blocks, nseq, projections); every workgroup rebuilds its sequence's G and scores
 // GR_THREADS channels.
 //
 // G = Z^T Z runs on the fp64 matrix cores (16x16x4, K = 4 tokens per step):
@@ -404,7 +404,7 @@ struct GramArgs {
   SeqTab st;
   const float* Zh; long long ldz;
   int rank;
-  int zc[2]; const void* Q[2]; int N[2]; float* part[2];
+  int zc[4]; const void* Q[4]; int N[4]; float* part[4];   // up to 4 projections
 };
 
 template <typename T, int RM>
@@ -586,8 +586,8 @@ score_swiglu_kernel(const SwiArgs a) {
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_MAXN = 32768;
 
-struct SelectArgs {
-  SeqTab st;
+// One selection job: its partial sums, channel count, k and outputs.
+struct SelJob {
   int qk;                 // 0: score = sum of part0 chunks; 1: QK combination
   const float* part0; const float* part1;
   int nchunk_max;
@@ -597,6 +597,14 @@ struct SelectArgs {
   int group, head_dim;    // QK: query heads per kv head, head size
   int k;
   int* idx; float* scores;
+};
+constexpr int SEL_MAXJOBS = 3;
+
+// grid (sequences, jobs): workgroup (b, j) selects job j's set for sequence b.
+struct SelectArgs {
+  SeqTab st;
+  int njobs;
+  SelJob job[SEL_MAXJOBS];
 };
 
 __device__ inline int wave_incl_scan(int v) {
@@ -636,9 +644,10 @@ select_kernel(const SelectArgs a) {
   __shared__ uint32_t wmax[SEL_THREADS / 64], wmin[SEL_THREADS / 64];
   __shared__ int s_sel[2];
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const SelJob& J = a.job[blockIdx.y];
   const int ctx = a.st.ctx[b];
-  const int nch = (int)(((long long)ctx + a.chunk - 1) / a.chunk);
-  const long long pb = (long long)b * a.nchunk_max;
+  const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
+  const long long pb = (long long)b * J.nchunk_max;
 
   // Scores of SB channels at a time (n0 + j * SEL_THREADS, j < SB): the chunk
   // partials of the SB columns are loaded 4 chunks at a time (4 SB loads in
@@ -662,26 +671,26 @@ select_kernel(const SelectArgs a) {
     }
   };
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  for (int n0 = tid; n0 < a.N; n0 += SB * SEL_THREADS) {
+  for (int n0 = tid; n0 < J.N; n0 += SB * SEL_THREADS) {
     int col[SB];
 #pragma unroll
-    for (int j = 0; j < SB; ++j) col[j] = n0 + j * SEL_THREADS < a.N ? n0 + j * SEL_THREADS : -1;
+    for (int j = 0; j < SB; ++j) col[j] = n0 + j * SEL_THREADS < J.N ? n0 + j * SEL_THREADS : -1;
     float sc[SB];
-    if (!a.qk) {
-      sumb(a.part0, a.N0, col, sc);
+    if (!J.qk) {
+      sumb(J.part0, J.N0, col, sc);
     } else {
       float sq[SB], t[SB];
-      sumb(a.part1, a.N, col, sc);   // sc = sk for now
+      sumb(J.part1, J.N, col, sc);   // sc = sk for now
 #pragma unroll
       for (int j = 0; j < SB; ++j) sq[j] = 0.f;
-      for (int h = 0; h < a.group; ++h) {
+      for (int h = 0; h < J.group; ++h) {
         int qcol[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
           const int n = col[j];
-          qcol[j] = n < 0 ? -1 : ((n / a.head_dim) * a.group + h) * a.head_dim + n % a.head_dim;
+          qcol[j] = n < 0 ? -1 : ((n / J.head_dim) * J.group + h) * J.head_dim + n % J.head_dim;
         }
-        sumb(a.part0, a.N0, qcol, t);
+        sumb(J.part0, J.N0, qcol, t);
 #pragma unroll
         for (int j = 0; j < SB; ++j) sq[j] += t[j];
       }
@@ -692,7 +701,7 @@ select_kernel(const SelectArgs a) {
     for (int j = 0; j < SB; ++j) {
       const int n = col[j];
       if (n < 0) continue;
-      if (a.scores) a.scores[(long long)b * a.N + n] = sc[j];
+      if (J.scores) J.scores[(long long)b * J.N + n] = sc[j];
       const uint32_t kv = __float_as_uint(sc[j]);
       keys[n] = kv;
       kmax = kv > kmax ? kv : kmax;
@@ -718,7 +727,7 @@ select_kernel(const SelectArgs a) {
   const int hbit = kmax == kmin ? -1 : 31 - __clz(kmax ^ kmin);
   const uint32_t low = hbit >= 31 ? 0xFFFFFFFFu : ((1u << (hbit + 1)) - 1u);
   uint32_t mask = ~low, prefix = kmax & ~low;
-  int kr = a.k;   // still to take among keys matching prefix
+  int kr = J.k;   // still to take among keys matching prefix
 
   // radix passes of up to 8 bits from the highest differing bit down; three
   // barriers per pass: each bin's per-wave counts are cleared as they are read,
@@ -728,7 +737,7 @@ select_kernel(const SelectArgs a) {
     const int w = hi + 1 < 8 ? hi + 1 : 8;
     const int lo = hi - w + 1;
     const int nb = 1 << w;
-    for (int n = tid; n < a.N; n += SEL_THREADS) {
+    for (int n = tid; n < J.N; n += SEL_THREADS) {
       const uint32_t kv = keys[n];
       if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> lo) & (uint32_t)(nb - 1)], 1);
     }
@@ -766,8 +775,8 @@ select_kernel(const SelectArgs a) {
   const uint32_t tau = prefix;   // the k-th largest key; take kr of the keys equal to it
 
   // ordered compaction over contiguous per-thread ranges
-  const int per = (a.N + SEL_THREADS - 1) / SEL_THREADS;
-  const int lo = min(a.N, tid * per), hi = min(a.N, lo + per);
+  const int per = (J.N + SEL_THREADS - 1) / SEL_THREADS;
+  const int lo = min(J.N, tid * per), hi = min(J.N, lo + per);
   int n_gt = 0, n_eq = 0;
   for (int n = lo; n < hi; ++n) {
     const uint32_t kv = keys[n];
@@ -779,7 +788,7 @@ select_kernel(const SelectArgs a) {
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
   const int pos0 = block_excl_scan(n_gt + take_eq, wsum, tid, nullptr);
   int pos = pos0, eq_seen = 0;
-  int* out = a.idx + (long long)b * a.k;
+  int* out = J.idx + (long long)b * J.k;
   for (int n = lo; n < hi; ++n) {
     const uint32_t kv = keys[n];
     bool take = kv > tau;

@@ -257,6 +257,14 @@ class SparseLoRAQKVO(torch.nn.Module):
 
     def channel_sets(self, X, layout, k_qk, k_vo):
         B = layout.batch
+        if k_qk < self.nkv and k_vo < self.nkv:
+            # both sets estimated: one call projects X once for q, k and v
+            (Pq, Qq), (Pk, Qk), (Pv, Qv) = self.est["Wq"], self.est["Wk"], self.est["Wv"]
+            jobs = [dict(crit=sl.SL_CRIT_QK_NORM, Pt0=Pq, Q0=Qq, Pt1=Pk, Q1=Qk, N=self.nkv, k=k_qk,
+                         heads=self.heads),
+                    dict(crit=sl.SL_CRIT_L2, Pt0=Pv, Q0=Qv, N=self.nkv, k=k_vo)]
+            (iqk, _), (ivo, _) = sl.estimate_select_multi(X, layout, self.est_rank, jobs)
+            return iqk, ivo
         if k_qk == self.nkv:
             iqk = _all_channels(B, self.nkv, X.device)
         else:

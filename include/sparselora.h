@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SL_ABI_VERSION 2
+#define SL_ABI_VERSION 3
 #define SL_MAX_SEQS 64  /* sequences per call (batch) */
 
 typedef enum sl_status {
@@ -184,6 +184,35 @@ sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* la
                              const void* Pt0, const void* Q0, const void* Pt1, const void* Q1,
                              int64_t N, int32_t k, int32_t* idx, float* scores,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a1-a3 for several criteria over one input (SparseLoRA article §一, §二, §三:
+ * an attention layer scores q/k by the QK-norm and v/o by the L2 norm of the
+ * same layer input).  Same results as one sl_estimate_select call per job, but
+ * X is projected once onto every job's leading directions, all L2-type
+ * criteria share one launch and all selections share one launch.
+ *   jobs[j]: crit, heads (QK_NORM only), Pt0/Q0/Pt1/Q1, N, k, idx, scores as in
+ *            sl_estimate_select; every job shares X, the layout, d_in and rank.
+ * 1 <= njobs <= SL_EST_MAXJOBS, and the jobs' projections (2 for SWIGLU_L2 and
+ * QK_NORM, 1 for L2) number at most 4.  Jobs must write distinct idx / scores
+ * buffers.  The workspace query takes the same layout, d_in, rank and jobs
+ * (only crit, heads and N are read).
+ * ------------------------------------------------------------------------- */
+#define SL_EST_MAXJOBS 3
+typedef struct sl_est_job {
+  sl_criterion crit;
+  sl_heads heads;                  /* QK_NORM only */
+  const void *Pt0, *Q0, *Pt1, *Q1;  /* Pt1 / Q1 unused for L2 */
+  int64_t N;
+  int32_t k;
+  int32_t* idx;                    /* [batch, k] out */
+  float* scores;                   /* [batch, N] out, optional */
+} sl_est_job;
+size_t sl_estimate_select_multi_workspace_bytes(const sl_layout* lay, int64_t d_in, int32_t rank,
+                                                int32_t njobs, const sl_est_job* jobs);
+sl_status sl_estimate_select_multi(sl_dtype dt, const sl_layout* lay, const void* X, int64_t d_in,
+                                   int32_t rank, int32_t njobs, const sl_est_job* jobs, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a4/a5 — sparse SwiGLU FFN forward and backward (SparseLoRA article §一, §三,

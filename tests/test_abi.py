@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(sl):
 
 def test_status_strings(sl):
     L = sl.lib()
-    assert L.sl_abi_version() == 2
+    assert L.sl_abi_version() == 3
     for code in range(9):
         assert L.sl_status_string(code)
     assert L.sl_status_string(99) == b"unknown status"
@@ -121,6 +121,30 @@ def test_estimate_select_validation(sl):
     st = L.sl_estimate_select(0, 1, lay.ref, None, P, 64, 8, P, P, None, P, 16, 4, P, None, P,
                               1 << 30, None)
     assert st == 1          # SwiGLU needs both factor pairs
+
+
+def test_estimate_select_multi_validation(sl):
+    L = sl.lib()
+    lay = sl.Layout([10], 10)
+    P = 4096
+    J = sl.api.SlEstJob
+    jobs = (J * 3)()
+    for j in range(3):
+        jobs[j].crit, jobs[j].N, jobs[j].k = 2, 16, 4
+        jobs[j].heads = sl.api.SlHeads(4, 2, 8)
+        jobs[j].Pt0 = jobs[j].Q0 = jobs[j].Pt1 = jobs[j].Q1 = jobs[j].idx = P
+    # three QK-norm jobs are six projections: more than one call takes
+    assert L.sl_estimate_select_multi_workspace_bytes(lay.ref, 64, 8, 3, jobs) == 0
+    st = L.sl_estimate_select_multi(1, lay.ref, P, 64, 8, 3, jobs, P, 1 << 30, None)
+    assert st == 5
+    assert L.sl_estimate_select_multi(1, lay.ref, P, 64, 8, 0, jobs, P, 1 << 30, None) == 5   # no jobs
+    jobs[1].crit = 1                                                                            # QK + L2
+    assert L.sl_estimate_select_multi_workspace_bytes(lay.ref, 64, 8, 2, jobs) > 0
+    jobs[1].k = 17                                                                              # k > N
+    assert L.sl_estimate_select_multi(1, lay.ref, P, 64, 8, 2, jobs, P, 1 << 30, None) == 5
+    jobs[1].k = 4
+    jobs[1].idx = None
+    assert L.sl_estimate_select_multi(1, lay.ref, P, 64, 8, 2, jobs, P, 1 << 30, None) == 1
 
 
 def test_qkvo_validation(sl):

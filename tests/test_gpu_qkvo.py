@@ -200,6 +200,80 @@ def test_qk_norm_and_l2_select_high_rank(rank):
     check_selection(idx2.cpu().numpy(), ref_vo, k)
 
 
+@pytest.mark.parametrize("heads", [(4, 4, 16), (8, 2, 16)])
+def test_estimate_select_multi(heads):
+    """QK-norm on q/k and L2 on v in one call: the oracle's scores and sets, and
+    bit-for-bit the results of the two single-criterion calls."""
+    sl = _api()
+    D, r, L = 64, 4, 90
+    ctx = [90, 17, 64]
+    p = _case(D, heads, r, ctx, L, "bf16", seed=31)
+    Pq, Qq = factors(p["Wq"], 8, "bf16")
+    Pk, Qk = factors(p["Wk"], 8, "bf16")
+    Pv, Qv = factors(p["Wv"], 8, "bf16")
+    nkv = heads[1] * heads[2]
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], "bf16")
+    ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    kqk, kvo = nkv // 2, nkv // 3
+    d = {n: to_dev(v, "bf16") for n, v in (("Pq", Pq), ("Qq", Qq), ("Pk", Pk), ("Qk", Qk), ("Pv", Pv), ("Qv", Qv))}
+    jobs = [dict(crit=sl.SL_CRIT_QK_NORM, Pt0=d["Pq"], Q0=d["Qq"], Pt1=d["Pk"], Q1=d["Qk"], N=nkv, k=kqk,
+                 heads=heads, want_scores=True),
+            dict(crit=sl.SL_CRIT_L2, Pt0=d["Pv"], Q0=d["Qv"], N=nkv, k=kvo, want_scores=True)]
+    (iqk, sqk), (ivo, svo) = sl.estimate_select_multi(X, lay, 8, jobs)
+    i1, s1 = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, 8, d["Pq"], d["Qq"], d["Pk"], d["Qk"], nkv, kqk,
+                                heads=heads, want_scores=True)
+    i2, s2 = sl.estimate_select(sl.SL_CRIT_L2, X, lay, 8, d["Pv"], d["Qv"], None, None, nkv, kvo,
+                                want_scores=True)
+    torch.cuda.synchronize()
+    for got, ref in ((sqk.cpu().numpy(), ref_qk), (svo.cpu().numpy(), ref_vo)):
+        for b in range(len(ctx)):
+            e = np.abs(got[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+            assert e < 2e-4, f"score rel err {e:.2e}"
+    check_selection(iqk.cpu().numpy(), ref_qk, kqk)
+    check_selection(ivo.cpu().numpy(), ref_vo, kvo)
+    assert torch.equal(iqk, i1) and torch.equal(ivo, i2)
+    assert torch.equal(sqk, s1) and torch.equal(svo, s2)
+
+
+def test_estimate_select_multi_swiglu_offset():
+    """A SwiGLU job after an L2 job (its projections in later estimate columns)
+    and a third L2 job: every job matches its single call and the oracle."""
+    sl = _api()
+    from tests.test_gpu_ffn import _ffn_case, _oracle_scores
+    D, F, L = 128, 200, 70
+    ctx = [70, 25]
+    p = _ffn_case(D, F, 4, ctx, L, "f32", seed=33)
+    Pg, Qg = factors(p["Wg"], 8, "f32")
+    Pu, Qu = factors(p["Wu"], 8, "f32")
+    Pd, Qd = factors(np.ascontiguousarray(p["Wd"].T), 8, "f32")     # an L2 job: d_model -> d_ff factors
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], "f32")
+    dv = {n: to_dev(v, "f32") for n, v in (("Pg", Pg), ("Qg", Qg), ("Pu", Pu), ("Qu", Qu), ("Pd", Pd), ("Qd", Qd))}
+    k1, k2 = 60, 90
+    jobs = [dict(crit=sl.SL_CRIT_L2, Pt0=dv["Pd"], Q0=dv["Qd"], N=F, k=k1, want_scores=True),
+            dict(crit=sl.SL_CRIT_SWIGLU_L2, Pt0=dv["Pg"], Q0=dv["Qg"], Pt1=dv["Pu"], Q1=dv["Qu"], N=F, k=k2,
+                 want_scores=True)]
+    (ia, sa), (ib, sb) = sl.estimate_select_multi(X, lay, 8, jobs)
+    ja, ta = sl.estimate_select(sl.SL_CRIT_L2, X, lay, 8, dv["Pd"], dv["Qd"], None, None, F, k1, want_scores=True)
+    jb, tb = sl.estimate_select(sl.SL_CRIT_SWIGLU_L2, X, lay, 8, dv["Pg"], dv["Qg"], dv["Pu"], dv["Qu"], F, k2,
+                                want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ja) and torch.equal(sa, ta)
+    assert torch.equal(ib, jb) and torch.equal(sb, tb)
+    ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+    for b in range(len(ctx)):
+        e = np.abs(sb.cpu().numpy()[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
+        assert e < 1e-4, f"SwiGLU score rel err {e:.2e}"
+    check_selection(ib.cpu().numpy(), ref, k2)
+    ref_l2 = np.stack([O.scores_l2(p["X"][O.context_rows(ctx, L, b)], Pd.T, Qd, dtype=np.float32)
+                       for b in range(len(ctx))])
+    for b in range(len(ctx)):
+        e = np.abs(sa.cpu().numpy()[b] - ref_l2[b]).max() / max(ref_l2[b].max(), 1e-30)
+        assert e < 1e-4, f"L2 score rel err {e:.2e}"
+    check_selection(ia.cpu().numpy(), ref_l2, k1)
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_full_size_workloads(cfg):
     """LLaMA2-7B q/k/v/o (multi-head) and LLaMA3-8B (grouped-query) at their sizes."""

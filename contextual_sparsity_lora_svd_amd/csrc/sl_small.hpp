@@ -1054,6 +1054,9 @@ colred_batch_kernel(const CbArgs a) {
 // c < N and q < r1, the sum over the groups that hold c (context groups
 // through the inverse map inv, the output group always) into out1.  Outputs
 // are [N, r] or, transposed, [r, N], times scale.  One thread per (job, c, q).
+// (Issuing every group's loads in one predicated batch, 8 groups x 8 chunks,
+// measured slower: the address arithmetic of the idle slots costs more issue
+// time than the saved round trips.)
 struct FbJob {
   int kind;                 // 0 dense, 1 scatter
   const float* part; int RM, N, kidx, nchunk;

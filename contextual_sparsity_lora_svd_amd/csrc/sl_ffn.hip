@@ -287,7 +287,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
-  // packed LoRA operands (one launch)
+  // packed LoRA operands and the inverse map of the channel sets (one launch)
   {
     Packer pk;
     pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
@@ -299,9 +299,9 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(BgTo, F, r, F, w->Bg, r, r, F, 1);
     pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
+    pk.inverse(inv, idx, g.k, F, st.nseq);
     if ((rc = pk.launch<T>(strm))) return rc;
   }
-  if ((rc = inverse_maps(idx, g.k, st.nseq, F, inv, strm))) return rc;
 
   // dz_d = s dY Bd
   {

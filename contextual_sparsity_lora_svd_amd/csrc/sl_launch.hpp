@@ -161,6 +161,11 @@ struct Packer {
     PackJob& j = next();
     j.type = 2; j.dst = dst; j.rows = 1; j.cols = n;
   }
+  // inv [nseq, n] <- positions of channels 0..n-1 in the ascending sets idx [nseq, k]
+  void inverse(int* inv, const int* idx, int k, int n, int nseq) {
+    PackJob& j = next();
+    j.type = 3; j.dst = inv; j.rows = 1; j.cols = n; j.idx = idx; j.k = k; j.nseq = nseq;
+  }
   template <typename T>
   sl_status launch(hipStream_t s) {
     if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d pack jobs", PK_MAXJOBS);
@@ -168,34 +173,11 @@ struct Packer {
     for (int i = 0; i < a.njobs; ++i) {
       a.start[i] = n;
       const PackJob& j = a.job[i];
-      n += (long long)j.rows * j.cols * (j.type == 1 ? j.nseq : 1);
+      n += (long long)j.rows * j.cols * (j.type == 1 || j.type == 3 ? j.nseq : 1);
     }
     a.start[a.njobs] = n;
     if (n == 0) return SL_OK;
     hipLaunchKernelGGL((pack_kernel<T>), grid1d(n), dim3(256), 0, s, a);
-    SL_HIP(hipGetLastError());
-    return SL_OK;
-  }
-};
-
-// Builder of one inverse-map launch (up to IV_MAXSETS ascending channel sets).
-struct Inverter {
-  InvArgs a;
-  bool overflow = false;
-  explicit Inverter(int nseq) { std::memset(&a, 0, sizeof(a)); a.nseq = nseq; }
-  // inv [nseq, n] <- positions of channels 0..n-1 in idx [nseq, k]
-  void add(const int* idx, int k, int n, int* inv) {
-    if (a.nset >= IV_MAXSETS) { overflow = true; return; }
-    const int j = a.nset++;
-    a.idx[j] = idx; a.k[j] = k; a.n[j] = n; a.inv[j] = inv;
-  }
-  sl_status launch(hipStream_t s) {
-    if (overflow) SL_FAIL(SL_ERR_SHAPE, "internal: more than %d inverse maps", IV_MAXSETS);
-    long long t = 0;
-    for (int j = 0; j < a.nset; ++j) { a.start[j] = t; t += (long long)a.nseq * a.n[j]; }
-    a.start[a.nset] = t;
-    if (t == 0) return SL_OK;
-    hipLaunchKernelGGL(inverse_sets_kernel, grid1d(t), dim3(256), 0, s, a);
     SL_HIP(hipGetLastError());
     return SL_OK;
   }
@@ -262,11 +244,6 @@ struct Layouter {
   }
 };
 
-inline sl_status inverse_maps(const int* idx, int k, int nseq, int Nfull, int* inv, hipStream_t s) {
-  Inverter iv(nseq);
-  iv.add(idx, k, Nfull, inv);
-  return iv.launch(s);
-}
 
 template <typename T>
 inline sl_status splitk_reduce(const SeqTab& st, const float* part, int ks, int N, void* out,

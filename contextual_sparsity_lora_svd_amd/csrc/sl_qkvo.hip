@@ -322,19 +322,18 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
                reinterpret_cast<T*>(ws + g.w_BvTo)};
   float* dB[3] = {gr->dBq, gr->dBk, gr->dBv};
 
-  // query-channel sets; then one launch each for operand packing, row layout
-  // and the inverse maps of the channel sets
+  // query-channel sets; then one launch for operand packing with the inverse
+  // maps of the channel sets, and one for the row layout
   if (g.G > 1 && d_out && (rc = expand_set(g, idx_vo, g.kvo, idx_o, strm))) return rc;
   if (g.G > 1 && dq && (rc = expand_set(g, idx_qk, g.kqk, idx_q, strm))) return rc;
   Packer pk;
   pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
   Layouter L(st);
-  Inverter iv(st.nseq);
   if (d_out) {
     pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);          // Bo^T [rp, D]
     pk.copy(AoTp, rp, g.nq, rp, w->Ao, g.nq, g.nq, r, 1);  // Ao^T [nq, rp]
     add_compact(L, g.co, a, idx_o, ac, g.esz);
-    iv.add(idx_o, g.ko, g.nq, inv_o);
+    pk.inverse(inv_o, idx_o, g.ko, g.nq, st.nseq);
   }
   if (dq) {
     for (int j = 0; j < 3; ++j) {
@@ -344,12 +343,11 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
                 st.nseq);                                                    // B_j[S_j]^T per sequence
       pk.copy(BTo[j], c.n, r, c.n, Bl[j], r, r, c.n, 1);                     // B_j^T
       add_compact(L, c, dsrc[j], sets[j], dcomp[j], g.esz);
-      iv.add(sets[j], c.kc, c.n, inv[j]);
+      pk.inverse(inv[j], sets[j], c.kc, c.n, st.nseq);
     }
   }
   if ((rc = pk.launch<T>(strm))) return rc;
   if ((rc = L.launch<T>(strm))) return rc;
-  if ((rc = iv.launch(strm))) return rc;
   ColredBatch cb(st, g.esz, crp, g.cr_floats);
 
   if (d_out) {

@@ -1183,30 +1183,6 @@ static __global__ void finish_scatter_kernel(const FinishScatterArgs a) {
   else a.out[(long long)c * a.r + q] = s;
 }
 
-// Inverse maps of up to IV_MAXSETS channel sets in one launch:
-// inv_j[g][c] = position of channel c in the ascending set idx_j[g], or -1.
-constexpr int IV_MAXSETS = 4;
-struct InvArgs {
-  int nset, nseq;
-  const int* idx[IV_MAXSETS];
-  int k[IV_MAXSETS], n[IV_MAXSETS];
-  int* inv[IV_MAXSETS];
-  long long start[IV_MAXSETS + 1];
-};
-static __global__ void inverse_sets_kernel(const InvArgs a) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.start[a.nset]) return;
-  int j = 0;
-  while (j + 1 < a.nset && a.start[j + 1] <= i) ++j;
-  const long long e = i - a.start[j];
-  const int n = a.n[j], k = a.k[j];
-  const int g = (int)(e / n), c = (int)(e % n);
-  const int* set = a.idx[j] + (long long)g * k;
-  int lo = 0, hi = k;
-  while (lo < hi) { const int mid = (lo + hi) >> 1; if (set[mid] < c) lo = mid + 1; else hi = mid; }
-  a.inv[j][e] = (lo < k && set[lo] == c) ? lo : -1;
-}
-
 // ===========================================================================
 // Packing of the LoRA operands in one launch.  Each job writes a whole
 // destination region (padding included):
@@ -1215,6 +1191,8 @@ static __global__ void inverse_sets_kernel(const InvArgs a) {
 //   type 1:  per context group g: dst[g][q][p] = src(q, idx[g][p]) for q < src_rows,
 //            p < k, 0 elsewhere; src(q, c) = src[q*lds + c] or, transposed, src[c*lds + q]
 //   type 2:  int32 dst[p] = p for p < cols (identity rows)
+//   type 3:  int32 inverse map of an ascending channel set, per context group g:
+//            dst[g][c] = position of channel c in idx[g][0..k), or -1, c < cols
 // ===========================================================================
 constexpr int PK_MAXJOBS = 16;
 
@@ -1245,6 +1223,14 @@ __global__ void pack_kernel(const PackArgs a) {
   T* dst = reinterpret_cast<T*>(b.dst);
   if (b.type == 2) {
     reinterpret_cast<int*>(b.dst)[e] = (int)e;
+    return;
+  }
+  if (b.type == 3) {
+    const int g = (int)(e / b.cols), c = (int)(e % b.cols);
+    const int* set = b.idx + (long long)g * b.k;
+    int lo = 0, hi = b.k;
+    while (lo < hi) { const int mid = (lo + hi) >> 1; if (set[mid] < c) lo = mid + 1; else hi = mid; }
+    reinterpret_cast<int*>(b.dst)[e] = (lo < b.k && set[lo] == c) ? lo : -1;
     return;
   }
   if (b.type == 0) {

@@ -353,8 +353,24 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     u.col0 = rp;
     if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
-  // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au
+  // LoRA factor gradients (one reduction launch, one finish launch) on the
+  // side stream: they read only what is ready now and write their own
+  // buffers, so they overlap the dX product below.
+  // dAg, dAu = dz^T X;  dBd = s dY^T z_d;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u;
+  // dAd[:, S] = dz_d^T H
+  SideFork fork;
+  if ((rc = fork.begin(strm))) return rc;
   {
+    ColredBatch cb(st, g.esz, crp, g.cr_floats);
+    cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
+    cb.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
+    cb.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
+    cb.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
+    cb.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
+    if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
+  }
+  // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au
+  auto dx = [&]() -> sl_status {
     GemmArgs a;
     std::memset(&a, 0, sizeof(a));
     a.st = st;
@@ -371,21 +387,11 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.part = part;
     a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DX_BWD)));
-    if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
-  }
-  // LoRA factor gradients (one reduction launch, one finish launch):
-  // dAg, dAu = dz^T X;  dBd = s dY^T z_d;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u;
-  // dAd[:, S] = dz_d^T H
-  {
-    ColredBatch cb(st, g.esz, crp, g.cr_floats);
-    cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
-    cb.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
-    cb.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
-    cb.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
-    cb.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
-    if ((rc = cb.launch<T>(strm))) return rc;
-  }
-  return SL_OK;
+    return splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm);
+  };
+  rc = dx();
+  const sl_status rj = fork.end(strm);   // joined on every path
+  return rc != SL_OK ? rc : rj;
 }
 
 }  // namespace

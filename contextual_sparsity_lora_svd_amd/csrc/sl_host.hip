@@ -2,6 +2,7 @@
 #include "sl_host.hpp"
 #include "sl_gemm.hpp"
 
+#include <mutex>
 #include <vector>
 
 namespace sl {
@@ -44,6 +45,36 @@ sl_status check_arch() {
             prop.gcnArchName);
   return SL_OK;
 }
+
+namespace {
+std::mutex g_side_mu;
+hipStream_t g_side[64] = {};
+
+// One event, recorded on `from` and waited for on `to`; released once done.
+sl_status link_streams(hipStream_t from, hipStream_t to) {
+  hipEvent_t ev;
+  SL_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  hipError_t e = hipEventRecord(ev, from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
+  (void)hipEventDestroy(ev);   // released by the runtime once the record completes
+  SL_HIP(e);
+  return SL_OK;
+}
+}  // namespace
+
+sl_status SideFork::begin(hipStream_t main) {
+  int dev = 0;
+  SL_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) SL_FAIL(SL_ERR_HIP, "device %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    if (!g_side[dev]) SL_HIP(hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking));
+    side = g_side[dev];
+  }
+  return link_streams(main, side);
+}
+
+sl_status SideFork::end(hipStream_t main) { return link_streams(side, main); }
 
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   if (!lay) SL_FAIL(SL_ERR_NULL, "layout is NULL");

@@ -48,6 +48,18 @@ struct Bump {
   }
 };
 
+// Fork and join with a side stream, for work of a call that does not depend on
+// the launches it may overlap.  The side stream is created once per device
+// (default priority, non-blocking) and shared by all calls; each fork and join
+// records an event of its own.  begin(): the side stream waits for everything
+// enqueued on `main` so far.  end(): `main` waits for everything enqueued on
+// the side stream so far, so the call's work is again ordered on `main`.
+struct SideFork {
+  hipStream_t side = nullptr;
+  sl_status begin(hipStream_t main);
+  sl_status end(hipStream_t main);
+};
+
 // Optional per-launch timing: when enabled (sl_timer_enable), selected launches
 // are bracketed by HIP events on their stream and attributed to a slot.
 enum TimerSlot {

@@ -412,25 +412,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       if ((rc = launch_skinny<T>(sa, strm))) return rc;
       j0 = j;
     }
-    // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
-    GemmArgs ga;
-    std::memset(&ga, 0, sizeof(ga));
-    ga.st = st;
-    ga.kidx = 1; ga.n_out = 1;
-    ga.N = D;
-    ga.nseg = 4;
-    for (int j = 0; j < 3; ++j) {
-      const Comp& c = *cc[j];
-      ga.seg[j] = GSeg{dcomp[j], c.ld, c.n, c.out_off, 0, Wm[j], nullptr, D, 1, 0, sets[j], c.kc, c.n};
-      if (qq) { ga.seg[j].Bs = Ws[j]; ga.seg[j].bq4 = 1; }
-    }
-    ga.seg[3] = GSeg{dzs, 3 * rp, 0, 0, 1, Aqkvp, nullptr, D, 0, 3 * rp, nullptr, 0, 0};
-    ga.ksplit_out = g.ks_dx;
-    ga.o0 = dX; ga.ldo = D;
-    ga.part = part;
-    ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
-    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
-    if ((rc = splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm))) return rc;
     // dAq, dAk = dz^T X (one pass for q and k), dAv
     cb.dense(X, D, D, dz, 3 * rp, 0, 2 * rp, gr->dAq, r, 1, gr->dAk, r, 1, rp, 1.f);
     cb.dense(X, D, D, dz, 3 * rp, 2 * rp, rp, gr->dAv, r, 1, nullptr, 0, 0, 0, 1.f);
@@ -439,8 +420,38 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       const Comp& c = *cc[j];
       cb.scatter(dcomp[j], c.ld, c.n, c.out_off, c.kc, c.n, zqkv, 3 * rp, j * rp, rp, inv[j], dB[j], r, 0, s);
     }
+    // the factor gradients (one reduction launch, one finish launch) on the
+    // side stream: they read only what is ready now and write their own
+    // buffers, so they overlap the dX product below
+    SideFork fork;
+    if ((rc = fork.begin(strm))) return rc;
+    if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
+    // dX = dq Wq[Sq] + dk Wk[Sk] + dv Wv[Sv] + dz [Aq; Ak; Av]
+    auto dxq = [&]() -> sl_status {
+      GemmArgs ga;
+      std::memset(&ga, 0, sizeof(ga));
+      ga.st = st;
+      ga.kidx = 1; ga.n_out = 1;
+      ga.N = D;
+      ga.nseg = 4;
+      for (int j = 0; j < 3; ++j) {
+        const Comp& c = *cc[j];
+        ga.seg[j] = GSeg{dcomp[j], c.ld, c.n, c.out_off, 0, Wm[j], nullptr, D, 1, 0, sets[j], c.kc, c.n};
+        if (qq) { ga.seg[j].Bs = Ws[j]; ga.seg[j].bq4 = 1; }
+      }
+      ga.seg[3] = GSeg{dzs, 3 * rp, 0, 0, 1, Aqkvp, nullptr, D, 0, 3 * rp, nullptr, 0, 0};
+      ga.ksplit_out = g.ks_dx;
+      ga.o0 = dX; ga.ldo = D;
+      ga.part = part;
+      ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
+      SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
+      return splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm);
+    };
+    rc = dxq();
+    const sl_status rj = fork.end(strm);   // joined on every path
+    return rc != SL_OK ? rc : rj;
   }
-  // the factor gradients: one reduction launch and one finish launch
+  // the factor gradients of o alone: one reduction launch and one finish launch
   return cb.launch<T>(strm);
 }
 

@@ -33,6 +33,10 @@
  *     No pointer is kept after a call returns.
  *   - All work is enqueued on `stream` (a hipStream_t, NULL = default stream).
  *     Calls never synchronise, except sl_build_estimator (documented there).
+ *     The backward calls run their LoRA factor-gradient reductions on a side
+ *     stream (one per device, created at first use, default priority), forked
+ *     from and joined back to `stream` with events: the call's work completes
+ *     in order on `stream` as if it had all been enqueued there.
  *   - Every argument is validated on the host before anything is launched.  On
  *     error nothing is launched, the status says which class of error, and
  *     sl_last_error() (thread-local) holds a message.  Launch failures map to

@@ -358,6 +358,9 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   // buffers, so they overlap the dX product below.
   // dAg, dAu = dz^T X;  dBd = s dY^T z_d;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u;
   // dAd[:, S] = dz_d^T H
+  // (an optional timing event for the dX product goes before the fork, so that
+  // the product and the side work become ready together)
+  timer_begin(TS_DX_BWD, strm);
   SideFork fork;
   if ((rc = fork.begin(strm))) return rc;
   {
@@ -386,7 +389,8 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.o0 = dX; a.ldo = D;
     a.part = part;
     a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
-    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DX_BWD)));
+    SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, -1)));
+    timer_end(TS_DX_BWD, strm);
     return splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm);
   };
   rc = dx();

@@ -119,6 +119,7 @@ static int g_pending_slot = -1;
 bool timer_on() { return g_timer.on; }
 
 void timer_begin(int slot, hipStream_t s) {
+  if (slot < 0) return;   // untimed launch: leaves a pending measurement alone
   if (!g_timer.on || !((g_timer.mask >> slot) & 1u) || 2 * (g_timer.used + 1) > g_timer.ev.size()) {
     g_pending_slot = -1;
     return;
@@ -128,7 +129,7 @@ void timer_begin(int slot, hipStream_t s) {
 }
 
 void timer_end(int slot, hipStream_t s) {
-  if (!g_timer.on || g_pending_slot != slot) return;
+  if (slot < 0 || !g_timer.on || g_pending_slot != slot) return;
   hipEventRecord(g_timer.ev[2 * g_timer.used + 1], s);
   g_timer.slot[g_timer.used] = slot;
   ++g_timer.used;

@@ -423,6 +423,9 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     // the factor gradients (one reduction launch, one finish launch) on the
     // side stream: they read only what is ready now and write their own
     // buffers, so they overlap the dX product below
+    // (an optional timing event for the dX product goes before the fork, so
+    // that the product and the side work become ready together)
+    timer_begin(TS_DXQKV_BWD, strm);
     SideFork fork;
     if ((rc = fork.begin(strm))) return rc;
     if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
@@ -444,7 +447,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       ga.o0 = dX; ga.ldo = D;
       ga.part = part;
       ga.iota = reinterpret_cast<const int*>(ws + g.w_iota);
-      SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, TS_DXQKV_BWD)));
+      SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(ga, strm, -1)));
+      timer_end(TS_DXQKV_BWD, strm);
       return splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm);
     };
     rc = dxq();

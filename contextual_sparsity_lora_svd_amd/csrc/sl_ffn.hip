@@ -180,7 +180,10 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
   // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
-  // Adg[g] = Ad[:, S_g] (gathered per context group); one launch.
+  // Adg[g] = Ad[:, S_g] (gathered per context group); one launch, on the side
+  // stream: it overlaps the z product below, which does not read them.
+  SideFork fork;
+  if ((rc = fork.begin(strm))) return rc;
   {
     Packer pk;
     pk.copy(Pg, 2 * rp, F, 2 * rp, w->Bg, r, F, r, 0);
@@ -188,11 +191,10 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
     pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
-    if ((rc = pk.launch<T>(strm))) return rc;
+    rc = pk.launch<T>(fork.side);
   }
-
   // z = X [Ag; Au]^T  (fp32 saved, s*z in T for the GEMM)
-  {
+  if (rc == SL_OK) {
     SkinnyArgs a;
     std::memset(&a, 0, sizeof(a));
     a.st = st; a.mode = 0; a.T = g.T;
@@ -203,7 +205,12 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.out = zgu; a.ldo = 2 * rp; a.col0 = 0; a.oscale = 1.f;
     a.outs = zs_gu; a.ldos = 2 * rp; a.scale = s;
     a.part = skp;
-    if ((rc = launch_skinny<T>(a, strm))) return rc;
+    rc = launch_skinny<T>(a, strm);
+  }
+  {
+    const sl_status rj = fork.end(strm);   // joined on every path
+    if (rc != SL_OK) return rc;
+    if (rj != SL_OK) return rj;
   }
   // G, U, H on the selected channels (context) / all channels (output rows)
   {

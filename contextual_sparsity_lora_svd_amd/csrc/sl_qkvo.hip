@@ -213,10 +213,13 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
               st.nseq);                                             // Ao[:, So] per sequence
     add_compact(L, g.co, a, idx_o, ac, g.esz);
   }
-  if ((rc = pk.launch<T>(strm))) return rc;
-  if ((rc = L.launch<T>(strm))) return rc;
-
-  if (X) {
+  // packing and row layout on the side stream: they overlap the z product
+  // below, which reads neither
+  SideFork fork;
+  if ((rc = fork.begin(strm))) return rc;
+  rc = pk.launch<T>(fork.side);
+  if (rc == SL_OK) rc = L.launch<T>(fork.side);
+  if (rc == SL_OK && X) {
     // z = X [Aq; Ak; Av]^T
     SkinnyArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -229,7 +232,14 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.out = zqkv; sa.ldo = 3 * rp; sa.oscale = 1.f;
     sa.outs = zs_qkv; sa.ldos = 3 * rp; sa.scale = s;
     sa.part = skp;
-    if ((rc = launch_skinny<T>(sa, strm))) return rc;
+    rc = launch_skinny<T>(sa, strm);
+  }
+  {
+    const sl_status rj = fork.end(strm);   // joined on every path
+    if (rc != SL_OK) return rc;
+    if (rj != SL_OK) return rj;
+  }
+  if (X) {
     // the three projections in one launch: y_j = X W_j[S_j]^T + (s z_j) B_j[S_j]^T
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));

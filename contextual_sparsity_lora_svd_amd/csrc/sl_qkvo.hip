@@ -357,13 +357,12 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     }
   }
   if ((rc = pk.launch<T>(strm))) return rc;
-  if ((rc = L.launch<T>(strm))) return rc;
   ColredBatch cb(st, g.esz, crp, g.cr_floats);
-
-  if (d_out) {
-    float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
-    T* dzs_o = reinterpret_cast<T*>(ws + g.w_dzs_o);
-    // dz_o = s d_out Bo
+  float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
+  T* dzs_o = reinterpret_cast<T*>(ws + g.w_dzs_o);
+  // the o-branch products: dz_o = s d_out Bo, then da on So (dense at output
+  // rows, 0 at the other context columns)
+  auto o_branch = [&]() -> sl_status {
     SkinnyArgs sa;
     std::memset(&sa, 0, sizeof(sa));
     sa.st = st; sa.mode = 0; sa.T = g.T;
@@ -373,8 +372,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     sa.out = dz_o; sa.ldo = rp; sa.oscale = s;
     sa.outs = dzs_o; sa.ldos = rp; sa.scale = s;
     sa.part = skp;
-    if ((rc = launch_skinny<T>(sa, strm))) return rc;
-    // da on So (dense at output rows), 0 at the other context columns
+    sl_status st_ = launch_skinny<T>(sa, strm);
+    if (st_ != SL_OK) return st_;
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.st = st;
@@ -386,6 +385,20 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     ga.o0 = da; ga.ldo = g.nq; ga.swidth = g.nq;
     ga.rpart = reinterpret_cast<float*>(ws + g.w_rp);
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
+    return SL_OK;
+  };
+  // the row layout (compact a and dq / dk / dv) on the side stream: the
+  // o-branch reads neither, so the two overlap
+  {
+    SideFork lay;
+    if ((rc = lay.begin(strm))) return rc;
+    rc = L.launch<T>(lay.side);
+    if (rc == SL_OK && d_out) rc = o_branch();
+    const sl_status rj = lay.end(strm);   // joined on every path
+    if (rc != SL_OK) return rc;
+    if (rj != SL_OK) return rj;
+  }
+  if (d_out) {
     // dAo = dz_o^T a_m (scattered into So), dBo = s d_out^T z_o
     cb.scatter(ac, g.co.ld, g.co.n, g.co.out_off, g.co.kc, g.co.n, dz_o, rp, 0, rp, inv_o, gr->dAo, r, 1, 1.f);
     cb.dense(d_out, D, D, zo, rp, 0, rp, gr->dBo, r, 0, nullptr, 0, 0, 0, s);

@@ -225,3 +225,35 @@ def test_cfg2_full_size_parity():
     use = np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
     errs = _compare(p, ctx, w.seq_len, use, "bf16")
     print(f"exact sets {n_exact}/{len(ctx)}", flush=True)
+
+
+def test_backward_ordered_on_caller_stream():
+    """The backward forks its gradient reductions onto a side stream and joins
+    them back: on a stream of the caller's, work enqueued right after the call
+    (a copy of every gradient, with no synchronisation in between) sees the
+    final values, and the results equal those of the default stream bit for
+    bit.  Repeated calls on one buffer set keep the same values."""
+    sl = _api()
+    D, F, r, L = 512, 1104, 16, 300
+    ctx = [290, 200, 300]
+    p = _ffn_case(D, F, r, ctx, L, "bf16", seed=17)
+    rng = np.random.default_rng(18)
+    idx = np.stack([np.sort(rng.choice(F, 300, replace=False)) for _ in ctx]).astype(np.int32)
+    w = _dev_weights(p, "bf16", 1.0)
+    lay = sl.Layout(ctx, L)
+    X, dY = to_dev(p["X"], "bf16"), to_dev(p["dY"], "bf16")
+    idx_d = torch.from_numpy(idx).cuda()
+    _, buf = sl.ffn_fwd(w, X, lay, 300, idx_d)
+    ref = {n: v.clone() for n, v in sl.ffn_bwd(w, X, lay, 300, idx_d, buf, dY).items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    copies = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            sl.ffn_fwd(w, X, lay, 300, idx_d, buf)
+            g = sl.ffn_bwd(w, X, lay, 300, idx_d, buf, dY)
+            copies.append({n: v.clone() for n, v in g.items()})   # same stream, no sync
+    s.synchronize()
+    for c in copies:
+        for n, v in ref.items():
+            assert torch.equal(c[n], v), f"{n} differs on the caller's stream"

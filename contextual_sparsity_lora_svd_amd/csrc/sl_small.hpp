@@ -543,11 +543,12 @@ score_swiglu_kernel(const SwiArgs a) {
     zs[t * LDZ + c] = (t < nt && q < a.rank) ? zb[(long long)t * a.ldz + (pj ? a.zc1 : a.zc0) + q] : 0.f;
   }
   __syncthreads();
-  const int ntile = (nt + 31) / 32;
+  // Software pipeline over the chunk's SW_CHUNK / 32 tiles: tile t+1's
+  // products are issued before tile t's SiLU, so the matrix cores work while
+  // the VALU evaluates (sched_barrier keeps that order).  Tiles past the
+  // context hold zero rows and add exactly 0.
   float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-  for (int tt = 0; tt < SW_CHUNK / 32; ++tt) {
-    if (tt >= ntile) break;   // uniform
+  auto mm = [&](int tt, f32x16_s& g, f32x16_s& u) {
     const float* zr = &zs[(tt * 32 + (lane & 31)) * LDZ + h * KH];
     float ag[KH], au[KH];
 #pragma unroll
@@ -557,12 +558,15 @@ score_swiglu_kernel(const SwiArgs a) {
       ag[s] = x.x; ag[s + 1] = x.y; ag[s + 2] = x.z; ag[s + 3] = x.w;
       au[s] = y.x; au[s + 1] = y.y; au[s + 2] = y.z; au[s + 3] = y.w;
     }
-    f32x16_s g = {}, u = {};
+    g = f32x16_s{};
+    u = f32x16_s{};
 #pragma unroll
     for (int s = 0; s < KH; ++s) {
       g = __builtin_amdgcn_mfma_f32_32x32x2f32(ag[s], bg[s], g, 0, 0, 0);
       u = __builtin_amdgcn_mfma_f32_32x32x2f32(au[s], bu[s], u, 0, 0, 0);
     }
+  };
+  auto act = [&](const f32x16_s& g, const f32x16_s& u) {
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
       const float h0 = g[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e])) * u[e];
@@ -570,7 +574,22 @@ score_swiglu_kernel(const SwiArgs a) {
       acc0 = fmaf(h0, h0, acc0);
       acc1 = fmaf(h1, h1, acc1);
     }
-  }
+  };
+  static_assert(SW_CHUNK / 32 == 4, "four tiles per chunk");
+  f32x16_s g0, u0, g1, u1;
+  mm(0, g0, u0);
+  mm(1, g1, u1);
+  __builtin_amdgcn_sched_barrier(0);
+  act(g0, u0);
+  __builtin_amdgcn_sched_barrier(0);
+  mm(2, g0, u0);
+  __builtin_amdgcn_sched_barrier(0);
+  act(g1, u1);
+  __builtin_amdgcn_sched_barrier(0);
+  mm(3, g1, u1);
+  __builtin_amdgcn_sched_barrier(0);
+  act(g0, u0);
+  act(g1, u1);
   float v = acc0 + acc1;
   v += __shfl_xor(v, 32, 64);
   if (h == 0 && n < a.N) a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = v;

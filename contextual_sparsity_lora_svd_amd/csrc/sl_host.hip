@@ -63,6 +63,14 @@ sl_status link_streams(hipStream_t from, hipStream_t to) {
 }  // namespace
 
 sl_status SideFork::begin(hipStream_t main) {
+  // a stream being captured into a graph keeps all of the call's work: the
+  // graph then needs no cross-stream events
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  SL_HIP(hipStreamIsCapturing(main, &cs));
+  if (cs != hipStreamCaptureStatusNone) {
+    side = main;
+    return SL_OK;
+  }
   int dev = 0;
   SL_HIP(hipGetDevice(&dev));
   if (dev < 0 || dev >= 64) SL_FAIL(SL_ERR_HIP, "device %d out of range", dev);
@@ -74,7 +82,7 @@ sl_status SideFork::begin(hipStream_t main) {
   return link_streams(main, side);
 }
 
-sl_status SideFork::end(hipStream_t main) { return link_streams(side, main); }
+sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_streams(side, main); }
 
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   if (!lay) SL_FAIL(SL_ERR_NULL, "layout is NULL");

@@ -54,6 +54,8 @@ struct Bump {
 // records an event of its own.  begin(): the side stream waits for everything
 // enqueued on `main` so far.  end(): `main` waits for everything enqueued on
 // the side stream so far, so the call's work is again ordered on `main`.
+// While `main` is being captured into a graph, begin() makes `side` = `main`
+// and both are no-ops: the captured work stays on one stream.
 struct SideFork {
   hipStream_t side = nullptr;
   sl_status begin(hipStream_t main);

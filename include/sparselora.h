@@ -36,7 +36,9 @@
  *     The backward calls run their LoRA factor-gradient reductions on a side
  *     stream (one per device, created at first use, default priority), forked
  *     from and joined back to `stream` with events: the call's work completes
- *     in order on `stream` as if it had all been enqueued there.
+ *     in order on `stream` as if it had all been enqueued there.  While
+ *     `stream` is being captured into a graph, all of the call's work stays on
+ *     it (the graph holds no cross-stream events).
  *   - Every argument is validated on the host before anything is launched.  On
  *     error nothing is launched, the status says which class of error, and
  *     sl_last_error() (thread-local) holds a message.  Launch failures map to

@@ -257,3 +257,47 @@ def test_backward_ordered_on_caller_stream():
     for c in copies:
         for n, v in ref.items():
             assert torch.equal(c[n], v), f"{n} differs on the caller's stream"
+
+
+def test_graph_capture_replays_match_eager():
+    """Forward and backward captured into one graph (the library's side stream
+    stays out of a capture): three replays, with eager work between them, each
+    equal bit for bit to the eager results."""
+    sl = _api()
+    D, F, r, L = 256, 688, 8, 200
+    ctx = [200, 37, 130]
+    p = _ffn_case(D, F, r, ctx, L, "bf16", seed=19)
+    rng = np.random.default_rng(20)
+    k = 344
+    idx = np.stack([np.sort(rng.choice(F, k, replace=False)) for _ in ctx]).astype(np.int32)
+    w = _dev_weights(p, "bf16", 0.5)
+    lay = sl.Layout(ctx, L)
+    X, dY = to_dev(p["X"], "bf16"), to_dev(p["dY"], "bf16")
+    idx_d = torch.from_numpy(idx).cuda()
+    buf = sl.FFNWorkspace(w, lay, k, X.device)
+    Y = torch.empty_like(X)
+    sl.ffn_fwd(w, X, lay, k, idx_d, buf, Y=Y)
+    out = sl.ffn_bwd(w, X, lay, k, idx_d, buf, dY)
+    torch.cuda.synchronize()
+    ref_y, ref = Y.clone(), {n: v.clone() for n, v in out.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sl.ffn_fwd(w, X, lay, k, idx_d, buf, Y=Y)
+        sl.ffn_bwd(w, X, lay, k, idx_d, buf, dY, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sl.ffn_fwd(w, X, lay, k, idx_d, buf, Y=Y)
+        sl.ffn_bwd(w, X, lay, k, idx_d, buf, dY, out=out)
+    for rep in range(3):
+        Y.zero_()
+        for v in out.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref_y), f"replay {rep}: Y"
+        for n, v in ref.items():
+            assert torch.equal(out[n], v), f"replay {rep}: {n}"

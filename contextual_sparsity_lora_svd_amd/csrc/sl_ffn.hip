@@ -29,8 +29,8 @@ struct FfnGeom {
   long long comp, c_out_off;
   int ks_down, ks_dx, RM1, RM2, chunk;
   long long cr_floats, skp_floats;
-  size_t s_zgu, s_zd, s_G, s_U, s_H, saved_bytes;
-  size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_BdTp, w_Adg, w_part, w_dz_d, w_dzs_d, w_AdTp, w_dG, w_dU,
+  size_t s_zgu, s_zd, s_G, s_U, s_H, s_BdT, s_AdT, saved_bytes;
+  size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_Adg, w_part, w_dz_d, w_dzs_d, w_dG, w_dU,
       w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp, w_rp,
       ws_bytes;
 };
@@ -82,19 +82,20 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.s_G = sv.take(g.comp * e);
   g.s_U = sv.take(g.comp * e);
   g.s_H = sv.take(g.comp * e);
+  // Bd^T and Ad^T, packed by the forward for the backward's first products
+  g.s_BdT = sv.take((size_t)g.rp * D * e);
+  g.s_AdT = sv.take((size_t)F * g.rp * e);
   g.saved_bytes = sv.off;
   Bump w;
   g.w_zs_gu = w.take(T * 2 * g.rp * e);
   g.w_zs_d = w.take(T * g.rp * e);
   g.w_Pg = w.take((size_t)F * 2 * g.rp * e);
   g.w_Pu = w.take((size_t)F * 2 * g.rp * e);
-  g.w_BdTp = w.take((size_t)g.rp * D * e);
   g.w_Adg = w.take((size_t)st.nseq * g.rp * g.ldk * e);
   const int ks = g.ks_down > g.ks_dx ? g.ks_down : g.ks_dx;
   g.w_part = w.take(ks > 1 ? (size_t)ks * st.T_out * D * 4 : 0);
   g.w_dz_d = w.take(T * g.rp * 4);
   g.w_dzs_d = w.take(T * g.rp * e);
-  g.w_AdTp = w.take((size_t)F * g.rp * e);
   g.w_dG = w.take(g.comp * e);
   g.w_dU = w.take(g.comp * e);
   g.w_Bgg = w.take((size_t)st.nseq * g.rp * g.ldk * e);
@@ -174,13 +175,15 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   T* zs_d = reinterpret_cast<T*>(ws + g.w_zs_d);
   T* Pg = reinterpret_cast<T*>(ws + g.w_Pg);
   T* Pu = reinterpret_cast<T*>(ws + g.w_Pu);
-  T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
+  T* BdTp = reinterpret_cast<T*>(sv + g.s_BdT);
+  T* AdTp = reinterpret_cast<T*>(sv + g.s_AdT);
   T* Adg = reinterpret_cast<T*>(ws + g.w_Adg);
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
   // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
-  // Adg[g] = Ad[:, S_g] (gathered per context group); one launch, on the side
+  // Adg[g] = Ad[:, S_g] (gathered per context group), and AdTp = Ad^T kept in
+  // the saved buffer for the backward; one launch, on the side
   // stream: it overlaps the z product below, which does not read them.
   SideFork fork;
   if ((rc = fork.begin(strm))) return rc;
@@ -189,6 +192,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(Pg, 2 * rp, F, 2 * rp, w->Bg, r, F, r, 0);
     pk.copy(Pu, 2 * rp, F, 2 * rp, w->Bu, r, F, r, 0, 0, rp);
     pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
+    pk.copy(AdTp, rp, F, rp, w->Ad, F, F, r, 1);
     pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
     rc = pk.launch<T>(fork.side);
@@ -279,7 +283,7 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* dz_d = reinterpret_cast<float*>(ws + g.w_dz_d);
   T* dzs_d = reinterpret_cast<T*>(ws + g.w_dzs_d);
-  T* AdTp = reinterpret_cast<T*>(ws + g.w_AdTp);
+  const T* AdTp = reinterpret_cast<const T*>(sv + g.s_AdT);   // packed by the forward
   T* dGc = reinterpret_cast<T*>(ws + g.w_dG);
   T* dUc = reinterpret_cast<T*>(ws + g.w_dU);
   T* Bgg = reinterpret_cast<T*>(ws + g.w_Bgg);
@@ -289,16 +293,18 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* dz_gu = reinterpret_cast<float*>(ws + g.w_dz_gu);
   T* dzs_gu = reinterpret_cast<T*>(ws + g.w_dzs_gu);
   T* Agup = reinterpret_cast<T*>(ws + g.w_Agup);
-  T* BdTp = reinterpret_cast<T*>(ws + g.w_BdTp);
+  const T* BdTp = reinterpret_cast<const T*>(sv + g.s_BdT);
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
-  // packed LoRA operands and the inverse map of the channel sets (one launch)
+  // packed LoRA operands and the inverse map of the channel sets (one launch),
+  // on the side stream: the next two products read only Bd^T and Ad^T, which
+  // the forward left in the saved buffer; joined before the dz_g / dz_u product
+  SideFork pack_fork;
+  if ((rc = pack_fork.begin(strm))) return rc;
   {
     Packer pk;
-    pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
-    pk.copy(AdTp, rp, F, rp, w->Ad, F, F, r, 1);
     pk.copy(Agup, D, rp, D, w->Ag, D, r, D, 0);
     pk.copy(Agup + (long long)rp * D, D, rp, D, w->Au, D, r, D, 0);
     pk.gather(Bgg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bg, r, r, 1, idx, g.k, st.nseq);
@@ -307,37 +313,48 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
     pk.inverse(inv, idx, g.k, F, st.nseq);
-    if ((rc = pk.launch<T>(strm))) return rc;
+    if ((rc = pk.launch<T>(pack_fork.side))) { (void)pack_fork.end(strm); return rc; }
   }
 
-  // dz_d = s dY Bd
+  // dz_d = s dY Bd, then dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
+  auto dz_d_dh = [&]() -> sl_status {
+    // dz_d = s dY Bd
+    {
+      SkinnyArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.st = st; a.mode = 0; a.T = g.T;
+      a.A = dY; a.lda = D; a.K = D;
+      a.nblk = 1;
+      a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
+      a.out = dz_d; a.ldo = rp; a.oscale = s;
+      a.outs = dzs_d; a.ldos = rp; a.scale = s;
+      a.part = skp;
+      const sl_status r1 = launch_skinny<T>(a, strm);
+      if (r1 != SL_OK) return r1;
+    }
+    // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
+    {
+      GemmArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.st = st;
+      a.idx = idx; a.kidx = g.k; a.n_out = F;
+      a.nseg = 2;
+      a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
+      set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
+      a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
+      a.o0 = dGc; a.o1 = dUc;
+      a.i0 = Gc; a.i1 = Uc;
+      a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
+      a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
+      SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
+    }
+    return SL_OK;
+  };
+  rc = dz_d_dh();
   {
-    SkinnyArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.st = st; a.mode = 0; a.T = g.T;
-    a.A = dY; a.lda = D; a.K = D;
-    a.nblk = 1;
-    a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
-    a.out = dz_d; a.ldo = rp; a.oscale = s;
-    a.outs = dzs_d; a.ldos = rp; a.scale = s;
-    a.part = skp;
-    if ((rc = launch_skinny<T>(a, strm))) return rc;
-  }
-  // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
-  {
-    GemmArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.st = st;
-    a.idx = idx; a.kidx = g.k; a.n_out = F;
-    a.nseg = 2;
-    a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
-    set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
-    a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
-    a.o0 = dGc; a.o1 = dUc;
-    a.i0 = Gc; a.i1 = Uc;
-    a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
-    a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
-    SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
+    const sl_status rj = pack_fork.end(strm);   // joined on every path
+    if (rc != SL_OK) return rc;
+    if (rj != SL_OK) return rj;
   }
   // dz_g = s dG Bg[S], dz_u = s dU Bu[S]: one launch, two problems
   {

@@ -92,11 +92,12 @@ def test_size_queries_follow_the_layout(sl):
     s_big = L.sl_ffn_saved_bytes(1, lay.ref, 64, 128, 4, 64)
     assert 0 < s_small < s_big
     # saved = z (fp32, T x 2rp) + z_d (T x rp) + G, U, H compact (bf16)
-    T, rp = 8, 8
+    #         + Bd^T (rp x d_model) + Ad^T (d_ff x rp), bf16, packed for the backward
+    T, rp, D, F = 8, 8, 64, 128
     comp = 3 * 8 + 1 * 128     # 3 context rows x ldk(8) + 1 output row x d_ff
     def up(x):
         return (x + 255) // 256 * 256
-    expect = up(T * 2 * rp * 4) + up(T * rp * 4) + 3 * up(comp * 2)
+    expect = up(T * 2 * rp * 4) + up(T * rp * 4) + 3 * up(comp * 2) + up(rp * D * 2) + up(F * rp * 2)
     assert s_small == expect
     assert L.sl_ffn_workspace_bytes(1, lay.ref, 64, 128, 4, 0) == 0   # invalid k
     assert L.sl_estimator_workspace_bytes(100, 50, 65) == 0

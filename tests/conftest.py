@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) where no GPU is visible; on a GPU machine
+    # GPU tests are skipped (not failed) where no GPU is visible; on a machine with a GPU
     # they run and must find the built library.
     try:
         import torch

@@ -347,7 +347,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; sharding by sequence across GPUs is a design "
+        print("bench.py: the benchmark measures one GPU; sharding by sequence across GPUs is a design "
               "note, not built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

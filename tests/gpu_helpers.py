@@ -51,16 +51,18 @@ def factors(W: np.ndarray, rank: int, dt: str):
 
 def check_selection(gpu_idx: np.ndarray, ora_scores: np.ndarray, k: int):
     """Index sets must be bit-exact wherever the k-th and (k+1)-th oracle scores
-    differ by more than GAP relative; otherwise the GPU set must be a valid
-    top-k of the oracle scores within that gap.  Returns the number of
+    differ by more than GAP relative.  Otherwise the GPU set must be a top-k of
+    the oracle scores up to GAP: it holds every channel whose oracle score
+    exceeds s_k (1 + GAP), and every channel it holds scores at least
+    s_k (1 - GAP) (s_k = the k-th largest oracle score).  Returns the number of
     sequences compared exactly."""
     B, N = ora_scores.shape
     exact = 0
     for b in range(B):
         g = np.asarray(gpu_idx[b])
-        assert len(np.unique(g)) == k, "indices not distinct"
-        assert np.all(np.diff(g) > 0), "indices not ascending"
-        assert g.min() >= 0 and g.max() < N
+        assert len(g) == k and len(np.unique(g)) == k, f"seq {b}: indices not k distinct"
+        assert np.all(np.diff(g) > 0), f"seq {b}: indices not ascending"
+        assert g.min() >= 0 and g.max() < N, f"seq {b}: index out of range"
         s = ora_scores[b].astype(np.float64)
         ref = O.select_topk(ora_scores[b], k)
         if k == N:
@@ -73,9 +75,19 @@ def check_selection(gpu_idx: np.ndarray, ora_scores: np.ndarray, k: int):
             assert np.array_equal(g, ref), f"seq {b}: index set differs with gap {(sk - sk1) / sk:.2e}"
             exact += 1
         else:
-            # valid within the gap: every chosen score is >= the (k+1)-th up to GAP
-            assert s[g].min() >= sk1 * (1 - GAP) - 1e-30, f"seq {b}: chosen score below threshold"
+            must = np.nonzero(s > sk * (1 + GAP))[0]
+            missing = np.setdiff1d(must, g)
+            assert missing.size == 0, f"seq {b}: channels {missing[:8].tolist()} above s_k (1 + GAP) not chosen"
+            assert s[g].min() >= sk * (1 - GAP) - 1e-30, f"seq {b}: a chosen score is below s_k (1 - GAP)"
     return exact
+
+
+def check_scores(gpu_scores: np.ndarray, ora_scores: np.ndarray, tol: float, what: str = "scores"):
+    """Per sequence, max |gpu - oracle| / max(oracle) <= tol."""
+    for b in range(ora_scores.shape[0]):
+        den = max(float(np.abs(ora_scores[b]).max()), 1e-30)
+        e = float(np.abs(np.asarray(gpu_scores[b], np.float64) - ora_scores[b]).max()) / den
+        assert e <= tol, f"{what}: seq {b} relative error {e:.2e} > {tol:.0e}"
 
 
 @contextlib.contextmanager

@@ -5,7 +5,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_helpers import (assert_close, check_selection, factors, gemm_variant, rel_err, to_dev,
+from tests.gpu_helpers import (assert_close, check_scores, check_selection, factors, gemm_variant, rel_err, to_dev,
                                to_np)
 
 pytestmark = pytest.mark.gpu
@@ -205,6 +205,7 @@ def test_cfg1_workload_end_to_end():
     Pu, Qu = factors(p["Wu"], w.est_rank, "f32")
     idx, sc = _estimate(p, ctx, w.seq_len, Pg, Qg, Pu, Qu, w.est_rank, k, "f32")
     ref = _oracle_scores(p, ctx, w.seq_len, Pg, Qg, Pu, Qu)
+    check_scores(sc, ref, 1e-4, "SwiGLU scores")
     n_exact = check_selection(idx, ref, k)
     use = idx if n_exact == len(ctx) else np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
     _compare(p, ctx, w.seq_len, use, "f32")
@@ -221,6 +222,7 @@ def test_cfg2_full_size_parity():
     Pu, Qu = factors(p["Wu"], w.est_rank, "bf16")
     idx, sc = _estimate(p, ctx, w.seq_len, Pg, Qg, Pu, Qu, w.est_rank, k, "bf16")
     ref = _oracle_scores(p, ctx, w.seq_len, Pg, Qg, Pu, Qu)
+    check_scores(sc, ref, 1e-4, "SwiGLU scores")
     n_exact = check_selection(idx, ref, k)
     use = np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
     errs = _compare(p, ctx, w.seq_len, use, "bf16")

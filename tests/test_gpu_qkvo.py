@@ -5,7 +5,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_helpers import assert_close, check_selection, factors, to_dev, to_np
+from tests.gpu_helpers import assert_close, check_scores, check_selection, factors, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -292,16 +292,21 @@ def test_full_size_workloads(cfg):
     Pv, Qv = factors(p["Wv"], wl.est_rank, "bf16")
     lay = sl.Layout(ctx, L)
     X = to_dev(p["X"], "bf16")
-    idx, _ = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, wl.est_rank, to_dev(Pq, "bf16"),
-                                to_dev(Qq, "bf16"), to_dev(Pk, "bf16"), to_dev(Qk, "bf16"), nkv, kqk,
-                                heads=heads)
+    idx, sc = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, wl.est_rank, to_dev(Pq, "bf16"),
+                                 to_dev(Qq, "bf16"), to_dev(Pk, "bf16"), to_dev(Qk, "bf16"), nkv, kqk,
+                                 heads=heads, want_scores=True)
+    idx_vo, sc_vo = sl.estimate_select(sl.SL_CRIT_L2, X, lay, wl.est_rank, to_dev(Pv, "bf16"),
+                                       to_dev(Qv, "bf16"), None, None, nkv, kvo, want_scores=True)
     torch.cuda.synchronize()
     ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    check_scores(sc.cpu().numpy(), ref_qk, 2e-4, "QK-norm scores")
+    check_scores(sc_vo.cpu().numpy(), ref_vo, 1e-4, "L2 scores")
     n_exact = check_selection(idx.cpu().numpy(), ref_qk, kqk)
+    n_vo = check_selection(idx_vo.cpu().numpy(), ref_vo, kvo)
     iqk = np.stack([O.select_topk(ref_qk[b], kqk) for b in range(len(ctx))])
     ivo = np.stack([O.select_topk(ref_vo[b], kvo) for b in range(len(ctx))])
     _compare(p, heads, ctx, L, iqk, ivo, "bf16", s=1.0)
-    print(f"exact qk sets {n_exact}/{len(ctx)}", flush=True)
+    print(f"exact qk sets {n_exact}/{len(ctx)}, vo sets {n_vo}/{len(ctx)}", flush=True)
 
 
 def test_side_stream_ordering_and_graph_capture():

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_helpers import check_selection, factors, to_dev
+from tests.gpu_helpers import check_scores, check_selection, factors, to_dev
 from tests.test_gpu_ffn import _compare as ffn_compare
 from tests.test_gpu_ffn import _estimate as ffn_estimate
 from tests.test_gpu_ffn import _oracle_scores as ffn_scores
@@ -44,8 +44,9 @@ def _ffn_layer(wl, layer):
     else:
         Pg, Qg = factors(p["Wg"], wl.est_rank, "bf16")
         Pu, Qu = factors(p["Wu"], wl.est_rank, "bf16")
-        idx, _ = ffn_estimate(p, ctx, L, Pg, Qg, Pu, Qu, wl.est_rank, k, "bf16")
+        idx, sc = ffn_estimate(p, ctx, L, Pg, Qg, Pu, Qu, wl.est_rank, k, "bf16")
         ref = ffn_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+        check_scores(sc, ref, 1e-4, "SwiGLU scores")
         n_exact = check_selection(idx, ref, k)
         print(f"exact sets {n_exact}/{len(ctx)}", flush=True)
         use = np.stack([O.select_topk(ref[b], k) for b in range(len(ctx))])
@@ -84,13 +85,15 @@ def _qkvo_layer(wl, layer):
     Pv, Qv = factors(p["Wv"], wl.est_rank, "bf16")
     lay = sl.Layout(ctx, L)
     X = to_dev(p["X"], "bf16")
-    idx_qk, _ = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, wl.est_rank, to_dev(Pq, "bf16"),
-                                   to_dev(Qq, "bf16"), to_dev(Pk, "bf16"), to_dev(Qk, "bf16"), nkv,
-                                   kqk, heads=heads)
-    idx_vo, _ = sl.estimate_select(sl.SL_CRIT_L2, X, lay, wl.est_rank, to_dev(Pv, "bf16"),
-                                   to_dev(Qv, "bf16"), None, None, nkv, kvo)
+    idx_qk, sc_qk = sl.estimate_select(sl.SL_CRIT_QK_NORM, X, lay, wl.est_rank, to_dev(Pq, "bf16"),
+                                       to_dev(Qq, "bf16"), to_dev(Pk, "bf16"), to_dev(Qk, "bf16"), nkv,
+                                       kqk, heads=heads, want_scores=True)
+    idx_vo, sc_vo = sl.estimate_select(sl.SL_CRIT_L2, X, lay, wl.est_rank, to_dev(Pv, "bf16"),
+                                       to_dev(Qv, "bf16"), None, None, nkv, kvo, want_scores=True)
     torch.cuda.synchronize()
     ref_qk, ref_vo = _qk_l2_oracle(p, ctx, L, heads, Pq, Qq, Pk, Qk, Pv, Qv)
+    check_scores(sc_qk.cpu().numpy(), ref_qk, 2e-4, "QK-norm scores")
+    check_scores(sc_vo.cpu().numpy(), ref_vo, 1e-4, "L2 scores")
     n1 = check_selection(idx_qk.cpu().numpy(), ref_qk, kqk)
     n2 = check_selection(idx_vo.cpu().numpy(), ref_vo, kvo)
     print(f"exact sets qk {n1}/{len(ctx)} vo {n2}/{len(ctx)}", flush=True)

@@ -412,3 +412,142 @@ def test_qkvo_zero_b_is_library_linear_and_masks_zero_context():
     np.testing.assert_allclose(out["q"][:3, keep], q_ref[:3, keep], atol=1e-12)
     drop = np.setdiff1d(np.arange(8), keep)
     assert np.abs(out["q"][:3, drop]).max() == 0
+
+
+# ------------------------------------------- q/k/v/o: zeroed-weights model
+# An independent statement of the masked q/k/v/o layer (SparseLoRA article
+# §一: q/k channels by the QK-norm, the rest by the L2 norm; SparseLoRA
+# abstract: loss and gradients on the selected subset).  For the context rows
+# of sequence b the sparse layer is the dense layer whose weights are
+# multiplied by 0/1 masks built here from the sets by explicit loops over
+# heads: rows of Wk, Bk outside S_qk; rows of Wq, Bq whose kv channel
+# (h // G, d) is outside S_qk; rows of Wv, Bv outside S_vo; columns of Wo, Ao
+# whose kv channel is outside S_vo.  Output rows use the unmasked weights.
+# Gradients come from torch autograd in float64 through the masked weights.
+_QKVO_PARAMS = ("Wq", "Wk", "Wv", "Wo", "Aq", "Bq", "Ak", "Bk", "Av", "Bv", "Ao", "Bo")
+
+
+def _qkvo_zeroed_model(p, ctx, L, idx_qk, idx_vo, heads, grads_in, s):
+    torch = pytest.importorskip("torch")
+    hq, hkv, hd = heads
+    G = hq // hkv
+    nq, nkv = hq * hd, hkv * hd
+    t = {n: torch.tensor(p[n], dtype=torch.float64, requires_grad=True)
+         for n in _QKVO_PARAMS + ("X", "a")}
+    outs = {n: [] for n in ("q", "k", "v", "o")}
+    loss = 0.0
+    row_groups = []
+    for b in range(len(ctx)):
+        rows = list(range(b * L, b * L + ctx[b]))
+        row_groups.append((rows, set(int(c) for c in idx_qk[b]), set(int(c) for c in idx_vo[b])))
+    out_rows = [r for b in range(len(ctx)) for r in range(b * L + ctx[b], (b + 1) * L)]
+    row_groups.append((out_rows, None, None))
+    order = []
+    for rows, sqk, svo in row_groups:
+        if not rows:
+            continue
+        order += rows
+        kq = torch.ones(nq, dtype=torch.float64)
+        kk = torch.ones(nkv, dtype=torch.float64)
+        kv = torch.ones(nkv, dtype=torch.float64)
+        ko = torch.ones(nq, dtype=torch.float64)
+        if sqk is not None:
+            for c in range(nkv):
+                kk[c] = 1.0 if c in sqk else 0.0
+                kv[c] = 1.0 if c in svo else 0.0
+            for h in range(hq):
+                for d in range(hd):
+                    kvch = (h // G) * hd + d
+                    kq[h * hd + d] = 1.0 if kvch in sqk else 0.0
+                    ko[h * hd + d] = 1.0 if kvch in svo else 0.0
+        Xr, ar = t["X"][rows], t["a"][rows]
+        q = Xr @ (t["Wq"] * kq[:, None]).T + s * (Xr @ t["Aq"].T) @ (t["Bq"] * kq[:, None]).T
+        k = Xr @ (t["Wk"] * kk[:, None]).T + s * (Xr @ t["Ak"].T) @ (t["Bk"] * kk[:, None]).T
+        v = Xr @ (t["Wv"] * kv[:, None]).T + s * (Xr @ t["Av"].T) @ (t["Bv"] * kv[:, None]).T
+        o = ar @ (t["Wo"] * ko[None, :]).T + s * (ar @ (t["Ao"] * ko[None, :]).T) @ t["Bo"].T
+        for n, val in (("q", q), ("k", k), ("v", v), ("o", o)):
+            outs[n].append(val)
+            gname = "d_out" if n == "o" else "d" + n
+            loss = loss + (val * torch.tensor(grads_in[gname][rows], dtype=torch.float64)).sum()
+    names = list(_QKVO_PARAMS) + ["X", "a"]
+    gr = torch.autograd.grad(loss, [t[n] for n in names])
+    inv = np.argsort(order)
+    fwd = {n: torch.cat(v, 0).detach().numpy()[inv] for n, v in outs.items()}
+    grad = {n: g.numpy() for n, g in zip(names, gr)}
+    return fwd, grad
+
+
+def _qkvo_pin_case():
+    rng = _rng(40)
+    heads = (4, 2, 3)                 # GQA: two query heads per kv head
+    D, r, L = 5, 2, 4
+    ctx = [4, 2]                      # one all-context sequence, one mixed
+    p = _tiny_attn(rng, D=D, hq=4, hkv=2, hd=3, r=r, T=len(ctx) * L)
+    nq, nkv = 12, 6
+    # q/k and v/o sets differ in every sequence, and differ between sequences
+    idx_qk = [np.array([0, 2, 4]), np.array([1, 3, 5])]
+    idx_vo = [np.array([1, 4]), np.array([0, 5])]
+    T = len(ctx) * L
+    grads_in = {"dq": rng.standard_normal((T, nq)), "dk": rng.standard_normal((T, nkv)),
+                "dv": rng.standard_normal((T, nkv)), "d_out": rng.standard_normal((T, D))}
+    return p, ctx, L, idx_qk, idx_vo, heads, grads_in
+
+
+def _qkvo_mismatch(p, ctx, L, idx_qk, idx_vo, heads, grads_in, s=0.7):
+    """Largest relative difference over every output and gradient between the
+    oracle and the zeroed-weights model."""
+    out, cache = O.qkvo_forward(p, ctx, L, idx_qk, idx_vo, heads, s)
+    g = O.qkvo_backward(p, cache, grads_in, s)
+    fwd, grad = _qkvo_zeroed_model(p, ctx, L, idx_qk, idx_vo, heads, grads_in, s)
+    pairs = [(out[n], fwd[n]) for n in ("q", "k", "v", "o")]
+    pairs += [(g["dX"], grad["X"]), (g["da"], grad["a"])]
+    for n in ("q", "k", "v", "o"):
+        pairs += [(g["dA" + n], grad["A" + n]), (g["dB" + n], grad["B" + n])]
+    worst = 0.0
+    for got, ref in pairs:
+        den = max(np.abs(ref).max(), 1e-300)
+        worst = max(worst, float(np.abs(got - ref).max() / den))
+    return worst
+
+
+def test_qkvo_mask_equals_zeroed_weights_model():
+    case = _qkvo_pin_case()
+    assert _qkvo_mismatch(*case) < 1e-12
+    # the frozen weights get no gradient: the model's gradients of W are not compared,
+    # and the oracle's da is zero in dropped columns of context rows
+    p, ctx, L, idx_qk, idx_vo, heads, gi = case
+    out, cache = O.qkvo_forward(p, ctx, L, idx_qk, idx_vo, heads, 0.7)
+    g = O.qkvo_backward(p, cache, gi, 0.7)
+    # seq 0 keeps kv channels {1, 4} = (head 0, d 1), (head 1, d 1) for o: query heads 0, 1
+    # read kv head 0 and heads 2, 3 kv head 1, so only query columns 1, 4, 7, 10 survive
+    assert np.abs(g["da"][0:4][:, [0, 2, 3, 5, 6, 8, 9, 11]]).max() == 0
+    assert np.abs(g["da"][0:4][:, [1, 4, 7, 10]]).min() > 0
+
+
+def _mutated_masks(kind):
+    real = O.attn_masks
+
+    def masks(ctx_len, seq_len, idx_qk, idx_vo, hq, hkv, hd):
+        mq, mk, mv, mo = real(ctx_len, seq_len, idx_qk, idx_vo, hq, hkv, hd)
+        if kind == "v_by_qk":
+            return mq, mk, mk, mo
+        if kind == "o_by_qk":
+            return mq, mk, mv, mq
+        if kind == "k_by_vo":
+            return mq, mv, mv, mo
+        if kind == "q_head_modulo":
+            # query head h mapped to kv head h % hkv instead of h // G
+            G = hq // hkv
+            perm = np.array([((h % hkv) * G + h // hkv) * hd + d for h in range(hq) for d in range(hd)])
+            inv = np.argsort(perm)
+            return mq[:, inv], mk, mv, mo
+        raise ValueError(kind)
+    return masks
+
+
+@pytest.mark.parametrize("kind", ["v_by_qk", "o_by_qk", "k_by_vo", "q_head_modulo"])
+def test_qkvo_zeroed_model_rejects_wrong_masks(monkeypatch, kind):
+    """Plant a wrong set pairing in the oracle (on the CPU) and show the pin catches it."""
+    import oracle.sparselora_oracle as core
+    monkeypatch.setattr(core, "attn_masks", _mutated_masks(kind))
+    assert _qkvo_mismatch(*_qkvo_pin_case()) > 1e-3

@@ -64,3 +64,53 @@ def test_zero_blocks_and_width_check():
     assert np.allclose(deq[1, 64:], -3.0, rtol=0, atol=float(scales[1, 1]) / 2)
     with pytest.raises(ValueError):
         O.quantize_int4_rows(np.zeros((1, 100)))
+
+
+# The code is an integer decided by floating point; the pages fix no precision,
+# so the reading is IEEE fp32 (s = fp32(max|w| / 7), q = rint(fp32(w / s)), ties
+# to even).  These elements pin that reading against exact rational arithmetic:
+# with max|w| = 1 the scale is fp32(1/7) = 9586981 / 2^26, and the two weights
+# below have fp32 quotients exactly 1.5 and 4.5 (codes 2 and 4 by ties to even)
+# while their exact quotients, 1.49999995 and 4.50000016, round to 1 and 5.
+from fractions import Fraction
+
+
+def _round_fp32(x: Fraction) -> Fraction:
+    """Nearest fp32 value of a rational (normal range), ties to even."""
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    return sgn * _rint_even(a / ulp) * ulp
+
+
+def _rint_even(x: Fraction) -> int:
+    f = x.numerator // x.denominator          # floor
+    rem = x - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return f
+
+
+def test_code_decided_in_fp32_with_ties_to_even():
+    w_tie_lo = np.float32(0.2142857164144516)
+    w_tie_hi = np.float32(0.6428571939468384)
+    rng = np.random.default_rng(5)
+    row = (rng.standard_normal(64) * 0.3).astype(np.float32)
+    row[0] = np.float32(1.0)                 # block maximum
+    row[1], row[2] = w_tie_lo, w_tie_hi
+    row[3], row[4] = -w_tie_lo, -w_tie_hi
+    codes, scales = O.quantize_int4_rows(row[None, :])
+    s = _round_fp32(Fraction(1) / 7)
+    assert Fraction(float(scales[0, 0])) == s
+    expect = [max(-7, min(7, _rint_even(_round_fp32(Fraction(float(w)) / s)))) for w in row]
+    assert O.int4_codes(codes)[0].tolist() == expect
+    assert expect[1:5] == [2, 4, -2, -4]
+    # the exact quotient would decide differently: the pin separates the readings
+    assert [_rint_even(Fraction(float(w)) / s) for w in row[1:3]] == [1, 5]

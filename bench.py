@@ -99,9 +99,14 @@ def cpu_baseline(p, ctx, L, Pt_g, Q_g, Pt_u, Q_u, k, budget_s):
     t1 = run(1)
     nseq = int(max(1, min(len(ctx), budget_s // max(t1, 1e-3))))
     t = run(nseq) if nseq > 1 else t1
+    env = {n: os.environ.get(n) for n in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     return {"value": nseq * L / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "blas_threads": int(threads),
+            "thread_env": {n: v for n, v in env.items() if v is not None},
+            "precision": "scores fp32 (they decide the selected set); forward and backward fp64",
             "sample": f"{nseq} of {len(ctx)} sequences ({nseq * L} tokens), estimate+select+fwd+bwd "
-                      f"in numpy (scores fp32, fwd/bwd fp64), one run of {t:.2f} s"}
+                      f"in numpy (scores fp32, fwd/bwd fp64, so the rate is an fp64-BLAS rate), "
+                      f"one run of {t:.2f} s; cores = the BLAS threads numpy used"}
 
 
 def attn_flops(D, nq, nkv, G, r, ctx, L, kqk, kvo):
@@ -312,6 +317,200 @@ def attn_bench(args, torch, sl, cfg=3, quant=False):
             "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None}
 
 
+def workload_bench(args, torch, sl, cfg):
+    """Every layer of a workload (FFN and q/k/v/o rows where the workload has
+    them): estimate + select where a layer is sparse (a layer at 0 % keeps
+    every channel and needs no estimate), forward and backward, against the
+    same kernels run dense (k = N, no estimator).  Reports tokens/s, effective
+    TFLOP/s, the per-kernel breakdown with the dominant kernel's roofline, and
+    the estimator's share of time and FLOPs."""
+    wl = W.WORKLOADS[cfg]
+    fp32 = wl.dtype == "f32"
+    tdt = torch.float32 if fp32 else torch.bfloat16
+    peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    L, r_e = wl.seq_len, wl.est_rank
+    ctx = [int(c) for c in W.ctx_lengths(wl)]
+    B, T = len(ctx), len(ctx) * L
+    Tc = sum(ctx)
+    nlay = max(len(wl.ffn), len(wl.attn))
+    print(f"[bench] {wl.name}: {nlay} layer(s), B={B} L={L} ctx={ctx}", file=sys.stderr, flush=True)
+    dev = torch.device("cuda")
+    lay = sl.Layout(ctx, L)
+    sparse_steps, dense_steps = [], []
+    kfl = {}                       # timer slot -> algorithmic FLOPs over all layers of one step
+    est_fl = 0.0
+    total_fl = 0.0
+    dense_fl = 0.0
+    desc = []
+
+    def add(slot, v):
+        kfl[slot] = kfl.get(slot, 0.0) + v
+
+    def rows(kc, n):
+        return sum(c * kc + (L - c) * n for c in ctx)
+
+    for li in range(nlay):
+        if li < len(wl.ffn):
+            f = wl.ffn[li]
+            D, F, r = f.d_model, f.d_ff, f.lora_rank
+            k = sl.k_from_ratio(F, f.sparsity_pct)
+            p = W.make_ffn_tensors(wl, li)
+            t = {n: to_dev(p[n], torch, tdt) for n in ("Wg", "Wu", "Ag", "Bg", "Au", "Bu", "Ad", "Bd")}
+            t["WdT"] = to_dev(np.ascontiguousarray(p["Wd"].T), torch, tdt)
+            X, dY = to_dev(p["X"], torch, tdt), to_dev(p["dY"], torch, tdt)
+            del p
+            w = sl.FFNWeights(t, lora_scale=1.0)
+            full = torch.arange(F, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+            grads = {"dX": torch.empty_like(X)}
+            for n in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd"):
+                grads["d" + n] = torch.empty(t[n].shape, dtype=torch.float32, device=dev)
+            Y = torch.empty_like(X)
+            buf = sl.FFNWorkspace(w, lay, k, dev)
+            bufd = sl.FFNWorkspace(w, lay, F, dev) if k < F else buf
+            if k < F:
+                Ptg, Qg, _ = sl.build_estimator(t["Wg"], r_e)
+                Ptu, Qu, _ = sl.build_estimator(t["Wu"], r_e)
+                est = sl.EstimateBuffers(sl.SL_CRIT_SWIGLU_L2, lay, D, r_e, F, k, dev)
+                est_fl += 2 * Tc * D * 2 * r_e + 2 * Tc * r_e * 2 * F
+
+                def s_ffn(X=X, dY=dY, w=w, buf=buf, Y=Y, grads=grads, k=k, F=F, est=est,
+                          fac=(Ptg, Qg, Ptu, Qu)):
+                    idx, _ = sl.estimate_select(sl.SL_CRIT_SWIGLU_L2, X, lay, r_e, *fac, F, k, bufs=est)
+                    sl.ffn_fwd(w, X, lay, k, idx, buf, Y=Y)
+                    sl.ffn_bwd(w, X, lay, k, idx, buf, dY, out=grads)
+            else:
+                def s_ffn(X=X, dY=dY, w=w, buf=buf, Y=Y, grads=grads, F=F, full=full):
+                    sl.ffn_fwd(w, X, lay, F, full, buf, Y=Y)
+                    sl.ffn_bwd(w, X, lay, F, full, buf, dY, out=grads)
+
+            def d_ffn(X=X, dY=dY, w=w, buf=bufd, Y=Y, grads=grads, F=F, full=full):
+                sl.ffn_fwd(w, X, lay, F, full, buf, Y=Y)
+                sl.ffn_bwd(w, X, lay, F, full, buf, dY, out=grads)
+            sparse_steps.append(s_ffn)
+            dense_steps.append(d_ffn)
+            R = rows(k, F)
+            add("gu_fwd", 4 * D * R + 4 * r * R)
+            add("down_fwd", 2 * D * R + 2 * r * T * D)
+            add("dh_bwd", 2 * D * R + 2 * r * R)
+            add("dx_bwd", 4 * D * R + 4 * r * T * D)
+            total_fl += ffn_flops(D, F, r, ctx, L, k)
+            dense_fl += ffn_flops(D, F, r, ctx, L, F)
+            desc.append(f"layer {li} FFN d_ff {F} k {k}")
+        if li < len(wl.attn):
+            a_ = wl.attn[li]
+            heads = (a_.n_q_heads, a_.n_kv_heads, a_.head_dim)
+            D, r = a_.d_model, a_.lora_rank
+            nq, nkv = heads[0] * heads[2], heads[1] * heads[2]
+            G = heads[0] // heads[1]
+            kqk = sl.k_from_ratio(nkv, a_.sparsity_qk_pct)
+            kvo = sl.k_from_ratio(nkv, a_.sparsity_vo_pct)
+            p = W.make_attn_tensors(wl, li)
+            t = {n: to_dev(p[n], torch, tdt) for n in ("Wq", "Wk", "Wv", "Aq", "Bq", "Ak", "Bk", "Av", "Bv",
+                                                       "Ao", "Bo")}
+            t["WoT"] = to_dev(np.ascontiguousarray(p["Wo"].T), torch, tdt)
+            X, a = to_dev(p["X"], torch, tdt), to_dev(p["a"], torch, tdt)
+            gin = {n: to_dev(p[n], torch, tdt) for n in ("dq", "dk", "dv", "d_out")}
+            del p
+            w = sl.QKVOWeights(t, heads)
+            full = torch.arange(nkv, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+            jobs = []
+            if kqk < nkv:
+                fq, fk = sl.build_estimator(t["Wq"], r_e), sl.build_estimator(t["Wk"], r_e)
+                jobs.append(dict(crit=sl.SL_CRIT_QK_NORM, Pt0=fq[0], Q0=fq[1], Pt1=fk[0], Q1=fk[1], N=nkv,
+                                 k=kqk, heads=heads))
+                est_fl += 2 * Tc * D * 2 * r_e + 2 * Tc * r_e * (nq + nkv)
+            if kvo < nkv:
+                fv = sl.build_estimator(t["Wv"], r_e)
+                jobs.append(dict(crit=sl.SL_CRIT_L2, Pt0=fv[0], Q0=fv[1], N=nkv, k=kvo))
+                est_fl += 2 * Tc * D * r_e + 2 * Tc * r_e * nkv
+            est = sl.EstimateMultiBuffers(lay, D, r_e, jobs, dev) if jobs else None
+            buf = sl.QKVOWorkspace(w, lay, kqk, kvo, dev)
+            bufd = sl.QKVOWorkspace(w, lay, nkv, nkv, dev)
+            outs, grads = {}, {}
+
+            def s_att(X=X, a=a, w=w, buf=buf, gin=gin, jobs=jobs, est=est, kqk=kqk, kvo=kvo, full=full,
+                      outs=outs, grads=grads, nkv=nkv):
+                res = sl.estimate_select_multi(X, lay, r_e, jobs, bufs=est) if jobs else []
+                it = iter(res)
+                iqk = next(it)[0] if kqk < nkv else full
+                ivo = next(it)[0] if kvo < nkv else full
+                o, _ = sl.qkvo_fwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf=buf, outs=outs)
+                outs.update(o)
+                g = sl.qkvo_bwd(w, X, a, lay, kqk, iqk, kvo, ivo, buf, out=grads, **gin)
+                grads.update(g)
+
+            def d_att(X=X, a=a, w=w, buf=bufd, gin=gin, full=full, outs=outs, grads=grads, nkv=nkv):
+                o, _ = sl.qkvo_fwd(w, X, a, lay, nkv, full, nkv, full, buf=buf, outs=outs)
+                outs.update(o)
+                g = sl.qkvo_bwd(w, X, a, lay, nkv, full, nkv, full, buf, out=grads, **gin)
+                grads.update(g)
+            sparse_steps.append(s_att)
+            dense_steps.append(d_att)
+            Rq, Rk, Rv, Ro = rows(kqk * G, nq), rows(kqk, nkv), rows(kvo, nkv), rows(kvo * G, nq)
+            add("qkv_fwd", 2 * D * (Rq + Rk + Rv) + 2 * r * (Rq + Rk + Rv))
+            add("o_fwd", 2 * D * Ro + 2 * r * T * D)
+            add("da_bwd", 2 * D * Ro + 2 * r * Ro)
+            add("dxqkv_bwd", 2 * D * (Rq + Rk + Rv) + 6 * r * T * D)
+            total_fl += attn_flops(D, nq, nkv, G, r, ctx, L, kqk, kvo)
+            dense_fl += attn_flops(D, nq, nkv, G, r, ctx, L, nkv, nkv)
+            desc.append(f"layer {li} q/k/v/o heads {list(heads)} k_qk {kqk} k_vo {kvo}")
+    torch.cuda.synchronize()
+
+    def step():
+        for fn in sparse_steps:
+            fn()
+
+    def step_dense():
+        for fn in dense_steps:
+            fn()
+
+    # per-kernel breakdown (events around every main kernel), then the timed region
+    sl.timer_enable(64 * nlay * (args.steps + 1))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sl.timer_reset()
+    timed(torch, step, args.steps, 0)
+    kern = {}
+    for name in TIMER_NAMES:
+        tot, n = sl.timer_read(name)
+        if n:
+            kern[name] = {"ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
+                          "avg_launch_ms": tot / n}
+    sl.timer_enable(0)
+    ms = timed(torch, step, args.steps, 0)
+    dense_ms = timed(torch, step_dense, max(3, args.steps // 2), 2) if not args.no_dense else None
+    for name, v in kern.items():
+        if name in kfl:
+            v["tflops"] = kfl[name] / (v["ms_per_step"] * 1e-3) / 1e12
+            v["mfma_frac"] = v["tflops"] / peak
+    gem = [n for n in kern if n in kfl]
+    dom = max(gem, key=lambda n: kern[n]["ms_per_step"]) if gem else None
+    est_ms = sum(kern.get(n, {}).get("ms_per_step", 0.0) for n in ("estimate", "select"))
+    print(f"[bench] {wl.name} step {ms:.3f} ms" + (f", dense {dense_ms:.3f} ms" if dense_ms else ""),
+          file=sys.stderr, flush=True)
+    out = {"workload": wl.name, "dtype": "f32" if fp32 else "bf16", "layers": desc, "batch": B,
+           "seq_len": L, "ctx_len": ctx, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+           "effective_tflops": total_fl / (ms * 1e-3) / 1e12, "algorithmic_gflop": total_fl / 1e9,
+           "dense_algorithmic_gflop": dense_fl / 1e9,
+           "dense_ms_per_step": dense_ms, "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
+           "estimator_share": {"time": est_ms / ms, "flops": est_fl / total_fl},
+           "kernels": kern}
+    if dom:
+        fl_launch = kfl[dom] / kern[dom]["launches_per_step"]
+        ach = fl_launch / (kern[dom]["avg_launch_ms"] * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                           "frac": ach / peak, "avg_launch_ms": kern[dom]["avg_launch_ms"],
+                           "flops_per_launch": fl_launch}
+    del sparse_steps, dense_steps
+    torch.cuda.empty_cache()
+    return out
+
+
+TIMER_NAMES = ("estimate", "select", "gu_fwd", "down_fwd", "dh_bwd", "dx_bwd", "qkv_fwd", "o_fwd", "da_bwd",
+               "dxqkv_bwd")
+
+
 def timed(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -338,6 +537,14 @@ def main():
                     help="skip the extreme-sparsity workload (99 %% FFN, 75 %% q/k/v/o)")
     ap.add_argument("--no-qlora", action="store_true",
                     help="skip the FFN over a 4-bit quantized frozen base")
+    ap.add_argument("--gemm-variants", type=int, default=-1,
+                    help="GEMM tile variants to allow (bit mask: 1 wide N-gather, 2 tall K-gather, 4 tall always; "
+                         "default: the library's)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the tiny fp32 FFN, 4-layer stack and LLaMA3-8B long-context workloads")
+    ap.add_argument("--workload", type=int, default=0,
+                    help="run only workload N's whole-path measurement and print it as the JSON line "
+                         "(for profiling)")
     ap.add_argument("--attn-only", action="store_true",
                     help="run only the q/k/v/o workload and print its measurements as the JSON line "
                          "(for profiling that step alone)")
@@ -353,9 +560,14 @@ def main():
 
     import torch
     import contextual_sparsity_lora_svd_amd as sl
+    if args.gemm_variants >= 0:
+        sl.gemm_config(args.gemm_variants)
 
     if args.attn_only:
         print(json.dumps(attn_bench(args, torch, sl)), flush=True)
+        return
+    if args.workload:
+        print(json.dumps(workload_bench(args, torch, sl, args.workload)), flush=True)
         return
 
     wl = W.WORKLOADS[2]
@@ -463,6 +675,14 @@ def main():
         torch.cuda.empty_cache()
         qlora = qlora_bench(args, torch, sl)
 
+    others = None
+    if not args.no_workloads:
+        others = {}
+        for c in (1, 4, 5):
+            torch.cuda.empty_cache()
+            o = workload_bench(args, torch, sl, c)
+            others[o["workload"]] = o
+
     if args.copy_calibration:
         n = 64 << 20
         src = torch.ones(n, dtype=torch.bfloat16, device=X.device)
@@ -508,6 +728,7 @@ def main():
         "attention": attn,
         "extreme_sparsity": extreme,
         "quantized_base": qlora,
+        "workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

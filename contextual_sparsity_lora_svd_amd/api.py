@@ -215,10 +215,15 @@ def quantize_q4(W: torch.Tensor):
     return codes, scales
 
 
-def gemm_config(wide_ng: int = -1) -> int:
-    """Allow (1) or forbid (0) the wide N-gather GEMM tiles; -1 only reads.
+GEMM_WIDE, GEMM_TALL, GEMM_TALL_ALWAYS = 1, 2, 4
+
+
+def gemm_config(variants: int = -1) -> int:
+    """GEMM tile variants the calling thread allows, a bit mask: GEMM_WIDE
+    (128 x 512 N-gather), GEMM_TALL (256 x 256 K-gather), GEMM_TALL_ALWAYS
+    (tall tiles whatever their grid); 0 = 128 x 256 only; -1 only reads.
     Returns the previous setting."""
-    return int(lib().sl_gemm_config(int(wide_ng)))
+    return int(lib().sl_gemm_config(int(variants)))
 
 
 def timer_read(slot: str):

@@ -10,6 +10,8 @@
 // launch.
 #include "sl_launch.hpp"
 
+#include <mutex>
+
 using namespace sl;
 
 namespace {
@@ -31,10 +33,12 @@ struct EJob {
   int nchunk_max;
   int zcol;         // first Zh column of the job's projections (rep columns each)
   size_t w_p0, w_p1;
+  size_t w_keys;    // select keys in workspace (every job, when some N > SEL_MAXN_LDS)
 };
 
 struct EstPlan {
   int njobs, nproj, rank, rep, ldz;
+  bool gkeys;       // the selection keeps its keys in workspace
   EJob job[SL_EST_MAXJOBS];
   size_t w_zh, w_skp, total;
 };
@@ -93,6 +97,11 @@ sl_status plan_estimate(const SeqTab& st, long long d_in, int rank, int njobs, c
     e.w_p0 = bp.take((size_t)st.nseq * e.nchunk_max * e.N0 * 4);
     e.w_p1 = e.crit == SL_CRIT_QK_NORM ? bp.take((size_t)st.nseq * e.nchunk_max * e.N * 4) : 0;
   }
+  long long nmax = 0;
+  for (int j = 0; j < njobs; ++j) nmax = P.job[j].N > nmax ? P.job[j].N : nmax;
+  P.gkeys = nmax > SEL_MAXN_LDS;
+  for (int j = 0; j < njobs; ++j)
+    P.job[j].w_keys = P.gkeys ? bp.take((size_t)st.nseq * P.job[j].N * 4) : 0;
   P.w_skp = bp.take((size_t)skinny_part_floats(T, d_in) * 4);   // K-sliced stage 1
   P.total = bp.off;
   return SL_OK;
@@ -135,16 +144,17 @@ sl_status launch_gram(const GramArgs& a, int nproj, int nseq, int rank, hipStrea
   return SL_OK;
 }
 
-sl_status launch_select(const SelectArgs& a, int nseq, int nmax, hipStream_t s) {
-  const size_t lds = (size_t)nmax * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    SL_HIP(hipFuncSetAttribute((const void*)select_kernel,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, SEL_MAXN * 4));
-    attr_set = true;
-  }
+sl_status launch_select(const SelectArgs& a, int nseq, int nmax, bool gkeys, hipStream_t s) {
+  static std::once_flag attr_once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(attr_once, [] {
+    attr_err = hipFuncSetAttribute((const void*)select_kernel<false>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, SEL_MAXN_LDS * 4);
+  });
+  SL_HIP(attr_err);
   timer_begin(TS_SELECT, s);
-  hipLaunchKernelGGL(select_kernel, dim3(nseq, a.njobs), dim3(SEL_THREADS), lds, s, a);
+  if (gkeys) hipLaunchKernelGGL(select_kernel<true>, dim3(nseq, a.njobs), dim3(SEL_THREADS), 0, s, a);
+  else hipLaunchKernelGGL(select_kernel<false>, dim3(nseq, a.njobs), dim3(SEL_THREADS), (size_t)nmax * 4, s, a);
   timer_end(TS_SELECT, s);
   SL_HIP(hipGetLastError());
   return SL_OK;
@@ -218,9 +228,10 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
     q.N = (int)e.N; q.N0 = e.N0;
     if (q.qk) { q.group = e.heads.n_q_heads / e.heads.n_kv_heads; q.head_dim = e.heads.head_dim; }
     q.k = e.k; q.idx = e.idx; q.scores = e.scores;
+    q.gkeys = P.gkeys ? reinterpret_cast<uint32_t*>(ws + e.w_keys) : nullptr;
     nmax = q.N > nmax ? q.N : nmax;
   }
-  return launch_select(se, st.nseq, nmax, stream);
+  return launch_select(se, st.nseq, nmax, P.gkeys, stream);
 }
 
 sl_est_job one_job(sl_criterion crit, const sl_heads* heads, const void* Pt0, const void* Q0, const void* Pt1,

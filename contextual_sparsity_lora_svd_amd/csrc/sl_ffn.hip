@@ -61,6 +61,11 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   if (r < 1 || r > 32) SL_FAIL(SL_ERR_RANGE, "lora_rank %d outside [1, 32]", r);
   if (k < 1 || k > F) SL_FAIL(SL_ERR_RANGE, "k = %d outside [1, %lld]", k, F);
   const SeqTab& st = g.st;
+  if ((s = check_extent("X / dY / Y / dX", (long long)st.nseq * st.L, D)) != SL_OK) return s;
+  if ((s = check_extent("a frozen weight", F, D)) != SL_OK) return s;
+  if ((s = check_extent("the compact G / U / H buffers", 1,
+                        (long long)st.T_ctx * round_up(k, 8) + (long long)st.T_out * F)) != SL_OK)
+    return s;
   g.T = st.nseq * st.L;
   g.D = (int)D; g.F = (int)F; g.r = r; g.k = k;
   g.rp = (int)round_up(r, 8);

@@ -37,6 +37,7 @@ enum { EPI_SWIGLU = 0, EPI_DSWIGLU = 1, EPI_TOKEN = 2, EPI_SCATTER = 3 };
 #define SL_GEMM_BM 128      // tile rows (128 or 256)
 #endif
 constexpr int G_BM = SL_GEMM_BM;
+constexpr int G_BM_TALL = 256;  // rows of the tall LDS-DMA tile (K-gather)
 constexpr int G_BN = 256;
 constexpr int G_THREADS = 256;
 constexpr int G_MAXSEG = 4;
@@ -247,6 +248,16 @@ __device__ inline int kgd_bswz(int k) { return ((k & 3) | ((k >> 1) & 4)) << 2; 
 // window, and any aligned 8 of them the 8 groups of a 128-byte one.
 __device__ inline int wng_swz(int r16) { return (r16 ^ (r16 >> 3)) & 7; }
 
+// A pointer that every lane holds alike, in scalar registers (the base
+// operand of the LDS-DMA loads must be scalar).
+template <typename P>
+__device__ inline const P* uniform_ptr(const P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const P*>(((uint64_t)hi << 32) | lo);
+}
+
 // Wait until at most n vector-memory operations of this wave are outstanding
 // (the LDS-DMA loads issued by inline assembly are not tracked by the
 // compiler).  The count field is split: bits 3:0 and 15:14 of the immediate.
@@ -303,24 +314,33 @@ __device__ inline void scatter_row8(T* row, const int* gidx, int c, int nch, int
 }
 
 template <typename T, int MODE, int EPI, bool DUAL, int BM, int WN, bool QB>
-__global__ void __launch_bounds__(WN == 4 ? 512 : G_THREADS, WN == 4 ? 1 : (BM == 128 ? 2 : 1))
+__global__ void __launch_bounds__((WN == 4 || BM > 128) ? 512 : G_THREADS,
+                                  (WN == 4 || BM > 128) ? 1 : 2)
 gather_gemm_kernel(const GemmArgs args) {
   // QB: segments with bq4 set read their B operand as 4-bit codes and scales
   // (bf16 only, register-staged tiles), dequantized on the way into LDS.
-  // WN = 2: BM x 256 tile, 4 waves in a 2 x 2 grid of (BM/2) x 128 blocks,
-  //   two workgroups per CU, operands staged through registers (K-gather bf16:
-  //   B by LDS-DMA).
+  // WN = 2, BM = 128: 128 x 256 tile, 4 waves in a 2 x 2 grid of 64 x 128
+  //   blocks, two workgroups per CU, operands staged through registers
+  //   (K-gather bf16: B by LDS-DMA).
   // WN = 4 (wide N-gather, bf16): 128 x 512 tile, 8 waves in a 2 x 4 grid of
   //   64 x 128 blocks, one workgroup per CU.  Both operands go from memory
   //   straight into LDS (LDS-DMA) through two stages of 64-element K-tiles, so
   //   no register staging or LDS store phase remains, and the tile moves 17 %
   //   fewer operand bytes per MFMA than two 128 x 256 tiles.
-  constexpr bool WIDE = WN == 4;
-  static_assert(WN == 2 || (WIDE && MODE == MODE_NG && sizeof(T) == 2 && BM == 128),
-                "the wide tile is an N-gather bf16 128-row tile");
+  // WN = 2, BM = 256 (tall K-gather, bf16): 256 x 256 tile, 8 waves in a 4 x 2
+  //   grid of 64 x 128 blocks, one workgroup per CU, both operands by LDS-DMA
+  //   through the wide tile's two-stage loop (2 x 64 KB stages).  A CU moves
+  //   64 KB per K-tile for 256 x 256 outputs, against 2 x 48 KB for two
+  //   128 x 256 workgroups.
+  constexpr bool TALL = BM > 128;           // tall: 8 waves in a 4 x 2 grid
+  constexpr bool WIDE = WN == 4 || TALL;
+  static_assert(BM == 128 || BM == G_BM_TALL, "tile rows: 128 or 256");
+  static_assert(!WIDE || (sizeof(T) == 2 && !QB && (WN == 4 ? MODE == MODE_NG && BM == 128 : MODE == MODE_KG)),
+                "LDS-DMA tiles: bf16, wide N-gather 128-row or tall K-gather");
   static_assert(!QB || (!WIDE && sizeof(T) == 2), "quantized B: bf16 register-staged tiles");
-  constexpr int NWAVE = WIDE ? 8 : 4;       // waves per workgroup
-  constexpr int BN_T = WIDE ? 512 : 256;    // B rows (accumulator columns) per tile
+  constexpr int NWAVE = (WN == 4 || TALL) ? 8 : 4;   // waves per workgroup
+  constexpr int WMROWS = NWAVE / WN;        // wave rows of the wave grid
+  constexpr int BN_T = 128 * WN;            // B rows (accumulator columns) per tile
   constexpr int VEC = GTraits<T>::VEC;
   constexpr int BK = GTraits<T>::BK;
   constexpr int KSTEP = GTraits<T>::KSTEP;
@@ -329,7 +349,7 @@ gather_gemm_kernel(const GemmArgs args) {
   constexpr int W_ROWB = 2 * BK;            // wide: bytes of a staged row (128)
   constexpr int W_STG = (BM + BN_T) * W_ROWB;   // wide: bytes per stage (A rows, then B rows)
   constexpr int KR = BK / 8;                // KG: k-rows per thread
-  constexpr int WM = BM / 2;                // wave tile rows
+  constexpr int WM = BM / WMROWS;           // wave tile rows
   constexpr int MB = WM / 32;               // 32-row accumulator blocks per wave
   constexpr int ACH = BM / 32;              // A chunks per thread (register staging)
 
@@ -341,7 +361,7 @@ gather_gemm_kernel(const GemmArgs args) {
   // staged through registers into padded [row][k] tiles.
   // (A 4-bit B takes the register path: its dequantized tile is transposed
   // on the way into LDS.)
-  constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128 && !QB;
+  constexpr bool KGD = SL_KG_DMA && MODE == MODE_KG && sizeof(T) == 2 && BM == 128 && !QB && !WIDE;
   constexpr int A_LD = KGD ? BK : LDS_LD;   // A tile row stride (elements)
   constexpr int B_STAGE = BK * G_BN * (int)sizeof(T);   // KGD: bytes per B stage
   constexpr int EP_LD = 64 + 4;             // epilogue staging row (floats)
@@ -360,8 +380,8 @@ gather_gemm_kernel(const GemmArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = WIDE ? wave >> 2 : wave >> 1;
-  const int wn = WIDE ? wave & 3 : wave & 1;
+  const int wm = __builtin_amdgcn_readfirstlane(wave / WN);
+  const int wn = __builtin_amdgcn_readfirstlane(wave % WN);
 
   // ---- locate the tile --------------------------------------------------
   const bool split_grid = MODE == MODE_NG && args.rem_split > 1;
@@ -374,33 +394,43 @@ gather_gemm_kernel(const GemmArgs args) {
   } else {
     tile = xcd_remap(blockIdx.x, split_grid ? args.rem_start : (int)gridDim.x);
   }
-  // flat group: the last one starting at or before the tile (empty groups
-  // start where the next one does)
-  int gg = 0;
+  int g, pid, mt, nt, ks;
   {
-    int hi = args.ngroups - 1;
-    while (gg < hi) {
-      const int mid = (gg + hi + 1) >> 1;
-      if (args.tile_start[mid] <= tile) gg = mid; else hi = mid - 1;
+    // flat group: the last one starting at or before the tile (empty groups
+    // start where the next one does)
+    int gg = 0;
+    {
+      int hi = args.ngroups - 1;
+      while (gg < hi) {
+        const int mid = (gg + hi + 1) >> 1;
+        if (args.tile_start[mid] <= tile) gg = mid; else hi = mid - 1;
+      }
     }
+    gg = __builtin_amdgcn_readfirstlane(gg);
+    const int t_in = tile - args.tile_start[gg];
+    pid = gg / (args.st.nseq + 1);
+    g = gg - pid * (args.st.nseq + 1);
+    const int m_g = group_rows(args.st, g);
+    const int ntm_g = (m_g + BM - 1) / BM;
+    const GProb& q = args.prob[pid];
+    const int nch_g = g == args.st.nseq ? q.n_out : q.kidx;
+    const int ntn_g = MODE == MODE_NG ? (nch_g + BNC - 1) / BNC : (args.N + G_BN - 1) / G_BN;
+    mt = t_in % ntm_g;
+    nt = (t_in / ntm_g) % ntn_g;
+    ks = MODE == MODE_NG ? rks : t_in / (ntm_g * ntn_g);
   }
-  gg = __builtin_amdgcn_readfirstlane(gg);
-  const int t_in = tile - args.tile_start[gg];
-  const int pid = gg / (args.st.nseq + 1);
-  const int g = gg - pid * (args.st.nseq + 1);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  ks = __builtin_amdgcn_readfirstlane(ks);
   const GProb& pr = args.prob[pid];
   const bool is_out = (g == args.st.nseq);
-  const int m_rows = group_rows(args.st, g);
+  const int m_rows = __builtin_amdgcn_readfirstlane(group_rows(args.st, g));
   const int ctx_pre_g = is_out ? 0 : args.st.ctx_pre[g];
   const int nch = is_out ? pr.n_out : pr.kidx;
   const int* gidx = is_out ? nullptr : pr.idx + (long long)g * pr.kidx;
-  const int ntm = (m_rows + BM - 1) / BM;
-  int ntn, nks;
-  if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = rnks; }
-  else { ntn = (args.N + G_BN - 1) / G_BN; nks = is_out ? args.ksplit_out : 1; }
-  const int mt = t_in % ntm;
-  const int nt = (t_in / ntm) % ntn;
-  const int ks = MODE == MODE_NG ? rks : t_in / (ntm * ntn);
+  int nks;
+  if (MODE == MODE_NG) nks = rnks;
+  else nks = is_out ? args.ksplit_out : 1;
   const int m0 = mt * BM;
   const int n0 = nt * BNC;
 
@@ -854,15 +884,21 @@ gather_gemm_kernel(const GemmArgs args) {
     }
   }
   } else {
-  // ---- wide N-gather main loop ----------------------------------------------
-  // Stage layout: A rows [0, BM) then B rows [0, BN_T), 128 bytes each, the
-  // 16-byte chunks of a row swizzled by wng_swz.  One LDS-DMA instruction fills
-  // one 1 KB block of 8 rows (lane l: row l / 8, physical chunk l % 8).  Per
-  // K-tile wave w issues A blocks 2w, 2w+1 and B blocks 8w..8w+7 (dual: blocks
-  // 0..31 hold gate rows, 32..63 up rows).  Rows past the group or channel
-  // count are clamped (their outputs are dropped).  A K-tile that ends inside
-  // its segment (k0 + BK > K) stages A through registers with the columns past
-  // K zeroed; its B columns past K are clamped to column 0 and meet those zeros.
+  // ---- LDS-DMA main loop (wide N-gather and tall K-gather tiles) -------------
+  // Stage layout: A rows [0, BM), 128 bytes each, then the B part (BN_T x 128
+  // bytes).  N-gather: B rows [0, BN_T), 128 bytes each; A and B rows have
+  // their 16-byte chunks swizzled by wng_swz.  K-gather: 64 k-rows of 256
+  // n-values (512 bytes), 16-byte chunk c of k-row k at c ^ kgd_bswz(k), read by
+  // the transposing LDS reads.  One LDS-DMA instruction fills one 1 KB block:
+  // 8 rows of A or N-gather B (lane l: row l / 8, physical chunk l % 8), or 2
+  // k-rows of K-gather B (lane l: k-row l / 32, physical chunk l % 32).  Per
+  // K-tile wave w issues A blocks W_AB w .. and B blocks W_BB w .. (dual: the
+  // first half of the B blocks hold gate rows, the second up rows).  Rows past
+  // the group or channel count, and K-gather columns past N, are clamped
+  // (their outputs are dropped).  A K-tile that ends inside its segment
+  // (k0 + BK > K) stages A through registers with the columns past K zeroed;
+  // its B columns (N-gather) or k-rows (K-gather) past K are clamped and meet
+  // those zeros.
   constexpr int W_AB = BM / 8 / NWAVE;       // A blocks per wave
   constexpr int W_BB = BN_T / 8 / NWAVE;     // B blocks per wave
   static_assert(W_AB % 2 == 0 && W_BB % 2 == 0, "a block's parity must follow its index");
@@ -870,28 +906,28 @@ gather_gemm_kernel(const GemmArgs args) {
   const int w_r = lane >> 3;
   // element offset of the logical chunk this lane fetches in even / odd blocks
   // (bit 3 of the row, which the swizzle reads, is the block's parity)
-  int kcl[2];
-  kcl[0] = 8 * ((lane & 7) ^ wng_swz(w_r));
-  kcl[1] = 8 * ((lane & 7) ^ wng_swz(8 + w_r));
-  int arow[W_AB];
+  auto kcl = [&](int par) __attribute__((always_inline)) -> int { return 8 * ((lane & 7) ^ wng_swz(8 * par + w_r)); };
+  // A row of block j of this wave (rows past the group clamp to its last)
+  auto arow = [&](int j) __attribute__((always_inline)) -> int {
+    const int r = m0 + 8 * (W_AB * wv + j) + w_r;
+    return r < m_rows ? r : m_rows - 1;
+  };
+  int bch[W_BB];        // N-gather: channel (B row) of each B block row this lane fetches
+  if constexpr (MODE == MODE_NG) {
 #pragma unroll
-  for (int j = 0; j < W_AB; ++j) {
-    arow[j] = m0 + 8 * (W_AB * wv + j) + w_r;
-    if (arow[j] >= m_rows) arow[j] = m_rows - 1;
-  }
-  int bch[W_BB];
-#pragma unroll
-  for (int j = 0; j < W_BB; ++j) {
-    int c = n0 + (8 * (W_BB * wv + j) + w_r) % BNC;
-    if (c >= nch) c = nch - 1;
-    bch[j] = gidx ? gidx[c] : c;
+    for (int j = 0; j < W_BB; ++j) {
+      int c = n0 + (8 * (W_BB * wv + j) + w_r) % BNC;
+      if (c >= nch) c = nch - 1;
+      bch[j] = gidx ? gidx[c] : c;
+    }
   }
   int cur_s = 0, cur_kk = 0, cur_K = 0, cur_nkt = 0;
   const T* a_base = nullptr;
   const T* b_base = nullptr;
   const T* b2_base = nullptr;
-  unsigned a_off[W_AB], b_off[W_BB];
-  auto enter_seg = [&](int s) {
+  int cur_ldb = 0;
+  unsigned a_off[W_AB];   // element offset of each A block row of this lane (current segment)
+  auto enter_seg = [&](int s) __attribute__((always_inline)) {
     s = __builtin_amdgcn_readfirstlane(s);
     const GSeg& sg = args.seg[s];
     cur_s = s;
@@ -900,14 +936,14 @@ gather_gemm_kernel(const GemmArgs args) {
     a_base = reinterpret_cast<const T*>(sg.A) + pr.a_col[s];
     b_base = reinterpret_cast<const T*>(pr.B[s]);
     b2_base = reinterpret_cast<const T*>(DUAL ? sg.B2 : pr.B[s]);
+    cur_ldb = __builtin_amdgcn_readfirstlane((int)sg.ldb);
 #pragma unroll
     for (int j = 0; j < W_AB; ++j) {
-      if (sg.a_tok) a_off[j] = (unsigned)group_token(args.st, g, arow[j]) * (unsigned)sg.lda;
-      else a_off[j] = is_out ? (unsigned)sg.a_out_off + (unsigned)arow[j] * (unsigned)sg.lda_out
-                             : (unsigned)(ctx_pre_g + arow[j]) * (unsigned)sg.lda;
+      const int r = arow(j);
+      if (sg.a_tok) a_off[j] = (unsigned)group_token(args.st, g, r) * (unsigned)sg.lda;
+      else a_off[j] = is_out ? (unsigned)sg.a_out_off + (unsigned)r * (unsigned)sg.lda_out
+                             : (unsigned)(ctx_pre_g + r) * (unsigned)sg.lda;
     }
-#pragma unroll
-    for (int j = 0; j < W_BB; ++j) b_off[j] = (unsigned)bch[j] * (unsigned)sg.ldb;
   };
   if (nkt > 0) {
     int s = 0, kk = kt_begin;
@@ -921,10 +957,29 @@ gather_gemm_kernel(const GemmArgs args) {
     cur_kk = __builtin_amdgcn_readfirstlane(kk);
   }
 
-  // Issue the loads of the cursor's K-tile into the stage at byte offset st;
-  // returns the LDS-DMA instructions issued (a register-staged A is waited for
-  // before its LDS store, so only DMA instructions stay outstanding).
-  auto issue = [&](int st) -> int {
+  // K-gather: the weight rows of a K-tile (lane p: the row of k-position p;
+  // positions past K clamp to K-1, whose A columns are zero), fetched one
+  // K-tile ahead of its DMA issue by a cursor of their own.
+  int f_s = cur_s, f_kk = cur_kk;
+  auto fetch_rows = [&]() __attribute__((always_inline)) -> int {
+    int r = 0;
+    if constexpr (MODE == MODE_KG) {
+      const int s = __builtin_amdgcn_readfirstlane(f_s);
+      const GSeg& sg = args.seg[s];
+      const int K = seg_len(s);
+      const int* sidx = (sg.b_gather && !is_out) ? sg.idx + (long long)g * sg.kidx : args.iota;
+      r = sidx[min(f_kk * BK + min(lane, BK - 1), K - 1)];
+      ++f_kk;
+      if (f_kk >= (K + BK - 1) / BK && s + 1 < args.nseg) { f_s = s + 1; f_kk = 0; }
+    }
+    return r;
+  };
+
+  // Issue the loads of the cursor's K-tile into the stage at byte offset st
+  // (K-gather: krow = its weight rows); returns the LDS-DMA instructions issued
+  // (a register-staged A is waited for before its LDS store, so only DMA
+  // instructions stay outstanding).
+  auto issue = [&](int st, int krow) __attribute__((always_inline)) -> int {
     if (cur_kk >= cur_nkt && cur_s + 1 < args.nseg) {   // segments are never empty
       enter_seg(cur_s + 1);
       cur_kk = 0;
@@ -939,29 +994,55 @@ gather_gemm_kernel(const GemmArgs args) {
         const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
             __attribute__((address_space(3))) unsigned char*)(sb + 1024 * (W_AB * wv + j)));
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
-                     :: "v"((a_off[j] + (unsigned)(k0 + kcl[j & 1])) * 2u), "s"(la), "s"(a_base)
+                     :: "v"((a_off[j] + (unsigned)(k0 + kcl(j & 1))) * 2u), "s"(la), "s"(uniform_ptr(a_base))
                      : "memory", "m0");
       }
       n += W_AB;
     } else {
 #pragma unroll
       for (int j = 0; j < W_AB; ++j) {
-        const int kc = k0 + kcl[j & 1];
-        Chunk v = kc < cur_K ? load_chunk(a_base + (a_off[j] + (unsigned)kc)) : zero_chunk();
+        const int kc = k0 + kcl(j & 1);
+        Chunk v = zero_chunk();
+        if (kc < cur_K) {
+          // the chunk that straddles K (a K-gather segment's channel count
+          // need not be a multiple of 8) keeps only its elements below K
+          v = load_chunk(a_base + (a_off[j] + (unsigned)kc));
+          mask_chunk<T>(v, cur_K - kc);
+        }
         *reinterpret_cast<uint4*>(sb + 1024 * (W_AB * wv + j) + 16 * lane) =
             make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
       }
     }
+    if constexpr (MODE == MODE_NG) {
 #pragma unroll
-    for (int j = 0; j < W_BB; ++j) {
-      const int q = W_BB * wv + j;
-      const T* base = (DUAL && q >= BN_T / 16) ? b2_base : b_base;
-      const int kc = k0 + kcl[j & 1];
-      const unsigned kb = kc < cur_K ? (unsigned)kc : 0u;
-      const unsigned la = __builtin_amdgcn_readfirstlane(
-          (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(sb + BM * W_ROWB + 1024 * q));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
-                   :: "v"((b_off[j] + kb) * 2u), "s"(la), "s"(base) : "memory", "m0");
+      for (int j = 0; j < W_BB; ++j) {
+        const int q = W_BB * wv + j;
+        const T* base = (DUAL && q >= BN_T / 16) ? b2_base : b_base;
+        const int kc = k0 + kcl(j & 1);
+        const unsigned kb = kc < cur_K ? (unsigned)kc : 0u;
+        const unsigned la = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(sb + BM * W_ROWB + 1024 * q));
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                     :: "v"(((unsigned)bch[j] * (unsigned)cur_ldb + kb) * 2u), "s"(la), "s"(uniform_ptr(base))
+                     : "memory", "m0");
+      }
+    } else {
+      // block q: k-rows 2 q and 2 q + 1 (lanes 0-31 / 32-63)
+#pragma unroll
+      for (int j = 0; j < W_BB; ++j) {
+        const int q = W_BB * wv + j;
+        const int r0 = __builtin_amdgcn_readlane(krow, 2 * q);
+        const int r1 = __builtin_amdgcn_readlane(krow, 2 * q + 1);
+        const int kr = 2 * q + (lane >> 5);
+        const int c = (lane & 31) ^ kgd_bswz(kr);
+        int col = n0 + 8 * c;
+        if (col >= args.N) col = 0;
+        const unsigned off = ((unsigned)(lane < 32 ? r0 : r1) * (unsigned)cur_ldb + (unsigned)col) * 2u;
+        const unsigned la = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(sb + BM * W_ROWB + 1024 * q));
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                     :: "v"(off), "s"(la), "s"(uniform_ptr(b_base)) : "memory", "m0");
+      }
     }
     ++cur_kk;
     return n;
@@ -971,17 +1052,49 @@ gather_gemm_kernel(const GemmArgs args) {
   // the logical chunk 2 s + lane / 32 differing from K-step 0's in bits 1..2).
   // Fragment rows start on 32-row boundaries, so a lane's row has
   // row % 16 = lane % 16.
+  // Block mb's rows start 32 mb rows (4096 mb bytes) after block 0's, and
+  // N-gather B block nb's at a fixed offset from block 0's, so one base per
+  // operand plus an immediate offset addresses those fragments (the K-step
+  // XOR touches bits 5-6 only, below every block offset).  K-gather B blocks
+  // keep an offset each: their k-row swizzle XORs the chunk bits a block
+  // offset would add to.
   const int f_ch = (((lane >> 5) ^ wng_swz(lane & 15)) << 4);
-  unsigned fa[MB], fb[4];
+  const unsigned fa0 = (unsigned)((WM * wm + (lane & 31)) * W_ROWB + f_ch);
+  unsigned fb[MODE == MODE_NG ? 1 : 4];
+  if constexpr (MODE == MODE_NG) {
+    fb[0] = (unsigned)(BM * W_ROWB + (brow(0) + (lane & 31)) * W_ROWB + f_ch);
+  } else {
+    // transposing reads: in each 16-lane group lane i supplies the address of
+    // 4 consecutive n (4 (i % 4) ..) of k-row i / 4 (+ 8 for the second pair
+    // of groups); K-step s adds 16 s k-rows and the second read 4 more (the
+    // swizzle ignores k-row bits 2, 4 and 5)
+    const int grp = lane >> 4, gi = lane & 15;
+    const int kr = 8 * (grp >> 1) + (gi >> 2);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) fa[mb] = (unsigned)((WM * wm + 32 * mb + (lane & 31)) * W_ROWB + f_ch);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) fb[nb] = (unsigned)(BM * W_ROWB + (brow(nb) + (lane & 31)) * W_ROWB + f_ch);
-  auto rda = [&](int st, int ks, int mb) -> bf16x8_t {
-    return *reinterpret_cast<const bf16x8_t*>(smem + st + (fa[mb] ^ (unsigned)(32 * ks)));
+    for (int nb = 0; nb < 4; ++nb) {
+      const int ncol = brow(nb) + 16 * (grp & 1) + 4 * (gi & 3);
+      fb[nb] = (unsigned)(BM * W_ROWB) + (unsigned)(kr * (G_BN * 2)) +
+               ((unsigned)((ncol >> 3) ^ kgd_bswz(kr)) << 4) + (unsigned)(ncol & 7) * 2u;
+    }
+  }
+  auto rda = [&](int st, int ks, int mb) __attribute__((always_inline)) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(smem + st + (fa0 ^ (unsigned)(32 * ks)) + 4096u * mb);
   };
-  auto rdb = [&](int st, int ks, int nb) -> bf16x8_t {
-    return *reinterpret_cast<const bf16x8_t*>(smem + st + (fb[nb] ^ (unsigned)(32 * ks)));
+  auto rdb = [&](int st, int ks, int nb) __attribute__((always_inline)) -> bf16x8_t {
+    if constexpr (MODE == MODE_NG) {
+      return *reinterpret_cast<const bf16x8_t*>(smem + st + (fb[0] ^ (unsigned)(32 * ks)) +
+                                                 (unsigned)((brow(nb) - brow(0)) * W_ROWB));
+    } else {
+      v4i16_t h2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned char* pa = smem + st + fb[nb] + (16 * ks + 4 * h) * (G_BN * 2);
+        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(
+                (__attribute__((address_space(3))) unsigned char*)(pa)));
+      }
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   // One K-step: MFMAs on (ac, b); meanwhile the A fragments of the next step
   // go to an and each B fragment is re-read for the next step (stage nst,
@@ -1008,12 +1121,17 @@ gather_gemm_kernel(const GemmArgs args) {
   // Two stages: K-tile i is consumed from stage i % 2 while K-tile i+1 lands
   // in the other.  Each K-tile's loads are issued as soon as the stage it
   // fills is free: right after the barrier that follows the last fragment
-  // read of the K-tile two before it.
+  // read of the K-tile two before it.  K-gather rows of K-tile i+3 are fetched
+  // right after K-tile i+2 is issued; the wait before the next barrier covers
+  // them.
   if (nkt > 0) {
     static_assert(BK / KSTEP == 4, "four K-steps per K-tile");
     bf16x8_t a0[MB], a1[MB], b[4];
-    issue(0);
-    const int n1 = nkt > 1 ? issue(W_STG) : 0;
+    const int kr0 = fetch_rows();
+    const int kr1 = fetch_rows();
+    issue(0, kr0);
+    const int n1 = nkt > 1 ? issue(W_STG, kr1) : 0;
+    int krow_next = fetch_rows();
     wait_vmcnt(n1);    // K-tile 0 has landed (K-tile 1 may be in flight)
     __syncthreads();
 #pragma unroll
@@ -1024,14 +1142,20 @@ gather_gemm_kernel(const GemmArgs args) {
     for (int i = 0; i < nkt; ++i) {
       const int st_next = st ^ W_STG;
       const bool more = i + 1 < nkt;
+      auto handover = [&]() __attribute__((always_inline)) {
+        if (more) {
+          wait_vmcnt(0);       // K-tile i+1 (the only loads in flight) has landed
+          __syncthreads();     // ... for every wave; and stage i is read by none
+          if (i + 2 < nkt) {
+            issue(st, krow_next);
+            krow_next = fetch_rows();
+          }
+        }
+      };
       kstep(a0, a1, b, true, st, 1);
       kstep(a1, a0, b, true, st, 2);
       kstep(a0, a1, b, true, st, 3);
-      if (more) {
-        wait_vmcnt(0);       // K-tile i+1 (the only loads in flight) has landed
-        __syncthreads();     // ... for every wave; and stage i is read by none
-        if (i + 2 < nkt) issue(st);
-      }
+      handover();
       kstep(a1, a0, b, more, st_next, 0);
       st = st_next;
     }
@@ -1151,10 +1275,9 @@ gather_gemm_kernel(const GemmArgs args) {
 // Adds the K pieces of every split N-gather tile in piece order and applies
 // the tile's element-wise epilogue (the same arithmetic as the GEMM's own).
 // One thread per (split tile, row, 8 channels).
-template <typename T, int EPI, bool DUAL, int WN>
+template <typename T, int EPI, bool DUAL, int WN, int BM>
 __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
-  constexpr int BM = G_BM;
-  constexpr int BN_T = WN == 4 ? 512 : 256;   // partial-tile row: accumulator columns of the GEMM tile
+  constexpr int BN_T = 128 * WN;   // partial-tile row: accumulator columns of the GEMM tile
   constexpr int BNC = DUAL ? BN_T / 2 : BN_T;
   constexpr int CG = BNC / 8;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1167,11 +1290,11 @@ __global__ void __launch_bounds__(256) ng_fixup_kernel(const GemmArgs args) {
   int g = 0;   // split launches hold one problem: flat group = group
   while (g + 1 < args.ngroups && args.tile_start[g + 1] <= tile) ++g;
   const int t_in = tile - args.tile_start[g];
+  const int ntm = (group_rows(args.st, g) + BM - 1) / BM;
+  const int mt = t_in % ntm, nt = t_in / ntm;
   const bool is_out = (g == args.st.nseq);
   const int m_rows = group_rows(args.st, g);
   const int nch = is_out ? args.n_out : args.kidx;
-  const int ntm = (m_rows + BM - 1) / BM;
-  const int mt = t_in % ntm, nt = t_in / ntm;
   const int r = mt * BM + rloc;
   if (r >= m_rows) return;
   const int cl = cg * 8;
@@ -1253,15 +1376,15 @@ void timer_begin(int slot, hipStream_t s);
 void timer_end(int slot, hipStream_t s);
 int device_cus();
 
-// N-gather tiles of a launch (all groups) at bnc channels per tile.
-inline long long ng_tiles(const SeqTab& st, int kidx, int n_out, int bnc) {
+// N-gather tiles of a launch (all groups) at bm rows and bnc channels per tile.
+inline long long ng_tiles(const SeqTab& st, int kidx, int n_out, int bnc, int bm = G_BM) {
   long long total = 0;
   for (int g = 0; g <= st.nseq; ++g) {
     const bool is_out = g == st.nseq;
     const int m = is_out ? st.T_out : st.ctx[g];
     const int nch = is_out ? n_out : kidx;
     if (m <= 0 || nch <= 0) continue;
-    total += (long long)((m + G_BM - 1) / G_BM) * ((nch + bnc - 1) / bnc);
+    total += (long long)((m + bm - 1) / bm) * ((nch + bnc - 1) / bnc);
   }
   return total;
 }
@@ -1287,11 +1410,24 @@ inline void ng_split_plan(long long total, int total_kt, int slots, int& rem_sta
 }
 
 // Workgroup slots of a gather-GEMM variant on the current device: two 128 x 256
-// workgroups or one wide 128 x 512 workgroup per CU.
-inline int gemm_slots(int wn) { return (wn == 4 ? 1 : 2) * device_cus(); }
+// workgroups, or one wide 128 x 512 or tall 256 x 256 workgroup, per CU.
+inline int gemm_slots(int wn, int bm = G_BM) { return (wn == 4 || bm > 128 ? 1 : 2) * device_cus(); }
 
-// N-gather variant: 1 = wide tiles where the operands allow (default), 0 = 128 x 256 only.
-inline int g_gemm_wide_ng = 1;
+// Rounds of resident workgroups a grid of `total` tiles takes: a last round at
+// most half full runs as K pieces (ng_split_plan) and counts by its fill.
+inline double grid_rounds(long long total, int slots) {
+  if (slots <= 0 || total <= 0) return 0.0;
+  const long long full = total / slots, rem = total % slots;
+  if (full == 0) return 1.0;
+  return (double)full + (2 * rem <= slots ? (double)rem / slots : 1.0);
+}
+
+// GEMM variants the calling thread allows (bit mask): bit 0 = wide 128 x 512
+// N-gather tiles, bit 1 = tall 256 x 256 K-gather tiles, bit 2 = tall tiles
+// whatever their grid (tests); 0 = 128 x 256 tiles only.  Default: wide and
+// tall.  The LDS-DMA variants need 16-byte aligned operands.
+enum { GV_WIDE = 1, GV_TALL = 2, GV_TALL_ALWAYS = 4 };
+inline thread_local int g_gemm_variants = GV_WIDE | GV_TALL;
 
 // K-tiles of a set of N-gather segments (fixed lengths) at depth bk.
 inline int ng_ktiles(std::initializer_list<int> seg_k, int bk) {
@@ -1305,13 +1441,16 @@ inline int ng_ktiles(std::initializer_list<int> seg_k, int bk) {
 inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, bool dual, int esz,
                                  std::initializer_list<int> seg_k) {
   long long best = 0;
-  for (int wn = 2; wn <= (esz == 2 ? 4 : 2); wn += 2) {
+  // (tile rows, waves in N) of the narrow and wide N-gather variants
+  const int vars[2][2] = {{G_BM, 2}, {G_BM, 4}};
+  for (int v = 0; v < (esz == 2 ? 2 : 1); ++v) {
+    const int bm = vars[v][0], wn = vars[v][1];
     const int bn = 128 * wn;
     const int bk = esz == 2 ? 64 : 32;
     int rs, sp;
-    const long long total = ng_tiles(st, kidx, n_out, dual ? bn / 2 : bn);
-    ng_split_plan(total, ng_ktiles(seg_k, bk), gemm_slots(wn), rs, sp);
-    const long long f = sp > 1 ? (total - rs) * sp * (long long)G_BM * bn : 0;
+    const long long total = ng_tiles(st, kidx, n_out, dual ? bn / 2 : bn, bm);
+    ng_split_plan(total, ng_ktiles(seg_k, bk), gemm_slots(wn, bm), rs, sp);
+    const long long f = sp > 1 ? (total - rs) * sp * (long long)bm * bn : 0;
     if (f > best) best = f;
   }
   return best;
@@ -1336,12 +1475,46 @@ inline bool wide_ng_ok(const GemmArgs& a, int esz) {
   return true;
 }
 
+// K-gather tiles of a launch at bm rows (256-column tiles, the output group split ksplit_out ways).
+inline long long kg_tiles(const GemmArgs& a, int bm) {
+  const long long ntn = (a.N + G_BN - 1) / G_BN;
+  long long total = 0;
+  for (int g = 0; g <= a.st.nseq; ++g) {
+    const bool is_out = g == a.st.nseq;
+    const int m = is_out ? a.st.T_out : a.st.ctx[g];
+    if (m > 0) total += (long long)((m + bm - 1) / bm) * ntn * (is_out ? a.ksplit_out : 1);
+  }
+  return total;
+}
+
+// Whether a bf16 K-gather launch takes the tall 256-row LDS-DMA tiles: its
+// operands suit the LDS-DMA loads, and its grid, priced as rounds of resident
+// workgroups times the operand bytes a CU moves per K-tile (tall: one 64 KB
+// workgroup; narrow: two of 48 KB), costs less.
+inline bool tall_kg_ok(const GemmArgs& a, bool always) {
+  auto al = [](const void* p, long long off_el) {
+    return ((uintptr_t)p + (uintptr_t)(off_el * 2)) % 16 == 0;
+  };
+  for (int s = 0; s < a.nseg; ++s) {
+    const GSeg& g = a.seg[s];
+    if (g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
+    if (!g.a_tok && (g.lda_out % 8 != 0 || g.a_out_off % 8 != 0)) return false;
+    if (!al(g.A, 0) || !al(g.B, 0)) return false;
+  }
+  if (a.N % 8 != 0 || a.nprob > 1) return false;
+  if (always) return true;
+  const double rt = grid_rounds(kg_tiles(a, G_BM_TALL), gemm_slots(2, G_BM_TALL));
+  const double rn = grid_rounds(kg_tiles(a, G_BM), gemm_slots(2));
+  return rt > 0 && rt * 64.0 < 0.97 * rn * 96.0;
+}
+
 // Host side: count tiles per group and launch one variant.
-template <typename T, int MODE, int EPI, bool DUAL, int WN, bool QB>
+template <typename T, int MODE, int EPI, bool DUAL, int BM, int WN, bool QB>
 hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot) {
-  constexpr int BN_T = WN == 4 ? 512 : 256;
+  constexpr int BN_T = 128 * WN;
   constexpr int BNC = DUAL ? BN_T / 2 : BN_T;
   constexpr int BK = GTraits<T>::BK;
+  constexpr bool TALL = BM > 128;
   const int gpp = a.st.nseq + 1;
   a.ngroups = a.nprob * gpp;
   int total = 0;
@@ -1353,7 +1526,7 @@ hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot
     const int m = is_out ? a.st.T_out : a.st.ctx[g];
     const int nch = is_out ? pr.n_out : pr.kidx;
     if (m <= 0 || (MODE == MODE_NG && nch <= 0)) continue;
-    const int ntm = (m + G_BM - 1) / G_BM;
+    const int ntm = (m + BM - 1) / BM;
     int ntn, nks;
     if (MODE == MODE_NG) { ntn = (nch + BNC - 1) / BNC; nks = 1; }
     else { ntn = (a.N + G_BN - 1) / G_BN; nks = is_out ? a.ksplit_out : 1; }
@@ -1369,19 +1542,19 @@ hipError_t launch_gather_gemm_wn(GemmArgs& a, hipStream_t stream, int timer_slot
     if (a.rpart && a.nprob == 1) {
       int total_kt = 0;
       for (int s = 0; s < a.nseg; ++s) total_kt += (a.seg[s].K + BK - 1) / BK;   // NG segments: fixed K
-      ng_split_plan(total, total_kt, gemm_slots(WN), a.rem_start, a.rem_split);
+      ng_split_plan(total, total_kt, gemm_slots(WN, BM), a.rem_start, a.rem_split);
       grid = a.rem_start + (long long)(total - a.rem_start) * a.rem_split;
     }
   }
   timer_begin(timer_slot, stream);
-  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, G_BM, WN, QB>), dim3((unsigned)grid),
-                     dim3(WN == 4 ? 512 : G_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((gather_gemm_kernel<T, MODE, EPI, DUAL, BM, WN, QB>), dim3((unsigned)grid),
+                     dim3((WN == 4 || TALL) ? 512 : G_THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if constexpr (MODE == MODE_NG && (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER)) {
     if (e == hipSuccess && a.rem_split > 1) {
       constexpr int CG = BNC / 8;
-      const long long n = (long long)(total - a.rem_start) * G_BM * CG;
-      hipLaunchKernelGGL((ng_fixup_kernel<T, EPI, DUAL, WN>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+      const long long n = (long long)(total - a.rem_start) * BM * CG;
+      hipLaunchKernelGGL((ng_fixup_kernel<T, EPI, DUAL, WN, BM>), dim3((unsigned)((n + 255) / 256)), dim3(256),
                          0, stream, a);
       e = hipGetLastError();
     }
@@ -1404,15 +1577,19 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
   bool quant = false;
   for (int s = 0; s < a.nseg; ++s) quant |= a.seg[s].bq4 != 0;
   if constexpr (sizeof(T) == 2) {
-    if (quant) return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2, true>(a, stream, timer_slot);
+    if (quant) return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 2, true>(a, stream, timer_slot);
   } else {
     if (quant) return hipErrorInvalidValue;   // 4-bit weights: bf16 launches only
   }
-  if constexpr (MODE == MODE_NG && sizeof(T) == 2) {
-    if (g_gemm_wide_ng && wide_ng_ok(a, 2))
-      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 4, false>(a, stream, timer_slot);
+  if constexpr (sizeof(T) == 2 && MODE == MODE_KG) {
+    if ((g_gemm_variants & GV_TALL) && tall_kg_ok(a, (g_gemm_variants & GV_TALL_ALWAYS) != 0))
+      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM_TALL, 2, false>(a, stream, timer_slot);
   }
-  return launch_gather_gemm_wn<T, MODE, EPI, DUAL, 2, false>(a, stream, timer_slot);
+  if constexpr (MODE == MODE_NG && sizeof(T) == 2) {
+    if ((g_gemm_variants & GV_WIDE) && wide_ng_ok(a, 2))
+      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 4, false>(a, stream, timer_slot);
+  }
+  return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 2, false>(a, stream, timer_slot);
 }
 
 }  // namespace sl

@@ -2,6 +2,7 @@
 #include "sl_host.hpp"
 #include "sl_gemm.hpp"
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -23,23 +24,26 @@ const char* last_error() { return g_err.c_str(); }
 int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static int cus[64] = {0};   // per device, filled on first use (benign race: same value)
-  if (dev >= 0 && dev < 64 && cus[dev] > 0) return cus[dev];
+  static std::atomic<int> cus[64];   // per device, filled on first use (zero-initialised)
+  if (dev >= 0 && dev < 64) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cus[dev] = prop.multiProcessorCount;
+  if (dev >= 0 && dev < 64) cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
   return prop.multiProcessorCount;
 }
 
 sl_status check_arch() {
   int dev = 0;
   SL_HIP(hipGetDevice(&dev));
-  static int checked[64] = {0};   // 0 unknown, 1 ok, 2 wrong arch (benign race: same answer)
-  if (dev >= 0 && dev < 64 && checked[dev] == 1) return SL_OK;
+  static std::atomic<int> checked[64];   // 0 unknown, 1 ok, 2 wrong arch
+  if (dev >= 0 && dev < 64 && checked[dev].load(std::memory_order_relaxed) == 1) return SL_OK;
   hipDeviceProp_t prop;
   SL_HIP(hipGetDeviceProperties(&prop, dev));
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev >= 0 && dev < 64) checked[dev] = ok ? 1 : 2;
+  if (dev >= 0 && dev < 64) checked[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   if (!ok)
     SL_FAIL(SL_ERR_UNSUPPORTED_ARCH, "device %d is %s; this library is built for gfx950", dev,
             prop.gcnArchName);
@@ -47,8 +51,14 @@ sl_status check_arch() {
 }
 
 namespace {
+// Side streams, one per (device, caller stream), created on first use and
+// kept until the process ends.  Past kMaxSide caller streams per process a
+// call keeps all of its work on the caller's stream.
+constexpr int kMaxSide = 256;
+struct SideEntry { int dev; hipStream_t main; hipStream_t side; };
 std::mutex g_side_mu;
-hipStream_t g_side[64] = {};
+SideEntry g_side[kMaxSide];
+int g_nside = 0;
 
 // One event, recorded on `from` and waited for on `to`; released once done.
 sl_status link_streams(hipStream_t from, hipStream_t to) {
@@ -73,13 +83,19 @@ sl_status SideFork::begin(hipStream_t main) {
   }
   int dev = 0;
   SL_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= 64) SL_FAIL(SL_ERR_HIP, "device %d out of range", dev);
   {
     std::lock_guard<std::mutex> lk(g_side_mu);
-    if (!g_side[dev]) SL_HIP(hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking));
-    side = g_side[dev];
+    side = main;
+    for (int i = 0; i < g_nside; ++i)
+      if (g_side[i].dev == dev && g_side[i].main == main) { side = g_side[i].side; break; }
+    if (side == main && g_nside < kMaxSide) {
+      hipStream_t ns = nullptr;
+      SL_HIP(hipStreamCreateWithFlags(&ns, hipStreamNonBlocking));
+      g_side[g_nside++] = SideEntry{dev, main, ns};
+      side = ns;
+    }
   }
-  return link_streams(main, side);
+  return side == main ? SL_OK : link_streams(main, side);
 }
 
 sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_streams(side, main); }
@@ -121,8 +137,8 @@ struct TimerState {
   size_t used = 0;
   uint32_t mask = ~0u;             // slots recorded
 };
-static TimerState g_timer;         // single-threaded diagnostic facility
-static int g_pending_slot = -1;
+static thread_local TimerState g_timer;   // per calling thread
+static thread_local int g_pending_slot = -1;
 
 bool timer_on() { return g_timer.on; }
 
@@ -170,9 +186,9 @@ int sl_timer_enable(int max_launches) {
 
 void sl_timer_select(uint32_t slot_mask) { sl::g_timer.mask = slot_mask; }
 
-int sl_gemm_config(int wide_ng) {
-  const int prev = sl::g_gemm_wide_ng;
-  if (wide_ng >= 0) sl::g_gemm_wide_ng = wide_ng ? 1 : 0;
+int sl_gemm_config(int variants) {
+  const int prev = sl::g_gemm_variants;
+  if (variants >= 0) sl::g_gemm_variants = variants & (sl::GV_WIDE | sl::GV_TALL | sl::GV_TALL_ALWAYS);
   return prev;
 }
 

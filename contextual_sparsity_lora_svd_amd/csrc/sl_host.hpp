@@ -35,6 +35,17 @@ int device_cus();   // compute units of the current device (0 when none)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The gather-GEMM addresses its operands with 32-bit element offsets, and its
+// LDS-DMA loads with 32-bit byte offsets of 2-byte elements: every matrix it
+// reads or writes (token-major activations, weights, compact buffers) must
+// hold fewer than 2^31 elements.  Checked on the host before any launch.
+constexpr long long kMaxOperandElems = (1LL << 31) - 1;
+inline sl_status check_extent(const char* what, long long rows, long long cols) {
+  if (rows > 0 && cols > 0 && rows > kMaxOperandElems / cols)
+    SL_FAIL(SL_ERR_RANGE, "%s holds %lld x %lld elements; at most 2^31 - 1 are supported", what, rows, cols);
+  return SL_OK;
+}
+
 // Validate and tabulate a sequence layout.
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st);
 
@@ -49,9 +60,10 @@ struct Bump {
 };
 
 // Fork and join with a side stream, for work of a call that does not depend on
-// the launches it may overlap.  The side stream is created once per device
-// (default priority, non-blocking) and shared by all calls; each fork and join
-// records an event of its own.  begin(): the side stream waits for everything
+// the launches it may overlap.  Each caller stream of each device gets a side
+// stream of its own (default priority, non-blocking), created at its first
+// fork, so calls on independent streams never wait for each other; each fork
+// and join records an event of its own.  begin(): the side stream waits for everything
 // enqueued on `main` so far.  end(): `main` waits for everything enqueued on
 // the side stream so far, so the call's work is again ordered on `main`.
 // While `main` is being captured into a graph, begin() makes `side` = `main`

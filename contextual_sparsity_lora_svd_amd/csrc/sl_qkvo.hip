@@ -88,6 +88,11 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.ck = make_comp(st, g.kqk, g.nkv);
   g.cv = make_comp(st, g.kvo, g.nkv);
   g.co = make_comp(st, g.ko, g.nq);
+  if ((s = check_extent("X / dX / o / d_out", g.T, D)) != SL_OK) return s;
+  if ((s = check_extent("q / a / dq / da", g.T, nq)) != SL_OK) return s;
+  if ((s = check_extent("Wq / WoT", nq, D)) != SL_OK) return s;
+  for (const Comp* c : {&g.cq, &g.ck, &g.cv, &g.co})
+    if ((s = check_extent("a compact projection buffer", 1, c->elems)) != SL_OK) return s;
   const int bk = dt == SL_BF16 ? 64 : 32;
   g.ks_o = choose_ks(st, g.ko + g.rp, g.nq + g.rp, g.D, bk);
   g.ks_dx = choose_ks(st, (long long)g.kq + g.kqk + g.kvo + 3 * g.rp,

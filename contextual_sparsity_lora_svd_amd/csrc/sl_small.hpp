@@ -600,10 +600,13 @@ score_swiglu_kernel(const SwiArgs a) {
 // channels).  One 1024-thread workgroup per sequence.  Scores are >= 0, so the
 // fp32 bit pattern is an order-preserving unsigned key.  Four 8-bit radix
 // passes find the k-th largest key tau; the set is every key > tau plus the
-// lowest-index keys == tau, written in ascending channel order.
+// lowest-index keys == tau, written in ascending channel order.  Jobs of up
+// to SEL_MAXN_LDS channels keep their keys in LDS; larger ones (up to
+// SEL_MAXN) in a workspace array of their own.
 // ===========================================================================
 constexpr int SEL_THREADS = 1024;
-constexpr int SEL_MAXN = 32768;
+constexpr int SEL_MAXN_LDS = 32768;
+constexpr int SEL_MAXN = 65536;
 
 // One selection job: its partial sums, channel count, k and outputs.
 struct SelJob {
@@ -616,6 +619,7 @@ struct SelJob {
   int group, head_dim;    // QK: query heads per kv head, head size
   int k;
   int* idx; float* scores;
+  uint32_t* gkeys;        // N > SEL_MAXN_LDS: [batch][N] keys in workspace
 };
 constexpr int SEL_MAXJOBS = 3;
 
@@ -655,9 +659,11 @@ __device__ inline int block_excl_scan(int v, int* wsum, int tid, int* total) {
   return base + incl - v;
 }
 
-static __global__ void __launch_bounds__(SEL_THREADS)
+template <bool GK>
+__global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs a) {
-  extern __shared__ uint32_t keys[];   // N keys
+  // GK: the keys live in the job's workspace array (N > SEL_MAXN_LDS)
+  extern __shared__ uint32_t lkeys[];   // N keys (GK: unused)
   __shared__ int hist[16][256];
   __shared__ int wsum[SEL_THREADS / 64];
   __shared__ uint32_t wmax[SEL_THREADS / 64], wmin[SEL_THREADS / 64];
@@ -667,6 +673,7 @@ select_kernel(const SelectArgs a) {
   const int ctx = a.st.ctx[b];
   const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
   const long long pb = (long long)b * J.nchunk_max;
+  uint32_t* keys = GK ? J.gkeys + (long long)b * J.N : lkeys;
 
   // Scores of SB channels at a time (n0 + j * SEL_THREADS, j < SB): the chunk
   // partials of the SB columns are loaded 4 chunks at a time (4 SB loads in

@@ -33,12 +33,15 @@
  *     No pointer is kept after a call returns.
  *   - All work is enqueued on `stream` (a hipStream_t, NULL = default stream).
  *     Calls never synchronise, except sl_build_estimator (documented there).
- *     The backward calls run their LoRA factor-gradient reductions on a side
- *     stream (one per device, created at first use, default priority), forked
- *     from and joined back to `stream` with events: the call's work completes
- *     in order on `stream` as if it had all been enqueued there.  While
- *     `stream` is being captured into a graph, all of the call's work stays on
- *     it (the graph holds no cross-stream events).
+ *     Calls overlap independent parts of their work on a side stream (default
+ *     priority, non-blocking), forked from and joined back to `stream` with
+ *     events: the call's work completes in order on `stream` as if it had all
+ *     been enqueued there.  Each (device, `stream`) pair gets a side stream of
+ *     its own at its first call, kept until the process ends, so calls on
+ *     independent streams never wait for each other; past 256 such pairs a
+ *     call keeps all of its work on `stream`.  While `stream` is being
+ *     captured into a graph, all of the call's work stays on it (the graph
+ *     holds no cross-stream events).
  *   - Every argument is validated on the host before anything is launched.  On
  *     error nothing is launched, the status says which class of error, and
  *     sl_last_error() (thread-local) holds a message.  Launch failures map to
@@ -179,7 +182,8 @@ sl_status sl_build_estimator(sl_dtype dt, const void* W, int64_t out_f, int64_t 
  *          ties in score go to the lower channel index.
  *   scores [batch, N] fp32 out, optional (NULL = not written): the criterion
  *          (a sum of squares over the sequence's context tokens).
- * 1 <= k <= N <= 65536.  heads is read for QK_NORM only.  The workspace size
+ * 1 <= k <= N <= 65536 (jobs over more than 32768 channels keep their
+ * selection keys in the workspace).  heads is read for QK_NORM only.  The workspace size
  * query takes the same criterion, layout, heads, d_in, rank and N as the call.
  * ------------------------------------------------------------------------- */
 size_t sl_estimate_select_workspace_bytes(sl_criterion crit, const sl_layout* lay,
@@ -228,6 +232,10 @@ sl_status sl_estimate_select_multi(sl_dtype dt, const sl_layout* lay, const void
  *   bwd:  dY [T, d_model] + saved -> dX [T, d_model] and the six LoRA gradients.
  *         X, w, k, idx and the layout must be those of the forward call.
  * d_model % 8 == 0, d_ff % 8 == 0, 1 <= lora_rank <= 32, 1 <= k <= d_ff.
+ * Every matrix a call reads or writes holds fewer than 2^31 elements:
+ * batch*seq_len*d_model, d_ff*d_model and the compact activation buffers
+ * (sum of ctx_len * round_up(k, 8) + output rows * d_ff); SL_ERR_RANGE
+ * otherwise, before anything is launched.
  * ------------------------------------------------------------------------- */
 size_t sl_ffn_saved_bytes(sl_dtype dt, const sl_layout* lay, int64_t d_model, int64_t d_ff,
                           int32_t lora_rank, int32_t k);
@@ -255,7 +263,9 @@ sl_status sl_ffn_bwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w,
  *         dq, dk, dv -> dX and dAq..dBv                      (if dq != NULL)
  *         X and a (the forward's inputs) are read for the factor gradients.
  * d_model, Hq*hd and Hkv*hd multiples of 8; 1 <= lora_rank <= 32;
- * 1 <= k_qk, k_vo <= Hkv*hd.
+ * 1 <= k_qk, k_vo <= Hkv*hd.  Every matrix a call reads or writes holds
+ * fewer than 2^31 elements (T*d_model, T*Hq*hd, Hq*hd*d_model and the compact
+ * projection buffers); SL_ERR_RANGE otherwise, before anything is launched.
  * ------------------------------------------------------------------------- */
 size_t sl_qkvo_saved_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w);
 size_t sl_qkvo_workspace_bytes(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
@@ -294,7 +304,8 @@ sl_status sl_quantize_q4(sl_dtype dt, const void* W, int64_t rows, int64_t cols,
  * Diagnostics (not part of the computation).  When enabled, the library's main
  * launches are bracketed by HIP events on the caller's stream and attributed
  * to the slots below, so a caller can time individual kernels inside a timed
- * region.  Single-threaded use only.  sl_timer_enable(n) keeps room for n
+ * region.  The timer state is per calling thread: it covers the calls that
+ * thread makes.  sl_timer_enable(n) keeps room for n
  * launches (0 disables and frees the events); sl_timer_read waits for the
  * recorded events and returns the slot's total milliseconds and launch count
  * since the last sl_timer_reset.  sl_timer_select(mask) records only the slots
@@ -316,15 +327,19 @@ void sl_timer_reset(void);
 int sl_timer_read(int slot, double* total_ms, int* count);
 
 /* ---------------------------------------------------------------------------
- * GEMM variant (tuning and testing; results agree to the same tolerance).  The
- * bf16 N-gather GEMMs (gate/up, dH, q/k/v, da) run as wide 128 x 512 tiles fed
- * by LDS-DMA when every operand is 16-byte aligned with K a multiple of 8, and
- * as 128 x 256 tiles otherwise.  wide_ng = 1 allows the wide tiles (default),
- * 0 forbids them, a negative value leaves the setting; returns the previous
- * setting.  Process-wide, not synchronised: set it between calls, from one
- * thread.
+ * GEMM variants (tuning and testing; results agree to the same tolerance).
+ * The gather-GEMMs run as 128 x 256 tiles staged through registers, as wide
+ * 128 x 512 N-gather tiles fed by LDS-DMA, or as tall 256 x 256 K-gather
+ * tiles fed by LDS-DMA.  The LDS-DMA tiles need bf16 calls with every operand
+ * 16-byte aligned (wide: K a multiple of 8); the tall tiles are taken when
+ * their grid moves fewer operand bytes per CU than the 128 x 256 one.
+ * `variants` is a bit mask of what the calling thread allows: 1 = wide
+ * tiles, 2 = tall tiles, 4 = tall tiles whatever their grid (with 2); 0 =
+ * 128 x 256 tiles only; a negative value leaves the setting.  Default 3.
+ * Returns the previous setting.  The setting is per calling thread and
+ * applies to the calls that thread makes.
  * ------------------------------------------------------------------------- */
-int sl_gemm_config(int wide_ng);
+int sl_gemm_config(int variants);
 
 #ifdef __cplusplus
 }

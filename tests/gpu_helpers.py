@@ -91,10 +91,11 @@ def check_scores(gpu_scores: np.ndarray, ora_scores: np.ndarray, tol: float, wha
 
 
 @contextlib.contextmanager
-def gemm_variant(wide_ng: int):
-    """Run the block with the wide N-gather GEMM tiles allowed (1) or not (0)."""
+def gemm_variant(variants: int):
+    """Run the block with the given GEMM tile variants allowed (bit mask: 1
+    wide N-gather, 2 tall K-gather, 4 tall whatever the grid; 0 = 128 x 256 only)."""
     import contextual_sparsity_lora_svd_amd as sl
-    prev = sl.gemm_config(wide_ng)
+    prev = sl.gemm_config(variants)
     try:
         yield
     finally:

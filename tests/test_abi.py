@@ -173,11 +173,71 @@ def test_k_rule_matches_oracle(sl):
 
 
 def test_gemm_config_round_trip(sl):
-    """The GEMM variant switch is host state: set, read back, restore."""
+    """The GEMM variant switch is per-thread host state: set, read back, restore."""
+    import threading
     prev = sl.gemm_config(-1)
-    assert prev in (0, 1)
+    assert prev == 3                       # wide and tall tiles allowed by default
     assert sl.gemm_config(0) == prev
     assert sl.gemm_config(-1) == 0
-    assert sl.gemm_config(7) == 0          # any non-zero value allows the wide tiles
-    assert sl.gemm_config(-1) == 1
+    assert sl.gemm_config(15) == 0         # bits past the known variants are dropped
+    assert sl.gemm_config(-1) == 7
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(sl.gemm_config(-1)))
+    t.start()
+    t.join()
+    assert seen == [3]                     # another thread keeps its own default
     sl.gemm_config(prev)
+
+
+def test_operand_extent_limits_rejected_before_launch(sl):
+    """Every matrix the gather-GEMMs address must hold fewer than 2^31 elements;
+    calls past that return SL_ERR_RANGE from host validation (nothing launched:
+    the host has no GPU, so reaching the device check would give 7 or 8)."""
+    L = sl.lib()
+    P = 4096
+    # X / dY: 64 x 4096 tokens x d_model 8192 = 2^31 elements
+    lay = sl.Layout([2048] * 64, 4096)
+    w = _ffn_weights(sl, D=8192, F=128, r=4)
+    assert L.sl_ffn_workspace_bytes(1, lay.ref, 8192, 128, 4, 8) == 0
+    assert L.sl_ffn_fwd(1, lay.ref, ctypes.byref(w), P, 8, P, P, P, 1 << 40, P, 1 << 40, None) == 5
+    assert b"2^31" in L.sl_last_error()
+    # one fewer sequence fits
+    lay2 = sl.Layout([2048] * 63, 4096)
+    assert L.sl_ffn_workspace_bytes(1, lay2.ref, 8192, 128, 4, 8) > 0
+    # a frozen weight of d_ff x d_model = 2^31 elements (d_model and d_ff within their own limits)
+    small = sl.Layout([3, 4], 4)
+    w = _ffn_weights(sl, D=1 << 16, F=1 << 15, r=4)
+    assert L.sl_ffn_fwd(1, small.ref, ctypes.byref(w), P, 8, P, P, P, 1 << 40, P, 1 << 40, None) == 5
+    # the compact G / U / H buffers of a dense warm-up step: 64 x 8192 output rows x d_ff 14336 > 2^31
+    lay3 = sl.Layout([0] * 64, 8192)
+    assert L.sl_ffn_saved_bytes(1, lay3.ref, 64, 14336, 4, 14336) == 0
+    w = _ffn_weights(sl, D=64, F=14336, r=4)
+    assert L.sl_ffn_bwd(1, lay3.ref, ctypes.byref(w), P, 14336, P, P, 1 << 40, P, P,
+                        ctypes.byref(sl.api.SlFfnGrads(*([P] * 6))), P, 1 << 40, None) == 5
+    # q/k/v/o: T x Hq*hd past the limit
+    heads = sl.api.SlHeads(128, 8, 256)               # Hq*hd = 32768
+    wq = sl.api.SlQkvoWeights(64, heads, 4, 1.0, *([P] * 12))
+    lay4 = sl.Layout([4096] * 16, 4096)               # T = 65536: T x 32768 = 2^31
+    st = L.sl_qkvo_fwd(1, lay4.ref, ctypes.byref(wq), P, P, 4, P, 4, P, P, P, P, P, P, 1 << 40, P,
+                       1 << 40, None)
+    assert st == 5
+
+
+def test_select_channel_limit(sl):
+    """Selection runs over up to 65536 channels (keys in the workspace past 32768)."""
+    L = sl.lib()
+    lay = sl.Layout([10, 4], 10)
+    P = 4096
+    ws_lds = L.sl_estimate_select_workspace_bytes(1, lay.ref, None, 64, 8, 32768)
+    ws_big = L.sl_estimate_select_workspace_bytes(1, lay.ref, None, 64, 8, 32769)
+    assert ws_lds > 0 and ws_big > 0
+    # past the LDS limit every sequence's keys take N fp32 words of workspace
+    assert ws_big - ws_lds >= 2 * 32769 * 4
+    assert L.sl_estimate_select_workspace_bytes(1, lay.ref, None, 64, 8, 65536) > 0
+    assert L.sl_estimate_select_workspace_bytes(1, lay.ref, None, 64, 8, 65537) == 0
+    st = L.sl_estimate_select(1, 1, lay.ref, None, P, 64, 8, P, P, None, None, 65537, 4, P, None, P,
+                              1 << 30, None)
+    assert st == 5
+    st = L.sl_estimate_select(1, 1, lay.ref, None, P, 64, 8, P, P, None, None, 65536, 65536, P, None, P,
+                              1 << 40, None)
+    assert st in (7, 8)     # valid: stops at the device check on a host without a GPU

@@ -102,6 +102,35 @@ def test_ffn_multi_tile(dt):
     _multi_case(dt)
 
 
+@pytest.mark.parametrize("case", ["ragged", "multi", "dense_single"])
+def test_ffn_bf16_tall_kgather_tiles(case):
+    """The same cases with the down and dX products on the tall 256 x 256
+    LDS-DMA tiles, taken whatever their grid (ragged groups, a K segment whose
+    channel count is not a multiple of 8, partial row tiles, k = N, k = 1)."""
+    with gemm_variant(1 | 2 | 4):
+        if case == "dense_single":
+            D, F, r, L = 128, 264, 8, 80
+            ctx = [60, 80]
+            p = _ffn_case(D, F, r, ctx, L, "bf16", seed=7)
+            _compare(p, ctx, L, np.tile(np.arange(F, dtype=np.int32), (2, 1)), "bf16")
+            _compare(p, ctx, L, np.array([[5], [263]], dtype=np.int32), "bf16")
+        else:
+            (_ragged_case if case == "ragged" else _multi_case)("bf16")
+
+
+def test_ffn_bf16_tall_tiles_at_group_size():
+    """Context groups of 384 rows (one full and one partial 256-row tile) and
+    a 512-row output group split along K, several column tiles."""
+    with gemm_variant(2):
+        D, F, r, L = 512, 2000, 16, 512
+        ctx = [384, 384]
+        p = _ffn_case(D, F, r, ctx, L, "bf16", seed=21)
+        rng = np.random.default_rng(22)
+        k = 600
+        idx = np.stack([np.sort(rng.choice(F, k, replace=False)) for _ in ctx]).astype(np.int32)
+        _compare(p, ctx, L, idx, "bf16")
+
+
 @pytest.mark.parametrize("case", ["ragged", "multi"])
 def test_ffn_bf16_narrow_gather_tiles(case):
     """The same cases with the wide N-gather tiles forbidden: the 128 x 256

@@ -112,11 +112,13 @@ def test_qkvo_split_calls_and_extremes(dt):
     _compare(p, heads, ctx, L, full, np.array([[0], [nkv - 1]], np.int32), dt)
 
 
-@pytest.mark.parametrize("wide", [1, 0])
-def test_qkvo_multi_tile_bf16(wide):
-    """Several tiles per group; wide = 0 forbids the wide N-gather tiles."""
+@pytest.mark.parametrize("variants", [1, 0, 6])
+def test_qkvo_multi_tile_bf16(variants):
+    """Several tiles per group on each GEMM variant: 1 the wide N-gather tiles,
+    0 the 128 x 256 tiles only, 6 the tall 256 x 256 K-gather tiles whatever
+    their grid (the o and dX products)."""
     from tests.gpu_helpers import gemm_variant
-    with gemm_variant(wide):
+    with gemm_variant(variants):
         _qkvo_multi_tile()
 
 
@@ -363,3 +365,26 @@ def test_side_stream_ordering_and_graph_capture():
         for n, v in ref.items():
             got = outs[n] if n in outs else grads[n]
             assert torch.equal(got, v), f"replay {rep}: {n}"
+
+
+@pytest.mark.parametrize("N", [32768, 65536])
+def test_l2_select_at_channel_limits(N):
+    """L2 criterion and top-k over 32768 channels (keys in LDS) and 65536 (keys
+    in the workspace), two sequences, one of them short."""
+    sl = _api()
+    rng = np.random.default_rng(41)
+    D, L, rank = 64, 48, 8
+    ctx = [48, 21]
+    X = W.round_to_bf16((rng.standard_normal((2 * L, D)) * rng.lognormal(0, 1, D)).astype(np.float32))
+    Pt = W.round_to_bf16(rng.standard_normal((rank, D)).astype(np.float32) * 0.1)
+    Q = W.round_to_bf16(rng.standard_normal((rank, N)).astype(np.float32) * 0.1)
+    k = N // 4 + 3
+    lay = sl.Layout(ctx, L)
+    idx, sc = sl.estimate_select(sl.SL_CRIT_L2, to_dev(X, "bf16"), lay, rank, to_dev(Pt, "bf16"),
+                                 to_dev(Q, "bf16"), None, None, N, k, want_scores=True)
+    torch.cuda.synchronize()
+    ref = np.stack([O.scores_l2(X[O.context_rows(ctx, L, b)], Pt.T, Q, dtype=np.float32)
+                    for b in range(len(ctx))])
+    check_scores(sc.cpu().numpy(), ref, 1e-4, "L2 scores")
+    n_exact = check_selection(idx.cpu().numpy(), ref, k)
+    print(f"\nN={N} k={k} exact sets {n_exact}/2", flush=True)

@@ -79,6 +79,9 @@ SIGNATURES = {
     "sl_estimate_select": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(SlLayout),
                                           ctypes.POINTER(SlHeads), _vp, _i64, _i32, _vp, _vp, _vp,
                                           _vp, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "sl_estimate_select_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(SlLayout),
+                                                  ctypes.POINTER(SlHeads), _vp, _i64, _i32, _vp, _vp, _vp,
+                                                  _vp, _i64, _i32, _vp, _vp, _vp]),
     "sl_estimate_select_multi_workspace_bytes": (_sz, [ctypes.POINTER(SlLayout), _i64, _i32, _i32,
                                                        ctypes.POINTER(SlEstJob)]),
     "sl_estimate_select_multi": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(SlLayout), _vp, _i64, _i32,
@@ -279,6 +282,21 @@ def estimate_select(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, 
                                 _ptr(bufs.scores), _ptr(bufs.ws), bufs.ws.numel(), _stream()),
            "sl_estimate_select")
     return bufs.idx, bufs.scores
+
+
+def estimate_select_noalloc(crit: int, X: torch.Tensor, layout: Layout, rank: int, Pt0, Q0, Pt1, Q1,
+                            N: int, k: int, idx: torch.Tensor, scores: Optional[torch.Tensor] = None,
+                            heads: Optional[Sequence[int]] = None):
+    """estimate_select into caller-owned idx [batch, k] (int32) and optional
+    scores [batch, N] (fp32), with the library's fixed per-device scratch in
+    place of a workspace: the call allocates no device memory."""
+    L = lib()
+    h = SlHeads(*heads) if heads is not None else None
+    _check(L.sl_estimate_select_noalloc(crit, _dtype_code(X), layout.ref, ctypes.byref(h) if h else None,
+                                        _ptr(X), X.shape[1], rank, _ptr(Pt0), _ptr(Q0), _ptr(Pt1), _ptr(Q1),
+                                        N, k, _ptr(idx), _ptr(scores), _stream()),
+           "sl_estimate_select_noalloc")
+    return idx, scores
 
 
 class EstimateMultiBuffers:

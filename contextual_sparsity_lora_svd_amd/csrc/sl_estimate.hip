@@ -245,8 +245,36 @@ sl_est_job one_job(sl_criterion crit, const sl_heads* heads, const void* Pt0, co
   return j;
 }
 
+// ---- allocation-free variant ------------------------------------------------
+// Scratch of sl_estimate_select_noalloc: one array per device, in the code
+// object's device memory (each device that loads the library holds its own
+// copy until the process ends).  In host code `scratch` names a host-side
+// stand-in, never the device array: its device address is resolved once per
+// device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SL_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+sl_status scratch_address(void** out) {
+  int dev = 0;
+  SL_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) SL_FAIL(SL_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      SL_FAIL(SL_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SL_OK;
+}
+
 sl_status estimate_select_call(sl_dtype dt, const sl_layout* lay, const void* X, int64_t d_in, int32_t rank,
-                               int32_t njobs, const sl_est_job* jobs, void* ws, size_t ws_bytes, void* stream) {
+                               int32_t njobs, const sl_est_job* jobs, void* ws, size_t ws_bytes, void* stream,
+                               bool use_scratch = false) {
   if (dt != SL_F32 && dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "unknown dtype %d", (int)dt);
   if (!jobs) SL_FAIL(SL_ERR_NULL, "jobs is NULL");
   SeqTab st;
@@ -262,10 +290,21 @@ sl_status estimate_select_call(sl_dtype dt, const sl_layout* lay, const void* X,
     e.Pt[0] = jobs[j].Pt0; e.Q[0] = jobs[j].Q0; e.Pt[1] = jobs[j].Pt1; e.Q[1] = jobs[j].Q1;
     e.k = jobs[j].k; e.idx = jobs[j].idx; e.scores = jobs[j].scores;
   }
-  if (!X || !ws) SL_FAIL(SL_ERR_NULL, "a required pointer is NULL");
-  if (!aligned16(X) || !aligned16(ws)) SL_FAIL(SL_ERR_ALIGN, "X and ws must be 16-byte aligned");
-  if (ws_bytes < P.total) SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);
-  if ((s = check_arch()) != SL_OK) return s;
+  if (use_scratch) {
+    if (!X) SL_FAIL(SL_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(X)) SL_FAIL(SL_ERR_ALIGN, "X must be 16-byte aligned");
+    if (P.total > (size_t)SL_NOALLOC_SCRATCH_BYTES)
+      SL_FAIL(SL_ERR_WORKSPACE,
+              "this call needs %zu bytes of scratch; the allocation-free variant holds %zu "
+              "(use sl_estimate_select with a workspace)", P.total, (size_t)SL_NOALLOC_SCRATCH_BYTES);
+    if ((s = check_arch()) != SL_OK) return s;
+    if ((s = scratch_address(&ws)) != SL_OK) return s;
+  } else {
+    if (!X || !ws) SL_FAIL(SL_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(X) || !aligned16(ws)) SL_FAIL(SL_ERR_ALIGN, "X and ws must be 16-byte aligned");
+    if (ws_bytes < P.total) SL_FAIL(SL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);
+    if ((s = check_arch()) != SL_OK) return s;
+  }
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   if (dt == SL_BF16) return estimate_select_impl<bf16>(st, X, d_in, P, reinterpret_cast<char*>(ws), strm);
   return estimate_select_impl<float>(st, X, d_in, P, reinterpret_cast<char*>(ws), strm);
@@ -300,6 +339,15 @@ sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* la
   if (crit == SL_CRIT_QK_NORM && !heads) SL_FAIL(SL_ERR_NULL, "heads is NULL for the QK-norm criterion");
   const sl_est_job j = one_job(crit, heads, Pt0, Q0, Pt1, Q1, N, k, idx, scores);
   return estimate_select_call(dt, lay, X, d_in, rank, 1, &j, ws, ws_bytes, stream);
+}
+
+sl_status sl_estimate_select_noalloc(sl_criterion crit, sl_dtype dt, const sl_layout* lay,
+                                     const sl_heads* heads, const void* X, int64_t d_in, int32_t rank,
+                                     const void* Pt0, const void* Q0, const void* Pt1, const void* Q1,
+                                     int64_t N, int32_t k, int32_t* idx, float* scores, void* stream) {
+  if (crit == SL_CRIT_QK_NORM && !heads) SL_FAIL(SL_ERR_NULL, "heads is NULL for the QK-norm criterion");
+  const sl_est_job j = one_job(crit, heads, Pt0, Q0, Pt1, Q1, N, k, idx, scores);
+  return estimate_select_call(dt, lay, X, d_in, rank, 1, &j, nullptr, 0, stream, true);
 }
 
 size_t sl_estimate_select_multi_workspace_bytes(const sl_layout* lay, int64_t d_in, int32_t rank,

@@ -196,6 +196,25 @@ sl_status sl_estimate_select(sl_criterion crit, sl_dtype dt, const sl_layout* la
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sl_estimate_select without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as sl_estimate_select,
+ * minus ws / ws_bytes: the scratch is a fixed array of SL_NOALLOC_SCRATCH_BYTES
+ * in the library's device memory, one per device, held from the library's
+ * load until the process ends.  A call whose sl_estimate_select_workspace_bytes
+ * exceeds that size returns SL_ERR_WORKSPACE (nothing launched).  The call
+ * allocates nothing.  Every call on one device shares that device's array, so
+ * calls that overlap on one device (different streams, or different threads
+ * without stream order) race; calls in one stream's order do not.  Nothing in
+ * the array needs to start at zero: every call writes what it reads.
+ * ------------------------------------------------------------------------- */
+#define SL_NOALLOC_SCRATCH_BYTES (32u << 20)
+sl_status sl_estimate_select_noalloc(sl_criterion crit, sl_dtype dt, const sl_layout* lay,
+                                     const sl_heads* heads, const void* X, int64_t d_in, int32_t rank,
+                                     const void* Pt0, const void* Q0, const void* Pt1, const void* Q1,
+                                     int64_t N, int32_t k, int32_t* idx, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
  * a1-a3 for several criteria over one input (SparseLoRA article §一, §二, §三:
  * an attention layer scores q/k by the QK-norm and v/o by the L2 norm of the
  * same layer input).  Same results as one sl_estimate_select call per job, but

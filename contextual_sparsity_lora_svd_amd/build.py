@@ -25,6 +25,10 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions.  The estimator's kernels feed MFMA results straight to
+# VALU work, so their accumulators are kept in VGPRs (no AGPR round trip).
+EXTRA = {"sl_estimate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _hipcc() -> str:
     h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -33,7 +37,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

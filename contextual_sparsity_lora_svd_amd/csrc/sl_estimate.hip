@@ -33,12 +33,11 @@ struct EJob {
   int nchunk_max;
   int zcol;         // first Zh column of the job's projections (rep columns each)
   size_t w_p0, w_p1;
-  size_t w_keys;    // select keys in workspace (every job, when some N > SEL_MAXN_LDS)
+  size_t w_keys;    // the job's selection keys [nseq][N]
 };
 
 struct EstPlan {
   int njobs, nproj, rank, rep, ldz;
-  bool gkeys;       // the selection keeps its keys in workspace
   EJob job[SL_EST_MAXJOBS];
   size_t w_zh, w_skp, total;
 };
@@ -99,9 +98,7 @@ sl_status plan_estimate(const SeqTab& st, long long d_in, int rank, int njobs, c
   }
   long long nmax = 0;
   for (int j = 0; j < njobs; ++j) nmax = P.job[j].N > nmax ? P.job[j].N : nmax;
-  P.gkeys = nmax > SEL_MAXN_LDS;
-  for (int j = 0; j < njobs; ++j)
-    P.job[j].w_keys = P.gkeys ? bp.take((size_t)st.nseq * P.job[j].N * 4) : 0;
+  for (int j = 0; j < njobs; ++j) P.job[j].w_keys = bp.take((size_t)st.nseq * P.job[j].N * 4);
   P.w_skp = bp.take((size_t)skinny_part_floats(T, d_in) * 4);   // K-sliced stage 1
   P.total = bp.off;
   return SL_OK;
@@ -125,9 +122,15 @@ sl_status check_jobs(int njobs, const sl_est_job* jobs, long long d_in, int rank
 template <typename T>
 sl_status launch_swiglu(const SwiArgs& a, int nseq, int rank, hipStream_t s) {
   const dim3 grid(ceil_div(a.N, 128), a.nchunk_max, nseq), block(SW_THREADS);
-  if (rank <= 8) hipLaunchKernelGGL((score_swiglu_kernel<T, 8>), grid, block, 0, s, a);
-  else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_kernel<T, 16>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((score_swiglu_kernel<T, 32>), grid, block, 0, s, a);
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (rank <= 8) hipLaunchKernelGGL((score_swiglu_split_kernel<8>), grid, block, 0, s, a);
+    else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_split_kernel<16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_swiglu_split_kernel<32>), grid, block, 0, s, a);
+  } else {
+    if (rank <= 8) hipLaunchKernelGGL((score_swiglu_kernel<T, 8>), grid, block, 0, s, a);
+    else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_kernel<T, 16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_swiglu_kernel<T, 32>), grid, block, 0, s, a);
+  }
   SL_HIP(hipGetLastError());
   return SL_OK;
 }
@@ -144,17 +147,38 @@ sl_status launch_gram(const GramArgs& a, int nproj, int nseq, int rank, hipStrea
   return SL_OK;
 }
 
-sl_status launch_select(const SelectArgs& a, int nseq, int nmax, bool gkeys, hipStream_t s) {
+// Selection launch(es).  With one or two partial sums per channel (every
+// job's chunks x terms <= SEL_FUSE_LOADS, at most 16 keys per thread: the
+// L2 and MHA QK-norm criteria) the select kernel forms the keys itself;
+// otherwise score_finish_kernel forms them first with one thread per channel
+// over many workgroups (one workgroup reading many partials is bound by its
+// CU's outstanding loads: 15k cycles against 8k for the two launches at the
+// LLaMA2-7B FFN shape).
+constexpr int SEL_FUSE_LOADS = 2;
+
+sl_status launch_select(const SelectArgs& a, int nseq, int nmax, bool fuse, hipStream_t s) {
   static std::once_flag attr_once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(attr_once, [] {
-    attr_err = hipFuncSetAttribute((const void*)select_kernel<false>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, SEL_MAXN_LDS * 4);
+    attr_err = hipFuncSetAttribute((const void*)select_kernel<16, true>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * SEL_THREADS * 4);
   });
   SL_HIP(attr_err);
   timer_begin(TS_SELECT, s);
-  if (gkeys) hipLaunchKernelGGL(select_kernel<true>, dim3(nseq, a.njobs), dim3(SEL_THREADS), 0, s, a);
-  else hipLaunchKernelGGL(select_kernel<false>, dim3(nseq, a.njobs), dim3(SEL_THREADS), (size_t)nmax * 4, s, a);
+  const dim3 grid(nseq, a.njobs), block(SEL_THREADS);
+  if (fuse && nmax <= 4 * SEL_THREADS) {
+    hipLaunchKernelGGL((select_kernel<4, true>), grid, block, (size_t)nmax * 4, s, a);
+  } else if (fuse && nmax <= 16 * SEL_THREADS) {
+    hipLaunchKernelGGL((select_kernel<16, true>), grid, block, (size_t)nmax * 4, s, a);
+  } else {
+    hipLaunchKernelGGL(score_finish_kernel, dim3(ceil_div(nmax, SF_THREADS), nseq, a.njobs), dim3(SF_THREADS), 0,
+                       s, a);
+    if (nmax <= 4 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<4, false>), grid, block, 0, s, a);
+    else if (nmax <= 16 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<16, false>), grid, block, 0, s, a);
+    else if (nmax <= SEL_KPT_REG * SEL_THREADS)
+      hipLaunchKernelGGL((select_kernel<SEL_KPT_REG, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((select_kernel<0, false>), grid, block, 0, s, a);
+  }
   timer_end(TS_SELECT, s);
   SL_HIP(hipGetLastError());
   return SL_OK;
@@ -228,10 +252,15 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
     q.N = (int)e.N; q.N0 = e.N0;
     if (q.qk) { q.group = e.heads.n_q_heads / e.heads.n_kv_heads; q.head_dim = e.heads.head_dim; }
     q.k = e.k; q.idx = e.idx; q.scores = e.scores;
-    q.gkeys = P.gkeys ? reinterpret_cast<uint32_t*>(ws + e.w_keys) : nullptr;
+    q.gkeys = reinterpret_cast<uint32_t*>(ws + e.w_keys);
     nmax = q.N > nmax ? q.N : nmax;
   }
-  return launch_select(se, st.nseq, nmax, P.gkeys, stream);
+  bool fuse = true;
+  for (int j = 0; j < P.njobs; ++j) {
+    const SelJob& q = se.job[j];
+    fuse &= (long long)q.nchunk_max * (q.qk ? q.group + 1 : 1) <= SEL_FUSE_LOADS;
+  }
+  return launch_select(se, st.nseq, nmax, fuse, stream);
 }
 
 sl_est_job one_job(sl_criterion crit, const sl_heads* heads, const void* Pt0, const void* Q0, const void* Pt1,

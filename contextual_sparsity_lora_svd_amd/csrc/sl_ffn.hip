@@ -35,22 +35,6 @@ struct FfnGeom {
       ws_bytes;
 };
 
-int choose_ksplit(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
-  if (st.T_out == 0) return 1;
-  const long long kt_out = (K_out + bk - 1) / bk;
-  int ks;
-  if (st.T_ctx > 0 && K_ctx > 0) {
-    ks = (int)((K_out + K_ctx / 2) / K_ctx);
-  } else {
-    const int tiles = ceil_div(st.T_out, G_BM) * ceil_div(D, G_BN);
-    ks = 512 / (tiles > 0 ? tiles : 1);
-  }
-  if (ks > kt_out / 8) ks = (int)(kt_out / 8);
-  if (ks > 16) ks = 16;
-  if (ks < 1) ks = 1;
-  return ks;
-}
-
 sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, int r, int k,
                    FfnGeom& g) {
   if (dt != SL_F32 && dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "unknown dtype %d", (int)dt);
@@ -75,8 +59,8 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.comp = (long long)st.T_ctx * g.ldk + (long long)st.T_out * g.ldF;
   g.c_out_off = (long long)st.T_ctx * g.ldk;
   const int bk = dt == SL_BF16 ? 64 : 32;
-  g.ks_down = choose_ksplit(st, k + g.rp, F + g.rp, g.D, bk);
-  g.ks_dx = choose_ksplit(st, 2LL * k + 2 * g.rp, 2 * F + 2 * g.rp, g.D, bk);
+  g.ks_down = kg_choose_ksplit(st, k + g.rp, F + g.rp, g.D, bk, dt == SL_BF16);
+  g.ks_dx = kg_choose_ksplit(st, 2LL * k + 2 * g.rp, 2 * F + 2 * g.rp, g.D, bk, dt == SL_BF16);
   g.RM1 = cr_rm(g.esz, g.rp);
   g.RM2 = cr_rm(g.esz, 2 * g.rp);
   g.chunk = cr_chunk(g.esz);

@@ -109,6 +109,39 @@ inline sl_status launch_skinny(SkinnyArgs& a, hipStream_t s) {
   return SL_OK;
 }
 
+// Split-K of a K-gather launch's output group, whose K (every channel) is much
+// longer than a context group's (its selected channels).  Pieces balanced
+// against the context tiles: round(K_out / K_ctx).  When the context tiles
+// take at most half a round of the machine, the pieces are capped so that the
+// whole launch fits one round: past that, more pieces add fp32 partial traffic
+// and a second round, not balance (down product at 99 % sparsity, 4 x 512
+// tokens: 4 pieces 114 us, 8 pieces 127 us, 16 pieces 132 us).  Tile geometry:
+// the tall 256 x 256 tile (one per CU) for bf16, 128 x 256 (two per CU) else.
+inline int kg_choose_ksplit(const SeqTab& st, long long K_ctx, long long K_out, long long N, int bk, bool tall) {
+  if (st.T_out == 0) return 1;
+  const long long kt_out = (K_out + bk - 1) / bk;
+  const int bm = tall ? G_BM_TALL : G_BM;
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
+  const long long slots = (tall ? 1 : 2) * (long long)cus;
+  const long long ntn = (N + G_BN - 1) / G_BN;
+  long long ctx_tiles = 0;
+  for (int b = 0; b < st.nseq; ++b) ctx_tiles += (st.ctx[b] + bm - 1) / bm * ntn;
+  const long long out_tiles = (st.T_out + bm - 1) / bm * ntn;
+  long long ks;
+  if (st.T_ctx > 0 && K_ctx > 0) ks = (K_out + K_ctx / 2) / K_ctx;
+  else ks = slots / (out_tiles > 0 ? out_tiles : 1);
+  if (2 * ctx_tiles <= slots && out_tiles > 0) {
+    long long fill = (slots - ctx_tiles) / out_tiles;
+    if (fill < 1) fill = 1;
+    if (ks > fill) ks = fill;
+  }
+  if (ks > kt_out / 8) ks = kt_out / 8;
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
+  return (int)ks;
+}
+
 // Token rows per column-reduction chunk and the padded width of its partials.
 inline int cr_chunk(size_t esz) { return esz == 2 ? CRM_CHUNK : CR_CHUNK; }
 inline int cr_rm(size_t esz, int R) {

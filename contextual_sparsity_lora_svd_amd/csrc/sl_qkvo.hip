@@ -42,18 +42,6 @@ struct QkvoGeom {
       w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv_o, w_inv_q, w_inv_k, w_inv_v, w_iota, w_rp, w_skp, ws_bytes;
 };
 
-int choose_ks(const SeqTab& st, long long K_ctx, long long K_out, int D, int bk) {
-  if (st.T_out == 0) return 1;
-  const long long kt_out = (K_out + bk - 1) / bk;
-  int ks;
-  if (st.T_ctx > 0 && K_ctx > 0) ks = (int)((K_out + K_ctx / 2) / K_ctx);
-  else ks = 512 / std::max(1, ceil_div(st.T_out, G_BM) * ceil_div(D, G_BN));
-  if (ks > kt_out / 8) ks = (int)(kt_out / 8);
-  if (ks > 16) ks = 16;
-  if (ks < 1) ks = 1;
-  return ks;
-}
-
 sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w, int kqk, int kvo,
                     bool check_k, QkvoGeom& g) {
   if (dt != SL_F32 && dt != SL_BF16) SL_FAIL(SL_ERR_DTYPE, "unknown dtype %d", (int)dt);
@@ -94,9 +82,9 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   for (const Comp* c : {&g.cq, &g.ck, &g.cv, &g.co})
     if ((s = check_extent("a compact projection buffer", 1, c->elems)) != SL_OK) return s;
   const int bk = dt == SL_BF16 ? 64 : 32;
-  g.ks_o = choose_ks(st, g.ko + g.rp, g.nq + g.rp, g.D, bk);
-  g.ks_dx = choose_ks(st, (long long)g.kq + g.kqk + g.kvo + 3 * g.rp,
-                      (long long)g.nq + 2 * g.nkv + 3 * g.rp, g.D, bk);
+  g.ks_o = kg_choose_ksplit(st, g.ko + g.rp, g.nq + g.rp, g.D, bk, dt == SL_BF16);
+  g.ks_dx = kg_choose_ksplit(st, (long long)g.kq + g.kqk + g.kvo + 3 * g.rp,
+                             (long long)g.nq + 2 * g.nkv + 3 * g.rp, g.D, bk, dt == SL_BF16);
   const size_t T = g.T, e = g.esz, rp = g.rp, B = st.nseq;
   Bump sv;
   g.s_zqkv = sv.take(T * 3 * rp * 4);

@@ -34,6 +34,7 @@ constexpr int SK_LDB = SK_CB + 16;         // LDS row pitch in bytes (bank sprea
 constexpr int SK_SLICE_BYTES = 1024;       // bytes of a row per K slice (4 chunks)
 constexpr int SK_MAXSL = 64;               // slices per row block at most
 constexpr int SK_PC = 64;                  // partial-sum row pitch at most (pc = NB*16)
+constexpr int SK_PF = SK_SLICE_BYTES / SK_CB;   // chunks loaded at once (a whole slice)
 
 struct SkinnyArgs {
   SeqTab st;
@@ -135,17 +136,20 @@ __device__ inline int skinny_padded_cols(const SkinnyArgs& a) {
   return p;
 }
 
+// Keep the first `valid` elements of a 16-byte vector and zero the rest,
+// without branches: the selects depend on `valid` only, so a batch of loads
+// can all be in flight before the first mask is applied.
 template <typename T>
 __device__ inline uint4 mask_tail(uint4 v, int valid) {
-  // keep the first `valid` elements of a 16-byte vector, zero the rest
-  constexpr int E = 16 / sizeof(T);
-  if (valid >= E) return v;
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e < valid) continue;
-    if constexpr (sizeof(T) == 2) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    else w[e] = 0u;
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t m = valid >= 2 * i + 2 ? 0xFFFFFFFFu : (valid == 2 * i + 1 ? 0x0000FFFFu : 0u);
+      w[i] &= m;
+    } else {
+      w[i] = valid > i ? w[i] : 0u;
+    }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -227,32 +231,36 @@ skinny_kernel(const SkinnyArgs a) {
         c -= a.nbk[j];
       }
     }
-    if (!brow[i]) brow[i] = A;   // never dereferenced
+    if (!brow[i]) brow[i] = arow[0];   // in range; loaded and zeroed
   }
 
-  uint4 ra[AL], rbv[BL];
-  auto load = [&](int c) {
-    const int k = kbeg + c * KC + q * E;
-    const int kc = k < kend ? k : kbeg;     // in-range address for tail pieces
+  // SK_PF chunks are loaded at once, unconditionally (a chunk past the slice
+  // reads in-range addresses and is never stored), so all their loads are in
+  // flight together; the masks are applied on the way into LDS.
+  uint4 ra[SK_PF][AL], rbv[SK_PF][BL];
+  auto load = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const uint4*>(arow[i] + kc);
+    for (int j = 0; j < SK_PF; ++j) {
+      const int k = kbeg + (c0 + j) * KC + q * E;
+      const int kc = k < kend ? k : kbeg;
 #pragma unroll
-    for (int i = 0; i < BL; ++i)
-      if (bok[i]) rbv[i] = *reinterpret_cast<const uint4*>(brow[i] + kc);
+      for (int i = 0; i < AL; ++i) ra[j][i] = *reinterpret_cast<const uint4*>(arow[i] + kc);
+#pragma unroll
+      for (int i = 0; i < BL; ++i) rbv[j][i] = *reinterpret_cast<const uint4*>(brow[i] + kc);
+    }
   };
-  auto store = [&](int c) {
+  auto store = [&](int c, int j) __attribute__((always_inline)) {
     const int valid = kend - (kbeg + c * KC + q * E);
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int r = tid / PR + i * (SK_THREADS / PR);
-      *reinterpret_cast<uint4*>(As + r * SK_LDB + q * 16) = mask_tail<T>(ra[i], valid);
+      *reinterpret_cast<uint4*>(As + r * SK_LDB + q * 16) = mask_tail<T>(ra[j][i], valid);
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int r = tid / PR + i * (SK_THREADS / PR);
       if (r < NB * 16)
-        *reinterpret_cast<uint4*>(Bs + r * SK_LDB + q * 16) =
-            bok[i] ? mask_tail<T>(rbv[i], valid) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(Bs + r * SK_LDB + q * 16) = mask_tail<T>(rbv[j][i], bok[i] ? valid : 0);
     }
   };
 
@@ -295,13 +303,18 @@ skinny_kernel(const SkinnyArgs a) {
     }
   };
 
-  if (nch > 0) load(0);
-  for (int c = 0; c < nch; ++c) {
-    store(c);
-    __syncthreads();
-    if (c + 1 < nch) load(c + 1);
-    compute();
-    __syncthreads();
+  for (int c0 = 0; c0 < nch; c0 += SK_PF) {
+    load(c0);
+    __builtin_amdgcn_sched_barrier(0);   // the batch's loads all issue before the first store waits
+#pragma unroll
+    for (int j = 0; j < SK_PF; ++j) {
+      if (c0 + j < nch) {
+        store(c0 + j, j);
+        __syncthreads();
+        compute();
+        __syncthreads();
+      }
+    }
   }
 
   // accumulator element e: row 4*(lane>>4) + e of the wave's 16, column lane & 15
@@ -595,17 +608,165 @@ score_swiglu_kernel(const SwiArgs a) {
   if (h == 0 && n < a.N) a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = v;
 }
 
+// bf16 form of the SwiGLU criterion.  Each context token's fp32 projection z
+// is split exactly into three bf16 terms, z = hi + mid + lo (each term takes
+// the next 8 significant bits; the bf16 factor Q is exact), so the bf16 matrix
+// cores form g = sum_q (hi_q + mid_q + lo_q) Q_q from exact products with fp32
+// accumulation, the accuracy of an fp32 dot product, in one 16x16x32 MFMA per
+// 16 tokens x 16 channels and 32 k (k = s RM + q for term s, rank index q;
+// padding k add zero).  The gate projection is scaled by -log2(e) first, so
+// the MFMA yields g' = -g log2(e), exp2(g') = e^{-g}, and
+//   (SiLU(g) u)^2 = (g' u / (1 + exp2(g')))^2 ln(2)^2,
+// with ln(2)^2 applied once per channel sum.  Per wave 32 channels (two
+// 16-column blocks) over the chunk's SW_CHUNK tokens (eight 16-row blocks);
+// a lane's accumulator values all belong to its column, so the square and the
+// token sum stay in the lane until the four lane groups are added at the end.
+template <int RM>
+__global__ void __launch_bounds__(SW_THREADS)
+score_swiglu_split_kernel(const SwiArgs a) {
+  constexpr int KA = (3 * RM + 31) / 32 * 32;   // k of the split products, whole MFMA steps
+  constexpr int NKB = KA / 32;
+  constexpr int PITCH = KA * 2 + 16;            // LDS row pitch in bytes (bank spread)
+  __shared__ __attribute__((aligned(16))) unsigned char zs[2][SW_CHUNK * PITCH];   // [g/u][token][k]
+  const int b = blockIdx.z, chunk = blockIdx.y;
+  const int ctx = a.st.ctx[b];
+  const int t0 = chunk * SW_CHUNK;
+  if (t0 >= ctx) return;
+  const int nt = min(SW_CHUNK, ctx - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // B operands (the factors' columns, k = s RM + q -> Q[q][n]) first, so
+  // their latency overlaps the Z staging
+  const uint16_t* Qp[2] = {reinterpret_cast<const uint16_t*>(a.Q0), reinterpret_cast<const uint16_t*>(a.Q1)};
+  bf16x8_t_s bq[2][2][NKB];   // [g/u][column block][k step]
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int n = blockIdx.x * 128 + wave * 32 + cb * 16 + col;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int k0 = kb * 32 + 8 * grp;
+        const int s = k0 / RM, q0 = k0 % RM;
+        uint16_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = (s < 3 && q0 + j < a.rank && n < a.N) ? Qp[pj][(long long)(q0 + j) * a.N + n] : (uint16_t)0;
+        uint4 w = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                             v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        bq[pj][cb][kb] = __builtin_bit_cast(bf16x8_t_s, w);
+      }
+    }
+  // Z staging: thread (t, pj) splits one token's RM projections into three
+  // bf16 rows hi | mid | lo at k = 0, RM, 2 RM; rows past the context are 0
+  {
+    const int t = tid >> 1, pj = tid & 1;
+    static_assert(SW_THREADS == 2 * SW_CHUNK, "one thread per token and projection");
+    const float sc = pj == 0 ? -1.4426950408889634f : 1.f;   // -log2(e) on the gate
+    const float* zr = a.Zh + (long long)(b * a.st.L + t0 + t) * a.ldz + (pj ? a.zc1 : a.zc0);
+    unsigned char* row = zs[pj] + t * PITCH;
+    static_assert(RM % 8 == 0, "whole 16-byte groups of k");
+#pragma unroll
+    for (int q0 = 0; q0 < RM; q0 += 8) {
+      uint32_t w[3][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < nt && q0 + 4 * h < a.rank) z4 = *reinterpret_cast<const float4*>(zr + q0 + 4 * h);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          uint16_t hi[2], mid[2], lo[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float z = q0 + 4 * h + j + i < a.rank ? zz[j + i] * sc : 0.f;
+            hi[i] = f2bf(z);
+            const float r1 = z - bf2f(hi[i]);
+            mid[i] = f2bf(r1);
+            lo[i] = f2bf(r1 - bf2f(mid[i]));
+          }
+          w[0][2 * h + j / 2] = hi[0] | (uint32_t)hi[1] << 16;
+          w[1][2 * h + j / 2] = mid[0] | (uint32_t)mid[1] << 16;
+          w[2][2 * h + j / 2] = lo[0] | (uint32_t)lo[1] << 16;
+        }
+      }
+#pragma unroll
+      for (int sgm = 0; sgm < 3; ++sgm)
+        *reinterpret_cast<uint4*>(row + 2 * (sgm * RM + q0)) = make_uint4(w[sgm][0], w[sgm][1], w[sgm][2], w[sgm][3]);
+    }
+#pragma unroll
+    for (int k = 3 * RM; k < KA; k += 8) *reinterpret_cast<uint4*>(row + 2 * k) = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  auto mm = [&](int rb, f32x4_t (&g)[2], f32x4_t (&u)[2]) __attribute__((always_inline)) {
+    const int off = (rb * 16 + col) * PITCH + 16 * grp;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) { g[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f}; u[cb] = g[cb]; }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bf16x8_t_s ag = *reinterpret_cast<const bf16x8_t_s*>(zs[0] + off + 64 * kb);
+      const bf16x8_t_s au = *reinterpret_cast<const bf16x8_t_s*>(zs[1] + off + 64 * kb);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        g[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bq[0][cb][kb], g[cb], 0, 0, 0);
+        u[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bq[1][cb][kb], u[cb], 0, 0, 0);
+      }
+    }
+  };
+  auto act = [&](const f32x4_t (&g)[2], const f32x4_t (&u)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float h = g[cb][e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g[cb][e])) * u[cb][e];
+        acc[cb][e] = fmaf(h, h, acc[cb][e]);
+      }
+  };
+  // two row blocks in flight: block rb + 1's products are issued before
+  // block rb's activation (row blocks past the context hold zero rows and
+  // add exactly 0)
+  static_assert(SW_CHUNK / 16 == 8, "eight row blocks per chunk");
+  f32x4_t g0[2], u0[2], g1[2], u1[2];
+  mm(0, g0, u0);
+#pragma unroll
+  for (int rb = 0; rb < 8; rb += 2) {
+    mm(rb + 1, g1, u1);
+    __builtin_amdgcn_sched_barrier(0);
+    act(g0, u0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rb + 2 < 8) mm(rb + 2, g0, u0);
+    __builtin_amdgcn_sched_barrier(0);
+    act(g1, u1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // lane sums (4 tokens each) -> column sums over the four lane groups
+  constexpr float LN2SQ = 0.480453013918201424667f;   // ln(2)^2
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    float v = (acc[cb][0] + acc[cb][1]) + (acc[cb][2] + acc[cb][3]);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    const int n = blockIdx.x * 128 + wave * 32 + cb * 16 + col;
+    if (grp == 0 && n < a.N) a.part[((long long)b * a.nchunk_max + chunk) * a.N + n] = v * LN2SQ;
+  }
+}
+
 // ===========================================================================
 // Per-sequence top-k (SparseLoRA article §一: per input, keep the most active
-// channels).  One 1024-thread workgroup per sequence.  Scores are >= 0, so the
-// fp32 bit pattern is an order-preserving unsigned key.  Four 8-bit radix
-// passes find the k-th largest key tau; the set is every key > tau plus the
-// lowest-index keys == tau, written in ascending channel order.  Jobs of up
-// to SEL_MAXN_LDS channels keep their keys in LDS; larger ones (up to
-// SEL_MAXN) in a workspace array of their own.
+// channels), in two launches.  score_finish_kernel adds each channel's
+// partial sums (many workgroups, chunks in chunk order) and writes the scores
+// as keys: scores are >= 0, so the fp32 bit pattern is an order-preserving
+// unsigned key.  select_kernel, one 1024-thread workgroup per sequence and
+// job, finds the k-th largest key tau with radix passes of up to 8 bits and
+// writes every key > tau plus the lowest-index keys == tau, in ascending
+// channel order, each thread owning a contiguous range of keys (in registers
+// up to SEL_KPT_REG keys per thread; SEL_MAXN channels at most).
 // ===========================================================================
 constexpr int SEL_THREADS = 1024;
-constexpr int SEL_MAXN_LDS = 32768;
+constexpr int SEL_KPT_REG = 32;
 constexpr int SEL_MAXN = 65536;
 
 // One selection job: its partial sums, channel count, k and outputs.
@@ -619,7 +780,7 @@ struct SelJob {
   int group, head_dim;    // QK: query heads per kv head, head size
   int k;
   int* idx; float* scores;
-  uint32_t* gkeys;        // N > SEL_MAXN_LDS: [batch][N] keys in workspace
+  uint32_t* gkeys;        // [batch][N] keys in workspace
 };
 constexpr int SEL_MAXJOBS = 3;
 
@@ -629,6 +790,47 @@ struct SelectArgs {
   int njobs;
   SelJob job[SEL_MAXJOBS];
 };
+
+// Scores of one sequence and job from the criterion's partial sums: grid
+// (channel blocks, sequences, jobs), one channel per thread.  The L2-type
+// score of channel n is the sum of its chunk partials in chunk order; the QK
+// score is sk_n sq_n with sk_n the key projection's sum and sq_n the sum over
+// the kv head's query heads of the query projection's sums.
+constexpr int SF_THREADS = 256;
+static __global__ void __launch_bounds__(SF_THREADS) score_finish_kernel(const SelectArgs a) {
+  const SelJob& J = a.job[blockIdx.z];
+  const int b = blockIdx.y;
+  const int n = (int)blockIdx.x * SF_THREADS + (int)threadIdx.x;
+  if (n >= J.N) return;
+  const int ctx = a.st.ctx[b];
+  const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
+  const long long pb = (long long)b * J.nchunk_max;
+  // chunks added in order, eight loads in flight
+  auto colsum = [&](const float* part, int ld, int col) {
+    float v = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = c0 + u < nch ? part[(pb + c0 + u) * ld + col] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nch) v += t[u];
+    }
+    return v;
+  };
+  float sc;
+  if (!J.qk) {
+    sc = colsum(J.part0, J.N0, n);
+  } else {
+    sc = colsum(J.part1, J.N, n);
+    float sq = 0.f;
+    for (int h = 0; h < J.group; ++h)
+      sq += colsum(J.part0, J.N0, ((n / J.head_dim) * J.group + h) * J.head_dim + n % J.head_dim);
+    sc *= sq;
+  }
+  if (J.scores) J.scores[(long long)b * J.N + n] = sc;
+  J.gkeys[(long long)b * J.N + n] = __float_as_uint(sc);
+}
 
 __device__ inline int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -640,100 +842,126 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive prefix over the workgroup's SEL_THREADS values (wave scans plus one
-// pass over the 16 wave totals); `total` receives the sum when non-null.
-__device__ inline int block_excl_scan(int v, int* wsum, int tid, int* total) {
+// Exclusive prefix of a pair of counts over the workgroup, packed as
+// (a << 32) | b in 64 bits (each sum stays below 2^32).
+__device__ inline unsigned long long block_excl_scan2(unsigned long long v, unsigned long long* wsum2, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
+  unsigned long long incl = v;
 #pragma unroll
-  for (int w = 0; w < SEL_THREADS / 64; ++w) {
-    const int x = wsum[w];
-    base += w < wave ? x : 0;
-    tot += x;
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
   }
-  if (total) *total = tot;
-  __syncthreads();   // wsum is reused by the next scan
+  if (lane == 63) wsum2[wave] = incl;
+  __syncthreads();
+  unsigned long long base = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_THREADS / 64; ++w) base += w < wave ? wsum2[w] : 0ull;
   return base + incl - v;
 }
 
-template <bool GK>
+template <int KPT, bool FUSED>
 __global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs a) {
-  // GK: the keys live in the job's workspace array (N > SEL_MAXN_LDS)
-  extern __shared__ uint32_t lkeys[];   // N keys (GK: unused)
+  // Thread tid owns keys [tid per, tid per + per), per = ceil(N / SEL_THREADS).
+  // KPT > 0: they are held in registers (per <= KPT), so the radix passes and
+  // the ordered compaction read no memory; KPT == 0: they are re-read from the
+  // workspace (L2-resident) in every pass.  FUSED (KPT > 0, few partials per
+  // channel): the keys are formed here from the criterion's partial sums, with
+  // the arithmetic of score_finish_kernel, and no finish launch precedes.
+  extern __shared__ float sdyn[];   // FUSED: the N scores (dynamic, N * 4 bytes)
   __shared__ int hist[16][256];
-  __shared__ int wsum[SEL_THREADS / 64];
+  __shared__ int cnt_s[4];
+  __shared__ unsigned long long wsum2[SEL_THREADS / 64];
   __shared__ uint32_t wmax[SEL_THREADS / 64], wmin[SEL_THREADS / 64];
-  __shared__ int s_sel[2];
+  __shared__ int s_sel[3];
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const SelJob& J = a.job[blockIdx.y];
-  const int ctx = a.st.ctx[b];
-  const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
-  const long long pb = (long long)b * J.nchunk_max;
-  uint32_t* keys = GK ? J.gkeys + (long long)b * J.N : lkeys;
+  const int N = J.N;
+  const int per = (N + SEL_THREADS - 1) / SEL_THREADS;
+  const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
+  const uint32_t* gk = J.gkeys + (long long)b * N;
 
-  // Scores of SB channels at a time (n0 + j * SEL_THREADS, j < SB): the chunk
-  // partials of the SB columns are loaded 4 chunks at a time (4 SB loads in
-  // flight) and added per column in chunk order.
-  constexpr int SB = 4;
-  auto sumb = [&](const float* part, int ld, const int* col, float* out) {
+  uint32_t key[KPT > 0 ? KPT : 1];
+  if constexpr (FUSED) {
+    static_assert(KPT > 0, "fused keys live in registers");
+    // Scores with coalesced loads (channel n = tid + SEL_THREADS i, up to four
+    // chunks' loads in flight at once), staged in LDS, then read back as this
+    // thread's contiguous range.  Same arithmetic and order as
+    // score_finish_kernel: chunks added in order from 0, QK = sk * sq.
+    const int ctx = a.st.ctx[b];
+    const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
+    const long long pb = (long long)b * J.nchunk_max;
+    constexpr int IB = KPT < 8 ? KPT : 8;   // channels per thread per load batch
+    auto colsum = [&](const float* part, int ld, auto col, float (&out)[KPT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < SB; ++j) out[j] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-      float v[4][SB];
+      for (int i = 0; i < KPT; ++i) out[i] = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int i0 = 0; i0 < KPT; i0 += IB) {
+        for (int c0 = 0; c0 < nch; c0 += 4) {
+          float t[4][IB];
 #pragma unroll
-        for (int j = 0; j < SB; ++j)
-          if (c0 + u < nch && col[j] >= 0) v[u][j] = part[(pb + c0 + u) * ld + col[j]];
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+            for (int i = 0; i < IB; ++i) {
+              const int n = tid + SEL_THREADS * (i0 + i);
+              t[u][i] = (c0 + u < nch && n < N) ? part[(pb + c0 + u) * ld + col(n)] : 0.f;
+            }
 #pragma unroll
-        for (int j = 0; j < SB; ++j)
-          if (c0 + u < nch && col[j] >= 0) out[j] += v[u][j];
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < IB; ++i)
+              if (c0 + u < nch) out[i0 + i] += t[u][i];
+        }
+      }
+    };
+    float sc[KPT];
+    if (!J.qk) {
+      colsum(J.part0, J.N0, [](int n) { return n; }, sc);
+    } else {
+      colsum(J.part1, J.N, [](int n) { return n; }, sc);
+      float sq[KPT], t[KPT];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) sq[i] = 0.f;
+      for (int h = 0; h < J.group; ++h) {
+        colsum(J.part0, J.N0,
+               [&](int n) { return ((n / J.head_dim) * J.group + h) * J.head_dim + n % J.head_dim; }, t);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) sq[i] += t[i];
+      }
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) sc[i] *= sq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int n = tid + SEL_THREADS * i;
+      if (n < N) {
+        sdyn[n] = sc[i];
+        if (J.scores) J.scores[(long long)b * N + n] = sc[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = n0 + j < n1 ? __float_as_uint(sdyn[n0 + j]) : 0u;
+  } else if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = n0 + j < n1 ? gk[n0 + j] : 0u;
+  }
+  // f(key, channel) over this thread's keys, in channel order
+  auto for_keys = [&](auto&& f) __attribute__((always_inline)) {
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (n0 + j < n1) f(key[j], n0 + j);
+    } else {
+      for (int n = n0; n < n1; ++n) f(gk[n], n);
     }
   };
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  for (int n0 = tid; n0 < J.N; n0 += SB * SEL_THREADS) {
-    int col[SB];
-#pragma unroll
-    for (int j = 0; j < SB; ++j) col[j] = n0 + j * SEL_THREADS < J.N ? n0 + j * SEL_THREADS : -1;
-    float sc[SB];
-    if (!J.qk) {
-      sumb(J.part0, J.N0, col, sc);
-    } else {
-      float sq[SB], t[SB];
-      sumb(J.part1, J.N, col, sc);   // sc = sk for now
-#pragma unroll
-      for (int j = 0; j < SB; ++j) sq[j] = 0.f;
-      for (int h = 0; h < J.group; ++h) {
-        int qcol[SB];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int n = col[j];
-          qcol[j] = n < 0 ? -1 : ((n / J.head_dim) * J.group + h) * J.head_dim + n % J.head_dim;
-        }
-        sumb(J.part0, J.N0, qcol, t);
-#pragma unroll
-        for (int j = 0; j < SB; ++j) sq[j] += t[j];
-      }
-#pragma unroll
-      for (int j = 0; j < SB; ++j) sc[j] *= sq[j];
-    }
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int n = col[j];
-      if (n < 0) continue;
-      if (J.scores) J.scores[(long long)b * J.N + n] = sc[j];
-      const uint32_t kv = __float_as_uint(sc[j]);
-      keys[n] = kv;
-      kmax = kv > kmax ? kv : kmax;
-      kmin = kv < kmin ? kv : kmin;
-    }
-  }
+  for_keys([&](uint32_t kv, int) {
+    kmax = kv > kmax ? kv : kmax;
+    kmin = kv < kmin ? kv : kmin;
+  });
   // range of the keys: bits above the highest one in which any two differ are common
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -755,72 +983,68 @@ select_kernel(const SelectArgs a) {
   uint32_t mask = ~low, prefix = kmax & ~low;
   int kr = J.k;   // still to take among keys matching prefix
 
-  // radix passes of up to 8 bits from the highest differing bit down; three
-  // barriers per pass: each bin's per-wave counts are cleared as they are read,
-  // and one wave scans the (at most 256) bins
-  __shared__ int cnt_s[256];
+  // radix passes of up to 8 bits from the highest differing bit down, three
+  // barriers per pass: the 256 bins (in descending digit order) are summed
+  // over the per-wave copies, which are cleared as they are read, and scanned
+  // by four waves.  The passes stop early once the bin that holds the k-th
+  // key is taken whole: then no tie inside the set needs breaking.
+  int cbin = 0;
   for (int hi = hbit; hi >= 0;) {
     const int w = hi + 1 < 8 ? hi + 1 : 8;
     const int lo = hi - w + 1;
     const int nb = 1 << w;
-    for (int n = tid; n < J.N; n += SEL_THREADS) {
-      const uint32_t kv = keys[n];
+    for_keys([&](uint32_t kv, int) {
       if ((kv & mask) == prefix) atomicAdd(&hist[wave][(kv >> lo) & (uint32_t)(nb - 1)], 1);
-    }
+    });
     __syncthreads();
-    // bins in descending digit order: position p <-> digit nb - 1 - p
-    if (tid < nb) {
-      const int d = nb - 1 - tid;
-      int c = 0;
+    int c = 0, incl = 0;
+    if (tid < 256) {
+      if (tid < nb) {
+        const int d = nb - 1 - tid;
 #pragma unroll
-      for (int wv = 0; wv < 16; ++wv) { c += hist[wv][d]; hist[wv][d] = 0; }
-      cnt_s[tid] = c;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds positions 4 l .. 4 l + 3
-      int c4[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { c4[q] = 4 * lane + q < nb ? cnt_s[4 * lane + q] : 0; sum += c4[q]; }
-      int before = wave_incl_scan(sum) - sum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * lane + q < nb && before < kr && kr <= before + c4[q]) {
-          s_sel[0] = nb - 1 - (4 * lane + q);
-          s_sel[1] = before;
-        }
-        before += c4[q];
+        for (int wv = 0; wv < 16; ++wv) { c += hist[wv][d]; hist[wv][d] = 0; }
       }
+      incl = wave_incl_scan(c);
+      if (lane == 63) cnt_s[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < nb) {
+      int before = incl - c;
+      for (int wv = 0; wv < wave; ++wv) before += cnt_s[wv];
+      if (before < kr && kr <= before + c) { s_sel[0] = nb - 1 - tid; s_sel[1] = before; s_sel[2] = c; }
     }
     __syncthreads();
     prefix |= (uint32_t)s_sel[0] << lo;
     mask |= (uint32_t)(nb - 1) << lo;
     kr -= s_sel[1];
+    cbin = s_sel[2];
     hi = lo - 1;
+    if (kr == cbin) break;
   }
-  const uint32_t tau = prefix;   // the k-th largest key; take kr of the keys equal to it
+  // The set: every key whose masked value exceeds prefix, plus the first kr
+  // (in channel order) of those equal to it.
 
-  // ordered compaction over contiguous per-thread ranges
-  const int per = (J.N + SEL_THREADS - 1) / SEL_THREADS;
-  const int lo = min(J.N, tid * per), hi = min(J.N, lo + per);
+  // ordered compaction over the contiguous per-thread ranges: one scan of the
+  // (greater, equal) counts; a thread's first output position is
+  // greater-before + min(kr, equal-before)
   int n_gt = 0, n_eq = 0;
-  for (int n = lo; n < hi; ++n) {
-    const uint32_t kv = keys[n];
-    n_gt += kv > tau;
-    n_eq += kv == tau;
-  }
-  const int eq_before = block_excl_scan(n_eq, wsum, tid, nullptr);
+  for_keys([&](uint32_t kv, int) {
+    const uint32_t m = kv & mask;
+    n_gt += m > prefix;
+    n_eq += m == prefix;
+  });
+  const unsigned long long sc2 = block_excl_scan2(((unsigned long long)n_gt << 32) | (unsigned)n_eq, wsum2, tid);
+  const int gt_before = (int)(sc2 >> 32), eq_before = (int)(sc2 & 0xFFFFFFFFull);
   int take_eq = kr - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
-  const int pos0 = block_excl_scan(n_gt + take_eq, wsum, tid, nullptr);
-  int pos = pos0, eq_seen = 0;
+  int pos = gt_before + (kr < eq_before ? kr : eq_before), eq_seen = 0;
   int* out = J.idx + (long long)b * J.k;
-  for (int n = lo; n < hi; ++n) {
-    const uint32_t kv = keys[n];
-    bool take = kv > tau;
-    if (kv == tau) { take = eq_seen < take_eq; ++eq_seen; }
+  for_keys([&](uint32_t kv, int n) {
+    const uint32_t m = kv & mask;
+    bool take = m > prefix;
+    if (m == prefix) { take = eq_seen < take_eq; ++eq_seen; }
     if (take) out[pos++] = n;
-  }
+  });
 }
 
 // ===========================================================================

@@ -182,9 +182,10 @@ sl_status sl_build_estimator(sl_dtype dt, const void* W, int64_t out_f, int64_t 
  *          ties in score go to the lower channel index.
  *   scores [batch, N] fp32 out, optional (NULL = not written): the criterion
  *          (a sum of squares over the sequence's context tokens).
- * 1 <= k <= N <= 65536 (jobs over more than 32768 channels keep their
- * selection keys in the workspace).  heads is read for QK_NORM only.  The workspace size
- * query takes the same criterion, layout, heads, d_in, rank and N as the call.
+ * 1 <= k <= N <= 65536.  The workspace holds the context tokens' projections,
+ * the criterion's partial sums and every sequence's N selection keys.  heads
+ * is read for QK_NORM only.  The workspace size query takes the same
+ * criterion, layout, heads, d_in, rank and N as the call.
  * ------------------------------------------------------------------------- */
 size_t sl_estimate_select_workspace_bytes(sl_criterion crit, const sl_layout* lay,
                                           const sl_heads* heads, int64_t d_in, int32_t rank,

@@ -55,19 +55,19 @@ namespace {
 // kept until the process ends.  Past kMaxSide caller streams per process a
 // call keeps all of its work on the caller's stream.
 constexpr int kMaxSide = 256;
-struct SideEntry { int dev; hipStream_t main; hipStream_t side; };
+// ev[0] links the caller's stream to the side stream (fork), ev[1] the side
+// stream back (join).  A wait takes the event's latest record at the time of
+// the wait, so each event is simply re-recorded by the next fork or join.
+// The events carry no timing and release to device scope only: both streams
+// run on one device, and the host never inspects them.
+struct SideEntry { int dev; hipStream_t main; hipStream_t side; hipEvent_t ev[2]; };
 std::mutex g_side_mu;
 SideEntry g_side[kMaxSide];
 int g_nside = 0;
 
-// One event, recorded on `from` and waited for on `to`; released once done.
-sl_status link_streams(hipStream_t from, hipStream_t to) {
-  hipEvent_t ev;
-  SL_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-  hipError_t e = hipEventRecord(ev, from);
-  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
-  (void)hipEventDestroy(ev);   // released by the runtime once the record completes
-  SL_HIP(e);
+sl_status link_streams(hipStream_t from, hipStream_t to, hipEvent_t ev) {
+  SL_HIP(hipEventRecord(ev, from));
+  SL_HIP(hipStreamWaitEvent(to, ev, 0));
   return SL_OK;
 }
 }  // namespace
@@ -87,18 +87,28 @@ sl_status SideFork::begin(hipStream_t main) {
     std::lock_guard<std::mutex> lk(g_side_mu);
     side = main;
     for (int i = 0; i < g_nside; ++i)
-      if (g_side[i].dev == dev && g_side[i].main == main) { side = g_side[i].side; break; }
-    if (side == main && g_nside < kMaxSide) {
-      hipStream_t ns = nullptr;
-      SL_HIP(hipStreamCreateWithFlags(&ns, hipStreamNonBlocking));
-      g_side[g_nside++] = SideEntry{dev, main, ns};
-      side = ns;
+      if (g_side[i].dev == dev && g_side[i].main == main) {
+        side = g_side[i].side;
+        ev_join = g_side[i].ev[1];
+        if (link_streams(main, side, g_side[i].ev[0]) != SL_OK) return SL_ERR_HIP;
+        return SL_OK;
+      }
+    if (g_nside < kMaxSide) {
+      SideEntry e{dev, main, nullptr, {nullptr, nullptr}};
+      const unsigned fl = hipEventDisableTiming | hipEventReleaseToDevice;
+      SL_HIP(hipStreamCreateWithFlags(&e.side, hipStreamNonBlocking));
+      SL_HIP(hipEventCreateWithFlags(&e.ev[0], fl));
+      SL_HIP(hipEventCreateWithFlags(&e.ev[1], fl));
+      g_side[g_nside++] = e;
+      side = e.side;
+      ev_join = e.ev[1];
+      return link_streams(main, side, e.ev[0]);
     }
   }
-  return side == main ? SL_OK : link_streams(main, side);
+  return SL_OK;   // no side stream left: the call keeps its work on `main`
 }
 
-sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_streams(side, main); }
+sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_streams(side, main, ev_join); }
 
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   if (!lay) SL_FAIL(SL_ERR_NULL, "layout is NULL");
@@ -179,7 +189,9 @@ int sl_timer_enable(int max_launches) {
   g_timer.ev.resize(2 * (size_t)max_launches);
   g_timer.slot.resize(max_launches);
   for (auto& e : g_timer.ev)
-    if (hipEventCreate(&e) != hipSuccess) return (int)SL_ERR_HIP;
+    // timing only: no system-scope fence at the record (the host reads the
+    // events after synchronizing the stream)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return (int)SL_ERR_HIP;
   g_timer.on = true;
   return 0;
 }

@@ -62,14 +62,16 @@ struct Bump {
 // Fork and join with a side stream, for work of a call that does not depend on
 // the launches it may overlap.  Each caller stream of each device gets a side
 // stream of its own (default priority, non-blocking), created at its first
-// fork, so calls on independent streams never wait for each other; each fork
-// and join records an event of its own.  begin(): the side stream waits for everything
+// fork, so calls on independent streams never wait for each other; the pair
+// keeps one fork and one join event, re-recorded by every fork and join
+// (device-scope release, no timing).  begin(): the side stream waits for everything
 // enqueued on `main` so far.  end(): `main` waits for everything enqueued on
 // the side stream so far, so the call's work is again ordered on `main`.
 // While `main` is being captured into a graph, begin() makes `side` = `main`
 // and both are no-ops: the captured work stays on one stream.
 struct SideFork {
   hipStream_t side = nullptr;
+  hipEvent_t ev_join = nullptr;
   sl_status begin(hipStream_t main);
   sl_status end(hipStream_t main);
 };

@@ -187,17 +187,20 @@ def test_estimate_select_matches_oracle(dt):
     print(f"\n[{dt}] exact sets {n_exact}/{len(ctx)}", flush=True)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("rank", [12, 32])
-def test_estimate_select_high_rank(rank):
+def test_estimate_select_high_rank(rank, dt):
     """SwiGLU criterion at estimator ranks past 8 (16- and 32-wide factor
-    tiles on the matrix cores), a ragged channel block and a ragged token chunk."""
+    tiles on the matrix cores; in bf16 the three-term split of each projection
+    spans two and three 32-wide k steps), a ragged channel block and a ragged
+    token chunk."""
     D, F, r, L = 128, 360, 8, 140
     ctx = [140, 33]
-    p = _ffn_case(D, F, r, ctx, L, "f32", seed=13, R_in=rank)
-    Pg, Qg = factors(p["Wg"], rank, "f32")
-    Pu, Qu = factors(p["Wu"], rank, "f32")
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=13, R_in=rank)
+    Pg, Qg = factors(p["Wg"], rank, dt)
+    Pu, Qu = factors(p["Wu"], rank, dt)
     k = 120
-    idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, rank, k, "f32")
+    idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, rank, k, dt)
     ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
     for b in range(len(ctx)):
         e = np.abs(sc[b] - ref[b]).max() / max(ref[b].max(), 1e-30)
@@ -205,17 +208,18 @@ def test_estimate_select_high_rank(rank):
     check_selection(idx, ref, k)
 
 
-def test_select_ties_and_k_extremes():
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_select_ties_and_k_extremes(dt):
     """Planted exact ties in the scores (zero factors) and k = 1, k = N."""
     sl = _api()
     D, F, L = 64, 96, 20
     ctx = [20, 10]
-    p = _ffn_case(D, F, 4, ctx, L, "f32", seed=12)
-    Pg, Qg = factors(p["Wg"], 4, "f32")
-    Pu, Qu = factors(p["Wu"], 4, "f32")
+    p = _ffn_case(D, F, 4, ctx, L, dt, seed=12)
+    Pg, Qg = factors(p["Wg"], 4, dt)
+    Pu, Qu = factors(p["Wu"], 4, dt)
     Qu[:, 40:] = 0.0          # channels 40.. score exactly 0 -> ties
     for k in (1, 50, 80, F):
-        idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, 4, k, "f32")
+        idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, 4, k, dt)
         ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
         check_selection(idx, ref, k)
         if k >= 50:

@@ -172,10 +172,10 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
 
   // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
   // Adg[g] = Ad[:, S_g] (gathered per context group), and AdTp = Ad^T kept in
-  // the saved buffer for the backward; one launch, on the side
-  // stream: it overlaps the z product below, which does not read them.
-  SideFork fork;
-  if ((rc = fork.begin(strm))) return rc;
+  // the saved buffer for the backward; one launch.  It stays on the caller's
+  // stream: on a side stream it overlapped the z product below, but the fork
+  // and join cost more than the 11 us it hid (FFN step 853 us with the fork,
+  // 849 us without, same box).
   {
     Packer pk;
     pk.copy(Pg, 2 * rp, F, 2 * rp, w->Bg, r, F, r, 0);
@@ -184,7 +184,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(AdTp, rp, F, rp, w->Ad, F, F, r, 1);
     pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
-    rc = pk.launch<T>(fork.side);
+    rc = pk.launch<T>(strm);
   }
   // z = X [Ag; Au]^T  (fp32 saved, s*z in T for the GEMM)
   if (rc == SL_OK) {
@@ -200,11 +200,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.part = skp;
     rc = launch_skinny<T>(a, strm);
   }
-  {
-    const sl_status rj = fork.end(strm);   // joined on every path
-    if (rc != SL_OK) return rc;
-    if (rj != SL_OK) return rj;
-  }
+  if (rc != SL_OK) return rc;
   // G, U, H on the selected channels (context) / all channels (output rows)
   {
     GemmArgs a;

@@ -225,7 +225,7 @@ def test_operand_extent_limits_rejected_before_launch(sl):
 
 def test_select_channel_limit(sl):
     """Selection runs over up to 65536 channels; every sequence's keys take N
-    words of workspace (selected in place past 32768 channels)."""
+    words of workspace."""
     L = sl.lib()
     lay = sl.Layout([10, 4], 10)
     P = 4096

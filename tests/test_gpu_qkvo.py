@@ -369,8 +369,9 @@ def test_side_stream_ordering_and_graph_capture():
 
 @pytest.mark.parametrize("N", [32768, 65536])
 def test_l2_select_at_channel_limits(N):
-    """L2 criterion and top-k over 32768 channels (keys in LDS) and 65536 (keys
-    in the workspace), two sequences, one of them short."""
+    """L2 criterion and top-k over 32768 channels (32 keys per thread held in
+    registers) and 65536 (keys re-read from the workspace in every radix
+    pass), two sequences, one of them short."""
     sl = _api()
     rng = np.random.default_rng(41)
     D, L, rank = 64, 48, 8

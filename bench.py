@@ -538,7 +538,7 @@ def main():
     ap.add_argument("--no-qlora", action="store_true",
                     help="skip the FFN over a 4-bit quantized frozen base")
     ap.add_argument("--gemm-variants", type=int, default=-1,
-                    help="GEMM tile variants to allow (bit mask: 1 wide N-gather, 2 tall K-gather, 4 tall always; "
+                    help="GEMM tile variants to allow (bit mask: 1 wide N-gather, 2 tall 256 x 256, 4 tall always; "
                          "default: the library's)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the tiny fp32 FFN, 4-layer stack and LLaMA3-8B long-context workloads")

@@ -327,16 +327,16 @@ gather_gemm_kernel(const GemmArgs args) {
   //   straight into LDS (LDS-DMA) through two stages of 64-element K-tiles, so
   //   no register staging or LDS store phase remains, and the tile moves 17 %
   //   fewer operand bytes per MFMA than two 128 x 256 tiles.
-  // WN = 2, BM = 256 (tall K-gather, bf16): 256 x 256 tile, 8 waves in a 4 x 2
-  //   grid of 64 x 128 blocks, one workgroup per CU, both operands by LDS-DMA
-  //   through the wide tile's two-stage loop (2 x 64 KB stages).  A CU moves
-  //   64 KB per K-tile for 256 x 256 outputs, against 2 x 48 KB for two
-  //   128 x 256 workgroups.
+  // WN = 2, BM = 256 (tall, bf16, N-gather or K-gather): 256 x 256 tile, 8
+  //   waves in a 4 x 2 grid of 64 x 128 blocks, one workgroup per CU, both
+  //   operands by LDS-DMA through the wide tile's two-stage loop (2 x 64 KB
+  //   stages).  A CU moves 64 KB per K-tile for 256 x 256 outputs, against
+  //   80 KB for a 128 x 512 tile and 2 x 48 KB for two 128 x 256 workgroups.
   constexpr bool TALL = BM > 128;           // tall: 8 waves in a 4 x 2 grid
   constexpr bool WIDE = WN == 4 || TALL;
   static_assert(BM == 128 || BM == G_BM_TALL, "tile rows: 128 or 256");
-  static_assert(!WIDE || (sizeof(T) == 2 && !QB && (WN == 4 ? MODE == MODE_NG && BM == 128 : MODE == MODE_KG)),
-                "LDS-DMA tiles: bf16, wide N-gather 128-row or tall K-gather");
+  static_assert(!WIDE || (sizeof(T) == 2 && !QB && (WN == 4 ? MODE == MODE_NG && BM == 128 : WN == 2)),
+                "LDS-DMA tiles: bf16, wide N-gather 128 x 512 or tall 256 x 256");
   static_assert(!QB || (!WIDE && sizeof(T) == 2), "quantized B: bf16 register-staged tiles");
   constexpr int NWAVE = (WN == 4 || TALL) ? 8 : 4;   // waves per workgroup
   constexpr int WMROWS = NWAVE / WN;        // wave rows of the wave grid
@@ -1413,6 +1413,17 @@ inline void ng_split_plan(long long total, int total_kt, int slots, int& rem_sta
 // workgroups, or one wide 128 x 512 or tall 256 x 256 workgroup, per CU.
 inline int gemm_slots(int wn, int bm = G_BM) { return (wn == 4 || bm > 128 ? 1 : 2) * device_cus(); }
 
+// Rounds of resident workgroups an N-gather grid of `total` tiles takes: its
+// whole rounds, plus the last partial round at the length of one K piece when
+// ng_split_plan splits it (can_split: the launch may split).
+inline double ng_grid_rounds(long long total, int total_kt, int slots, bool can_split) {
+  if (total <= 0 || slots <= 0) return 0.0;
+  int rs = (int)total, sp = 1;
+  if (can_split) ng_split_plan(total, total_kt, slots, rs, sp);
+  if (sp > 1) return (double)(rs / slots) + 1.0 / sp;
+  return (double)((total + slots - 1) / slots);
+}
+
 // Rounds of resident workgroups a grid of `total` tiles takes: a last round at
 // most half full runs as K pieces (ng_split_plan) and counts by its fill.
 inline double grid_rounds(long long total, int slots) {
@@ -1423,8 +1434,8 @@ inline double grid_rounds(long long total, int slots) {
 }
 
 // GEMM variants the calling thread allows (bit mask): bit 0 = wide 128 x 512
-// N-gather tiles, bit 1 = tall 256 x 256 K-gather tiles, bit 2 = tall tiles
-// whatever their grid (tests); 0 = 128 x 256 tiles only.  Default: wide and
+// N-gather tiles, bit 1 = tall 256 x 256 tiles (K-gather and N-gather), bit 2 =
+// tall tiles whatever their grid (tests); 0 = 128 x 256 tiles only.  Default: wide and
 // tall.  The LDS-DMA variants need 16-byte aligned operands.
 enum { GV_WIDE = 1, GV_TALL = 2, GV_TALL_ALWAYS = 4 };
 inline thread_local int g_gemm_variants = GV_WIDE | GV_TALL;
@@ -1441,9 +1452,9 @@ inline int ng_ktiles(std::initializer_list<int> seg_k, int bk) {
 inline long long ng_rpart_floats(const SeqTab& st, int kidx, int n_out, bool dual, int esz,
                                  std::initializer_list<int> seg_k) {
   long long best = 0;
-  // (tile rows, waves in N) of the narrow and wide N-gather variants
-  const int vars[2][2] = {{G_BM, 2}, {G_BM, 4}};
-  for (int v = 0; v < (esz == 2 ? 2 : 1); ++v) {
+  // (tile rows, waves in N) of the narrow, wide and tall N-gather variants
+  const int vars[3][2] = {{G_BM, 2}, {G_BM, 4}, {G_BM_TALL, 2}};
+  for (int v = 0; v < (esz == 2 ? 3 : 1); ++v) {
     const int bm = vars[v][0], wn = vars[v][1];
     const int bn = 128 * wn;
     const int bk = esz == 2 ? 64 : 32;
@@ -1473,6 +1484,28 @@ inline bool wide_ng_ok(const GemmArgs& a, int esz) {
     if (g.B2 && !al(g.B2, 0)) return false;
   }
   return true;
+}
+
+// Whether a bf16 N-gather launch whose operands suit the LDS-DMA loads
+// (wide_ng_ok) takes the tall 256 x 256 tiles: its grid, priced as rounds of
+// resident workgroups times the operand bytes a CU moves per K-tile (tall: one
+// 64 KB workgroup; wide: one of 80 KB; 128 x 256: two of 48 KB), costs less
+// than that of the other variant allowed.  The 256-row tiles leave rows idle
+// in a group whose row count is not a multiple of 256 (a 384-row context
+// group fills 3 of its 4 row halves), which the price counts in full.
+inline bool tall_ng_ok(const GemmArgs& a, bool dual, bool can_split, bool wide, bool always) {
+  if (always) return true;
+  int total_kt = 0;
+  for (int s = 0; s < a.nseg; ++s) total_kt += (a.seg[s].K + 63) / 64;
+  auto tiles = [&](int bnc, int bm) {
+    long long t = 0;
+    for (int p = 0; p < a.nprob; ++p) t += ng_tiles(a.st, a.prob[p].kidx, a.prob[p].n_out, bnc, bm);
+    return t;
+  };
+  const double rt = ng_grid_rounds(tiles(dual ? 128 : 256, G_BM_TALL), total_kt, gemm_slots(2, G_BM_TALL), can_split);
+  const double ro = wide ? ng_grid_rounds(tiles(dual ? 256 : 512, G_BM), total_kt, gemm_slots(4), can_split)
+                         : ng_grid_rounds(tiles(dual ? 128 : 256, G_BM), total_kt, gemm_slots(2), can_split);
+  return rt > 0 && rt * 64.0 < 0.97 * ro * (wide ? 80.0 : 96.0);
 }
 
 // K-gather tiles of a launch at bm rows (256-column tiles, the output group split ksplit_out ways).
@@ -1586,8 +1619,14 @@ hipError_t launch_gather_gemm(GemmArgs& a, hipStream_t stream, int timer_slot) {
       return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM_TALL, 2, false>(a, stream, timer_slot);
   }
   if constexpr (MODE == MODE_NG && sizeof(T) == 2) {
-    if ((g_gemm_variants & GV_WIDE) && wide_ng_ok(a, 2))
-      return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 4, false>(a, stream, timer_slot);
+    if ((g_gemm_variants & (GV_WIDE | GV_TALL)) && wide_ng_ok(a, 2)) {
+      constexpr bool SPLITS = EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU || EPI == EPI_SCATTER;
+      const bool wide = (g_gemm_variants & GV_WIDE) != 0;
+      if ((g_gemm_variants & GV_TALL) &&
+          tall_ng_ok(a, DUAL, SPLITS && a.rpart && a.nprob == 1, wide, (g_gemm_variants & GV_TALL_ALWAYS) != 0))
+        return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM_TALL, 2, false>(a, stream, timer_slot);
+      if (wide) return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 4, false>(a, stream, timer_slot);
+    }
   }
   return launch_gather_gemm_wn<T, MODE, EPI, DUAL, G_BM, 2, false>(a, stream, timer_slot);
 }

@@ -349,12 +349,12 @@ int sl_timer_read(int slot, double* total_ms, int* count);
 /* ---------------------------------------------------------------------------
  * GEMM variants (tuning and testing; results agree to the same tolerance).
  * The gather-GEMMs run as 128 x 256 tiles staged through registers, as wide
- * 128 x 512 N-gather tiles fed by LDS-DMA, or as tall 256 x 256 K-gather
- * tiles fed by LDS-DMA.  The LDS-DMA tiles need bf16 calls with every operand
- * 16-byte aligned (wide: K a multiple of 8); the tall tiles are taken when
- * their grid moves fewer operand bytes per CU than the 128 x 256 one.
- * `variants` is a bit mask of what the calling thread allows: 1 = wide
- * tiles, 2 = tall tiles, 4 = tall tiles whatever their grid (with 2); 0 =
+ * 128 x 512 N-gather tiles fed by LDS-DMA, or as tall 256 x 256 tiles (N- or
+ * K-gather) fed by LDS-DMA.  The LDS-DMA tiles need bf16 calls with every
+ * operand 16-byte aligned (N-gather: K a multiple of 8); the tall tiles are
+ * taken when their grid moves fewer operand bytes per CU than the other
+ * variant's.  `variants` is a bit mask of what the calling thread allows: 1 =
+ * wide tiles, 2 = tall tiles, 4 = tall tiles whatever their grid (with 2); 0 =
  * 128 x 256 tiles only; a negative value leaves the setting.  Default 3.
  * Returns the previous setting.  The setting is per calling thread and
  * applies to the calls that thread makes.

@@ -93,7 +93,8 @@ def check_scores(gpu_scores: np.ndarray, ora_scores: np.ndarray, tol: float, wha
 @contextlib.contextmanager
 def gemm_variant(variants: int):
     """Run the block with the given GEMM tile variants allowed (bit mask: 1
-    wide N-gather, 2 tall K-gather, 4 tall whatever the grid; 0 = 128 x 256 only)."""
+    wide N-gather, 2 tall 256 x 256 (N- and K-gather), 4 tall whatever the
+    grid; 0 = 128 x 256 only)."""
     import contextual_sparsity_lora_svd_amd as sl
     prev = sl.gemm_config(variants)
     try:

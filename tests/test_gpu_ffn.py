@@ -104,9 +104,11 @@ def test_ffn_multi_tile(dt):
 
 @pytest.mark.parametrize("case", ["ragged", "multi", "dense_single"])
 def test_ffn_bf16_tall_kgather_tiles(case):
-    """The same cases with the down and dX products on the tall 256 x 256
-    LDS-DMA tiles, taken whatever their grid (ragged groups, a K segment whose
-    channel count is not a multiple of 8, partial row tiles, k = N, k = 1)."""
+    """The same cases with every bf16 product on the tall 256 x 256 LDS-DMA
+    tiles wherever its operands allow them, whatever their grid: the down and
+    dX K-gathers, and the gate/up and dH N-gathers when aligned (ragged
+    groups, a K segment whose channel count is not a multiple of 8, partial
+    row tiles, k = N, k = 1)."""
     with gemm_variant(1 | 2 | 4):
         if case == "dense_single":
             D, F, r, L = 128, 264, 8, 80

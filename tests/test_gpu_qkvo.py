@@ -115,8 +115,9 @@ def test_qkvo_split_calls_and_extremes(dt):
 @pytest.mark.parametrize("variants", [1, 0, 6])
 def test_qkvo_multi_tile_bf16(variants):
     """Several tiles per group on each GEMM variant: 1 the wide N-gather tiles,
-    0 the 128 x 256 tiles only, 6 the tall 256 x 256 K-gather tiles whatever
-    their grid (the o and dX products)."""
+    0 the 128 x 256 tiles only, 6 the tall 256 x 256 tiles whatever their grid
+    (every product: the q/k/v and attention-output-gradient N-gathers, the o
+    and input-gradient K-gathers)."""
     from tests.gpu_helpers import gemm_variant
     with gemm_variant(variants):
         _qkvo_multi_tile()

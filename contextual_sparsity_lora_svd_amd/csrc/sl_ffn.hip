@@ -283,11 +283,15 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
-  // packed LoRA operands and the inverse map of the channel sets (one launch),
-  // on the side stream: the next two products read only Bd^T and Ad^T, which
-  // the forward left in the saved buffer; joined before the dz_g / dz_u product
+  // Side stream, first part: the packed LoRA operands and the inverse map of
+  // the channel sets (one launch); the next two products read only Bd^T and
+  // Ad^T, which the forward left in the saved buffer, and the dz_g / dz_u
+  // product waits for the packing alone.  Then, once dz_d is ready, the factor
+  // gradients that need neither dG nor dU (dBd = s dY^T z_d, dAd[:, S] =
+  // dz_d^T H) run beside the dH product, whose grid leaves CUs idle.
   SideFork pack_fork;
   if ((rc = pack_fork.begin(strm))) return rc;
+  auto side_fail = [&](sl_status e) { (void)pack_fork.end(strm); return e; };
   {
     Packer pk;
     pk.copy(Agup, D, rp, D, w->Ag, D, r, D, 0);
@@ -298,49 +302,51 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
     pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
     pk.inverse(inv, idx, g.k, F, st.nseq);
-    if ((rc = pk.launch<T>(pack_fork.side))) { (void)pack_fork.end(strm); return rc; }
+    if ((rc = pk.launch<T>(pack_fork.side))) return side_fail(rc);
+    if ((rc = pack_fork.mark(strm))) return side_fail(rc);
   }
 
-  // dz_d = s dY Bd, then dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
-  auto dz_d_dh = [&]() -> sl_status {
-    // dz_d = s dY Bd
-    {
-      SkinnyArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.st = st; a.mode = 0; a.T = g.T;
-      a.A = dY; a.lda = D; a.K = D;
-      a.nblk = 1;
-      a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
-      a.out = dz_d; a.ldo = rp; a.oscale = s;
-      a.outs = dzs_d; a.ldos = rp; a.scale = s;
-      a.part = skp;
-      const sl_status r1 = launch_skinny<T>(a, strm);
-      if (r1 != SL_OK) return r1;
-    }
-    // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
-    {
-      GemmArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.st = st;
-      a.idx = idx; a.kidx = g.k; a.n_out = F;
-      a.nseg = 2;
-      a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
-      set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
-      a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
-      a.o0 = dGc; a.o1 = dUc;
-      a.i0 = Gc; a.i1 = Uc;
-      a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
-      a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
-      SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD)));
-    }
-    return SL_OK;
-  };
-  rc = dz_d_dh();
+  // dz_d = s dY Bd
   {
-    const sl_status rj = pack_fork.end(strm);   // joined on every path
-    if (rc != SL_OK) return rc;
-    if (rj != SL_OK) return rj;
+    SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st; a.mode = 0; a.T = g.T;
+    a.A = dY; a.lda = D; a.K = D;
+    a.nblk = 1;
+    a.Bb[0] = BdTp; a.nbk[0] = r; a.ldbb[0] = D;
+    a.out = dz_d; a.ldo = rp; a.oscale = s;
+    a.outs = dzs_d; a.ldos = rp; a.scale = s;
+    a.part = skp;
+    if ((rc = launch_skinny<T>(a, strm))) return side_fail(rc);
   }
+  // dBd and dAd on the side stream (their own partials: the first part of the
+  // reduction workspace)
+  if ((rc = pack_fork.refork(strm))) return side_fail(rc);
+  ColredBatch cb_d(st, g.esz, crp, g.cr_floats);
+  cb_d.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
+  cb_d.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
+  if ((rc = cb_d.launch<T>(pack_fork.side))) return side_fail(rc);
+  // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
+  {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.st = st;
+    a.idx = idx; a.kidx = g.k; a.n_out = F;
+    a.nseg = 2;
+    a.seg[0] = GSeg{dY, D, 0, 0, 1, w->WdT, nullptr, D, 1, D, nullptr, 0, 0};
+    set_base(a.seg[0], w, w->WdT, w->WdT_q, w->WdT_s);
+    a.seg[1] = GSeg{dzs_d, rp, 0, 0, 1, AdTp, nullptr, rp, 1, rp, nullptr, 0, 0};
+    a.o0 = dGc; a.o1 = dUc;
+    a.i0 = Gc; a.i1 = Uc;
+    a.rpart = reinterpret_cast<float*>(ws + g.w_rp);
+    a.ldc_ctx = g.ldk; a.ldc_out = g.ldF; a.c_out_off = g.c_out_off;
+    const hipError_t e = launch_gather_gemm<T, MODE_NG, EPI_DSWIGLU, false>(a, strm, TS_DH_BWD);
+    if (e != hipSuccess) {
+      set_error("dH product launch failed: %s", hipGetErrorString(e));
+      return side_fail(SL_ERR_HIP);
+    }
+  }
+  if ((rc = pack_fork.join_mark(strm))) return side_fail(rc);   // the packing is done
   // dz_g = s dG Bg[S], dz_u = s dU Bu[S]: one launch, two problems
   {
     SkinnyArgs a;
@@ -360,25 +366,23 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     u.B0 = Bug; u.ldb0 = g.ldk; u.b0_gstride = (long long)rp * g.ldk;
     u.B0o = BuTo; u.ldb0o = F;
     u.col0 = rp;
-    if ((rc = launch_skinny<T>(a, strm))) return rc;
+    if ((rc = launch_skinny<T>(a, strm))) return side_fail(rc);
   }
-  // LoRA factor gradients (one reduction launch, one finish launch) on the
-  // side stream: they read only what is ready now and write their own
-  // buffers, so they overlap the dX product below.
-  // dAg, dAu = dz^T X;  dBd = s dY^T z_d;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u;
-  // dAd[:, S] = dz_d^T H
+  // The other LoRA factor gradients (one reduction launch, one finish launch)
+  // on the side stream, after dBd and dAd: they read only what is ready now
+  // and write their own buffers (the rest of the reduction workspace), so
+  // they overlap the dX product below.
+  // dAg, dAu = dz^T X;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u
   // (an optional timing event for the dX product goes before the fork, so that
   // the product and the side work become ready together)
   timer_begin(TS_DX_BWD, strm);
   SideFork fork;
-  if ((rc = fork.begin(strm))) return rc;
+  if ((rc = fork.begin(strm))) return side_fail(rc);
   {
-    ColredBatch cb(st, g.esz, crp, g.cr_floats);
+    ColredBatch cb(st, g.esz, crp + cb_d.used, g.cr_floats - cb_d.used);
     cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
-    cb.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
     cb.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
     cb.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
-    cb.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
     if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
   }
   // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au

@@ -89,8 +89,9 @@ sl_status SideFork::begin(hipStream_t main) {
     for (int i = 0; i < g_nside; ++i)
       if (g_side[i].dev == dev && g_side[i].main == main) {
         side = g_side[i].side;
+        ev_fork = g_side[i].ev[0];
         ev_join = g_side[i].ev[1];
-        if (link_streams(main, side, g_side[i].ev[0]) != SL_OK) return SL_ERR_HIP;
+        if (link_streams(main, side, ev_fork) != SL_OK) return SL_ERR_HIP;
         return SL_OK;
       }
     if (g_nside < kMaxSide) {
@@ -101,14 +102,28 @@ sl_status SideFork::begin(hipStream_t main) {
       SL_HIP(hipEventCreateWithFlags(&e.ev[1], fl));
       g_side[g_nside++] = e;
       side = e.side;
+      ev_fork = e.ev[0];
       ev_join = e.ev[1];
-      return link_streams(main, side, e.ev[0]);
+      return link_streams(main, side, ev_fork);
     }
   }
   return SL_OK;   // no side stream left: the call keeps its work on `main`
 }
 
 sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_streams(side, main, ev_join); }
+
+sl_status SideFork::refork(hipStream_t main) { return side == main ? SL_OK : link_streams(main, side, ev_fork); }
+
+sl_status SideFork::mark(hipStream_t main) {
+  if (side != main) SL_HIP(hipEventRecord(ev_join, side));
+  return SL_OK;
+}
+
+// (a stream wait takes the event's last record at the time of the call)
+sl_status SideFork::join_mark(hipStream_t main) {
+  if (side != main) SL_HIP(hipStreamWaitEvent(main, ev_join, 0));
+  return SL_OK;
+}
 
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   if (!lay) SL_FAIL(SL_ERR_NULL, "layout is NULL");

@@ -77,7 +77,8 @@ sl_status plan_estimate(const SeqTab& st, long long d_in, int rank, int njobs, c
                 h.n_kv_heads * h.head_dim, (long long)s.N);
       e.N0 = h.n_q_heads * h.head_dim;
     }
-    // SwiGLU partials per SW_CHUNK tokens; the L2 forms (Gram) one per sequence
+    // SwiGLU partials per SW_CHUNK tokens (the most a call can need: a bf16
+    // call may take longer chunks); the L2 forms (Gram) one per sequence
     e.chunk = s.crit == SL_CRIT_SWIGLU_L2 ? SW_CHUNK : (1 << 30);
     e.nchunk_max = s.crit == SL_CRIT_SWIGLU_L2 ? ceil_div(maxctx, SW_CHUNK) : 1;
     if (e.nchunk_max < 1) e.nchunk_max = 1;
@@ -119,13 +120,33 @@ sl_status check_jobs(int njobs, const sl_est_job* jobs, long long d_in, int rank
   return SL_OK;
 }
 
+// Context tokens per SwiGLU partial sum: 256 for the bf16 kernel at ranks up
+// to 16 when every context fits two such chunks (the select kernel then adds
+// the at most two partials of a channel itself, and no sum launch runs), else
+// 128.  The workspace is sized for 128-token chunks, which need the most.
 template <typename T>
-sl_status launch_swiglu(const SwiArgs& a, int nseq, int rank, hipStream_t s) {
+int swiglu_chunk(const SeqTab& st, int rank) {
+  int maxctx = 0;
+  for (int b = 0; b < st.nseq; ++b) maxctx = st.ctx[b] > maxctx ? st.ctx[b] : maxctx;
+  if (std::is_same<T, bf16>::value && rank <= 16 && maxctx > SW_CHUNK && maxctx <= 2 * SW_CHUNK_LONG)
+    return SW_CHUNK_LONG;
+  return SW_CHUNK;
+}
+
+template <typename T>
+sl_status launch_swiglu(const SwiArgs& a, int nseq, int rank, int chunk, hipStream_t s) {
   const dim3 grid(ceil_div(a.N, 128), a.nchunk_max, nseq), block(SW_THREADS);
   if constexpr (std::is_same<T, bf16>::value) {
-    if (rank <= 8) hipLaunchKernelGGL((score_swiglu_split_kernel<8>), grid, block, 0, s, a);
-    else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_split_kernel<16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((score_swiglu_split_kernel<32>), grid, block, 0, s, a);
+    if (chunk == SW_CHUNK_LONG) {
+      if (rank <= 8) hipLaunchKernelGGL((score_swiglu_split_kernel<8, SW_CHUNK_LONG>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((score_swiglu_split_kernel<16, SW_CHUNK_LONG>), grid, block, 0, s, a);
+    } else if (rank <= 8) {
+      hipLaunchKernelGGL((score_swiglu_split_kernel<8, SW_CHUNK>), grid, block, 0, s, a);
+    } else if (rank <= 16) {
+      hipLaunchKernelGGL((score_swiglu_split_kernel<16, SW_CHUNK>), grid, block, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((score_swiglu_split_kernel<32, SW_CHUNK>), grid, block, 0, s, a);
+    }
   } else {
     if (rank <= 8) hipLaunchKernelGGL((score_swiglu_kernel<T, 8>), grid, block, 0, s, a);
     else if (rank <= 16) hipLaunchKernelGGL((score_swiglu_kernel<T, 16>), grid, block, 0, s, a);
@@ -188,6 +209,14 @@ template <typename T>
 sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, const EstPlan& P, char* ws,
                                hipStream_t stream) {
   float* zh = reinterpret_cast<float*>(ws + P.w_zh);
+  const int sw_chunk = swiglu_chunk<T>(st, P.rank);
+  auto chunk_of = [&](const EJob& e) { return e.crit == SL_CRIT_SWIGLU_L2 ? sw_chunk : e.chunk; };
+  auto nchunk_of = [&](const EJob& e) {
+    if (e.crit != SL_CRIT_SWIGLU_L2) return e.nchunk_max;
+    int maxctx = 0;
+    for (int b = 0; b < st.nseq; ++b) maxctx = st.ctx[b] > maxctx ? st.ctx[b] : maxctx;
+    return std::max(1, ceil_div(maxctx, sw_chunk));
+  };
   auto p0 = [&](const EJob& e) { return reinterpret_cast<float*>(ws + e.w_p0); };
   auto p1 = [&](const EJob& e) { return reinterpret_cast<float*>(ws + e.w_p1); };
   timer_begin(TS_ESTIMATE, stream);
@@ -225,8 +254,8 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
         sc.st = st;
         sc.Zh = zh; sc.ldz = P.ldz; sc.zc0 = e.zcol; sc.zc1 = e.zcol + P.rep;
         sc.Q0 = e.Q[0]; sc.Q1 = e.Q[1]; sc.rank = P.rank; sc.N = (int)e.N;
-        sc.part = p0(e); sc.nchunk_max = e.nchunk_max;
-        if ((s = launch_swiglu<T>(sc, st.nseq, P.rank, stream)) != SL_OK) return s;
+        sc.part = p0(e); sc.nchunk_max = nchunk_of(e);
+        if ((s = launch_swiglu<T>(sc, st.nseq, P.rank, chunk_of(e), stream)) != SL_OK) return s;
         continue;
       }
       ga.zc[ng] = e.zcol; ga.Q[ng] = e.Q[0]; ga.N[ng] = e.N0; ga.part[ng] = p0(e); ++ng;
@@ -247,8 +276,8 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
     SelJob& q = se.job[j];
     q.qk = e.crit == SL_CRIT_QK_NORM;
     q.part0 = p0(e); q.part1 = p1(e);
-    q.nchunk_max = e.nchunk_max;
-    q.chunk = e.chunk;
+    q.nchunk_max = nchunk_of(e);
+    q.chunk = chunk_of(e);
     q.N = (int)e.N; q.N0 = e.N0;
     if (q.qk) { q.group = e.heads.n_q_heads / e.heads.n_kv_heads; q.head_dim = e.heads.head_dim; }
     q.k = e.k; q.idx = e.idx; q.scores = e.scores;

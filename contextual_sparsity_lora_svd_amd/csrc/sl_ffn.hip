@@ -347,6 +347,14 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     }
   }
   if ((rc = pack_fork.join_mark(strm))) return side_fail(rc);   // the packing is done
+  // dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u on the side stream as soon as dG
+  // and dU exist: they run beside the dz_g / dz_u product, whose small grid
+  // leaves CUs idle, instead of behind the dX product that fills every CU
+  if ((rc = pack_fork.refork(strm))) return side_fail(rc);
+  ColredBatch cb_gu(st, g.esz, crp + cb_d.used, g.cr_floats - cb_d.used);
+  cb_gu.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
+  cb_gu.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
+  if ((rc = cb_gu.launch<T>(pack_fork.side))) return side_fail(rc);
   // dz_g = s dG Bg[S], dz_u = s dU Bu[S]: one launch, two problems
   {
     SkinnyArgs a;
@@ -368,21 +376,18 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     u.col0 = rp;
     if ((rc = launch_skinny<T>(a, strm))) return side_fail(rc);
   }
-  // The other LoRA factor gradients (one reduction launch, one finish launch)
-  // on the side stream, after dBd and dAd: they read only what is ready now
-  // and write their own buffers (the rest of the reduction workspace), so
+  // dAg, dAu = dz^T X (one reduction launch, one finish launch) on the side
+  // stream, after the other factor gradients: they read only what is ready
+  // now and write their own buffers (the rest of the reduction workspace), so
   // they overlap the dX product below.
-  // dAg, dAu = dz^T X;  dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u
   // (an optional timing event for the dX product goes before the fork, so that
   // the product and the side work become ready together)
   timer_begin(TS_DX_BWD, strm);
   SideFork fork;
   if ((rc = fork.begin(strm))) return side_fail(rc);
   {
-    ColredBatch cb(st, g.esz, crp + cb_d.used, g.cr_floats - cb_d.used);
+    ColredBatch cb(st, g.esz, crp + cb_d.used + cb_gu.used, g.cr_floats - cb_d.used - cb_gu.used);
     cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
-    cb.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
-    cb.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
     if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
   }
   // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au

@@ -515,7 +515,8 @@ score_gram_kernel(const GramArgs a) {
 // tokens stay in the lane; the two lane halves are added at the end.  Rows past
 // the context are zero in LDS and contribute (SiLU(0) 0)^2 = 0.
 // Workgroup: 4 waves = 128 channels over a chunk of SW_CHUNK tokens.
-constexpr int SW_CHUNK = 128;
+constexpr int SW_CHUNK = 128;        // context tokens per partial sum (fp32 kernel, bf16 default)
+constexpr int SW_CHUNK_LONG = 256;   // bf16 kernel when every context fits two such chunks
 constexpr int SW_THREADS = 256;
 
 struct SwiArgs {
@@ -618,21 +619,25 @@ score_swiglu_kernel(const SwiArgs a) {
 // the MFMA yields g' = -g log2(e), exp2(g') = e^{-g}, and
 //   (SiLU(g) u)^2 = (g' u / (1 + exp2(g')))^2 ln(2)^2,
 // with ln(2)^2 applied once per channel sum.  Per wave 32 channels (two
-// 16-column blocks) over the chunk's SW_CHUNK tokens (eight 16-row blocks);
-// a lane's accumulator values all belong to its column, so the square and the
-// token sum stay in the lane until the four lane groups are added at the end.
-template <int RM>
+// 16-column blocks) over the chunk's CH tokens (CH / 16 row blocks, those
+// past the context skipped in pairs); a lane's accumulator values all belong
+// to its column, so the square and the token sum stay in the lane until the
+// four lane groups are added at the end.
+template <int RM, int CH>
 __global__ void __launch_bounds__(SW_THREADS)
 score_swiglu_split_kernel(const SwiArgs a) {
   constexpr int KA = (3 * RM + 31) / 32 * 32;   // k of the split products, whole MFMA steps
   constexpr int NKB = KA / 32;
   constexpr int PITCH = KA * 2 + 16;            // LDS row pitch in bytes (bank spread)
-  __shared__ __attribute__((aligned(16))) unsigned char zs[2][SW_CHUNK * PITCH];   // [g/u][token][k]
+  constexpr int NRB = CH / 16;                  // 16-token row blocks per chunk
+  static_assert(CH % 32 == 0 && CH <= SW_CHUNK_LONG, "row blocks in pairs");
+  __shared__ __attribute__((aligned(16))) unsigned char zs[2][CH * PITCH];   // [g/u][token][k]
   const int b = blockIdx.z, chunk = blockIdx.y;
   const int ctx = a.st.ctx[b];
-  const int t0 = chunk * SW_CHUNK;
+  const int t0 = chunk * CH;
   if (t0 >= ctx) return;
-  const int nt = min(SW_CHUNK, ctx - t0);
+  const int nt = min(CH, ctx - t0);
+  const int nrb = (nt + 31) / 32 * 2;           // row blocks holding context tokens, rounded to pairs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
@@ -660,9 +665,10 @@ score_swiglu_split_kernel(const SwiArgs a) {
     }
   // Z staging: thread (t, pj) splits one token's RM projections into three
   // bf16 rows hi | mid | lo at k = 0, RM, 2 RM; rows past the context are 0
-  {
-    const int t = tid >> 1, pj = tid & 1;
-    static_assert(SW_THREADS == 2 * SW_CHUNK, "one thread per token and projection");
+  static_assert(SW_THREADS == 2 * SW_CHUNK, "one thread per token and projection of a 128-token pass");
+#pragma unroll
+  for (int tp = 0; tp < CH; tp += SW_CHUNK) {
+    const int t = tp + (tid >> 1), pj = tid & 1;
     const float sc = pj == 0 ? -1.4426950408889634f : 1.f;   // -log2(e) on the gate
     const float* zr = a.Zh + (long long)(b * a.st.L + t0 + t) * a.ldz + (pj ? a.zc1 : a.zc0);
     unsigned char* row = zs[pj] + t * PITCH;
@@ -726,18 +732,18 @@ score_swiglu_split_kernel(const SwiArgs a) {
       }
   };
   // two row blocks in flight: block rb + 1's products are issued before
-  // block rb's activation (row blocks past the context hold zero rows and
-  // add exactly 0)
-  static_assert(SW_CHUNK / 16 == 8, "eight row blocks per chunk");
+  // block rb's activation (rows past the context are zero and add exactly 0;
+  // pairs of blocks wholly past it are skipped)
   f32x4_t g0[2], u0[2], g1[2], u1[2];
   mm(0, g0, u0);
 #pragma unroll
-  for (int rb = 0; rb < 8; rb += 2) {
+  for (int rb = 0; rb < NRB; rb += 2) {
+    if (rb >= nrb) break;
     mm(rb + 1, g1, u1);
     __builtin_amdgcn_sched_barrier(0);
     act(g0, u0);
     __builtin_amdgcn_sched_barrier(0);
-    if (rb + 2 < 8) mm(rb + 2, g0, u0);
+    if (rb + 2 < NRB && rb + 2 < nrb) mm(rb + 2, g0, u0);
     __builtin_amdgcn_sched_barrier(0);
     act(g1, u1);
     __builtin_amdgcn_sched_barrier(0);

@@ -210,6 +210,32 @@ def test_estimate_select_high_rank(rank, dt):
     check_selection(idx, ref, k)
 
 
+@pytest.mark.parametrize("rank", [6, 8, 12])
+@pytest.mark.parametrize("ctx", [[300, 0, 17, 260], [520, 129, 0]])
+def test_estimate_select_sliced_stage1(rank, ctx):
+    """bf16 SwiGLU estimate with d_in = 1544: the stage-1 product runs as four
+    K slices, the last one 8 wide.  At ranks that are multiples of 4 the
+    criterion kernel adds the slice partials itself (no finish launch); at
+    rank 6 a finish launch does.  Contexts of at most 512 tokens take
+    256-token criterion chunks (up to two partials per channel, added by the
+    select kernel); the 520-token context takes 128-token chunks and a
+    separate score-sum launch.  An empty context sits among the others."""
+    dt = "bf16"
+    D, F, r = 1544, 520, 8
+    L = max(ctx)
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=31 + rank, R_in=rank)
+    Pg, Qg = factors(p["Wg"], rank, dt)
+    Pu, Qu = factors(p["Wu"], rank, dt)
+    k = 130
+    idx, sc = _estimate(p, ctx, L, Pg, Qg, Pu, Qu, rank, k, dt)
+    ref = _oracle_scores(p, ctx, L, Pg, Qg, Pu, Qu)
+    check_scores(sc, ref, 1e-4)
+    check_selection(idx, ref, k)
+    for b, c in enumerate(ctx):
+        if c == 0:
+            assert list(idx[b]) == list(range(k))   # no context: all scores 0, lowest indices
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_select_ties_and_k_extremes(dt):
     """Planted exact ties in the scores (zero factors) and k = 1, k = N."""

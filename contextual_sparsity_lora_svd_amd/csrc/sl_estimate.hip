@@ -237,14 +237,8 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
       }
     sa.out = zh; sa.ldo = P.ldz; sa.col0 = 0; sa.oscale = 1.f;
     sa.part = reinterpret_cast<float*>(ws + P.w_skp);
-    // bf16 calls whose jobs are all SwiGLU (rank a multiple of 4, one skinny
-    // launch): the criterion kernel adds the K-slice partials itself
-    bool fold = std::is_same<T, bf16>::value && P.rank % 4 == 0 && P.nproj * P.rank <= 64;
-    for (int j = 0; j < P.njobs; ++j) fold &= P.job[j].crit == SL_CRIT_SWIGLU_L2;
-    sa.skip_finish = fold ? 1 : 0;
     sl_status s = launch_skinny<T>(sa, stream);
     if (s != SL_OK) return s;
-    const bool from_part = fold && sa.nsl[0] > 1;   // else the product wrote Zh itself
     // stage 2 + criterion: every L2-type projection in one Gram launch, each
     // SwiGLU job in a launch of its own
     GramArgs ga;
@@ -261,13 +255,6 @@ sl_status estimate_select_impl(const SeqTab& st, const void* X, long long d_in, 
         sc.Zh = zh; sc.ldz = P.ldz; sc.zc0 = e.zcol; sc.zc1 = e.zcol + P.rep;
         sc.Q0 = e.Q[0]; sc.Q1 = e.Q[1]; sc.rank = P.rank; sc.N = (int)e.N;
         sc.part = p0(e); sc.nchunk_max = nchunk_of(e);
-        if (from_part) {
-          // logical partial columns: the call's projections back to back, rank each
-          int pidx = 0;
-          for (int jj = 0; jj < j; ++jj) pidx += P.job[jj].nproj;
-          sc.zp = sa.part; sc.zstride = (long long)sa.mrows * sa.pc; sc.zpc = sa.pc; sc.znsl = sa.nsl[0];
-          sc.zl0 = pidx * P.rank; sc.zl1 = (pidx + 1) * P.rank;
-        }
         if ((s = launch_swiglu<T>(sc, st.nseq, P.rank, chunk_of(e), stream)) != SL_OK) return s;
         continue;
       }

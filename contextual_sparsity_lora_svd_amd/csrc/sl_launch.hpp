@@ -69,7 +69,7 @@ inline sl_status launch_skinny_one(SkinnyArgs& a, hipStream_t s) {
   else if (C <= 48) hipLaunchKernelGGL((skinny_kernel<T, 3>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((skinny_kernel<T, 4>), grid, block, 0, s, a);
   SL_HIP(hipGetLastError());
-  if (sliced && !a.skip_finish) {
+  if (sliced) {
     int ptot = 0;
     for (int j = 0; j < a.nblk; ++j) ptot += (a.nbk[j] + 7) / 8 * 8;
     hipLaunchKernelGGL((skinny_finish_kernel<T>), grid1d((long long)a.mrows * ptot * a.nprob), dim3(256), 0,

@@ -75,9 +75,6 @@ struct SkinnyArgs {
     const void* B0o; long long ldb0o;
     int col0;
   } xp[2];
-  // 1: a K-sliced launch leaves its slice partials for the consumer to add
-  // (no finish launch; `out` is then not written)
-  int skip_finish;
 };
 constexpr int SK_MAXPROB = 3;
 
@@ -527,12 +524,6 @@ struct SwiArgs {
   const float* Zh; long long ldz; int zc0, zc1;
   const void* Q0; const void* Q1; int rank; int N;
   float* part; int nchunk_max;
-  // bf16 kernel, rank a multiple of 4: when zp is set, the projections are
-  // read as the stage-1 product's K-slice partials instead of Zh and added in
-  // slice order: projection value (context row r of the call, logical column
-  // c) = sum over s < znsl of zp[s zstride + r zpc + c]; columns zl0 (gate)
-  // and zl1 (up) hold the first of each projection's rank values.
-  const float* zp; long long zstride; int zpc, znsl, zl0, zl1;
 };
 
 template <typename T, int RM>
@@ -680,42 +671,15 @@ score_swiglu_split_kernel(const SwiArgs a) {
     const int t = tp + (tid >> 1), pj = tid & 1;
     const float sc = pj == 0 ? -1.4426950408889634f : 1.f;   // -log2(e) on the gate
     const float* zr = a.Zh + (long long)(b * a.st.L + t0 + t) * a.ldz + (pj ? a.zc1 : a.zc0);
-    const float* zq = a.zp + (long long)(a.st.ctx_pre[b] + t0 + t) * a.zpc + (pj ? a.zl1 : a.zl0);
     unsigned char* row = zs[pj] + t * PITCH;
     static_assert(RM % 8 == 0, "whole 16-byte groups of k");
 #pragma unroll
     for (int q0 = 0; q0 < RM; q0 += 8) {
       uint32_t w[3][4];
-      // the 8 projection values at q0: from Zh, or as slice partials added in
-      // slice order from 0 (both halves' loads of 8 slices issued before any add)
-      float4 zv[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-      const bool ok[2] = {t < nt && q0 < a.rank, t < nt && q0 + 4 < a.rank};
-      if (!a.zp) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (ok[h]) zv[h] = *reinterpret_cast<const float4*>(zr + q0 + 4 * h);
-      } else {
-        for (int s0 = 0; s0 < a.znsl; s0 += 8) {
-          float4 v[2][8];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              v[h][j] = ok[h] && s0 + j < a.znsl
-                            ? *reinterpret_cast<const float4*>(zq + (s0 + j) * a.zstride + q0 + 4 * h)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (s0 + j < a.znsl) {
-                zv[h].x += v[h][j].x; zv[h].y += v[h][j].y; zv[h].z += v[h][j].z; zv[h].w += v[h][j].w;
-              }
-        }
-      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float4 z4 = zv[h];
+        float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < nt && q0 + 4 * h < a.rank) z4 = *reinterpret_cast<const float4*>(zr + q0 + 4 * h);
         const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {

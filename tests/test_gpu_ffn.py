@@ -214,12 +214,11 @@ def test_estimate_select_high_rank(rank, dt):
 @pytest.mark.parametrize("ctx", [[300, 0, 17, 260], [520, 129, 0]])
 def test_estimate_select_sliced_stage1(rank, ctx):
     """bf16 SwiGLU estimate with d_in = 1544: the stage-1 product runs as four
-    K slices, the last one 8 wide.  At ranks that are multiples of 4 the
-    criterion kernel adds the slice partials itself (no finish launch); at
-    rank 6 a finish launch does.  Contexts of at most 512 tokens take
-    256-token criterion chunks (up to two partials per channel, added by the
-    select kernel); the 520-token context takes 128-token chunks and a
-    separate score-sum launch.  An empty context sits among the others."""
+    K slices, the last one 8 wide, summed by its finish launch.  Contexts of
+    at most 512 tokens take 256-token criterion chunks (up to two partials per
+    channel, added by the select kernel); the 520-token context takes
+    128-token chunks and a separate score-sum launch.  An empty context sits
+    among the others; ranks 6, 8 and 12 take the 8- and 16-wide factor tiles."""
     dt = "bf16"
     D, F, r = 1544, 520, 8
     L = max(ctx)

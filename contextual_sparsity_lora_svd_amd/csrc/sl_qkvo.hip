@@ -36,9 +36,9 @@ struct QkvoGeom {
   Comp cq, ck, cv, co;
   int ks_o, ks_dx, chunk;
   long long cr_floats, skp_floats;
-  size_t s_zqkv, s_zo, saved_bytes;
-  size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_BoTp, w_Aog, w_ac, w_part,
-      w_dz_o, w_dzs_o, w_AoTp, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
+  size_t s_zqkv, s_zo, s_BoT, s_AoT, saved_bytes;
+  size_t w_idxq, w_idxo, w_zs_qkv, w_zs_o, w_Bqp, w_Bkp, w_Bvp, w_Aog, w_ac, w_part,
+      w_dz_o, w_dzs_o, w_dqc, w_dkc, w_dvc, w_Bqg, w_Bkg, w_Bvg, w_BqTo, w_BkTo, w_BvTo,
       w_dz_qkv, w_dzs_qkv, w_Aqkvp, w_cr, w_inv_o, w_inv_q, w_inv_k, w_inv_v, w_iota, w_rp, w_skp, ws_bytes;
 };
 
@@ -89,6 +89,10 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   Bump sv;
   g.s_zqkv = sv.take(T * 3 * rp * 4);
   g.s_zo = sv.take(T * rp * 4);
+  // Bo^T and Ao^T, packed by the forward: the backward's first products read
+  // them while its own packing runs on the side stream
+  g.s_BoT = sv.take(rp * D * e);
+  g.s_AoT = sv.take((size_t)g.nq * rp * e);
   g.saved_bytes = sv.off;
   Bump b;
   g.w_idxq = b.take(B * g.kq * 4);
@@ -98,14 +102,12 @@ sl_status qkvo_geom(sl_dtype dt, const sl_layout* lay, const sl_qkvo_weights* w,
   g.w_Bqp = b.take((size_t)g.nq * rp * e);
   g.w_Bkp = b.take((size_t)g.nkv * rp * e);
   g.w_Bvp = b.take((size_t)g.nkv * rp * e);
-  g.w_BoTp = b.take(rp * D * e);
   g.w_Aog = b.take(B * rp * g.co.ld * e);
   g.w_ac = b.take(g.co.elems * e);
   const int ks = std::max(g.ks_o, g.ks_dx);
   g.w_part = b.take(ks > 1 ? (size_t)ks * st.T_out * D * 4 : 0);
   g.w_dz_o = b.take(T * rp * 4);
   g.w_dzs_o = b.take(T * rp * e);
-  g.w_AoTp = b.take((size_t)g.nq * rp * e);
   g.w_dqc = b.take(g.cq.elems * e);
   g.w_dkc = b.take(g.ck.elems * e);
   g.w_dvc = b.take(g.cv.elems * e);
@@ -177,7 +179,8 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
   T* ac = reinterpret_cast<T*>(ws + g.w_ac);
   T* Aog = reinterpret_cast<T*>(ws + g.w_Aog);
-  T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
+  T* BoTp = reinterpret_cast<T*>(sv + g.s_BoT);
+  T* AoTp = reinterpret_cast<T*>(sv + g.s_AoT);
   const bool qq = w->Wq_q != nullptr;   // 4-bit q/k/v base
   const void* Wm[3] = {qq ? w->Wq_q : w->Wq, qq ? w->Wk_q : w->Wk, qq ? w->Wv_q : w->Wv};
   const float* Ws[3] = {w->Wq_s, w->Wk_s, w->Wv_s};
@@ -201,7 +204,8 @@ sl_status qkvo_fwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     }
   }
   if (a) {
-    pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);                      // Bo^T [rp, D]
+    pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);                      // Bo^T [rp, D] (saved)
+    pk.copy(AoTp, rp, g.nq, rp, w->Ao, g.nq, g.nq, r, 1);            // Ao^T [nq, rp] (saved)
     pk.gather(Aog, g.co.ld, (long long)rp * g.co.ld, rp, g.co.ld, w->Ao, g.nq, r, 0, idx_o, g.ko,
               st.nseq);                                             // Ao[:, So] per sequence
     add_compact(L, g.co, a, idx_o, ac, g.esz);
@@ -304,8 +308,8 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   int* inv_o = reinterpret_cast<int*>(ws + g.w_inv_o);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
   T* ac = reinterpret_cast<T*>(ws + g.w_ac);
-  T* BoTp = reinterpret_cast<T*>(ws + g.w_BoTp);
-  T* AoTp = reinterpret_cast<T*>(ws + g.w_AoTp);
+  const T* BoTp = reinterpret_cast<const T*>(sv + g.s_BoT);   // packed by the forward
+  const T* AoTp = reinterpret_cast<const T*>(sv + g.s_AoT);
   T* Aqkvp = reinterpret_cast<T*>(ws + g.w_Aqkvp);
   const void* dsrc[3] = {dq, dk, dv};
   T* dcomp[3] = {reinterpret_cast<T*>(ws + g.w_dqc), reinterpret_cast<T*>(ws + g.w_dkc),
@@ -333,8 +337,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
   pk.iota(reinterpret_cast<int*>(ws + g.w_iota), std::max(g.nq, 3 * g.rp));
   Layouter L(st);
   if (d_out) {
-    pk.copy(BoTp, D, rp, D, w->Bo, r, r, D, 1);          // Bo^T [rp, D]
-    pk.copy(AoTp, rp, g.nq, rp, w->Ao, g.nq, g.nq, r, 1);  // Ao^T [nq, rp]
     add_compact(L, g.co, a, idx_o, ac, g.esz);
     pk.inverse(inv_o, idx_o, g.ko, g.nq, st.nseq);
   }
@@ -349,7 +351,6 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
       pk.inverse(inv[j], sets[j], c.kc, c.n, st.nseq);
     }
   }
-  if ((rc = pk.launch<T>(strm))) return rc;
   ColredBatch cb(st, g.esz, crp, g.cr_floats);
   float* dz_o = reinterpret_cast<float*>(ws + g.w_dz_o);
   T* dzs_o = reinterpret_cast<T*>(ws + g.w_dzs_o);
@@ -380,12 +381,14 @@ sl_status qkvo_bwd_impl(const QkvoGeom& g, const sl_qkvo_weights* w, const void*
     SL_HIP((launch_gather_gemm<T, MODE_NG, EPI_SCATTER, false>(ga, strm, TS_DA_BWD)));
     return SL_OK;
   };
-  // the row layout (compact a and dq / dk / dv) on the side stream: the
-  // o-branch reads neither, so the two overlap
+  // the operand packing and the row layout (compact a and dq / dk / dv) on the
+  // side stream: the o-branch reads neither (its Bo^T and Ao^T come from the
+  // forward), so they overlap
   {
     SideFork lay;
     if ((rc = lay.begin(strm))) return rc;
-    rc = L.launch<T>(lay.side);
+    rc = pk.launch<T>(lay.side);
+    if (rc == SL_OK) rc = L.launch<T>(lay.side);
     if (rc == SL_OK && d_out) rc = o_branch();
     const sl_status rj = lay.end(strm);   // joined on every path
     if (rc != SL_OK) return rc;

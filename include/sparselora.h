@@ -282,6 +282,9 @@ sl_status sl_ffn_bwd(sl_dtype dt, const sl_layout* lay, const sl_ffn_weights* w,
  *   bwd:  d_out -> da [T, Hq*hd] and dAo, dBo                (if d_out != NULL)
  *         dq, dk, dv -> dX and dAq..dBv                      (if dq != NULL)
  *         X and a (the forward's inputs) are read for the factor gradients.
+ *         The d_out part reads what the forward's a part left in `saved`
+ *         (z_o and the packed Bo^T, Ao^T); the dq part what its X part left
+ *         (z_q, z_k, z_v).
  * d_model, Hq*hd and Hkv*hd multiples of 8; 1 <= lora_rank <= 32;
  * 1 <= k_qk, k_vo <= Hkv*hd.  Every matrix a call reads or writes holds
  * fewer than 2^31 elements (T*d_model, T*Hq*hd, Hq*hd*d_model and the compact

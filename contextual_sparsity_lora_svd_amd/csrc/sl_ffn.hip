@@ -29,10 +29,9 @@ struct FfnGeom {
   long long comp, c_out_off;
   int ks_down, ks_dx, RM1, RM2, chunk;
   long long cr_floats, skp_floats;
-  size_t s_zgu, s_zd, s_G, s_U, s_H, s_BdT, s_AdT, saved_bytes;
+  size_t s_zgu, s_zd, s_G, s_U, s_H, s_BdT, s_AdT, s_Agup, s_Bgg, s_Bug, s_BgTo, s_BuTo, s_iota, saved_bytes;
   size_t w_zs_gu, w_zs_d, w_Pg, w_Pu, w_Adg, w_part, w_dz_d, w_dzs_d, w_dG, w_dU,
-      w_Bgg, w_Bug, w_BgTo, w_BuTo, w_dz_gu, w_dzs_gu, w_Agup, w_cr, w_inv, w_iota, w_skp, w_rp,
-      ws_bytes;
+      w_dz_gu, w_dzs_gu, w_cr, w_inv, w_skp, w_rp, ws_bytes;
 };
 
 sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, int r, int k,
@@ -71,9 +70,17 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.s_G = sv.take(g.comp * e);
   g.s_U = sv.take(g.comp * e);
   g.s_H = sv.take(g.comp * e);
-  // Bd^T and Ad^T, packed by the forward for the backward's first products
+  // the backward's LoRA operands, packed by the forward: Bd^T and Ad^T for its
+  // first products, [Ag; Au] (rank padded), B_g[S]^T and B_u[S]^T per context
+  // group, B_g^T and B_u^T, and 0, 1, 2, ... for the K-gather products
   g.s_BdT = sv.take((size_t)g.rp * D * e);
   g.s_AdT = sv.take((size_t)F * g.rp * e);
+  g.s_Agup = sv.take((size_t)2 * g.rp * D * e);
+  g.s_Bgg = sv.take((size_t)st.nseq * g.rp * g.ldk * e);
+  g.s_Bug = sv.take((size_t)st.nseq * g.rp * g.ldk * e);
+  g.s_BgTo = sv.take((size_t)g.rp * F * e);
+  g.s_BuTo = sv.take((size_t)g.rp * F * e);
+  g.s_iota = sv.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
   g.saved_bytes = sv.off;
   Bump w;
   g.w_zs_gu = w.take(T * 2 * g.rp * e);
@@ -87,20 +94,14 @@ sl_status ffn_geom(sl_dtype dt, const sl_layout* lay, long long D, long long F, 
   g.w_dzs_d = w.take(T * g.rp * e);
   g.w_dG = w.take(g.comp * e);
   g.w_dU = w.take(g.comp * e);
-  g.w_Bgg = w.take((size_t)st.nseq * g.rp * g.ldk * e);
-  g.w_Bug = w.take((size_t)st.nseq * g.rp * g.ldk * e);
-  g.w_BgTo = w.take((size_t)g.rp * F * e);
-  g.w_BuTo = w.take((size_t)g.rp * F * e);
   g.w_dz_gu = w.take(T * 2 * g.rp * 4);
   g.w_dzs_gu = w.take(T * 2 * g.rp * e);
-  g.w_Agup = w.take((size_t)2 * g.rp * D * e);
   // partials of the five gradient reductions (dA_g,u; dB_d; dB_g, dB_u, dA_d)
   const long long cr = cb_dense_floats(st, e, D, 2 * g.rp) + cb_dense_floats(st, e, D, g.rp) +
                        3 * cb_scatter_floats(st, e, k, g.F, g.rp);
   g.cr_floats = cr;
   g.w_cr = w.take((size_t)cr * 4);
   g.w_inv = w.take((size_t)st.nseq * F * 4);
-  g.w_iota = w.take((size_t)(F > 2 * g.rp ? F : 2 * g.rp) * 4);
   // skinny partial sums: room for the two problems of the dz_g / dz_u launch
   g.skp_floats = skinny_part_floats(g.T, D > F ? D : F);
   g.w_skp = w.take((size_t)g.skp_floats * 2 * 4);
@@ -170,9 +171,12 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   float* part = reinterpret_cast<float*>(ws + g.w_part);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
-  // LoRA operands padded to rp columns: Pg = [Bg | 0], Pu = [0 | Bu], BdTp = Bd^T,
-  // Adg[g] = Ad[:, S_g] (gathered per context group), and AdTp = Ad^T kept in
-  // the saved buffer for the backward; one launch.  It stays on the caller's
+  // LoRA operands padded to rp columns, one launch: Pg = [Bg | 0], Pu = [0 |
+  // Bu] and Adg[g] = Ad[:, S_g] (gathered per context group) for this pass;
+  // for the backward, in the saved buffer, Bd^T, Ad^T, [Ag; Au], B_g[S]^T and
+  // B_u[S]^T per context group, B_g^T, B_u^T and the index ramp, so that the
+  // backward's products never wait for a packing launch (each wait or fork on
+  // the caller's stream leaves it idle about 5 us).  It stays on the caller's
   // stream: on a side stream it overlapped the z product below, but the fork
   // and join cost more than the 11 us it hid (FFN step 853 us with the fork,
   // 849 us without, same box).
@@ -183,7 +187,16 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     pk.copy(BdTp, D, rp, D, w->Bd, r, r, D, 1);
     pk.copy(AdTp, rp, F, rp, w->Ad, F, F, r, 1);
     pk.gather(Adg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Ad, F, r, 0, idx, g.k, st.nseq);
-    pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
+    T* Agup = reinterpret_cast<T*>(sv + g.s_Agup);
+    pk.copy(Agup, D, rp, D, w->Ag, D, r, D, 0);
+    pk.copy(Agup + (long long)rp * D, D, rp, D, w->Au, D, r, D, 0);
+    pk.gather(reinterpret_cast<T*>(sv + g.s_Bgg), g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bg, r, r, 1, idx,
+              g.k, st.nseq);
+    pk.gather(reinterpret_cast<T*>(sv + g.s_Bug), g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bu, r, r, 1, idx,
+              g.k, st.nseq);
+    pk.copy(reinterpret_cast<T*>(sv + g.s_BgTo), F, r, F, w->Bg, r, r, F, 1);
+    pk.copy(reinterpret_cast<T*>(sv + g.s_BuTo), F, r, F, w->Bu, r, r, F, 1);
+    pk.iota(reinterpret_cast<int*>(sv + g.s_iota), F > 2 * rp ? F : 2 * rp);
     rc = pk.launch<T>(strm);
   }
   // z = X [Ag; Au]^T  (fp32 saved, s*z in T for the GEMM)
@@ -245,7 +258,7 @@ sl_status ffn_fwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_down;
     a.o0 = Y; a.ldo = D;
     a.part = part;
-    a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
+    a.iota = reinterpret_cast<const int*>(sv + g.s_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, TS_DOWN_FWD)));
     if ((rc = splitk_reduce<T>(st, part, g.ks_down, D, Y, D, strm))) return rc;
   }
@@ -271,42 +284,21 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   const T* AdTp = reinterpret_cast<const T*>(sv + g.s_AdT);   // packed by the forward
   T* dGc = reinterpret_cast<T*>(ws + g.w_dG);
   T* dUc = reinterpret_cast<T*>(ws + g.w_dU);
-  T* Bgg = reinterpret_cast<T*>(ws + g.w_Bgg);
-  T* Bug = reinterpret_cast<T*>(ws + g.w_Bug);
-  T* BgTo = reinterpret_cast<T*>(ws + g.w_BgTo);
-  T* BuTo = reinterpret_cast<T*>(ws + g.w_BuTo);
+  // packed by the forward
+  const T* Bgg = reinterpret_cast<const T*>(sv + g.s_Bgg);
+  const T* Bug = reinterpret_cast<const T*>(sv + g.s_Bug);
+  const T* BgTo = reinterpret_cast<const T*>(sv + g.s_BgTo);
+  const T* BuTo = reinterpret_cast<const T*>(sv + g.s_BuTo);
   float* dz_gu = reinterpret_cast<float*>(ws + g.w_dz_gu);
   T* dzs_gu = reinterpret_cast<T*>(ws + g.w_dzs_gu);
-  T* Agup = reinterpret_cast<T*>(ws + g.w_Agup);
+  const T* Agup = reinterpret_cast<const T*>(sv + g.s_Agup);
   const T* BdTp = reinterpret_cast<const T*>(sv + g.s_BdT);
   float* crp = reinterpret_cast<float*>(ws + g.w_cr);
   int* inv = reinterpret_cast<int*>(ws + g.w_inv);
   float* skp = reinterpret_cast<float*>(ws + g.w_skp);
 
-  // Side stream, first part: the packed LoRA operands and the inverse map of
-  // the channel sets (one launch); the next two products read only Bd^T and
-  // Ad^T, which the forward left in the saved buffer, and the dz_g / dz_u
-  // product waits for the packing alone.  Then, once dz_d is ready, the factor
-  // gradients that need neither dG nor dU (dBd = s dY^T z_d, dAd[:, S] =
-  // dz_d^T H) run beside the dH product, whose grid leaves CUs idle.
-  SideFork pack_fork;
-  if ((rc = pack_fork.begin(strm))) return rc;
-  auto side_fail = [&](sl_status e) { (void)pack_fork.end(strm); return e; };
-  {
-    Packer pk;
-    pk.copy(Agup, D, rp, D, w->Ag, D, r, D, 0);
-    pk.copy(Agup + (long long)rp * D, D, rp, D, w->Au, D, r, D, 0);
-    pk.gather(Bgg, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bg, r, r, 1, idx, g.k, st.nseq);
-    pk.gather(Bug, g.ldk, (long long)rp * g.ldk, rp, g.ldk, w->Bu, r, r, 1, idx, g.k, st.nseq);
-    pk.copy(BgTo, F, r, F, w->Bg, r, r, F, 1);
-    pk.copy(BuTo, F, r, F, w->Bu, r, r, F, 1);
-    pk.iota(reinterpret_cast<int*>(ws + g.w_iota), F > 2 * rp ? F : 2 * rp);
-    pk.inverse(inv, idx, g.k, F, st.nseq);
-    if ((rc = pk.launch<T>(pack_fork.side))) return side_fail(rc);
-    if ((rc = pack_fork.mark(strm))) return side_fail(rc);
-  }
-
-  // dz_d = s dY Bd
+  // dz_d = s dY Bd (Bd^T and every other LoRA operand the backward reads come
+  // packed from the forward, so no product here waits for a packing launch)
   {
     SkinnyArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -317,15 +309,24 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.out = dz_d; a.ldo = rp; a.oscale = s;
     a.outs = dzs_d; a.ldos = rp; a.scale = s;
     a.part = skp;
-    if ((rc = launch_skinny<T>(a, strm))) return side_fail(rc);
+    if ((rc = launch_skinny<T>(a, strm))) return rc;
   }
-  // dBd and dAd on the side stream (their own partials: the first part of the
-  // reduction workspace)
-  if ((rc = pack_fork.refork(strm))) return side_fail(rc);
+  // Side stream: the inverse map of the channel sets, then the factor
+  // gradients that need neither dG nor dU (dBd = s dY^T z_d, dAd[:, S] =
+  // dz_d^T H), beside the dH product, whose grid leaves CUs idle (their own
+  // partials: the first part of the reduction workspace).
+  SideFork side;
+  if ((rc = side.begin(strm))) return rc;
+  auto side_fail = [&](sl_status e) { (void)side.end(strm); return e; };
+  {
+    Packer pk;
+    pk.inverse(inv, idx, g.k, F, st.nseq);
+    if ((rc = pk.launch<T>(side.side))) return side_fail(rc);
+  }
   ColredBatch cb_d(st, g.esz, crp, g.cr_floats);
   cb_d.dense(dY, D, D, zd, rp, 0, rp, gr->dBd, r, 0, nullptr, 0, 0, 0, s);
   cb_d.scatter(Hc, g.ldk, g.ldF, g.c_out_off, g.k, F, dz_d, rp, 0, rp, inv, gr->dAd, r, 1, 1.f);
-  if ((rc = cb_d.launch<T>(pack_fork.side))) return side_fail(rc);
+  if ((rc = cb_d.launch<T>(side.side))) return side_fail(rc);
   // dH = dY WdT[S]^T + dz_d Ad[:, S]  ->  dG, dU
   {
     GemmArgs a;
@@ -346,15 +347,14 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
       return side_fail(SL_ERR_HIP);
     }
   }
-  if ((rc = pack_fork.join_mark(strm))) return side_fail(rc);   // the packing is done
   // dBg[S] = s dG^T z_g, dBu[S] = s dU^T z_u on the side stream as soon as dG
   // and dU exist: they run beside the dz_g / dz_u product, whose small grid
   // leaves CUs idle, instead of behind the dX product that fills every CU
-  if ((rc = pack_fork.refork(strm))) return side_fail(rc);
+  if ((rc = side.refork(strm))) return side_fail(rc);
   ColredBatch cb_gu(st, g.esz, crp + cb_d.used, g.cr_floats - cb_d.used);
   cb_gu.scatter(dGc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, 0, rp, inv, gr->dBg, r, 0, s);
   cb_gu.scatter(dUc, g.ldk, g.ldF, g.c_out_off, g.k, F, zgu, 2 * rp, rp, rp, inv, gr->dBu, r, 0, s);
-  if ((rc = cb_gu.launch<T>(pack_fork.side))) return side_fail(rc);
+  if ((rc = cb_gu.launch<T>(side.side))) return side_fail(rc);
   // dz_g = s dG Bg[S], dz_u = s dU Bu[S]: one launch, two problems
   {
     SkinnyArgs a;
@@ -383,12 +383,11 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
   // (an optional timing event for the dX product goes before the fork, so that
   // the product and the side work become ready together)
   timer_begin(TS_DX_BWD, strm);
-  SideFork fork;
-  if ((rc = fork.begin(strm))) return side_fail(rc);
+  if ((rc = side.refork(strm))) return side_fail(rc);
   {
     ColredBatch cb(st, g.esz, crp + cb_d.used + cb_gu.used, g.cr_floats - cb_d.used - cb_gu.used);
     cb.dense(X, D, D, dz_gu, 2 * rp, 0, 2 * rp, gr->dAg, r, 1, gr->dAu, r, 1, rp, 1.f);
-    if ((rc = cb.launch<T>(fork.side))) { (void)fork.end(strm); return rc; }
+    if ((rc = cb.launch<T>(side.side))) return side_fail(rc);
   }
   // dX = dG Wg[S] + dU Wu[S] + dz_g Ag + dz_u Au
   auto dx = [&]() -> sl_status {
@@ -406,13 +405,13 @@ sl_status ffn_bwd_impl(const FfnGeom& g, const sl_ffn_weights* w, const void* X,
     a.ksplit_out = g.ks_dx;
     a.o0 = dX; a.ldo = D;
     a.part = part;
-    a.iota = reinterpret_cast<const int*>(ws + g.w_iota);
+    a.iota = reinterpret_cast<const int*>(sv + g.s_iota);
     SL_HIP((launch_gather_gemm<T, MODE_KG, EPI_TOKEN, false>(a, strm, -1)));
     timer_end(TS_DX_BWD, strm);
     return splitk_reduce<T>(st, part, g.ks_dx, D, dX, D, strm);
   };
   rc = dx();
-  const sl_status rj = fork.end(strm);   // joined on every path
+  const sl_status rj = side.end(strm);   // joined on every path
   return rc != SL_OK ? rc : rj;
 }
 

@@ -206,7 +206,9 @@ struct Packer {
     for (int i = 0; i < a.njobs; ++i) {
       a.start[i] = n;
       const PackJob& j = a.job[i];
-      n += (long long)j.rows * j.cols * (j.type == 1 || j.type == 3 ? j.nseq : 1);
+      // items of 8 consecutive destination elements of a row (inverse maps: 1)
+      const int per = j.type == 3 ? 1 : 8;
+      n += (long long)j.rows * ((j.cols + per - 1) / per) * (j.type == 1 || j.type == 3 ? j.nseq : 1);
     }
     a.start[a.njobs] = n;
     if (n == 0) return SL_OK;

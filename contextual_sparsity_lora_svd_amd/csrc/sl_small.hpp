@@ -1467,6 +1467,10 @@ struct PackArgs {
   PackJob job[PK_MAXJOBS];
 };
 
+// One thread per 8 consecutive destination elements of a row (an item): the
+// 8 source loads are independent, and a whole aligned item goes out as one
+// 16-byte store (two for fp32).  Inverse maps take one element per item: each
+// is a binary search, a chain of dependent loads.
 template <typename T>
 __global__ void pack_kernel(const PackArgs a) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1475,41 +1479,66 @@ __global__ void pack_kernel(const PackArgs a) {
   while (j + 1 < a.njobs && a.start[j + 1] <= i) ++j;
   const PackJob& b = a.job[j];
   const long long e = i - a.start[j];
-  const T* src = reinterpret_cast<const T*>(b.src);
-  T* dst = reinterpret_cast<T*>(b.dst);
+  const int per = b.type == 3 ? 1 : 8;         // elements per item
+  const int cg = (b.cols + per - 1) / per;     // items per destination row
+  const int c0 = (int)(e % cg) * per;
+  const long long row = e / cg;                // type 1: g * rows + q; type 3: g
+  const int n = b.cols - c0 < per ? b.cols - c0 : per;
   if (b.type == 2) {
-    reinterpret_cast<int*>(b.dst)[e] = (int)e;
+    int* d = reinterpret_cast<int*>(b.dst) + c0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < n) d[u] = c0 + u;
     return;
   }
   if (b.type == 3) {
-    const int g = (int)(e / b.cols), c = (int)(e % b.cols);
-    const int* set = b.idx + (long long)g * b.k;
+    const int* set = b.idx + row * b.k;
+    const int c = c0;
     int lo = 0, hi = b.k;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (set[mid] < c) lo = mid + 1; else hi = mid; }
-    reinterpret_cast<int*>(b.dst)[e] = (lo < b.k && set[lo] == c) ? lo : -1;
+    reinterpret_cast<int*>(b.dst)[row * b.cols + c] = (lo < b.k && set[lo] == c) ? lo : -1;
     return;
   }
+  const T* src = reinterpret_cast<const T*>(b.src);
+  T zero;
+  stv<T>(&zero, 0, 0.f);
+  alignas(16) T v[8];
+  T* d;
   if (b.type == 0) {
-    const int r = (int)(e / b.cols), c = (int)(e % b.cols);
-    const int sr = r - b.row_off, sc = c - b.col_off;
-    T v;
-    if (sr >= 0 && sr < b.src_rows && sc >= 0 && sc < b.src_cols)
-      v = b.tr ? src[(long long)sc * b.lds + sr] : src[(long long)sr * b.lds + sc];
-    else
-      stv<T>(&v, 0, 0.f);
-    dst[(long long)r * b.ldd + c] = v;
-  } else {
-    const int p = (int)(e % b.cols);
-    const int q = (int)((e / b.cols) % b.rows);
-    const int g = (int)(e / ((long long)b.cols * b.rows));
-    T v;
-    if (q < b.src_rows && p < b.k) {
-      const int c = b.idx[(long long)g * b.k + p];
-      v = b.tr ? src[(long long)c * b.lds + q] : src[(long long)q * b.lds + c];
-    } else {
-      stv<T>(&v, 0, 0.f);
+    const int sr = (int)row - b.row_off;
+    const bool rok = sr >= 0 && sr < b.src_rows;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sc = c0 + u - b.col_off;
+      v[u] = (u < n && rok && sc >= 0 && sc < b.src_cols)
+                 ? (b.tr ? src[(long long)sc * b.lds + sr] : src[(long long)sr * b.lds + sc])
+                 : zero;
     }
-    dst[g * b.gstride + (long long)q * b.ldd + p] = v;
+    d = reinterpret_cast<T*>(b.dst) + row * b.ldd + c0;
+  } else {
+    const int q = (int)(row % b.rows);
+    const long long g = row / b.rows;
+    const int* set = b.idx + g * b.k;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = c0 + u;
+      T x = zero;
+      if (u < n && q < b.src_rows && p < b.k) {
+        const int c = set[p];
+        x = b.tr ? src[(long long)c * b.lds + q] : src[(long long)q * b.lds + c];
+      }
+      v[u] = x;
+    }
+    d = reinterpret_cast<T*>(b.dst) + g * b.gstride + (long long)q * b.ldd + c0;
+  }
+  if (n == 8 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
+#pragma unroll
+    for (int h = 0; h < (int)sizeof(T) * 8 / 16; ++h)
+      reinterpret_cast<uint4*>(d)[h] = reinterpret_cast<const uint4*>(v)[h];
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < n) d[u] = v[u];
   }
 }
 

@@ -92,12 +92,15 @@ def test_size_queries_follow_the_layout(sl):
     s_big = L.sl_ffn_saved_bytes(1, lay.ref, 64, 128, 4, 64)
     assert 0 < s_small < s_big
     # saved = z (fp32, T x 2rp) + z_d (T x rp) + G, U, H compact (bf16)
-    #         + Bd^T (rp x d_model) + Ad^T (d_ff x rp), bf16, packed for the backward
-    T, rp, D, F = 8, 8, 64, 128
+    #         + the backward's LoRA operands, bf16, packed by the forward: Bd^T (rp x d_model),
+    #           Ad^T (d_ff x rp), [Ag; Au] (2rp x d_model), B_g[S]^T and B_u[S]^T (per sequence
+    #           rp x ldk), B_g^T and B_u^T (rp x d_ff); and the index ramp (d_ff ints)
+    T, rp, D, F, B, ldk = 8, 8, 64, 128, 2, 8
     comp = 3 * 8 + 1 * 128     # 3 context rows x ldk(8) + 1 output row x d_ff
     def up(x):
         return (x + 255) // 256 * 256
-    expect = up(T * 2 * rp * 4) + up(T * rp * 4) + 3 * up(comp * 2) + up(rp * D * 2) + up(F * rp * 2)
+    expect = (up(T * 2 * rp * 4) + up(T * rp * 4) + 3 * up(comp * 2) + up(rp * D * 2) + up(F * rp * 2)
+              + up(2 * rp * D * 2) + 2 * up(B * rp * ldk * 2) + 2 * up(rp * F * 2) + up(F * 4))
     assert s_small == expect
     assert L.sl_ffn_workspace_bytes(1, lay.ref, 64, 128, 4, 0) == 0   # invalid k
     assert L.sl_estimator_workspace_bytes(100, 50, 65) == 0

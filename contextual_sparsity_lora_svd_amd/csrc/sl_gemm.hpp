@@ -16,11 +16,15 @@
 // operand is the low-rank activation z and whose B operand the other factor,
 // so LoRA runs inside the same tiles as the frozen weight.
 //
-// Tile BM x 256 x BK (BM = 128 or 256), 256 threads = 4 waves in a 2 x 2 grid,
-// each wave a (BM/2) x 128 block of 32x32 MFMA accumulators.  bf16:
-// v_mfma_f32_32x32x16_bf16, BK = 64.  fp32: v_mfma_f32_32x32x2_f32 (true fp32),
-// BK = 32.  The global loads of the next K-tile are in flight in registers
-// while the current tile is consumed from LDS.
+// Three tile variants, every wave a 64 x 128 block of 32x32 MFMA accumulators
+// (bf16: v_mfma_f32_32x32x16_bf16, BK = 64; fp32: v_mfma_f32_32x32x2_f32, true
+// fp32, BK = 32):
+//   128 x 256, 4 waves, two workgroups per CU, operands staged through
+//     registers (the K-gather B operand of bf16 calls by LDS-DMA), the next
+//     K-tile's loads in flight while the current one is consumed from LDS;
+//   128 x 512 (wide, N-gather) and 256 x 256 (tall, N- or K-gather), 8 waves,
+//     one workgroup per CU, bf16 only: both operands go from memory straight
+//     into LDS (LDS-DMA) through two stages.
 #pragma once
 
 #include <initializer_list>

@@ -114,16 +114,6 @@ sl_status SideFork::end(hipStream_t main) { return side == main ? SL_OK : link_s
 
 sl_status SideFork::refork(hipStream_t main) { return side == main ? SL_OK : link_streams(main, side, ev_fork); }
 
-sl_status SideFork::mark(hipStream_t main) {
-  if (side != main) SL_HIP(hipEventRecord(ev_join, side));
-  return SL_OK;
-}
-
-// (a stream wait takes the event's last record at the time of the call)
-sl_status SideFork::join_mark(hipStream_t main) {
-  if (side != main) SL_HIP(hipStreamWaitEvent(main, ev_join, 0));
-  return SL_OK;
-}
 
 sl_status build_seqtab(const sl_layout* lay, SeqTab& st) {
   if (!lay) SL_FAIL(SL_ERR_NULL, "layout is NULL");

@@ -68,9 +68,8 @@ struct Bump {
 // enqueued on `main` so far.  end(): `main` waits for everything enqueued on
 // the side stream so far, so the call's work is again ordered on `main`.
 // refork(): the side stream waits again for everything enqueued on `main` so
-// far.  mark(): remembers the side stream's current point; join_mark(): `main`
-// waits for the side stream up to the last mark only (later side work keeps
-// running; a later end() joins it).
+// far.  Each fork or join point leaves `main` idle about 5 us on MI355X (an
+// event record or wait between two kernels), so calls use few of them.
 // While `main` is being captured into a graph, begin() makes `side` = `main`
 // and all of these are no-ops: the captured work stays on one stream.
 struct SideFork {
@@ -79,8 +78,6 @@ struct SideFork {
   sl_status begin(hipStream_t main);
   sl_status end(hipStream_t main);
   sl_status refork(hipStream_t main);
-  sl_status mark(hipStream_t main);
-  sl_status join_mark(hipStream_t main);
 };
 
 // Optional per-launch timing: when enabled (sl_timer_enable), selected launches

@@ -545,6 +545,9 @@ def main():
     ap.add_argument("--workload", type=int, default=0,
                     help="run only workload N's whole-path measurement and print it as the JSON line "
                          "(for profiling)")
+    ap.add_argument("--extreme-ffn-only", action="store_true",
+                    help="run only the 99 %% sparsity FFN step and print its measurements as the JSON line "
+                         "(for profiling that step alone)")
     ap.add_argument("--attn-only", action="store_true",
                     help="run only the q/k/v/o workload and print its measurements as the JSON line "
                          "(for profiling that step alone)")
@@ -563,6 +566,9 @@ def main():
     if args.gemm_variants >= 0:
         sl.gemm_config(args.gemm_variants)
 
+    if args.extreme_ffn_only:
+        print(json.dumps(ffn_extreme_bench(args, torch, sl)), flush=True)
+        return
     if args.attn_only:
         print(json.dumps(attn_bench(args, torch, sl)), flush=True)
         return

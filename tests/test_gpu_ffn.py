@@ -236,6 +236,36 @@ def test_estimate_select_sliced_stage1(rank, ctx):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_reads_only_saved(dt):
+    """Everything the backward takes from the forward is in `saved` (z, z_d,
+    G, U, H and the packed LoRA operands): a backward given a copy of the
+    saved buffer and a fresh workspace filled with 0xFF bytes (NaN in bf16 and
+    fp32) matches, bit for bit, the backward that shares the forward's
+    workspace."""
+    sl = _api()
+    D, F, r, L = 512, 1104, 16, 300
+    ctx = [290, 200, 300]
+    p = _ffn_case(D, F, r, ctx, L, dt, seed=29)
+    rng = np.random.default_rng(30)
+    k = 300
+    idx = np.stack([np.sort(rng.choice(F, k, replace=False)) for _ in ctx]).astype(np.int32)
+    w = _dev_weights(p, dt, 0.5)
+    lay = sl.Layout(ctx, L)
+    X = to_dev(p["X"], dt)
+    idx_d = torch.from_numpy(idx).cuda()
+    dY = to_dev(p["dY"], dt)
+    _, buf = sl.ffn_fwd(w, X, lay, k, idx_d)
+    g1 = sl.ffn_bwd(w, X, lay, k, idx_d, buf, dY)
+    buf2 = sl.FFNWorkspace(w, lay, k, X.device)
+    buf2.saved.copy_(buf.saved)
+    buf2.ws.fill_(255)
+    g2 = sl.ffn_bwd(w, X, lay, k, idx_d, buf2, dY)
+    torch.cuda.synchronize()
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), f"{n} differs with a fresh workspace"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_select_ties_and_k_extremes(dt):
     """Planted exact ties in the scores (zero factors) and k = 1, k = N."""
     sl = _api()

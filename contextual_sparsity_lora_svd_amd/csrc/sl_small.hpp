@@ -898,27 +898,26 @@ select_kernel(const SelectArgs a) {
     const int ctx = a.st.ctx[b];
     const int nch = (int)(((long long)ctx + J.chunk - 1) / J.chunk);
     const long long pb = (long long)b * J.nchunk_max;
-    constexpr int IB = KPT < 8 ? KPT : 8;   // channels per thread per load batch
+    // The fused form serves at most two partials per channel (the host's
+    // rule), so all KPT channels' loads of two chunks are in flight at once.
+    constexpr int CS = 2;                    // chunks per load batch
     auto colsum = [&](const float* part, int ld, auto col, float (&out)[KPT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) out[i] = 0.f;
+      for (int c0 = 0; c0 < nch; c0 += CS) {
+        float t[CS][KPT];
 #pragma unroll
-      for (int i0 = 0; i0 < KPT; i0 += IB) {
-        for (int c0 = 0; c0 < nch; c0 += 4) {
-          float t[4][IB];
+        for (int u = 0; u < CS; ++u)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int i = 0; i < KPT; ++i) {
+            const int n = tid + SEL_THREADS * i;
+            t[u][i] = (c0 + u < nch && n < N) ? part[(pb + c0 + u) * ld + col(n)] : 0.f;
+          }
 #pragma unroll
-            for (int i = 0; i < IB; ++i) {
-              const int n = tid + SEL_THREADS * (i0 + i);
-              t[u][i] = (c0 + u < nch && n < N) ? part[(pb + c0 + u) * ld + col(n)] : 0.f;
-            }
+        for (int u = 0; u < CS; ++u)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int i = 0; i < IB; ++i)
-              if (c0 + u < nch) out[i0 + i] += t[u][i];
-        }
+          for (int i = 0; i < KPT; ++i)
+            if (c0 + u < nch) out[i] += t[u][i];
       }
     };
     float sc[KPT];
